@@ -1,0 +1,187 @@
+"""Pins of the oracle's quantiser and record packer against exact arithmetic.
+
+Fathom review (evolve.pub), "Strengths" (paper Sec 3.2) and FAQ: 4-bit uniform
+codes under one shared block scale, stored channel-major as bit planes, so the
+first t planes of a channel are exactly its t-bit mid-rise quantizer.
+"""
+
+import math
+import struct
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import fathom_oracle as O
+from tests.exact import F16, fr, round_binary
+
+
+def exact_scale(values) -> Fraction:
+    m = max(abs(fr(v)) for v in values)
+    return round_binary(m / 8, *F16)
+
+
+def exact_code(x, delta: Fraction) -> int:
+    if delta == 0:
+        return 8
+    return min(15, max(0, math.floor(fr(x) / delta) + 8))
+
+
+def crafted_keys():
+    """Keys with exact threshold hits, clamping, zero, tiny and subnormal-scale blocks."""
+    n, d = 5 * 128 + 37, 6          # ragged: 5 full blocks + a 37-key tail
+    rng = np.random.default_rng(7)
+    k = rng.standard_normal((n, d)).astype(np.float32)
+    k *= np.float32(3.0)
+    # channel 0, block 0: max |k| = 8 -> Delta = 1; threshold hits and neighbours
+    blk = np.zeros(128, np.float32)
+    vals = [8.0, -8.0, 3.0, -3.0, 0.0, -0.0, 0.5, -0.5, 7.0, -7.0, 6.999999523, -6.999999523,
+            1.0, np.nextafter(np.float32(1.0), np.float32(0)), np.nextafter(np.float32(-1.0), np.float32(0))]
+    blk[: len(vals)] = np.array(vals, np.float32)
+    k[:128, 0] = blk
+    # channel 1, block 1: max/8 = 1 + 2^-11 -> ties to even -> Delta = 1, and 8(1+2^-11) clamps to 15
+    k[128:256, 1] = np.linspace(-4, 4, 128).astype(np.float32)
+    k[130, 1] = np.float32(8.0 * (1 + 2.0 ** -11))
+    # channel 2, block 2: all zeros -> Delta = 0 -> code 8
+    k[256:384, 2] = 0.0
+    # channel 3, block 3: tiny -> Delta underflows to 0 in fp16 -> code 8 although keys are nonzero
+    k[384:512, 3] = rng.standard_normal(128).astype(np.float32) * np.float32(1e-9)
+    # channel 4, block 4: scale is an fp16 subnormal
+    k[512:640, 4] = rng.standard_normal(128).astype(np.float32) * np.float32(1e-6)
+    # channel 5: large values (scale near the top of fp16)
+    k[:, 5] *= np.float32(1.0e4)
+    return k
+
+
+def test_scales_and_codes_match_exact_floor():
+    k = crafted_keys()
+    n, d = k.shape
+    delta = O.block_scales(k)
+    kappa = O.quantize_codes(k, delta)
+    assert delta.shape == (d, O.n_blocks(n)) and kappa.shape == (n, d)
+    for c in range(d):
+        for b in range(O.n_blocks(n)):
+            lo, hi = b * 128, min(n, (b + 1) * 128)
+            ds = exact_scale(k[lo:hi, c])
+            assert fr(delta[c, b]) == ds, (c, b)
+            for j in range(lo, hi):
+                assert kappa[j, c] == exact_code(k[j, c], ds), (j, c)
+
+
+def test_hand_worked_block():
+    # channel 0, block 0 of crafted_keys: Delta = 1 exactly
+    k = crafted_keys()
+    delta = O.block_scales(k)
+    kappa = O.quantize_codes(k, delta)
+    assert float(delta[0, 0]) == 1.0
+    # 8 -> floor 8 + 8 = 16 -> clamp 15; -8 -> 0; 3 -> 11; -3 -> 5; 0 and -0 -> 8;
+    # 0.5 -> 8; -0.5 -> 7; 7 -> 15; -7 -> 1; 6.9999995 -> 14; -6.9999995 -> 1;
+    # 1 -> 9; just below 1 -> 8; just above -1 -> 7
+    expect = [15, 0, 11, 5, 8, 8, 8, 7, 15, 1, 14, 1, 9, 8, 7]
+    assert list(kappa[: len(expect), 0]) == expect
+    # max/8 = 1 + 2^-11 is halfway between fp16 1 and 1 + 2^-10: ties to even -> 1
+    assert float(delta[1, 1]) == 1.0 and kappa[130, 1] == 15
+    assert float(delta[2, 2]) == 0.0 and np.all(kappa[256:384, 2] == 8)
+    assert float(delta[3, 3]) == 0.0 and np.all(kappa[384:512, 3] == 8)
+    assert 0 < float(delta[4, 4]) < 2.0 ** -14          # subnormal fp16 scale
+
+
+@pytest.mark.parametrize("t", [1, 2, 3, 4])
+def test_prefix_is_t_bit_midrise_quantizer(t):
+    """kappa >> (4-t) equals the t-bit mid-rise quantizer with step 2^(4-t) Delta,
+    and the oracle's reconstruction is the midpoint of that quantizer's cell."""
+    rng = np.random.default_rng(11 + t)
+    n = 2048
+    k = (rng.standard_normal((n, 1)) * 2.5).astype(np.float32)
+    k[::97] = np.float32(0.0)
+    delta = O.block_scales(k)
+    kappa = O.quantize_codes(k, delta)
+    for j in range(n):
+        dl = fr(delta[0, j // 128])
+        step = dl * 2 ** (4 - t)
+        code_t = min(2 ** t - 1, max(0, math.floor(fr(k[j, 0]) / step) + 2 ** (t - 1)))
+        assert (int(kappa[j, 0]) >> (4 - t)) == code_t
+        lo_edge = (code_t - 2 ** (t - 1)) * step
+        hi_edge = lo_edge + step
+        mid = (lo_edge + hi_edge) / 2
+        kh = O.reconstruct(kappa[j:j + 1, 0], t, delta[0, j // 128:j // 128 + 1])[0]
+        assert fr(kh) == mid
+
+
+def test_nesting_exhaustive_codes():
+    """For every 4-bit code and depth t, the t-bit prefix cell contains the 4-bit cell."""
+    delta = np.array([np.float16(0.375)])
+    for code in range(16):
+        fine_lo = (code - 8) * Fraction(3, 8)
+        fine_hi = fine_lo + Fraction(3, 8)
+        for t in range(1, 5):
+            step = Fraction(3, 8) * 2 ** (4 - t)
+            pref = code >> (4 - t)
+            lo = (pref - 2 ** (t - 1)) * step
+            assert lo <= fine_lo and fine_hi <= lo + step
+            kh = O.reconstruct(np.array([code], np.uint8), t, delta)[0]
+            assert fr(kh) == lo + step / 2
+
+
+def test_four_plane_prefix_is_full_dequant():
+    """Reading all 4 planes reconstructs (kappa - 7.5) * Delta (full 4-bit dequantisation)."""
+    rng = np.random.default_rng(3)
+    k = (rng.standard_normal((1024, 8)) * np.exp(rng.standard_normal(8))).astype(np.float32)
+    delta = O.block_scales(k)
+    kappa = O.quantize_codes(k, delta)
+    blk = np.arange(1024) // 128
+    for c in range(8):
+        full = (kappa[:, c].astype(np.float64) - 7.5) * delta[c, blk].astype(np.float64)
+        assert np.array_equal(O.reconstruct(kappa[:, c], 4, delta[c, blk]), full)
+        assert np.array_equal(O.reconstruct(kappa[:, c], 0, delta[c, blk]), np.zeros(1024))
+
+
+def test_record_layout_bit_by_bit():
+    """Decode records byte by byte from the layout definition (no numpy bit helpers)."""
+    k = crafted_keys()
+    n, d = k.shape
+    delta, kappa, rec = O.pack_head(k)
+    s, p, r = O.record_layout(n)
+    nb = O.n_blocks(n)
+    assert rec.shape == (d, r) and s % 16 == 0 and p == 16 * nb
+    for c in range(d):
+        raw = bytes(rec[c])
+        for b in range(nb):
+            (v,) = struct.unpack_from("<e", raw, 2 * b)
+            assert v == float(delta[c, b]) or (v == 0 and float(delta[c, b]) == 0)
+        assert all(x == 0 for x in raw[2 * nb: s])
+        for plane in range(4):
+            base = s + plane * p
+            for j in range(nb * 128):
+                bit = (raw[base + j // 8] >> (j % 8)) & 1
+                want = ((int(kappa[j, c]) >> (3 - plane)) & 1) if j < n else 0
+                assert bit == want, (c, plane, j)
+
+
+def test_record_sizes():
+    # n a multiple of 1024: R = n/64 + n/2 (scales then four n/8-byte planes)
+    for n in (4096, 131072, 262144, 1 << 20):
+        s, p, r = O.record_layout(n)
+        assert (s, p, r) == (n // 64, n // 8, n // 64 + n // 2)
+    assert O.record_layout(1) == (16, 16, 80)
+    assert O.record_layout(0) == (0, 0, 0)
+
+
+def test_unpack_roundtrip_and_prefix_read():
+    rng = np.random.default_rng(5)
+    k = rng.standard_normal((777, 5)).astype(np.float32)
+    delta, kappa, rec = O.pack_head(k)
+    for t in range(0, 5):
+        d2, code = O.unpack_codes(rec, 777, t)
+        assert np.array_equal(d2.view(np.uint16), delta.view(np.uint16))
+        assert np.array_equal(code, kappa >> (4 - t))
+
+
+def test_invalid_keys_raise():
+    k = np.zeros((128, 2), np.float32)
+    k[3, 1] = np.nan
+    with pytest.raises(ValueError):
+        O.block_scales(k)
+    k[3, 1] = np.float32(1e6)      # 1e6 / 8 = 125000 > fp16 max
+    with pytest.raises(ValueError):
+        O.block_scales(k)
