@@ -1,0 +1,172 @@
+/*
+ * fathom.h -- C ABI of the Fathom per-query variable-depth key scan on MI355X (gfx950).
+ *
+ * Method: "Fathom: Per-Query Read Depth for Sparse Decoding over Offloaded KV
+ * Caches" (arXiv 2609.17652).  Page citations below:
+ *   [Abstract]  the arXiv abstract;
+ *   [Review]    the evolve.pub review ("Summary", "Strengths" -> paper Sec 3.2,
+ *               3.3, 3.6, "Frequently asked questions");
+ *   [Digest]    the ai-feeds.com summary (Method: Inputs, Key modules 1-5, Output).
+ *
+ * A top-k step is three calls:
+ *   pack_bitplanes   once per cache: 4-bit codes as channel-major bit planes;
+ *   allocate_depths  per query step: read depth t_c of every channel per query head;
+ *   scan_topk        per query step: score every key from its read prefix, return top-k.
+ *
+ * Conventions shared by every call:
+ *   - Device pointers are HIP device memory unless stated; every call is
+ *     asynchronous on `stream` (a hipStream_t; NULL = the null stream) and
+ *     returns after validating its arguments and enqueueing work.
+ *   - The caller owns every buffer.  No call allocates device or host memory
+ *     and none keeps state between calls.
+ *   - Return value: FATHOM_OK or a negative fathom_status.  On a negative
+ *     status nothing was enqueued and no output was written;
+ *     fathom_last_error() gives a message (per calling thread).
+ *   - Shapes: h_kv KV heads, G = h_q / h_kv query heads per KV head
+ *     (G in {1, 2, 4, 8, 16}), d channels (1..256), n keys (n >= 0).
+ *     Query head h belongs to KV head h / G.  Independent sessions are passed
+ *     as extra KV heads (session-major), since sessions never mix.
+ */
+#ifndef FATHOM_H
+#define FATHOM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fathom_status {
+  FATHOM_OK = 0,
+  FATHOM_EINVAL = -1,     /* null pointer, bad mode/residency, misaligned pointer      */
+  FATHOM_ESHAPE = -2,     /* h_kv, h_q, d, n or k outside the supported range          */
+  FATHOM_EBUDGET = -3,    /* budget outside [0, 4d], or fixed mode with budget % 4 != 0 */
+  FATHOM_EWORKSPACE = -5, /* workspace smaller than fathom_workspace_bytes()           */
+  FATHOM_EHIP = -6,       /* a HIP runtime call or kernel launch failed                 */
+  FATHOM_ERESIDENCY = -7  /* records pointer does not match the residency it claims    */
+} fathom_status;
+
+/* Where scan_topk finds the records. */
+enum fathom_residency {
+  FATHOM_HBM = 0,          /* records in device memory                                  */
+  FATHOM_HOST_DIRECT = 1   /* records in pinned host memory (hipHostMalloc or torch
+                              pin_memory); the scan kernel reads only the budgeted plane
+                              prefixes straight over the host link, no staging copy     */
+};
+
+/* How allocate_depths spends the budget. */
+enum fathom_depth_mode {
+  FATHOM_WATERFILL = 0,    /* reverse water-filling (the method)                         */
+  FATHOM_TOPQ = 1          /* fixed-depth comparison scan: 4 planes on the budget/4
+                              channels of largest |q_c| (ties: lowest channel)           */
+};
+
+/* Flags OR-ed into the device status words. */
+#define FATHOM_FLAG_KEY_NONFINITE 1u        /* pack: a key is NaN or +-Inf              */
+#define FATHOM_FLAG_SCALE_OVERFLOW 2u       /* pack: max|k|/8 rounds past fp16 range    */
+#define FATHOM_FLAG_Q_NONFINITE 4u          /* allocate: q is NaN or +-Inf              */
+#define FATHOM_FLAG_SIGMA2_INVALID 8u       /* allocate: sigma2 negative or non-finite  */
+#define FATHOM_FLAG_IMPORTANCE_OVERFLOW 16u /* allocate: q^2 sigma2 overflows fp32      */
+
+/* ---------------------------------------------------------------------------
+ * Record layout.  [Digest] Inputs and key module 1, [Review] FAQ: the 4-bit K
+ * cache is stored channel-major as bit planes, the 4 planes of a channel
+ * contiguous, so the first t planes are the channel's t-bit quantizer;
+ * [Review] Strengths (paper Sec 3.6): a partial read is one contiguous run.
+ *
+ * records = [h_kv][d] records of fathom_record_bytes(n) bytes each:
+ *   bytes [0, S)        fp16 scale Delta of each 128-key block, little-endian,
+ *                       zero padded to S = fathom_scale_bytes(n) (multiple of 16);
+ *   bytes [S + p*P, S + (p+1)*P)   plane p (p = 0 is the most significant bit),
+ *                       P = fathom_plane_bytes(n) = 16 * ceil(n / 128):
+ *                       key j is bit (j % 8) of byte j / 8; bits past n are 0.
+ * For n a multiple of 1024: S = n/64, P = n/8, R = n/64 + n/2.
+ * ------------------------------------------------------------------------- */
+size_t fathom_scale_bytes(int64_t n);
+size_t fathom_plane_bytes(int64_t n);
+size_t fathom_record_bytes(int64_t n);
+
+/* pack_bitplanes -- quantise and pack the K cache (once per cache or layer).
+ * [Review] Strengths (paper Sec 3.2) and FAQ: 4-bit uniform codes under one
+ * shared block scale; prefix of t planes = the t-bit mid-rise quantizer.
+ *   k        device, float32 [h_kv][n][d] (token-major, as a serving stack holds K).
+ *   records  device, [h_kv][d][fathom_record_bytes(n)] bytes, written completely.
+ *   status   device, one uint32; cleared by the call, then FATHOM_FLAG_KEY_NONFINITE /
+ *            FATHOM_FLAG_SCALE_OVERFLOW are OR-ed in (asynchronously).  The
+ *            affected records are then unspecified.  May be NULL.
+ * Per (KV head, channel, 128-key block): Delta = fp16_RNE(max|k| / 8); per key:
+ * code = clamp(floor(k / Delta) + 8, 0, 15), evaluated exactly (code 8 when
+ * Delta = 0); plane p holds bit (3 - p) of the code.
+ * Alignment: k 4-byte, records 16-byte aligned.  n = 0 is a no-op. */
+int pack_bitplanes(const float* k, int h_kv, int64_t n, int d, void* records,
+                   uint32_t* status, void* stream);
+
+/* allocate_depths -- per-query read depths ([Abstract]; [Digest] key module 2;
+ * [Review] Strengths, paper Sec 3.3: each extra plane cuts the error 4x).
+ * One wavefront per query head.
+ *   q            device, float32 [h_q][d].
+ *   sigma2       device, float32 [h_kv][d] per-channel key variance (offline
+ *                statistics, [Digest] Inputs).
+ *   mode         FATHOM_WATERFILL: w_c = fl32(fl32(q_c*q_c)*sigma2_c); `budget`
+ *                greedy steps each give one plane to the channel with t_c < 4 of
+ *                largest w_c * 4^-t_c (compared exactly), lowest channel on ties --
+ *                the minimiser of sum_c w_c 4^-t_c with sum_c t_c = budget.
+ *                FATHOM_TOPQ: t_c = 4 on the budget/4 channels of largest |q_c|.
+ *   budget       bits per key and query head, 0..4d (multiple of 4 for TOPQ).
+ *   depth        device, uint8 [h_q][d] output.
+ *   union_depth  device, uint8 [h_kv][d] output: max over the KV head's query heads
+ *                (the longest prefix, which contains every head's prefix).
+ *   status       device, uint32 [h_kv], written (not OR-ed) by the call: the OR of
+ *                FATHOM_FLAG_Q_NONFINITE / _SIGMA2_INVALID / _IMPORTANCE_OVERFLOW
+ *                over the KV head's query heads; a flagged query head gets all-zero
+ *                depths.  May be NULL. */
+int allocate_depths(const float* q, const float* sigma2, int h_q, int h_kv, int d,
+                    int mode, int budget, uint8_t* depth, uint8_t* union_depth,
+                    uint32_t* status, void* stream);
+
+/* Bytes of device workspace scan_topk needs for this shape. */
+size_t fathom_workspace_bytes(int h_q, int h_kv, int64_t n, int d, int k);
+
+/* scan_topk -- score every key from its read prefix and select the top k
+ * ([Abstract]; [Digest] key modules 4-5 and Output: the scan pulls only the
+ * budgeted planes and outputs top-k indices per query).
+ *   records      packed records (layout above), device memory (FATHOM_HBM) or
+ *                pinned host memory (FATHOM_HOST_DIRECT); read-only.
+ *   q, depth, union_depth   as for allocate_depths (device).
+ *   k            0..n keys to return per query head.
+ *   topk_idx     device, int32 [h_q][k]: the k keys of largest score, lowest index
+ *                among equal scores, in ascending index order.
+ *   topk_score   device, float32 [h_q][k] or NULL: the scores of topk_idx.
+ *   workspace    device, >= fathom_workspace_bytes(h_q, h_kv, n, d, k) bytes,
+ *                256-byte aligned; contents on entry ignored, on exit unspecified.
+ * Score of key j for query head h (fp32 accumulation):
+ *   s = sum over channels with t_c > 0 of q_c * Delta_c,b(j) * 2^(4-t) *
+ *       ((code >> (4-t)) - 2^(t-1) + 1/2),
+ * the midpoint of the key's cell of the t-bit mid-rise quantizer ([Digest] key
+ * module 4; the paper's Sec 3.5 rule is not in the text, this is the reading).
+ * Within 1e-4 * sum_c |q_c * k_hat_c| of the exact value. */
+int scan_topk(const void* records, int residency, const float* q, const uint8_t* depth,
+              const uint8_t* union_depth, int h_q, int h_kv, int64_t n, int d, int k,
+              int32_t* topk_idx, float* topk_score, void* workspace,
+              size_t workspace_bytes, void* stream);
+
+/* fathom_scan_scores -- the scan stage alone (for tests and profiling): the same
+ * scores scan_topk ranks, written to device float32 [h_q][ld] (ld >= n, only the
+ * first n entries of each row are meaningful). */
+int fathom_scan_scores(const void* records, int residency, const float* q,
+                       const uint8_t* depth, const uint8_t* union_depth, int h_q,
+                       int h_kv, int64_t n, int d, float* scores, int64_t ld,
+                       void* stream);
+
+/* Message for the last failing call on this thread ("" if none). */
+const char* fathom_last_error(void);
+
+/* ABI version of this header (major * 100 + minor). */
+int fathom_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FATHOM_H */

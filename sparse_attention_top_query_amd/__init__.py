@@ -1,0 +1,26 @@
+"""Fathom per-query variable-depth key scan on MI355X (gfx950).
+
+The compute path is libfathom.so (hand-written HIP kernels behind the C ABI in
+include/fathom.h); this package is its thin Python binding.  There is no CPU
+fallback: calls fail if the library has not been built.
+"""
+
+from .fathom import (  # noqa: F401
+    HBM,
+    HOST_DIRECT,
+    TOPQ,
+    WATERFILL,
+    FathomError,
+    allocate,
+    load,
+    pack,
+    plane_bytes,
+    record_bytes,
+    scale_bytes,
+    scan_scores,
+    scan_topk,
+    workspace_bytes,
+)
+
+__all__ = ["HBM", "HOST_DIRECT", "TOPQ", "WATERFILL", "FathomError", "allocate", "load", "pack",
+           "plane_bytes", "record_bytes", "scale_bytes", "scan_scores", "scan_topk", "workspace_bytes"]

@@ -1,0 +1,189 @@
+// C ABI of the Fathom key scan: argument validation and launch sequencing.
+// The declarations, with their citations and contracts, are in include/fathom.h.
+#include "fathom.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "fathom_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return FATHOM_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(FATHOM_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool valid_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
+
+int check_heads(int h_q, int h_kv, int d) {
+  if (h_kv < 1 || h_kv > 65535) return fail(FATHOM_ESHAPE, "h_kv=%d outside [1, 65535]", h_kv);
+  if (h_q < h_kv || h_q % h_kv != 0)
+    return fail(FATHOM_ESHAPE, "h_q=%d is not a multiple of h_kv=%d", h_q, h_kv);
+  if (!valid_group(h_q / h_kv))
+    return fail(FATHOM_ESHAPE, "query heads per KV head %d not in {1,2,4,8,16}", h_q / h_kv);
+  if (d < 1 || d > fathom::kMaxD) return fail(FATHOM_ESHAPE, "d=%d outside [1, %d]", d, fathom::kMaxD);
+  return FATHOM_OK;
+}
+
+int64_t score_ld(int64_t n) { return (n + 63) / 64 * 64; }
+
+size_t al256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Resolve the device-visible address of the records for the claimed residency.
+int resolve_records(const void* records, int residency, const uint8_t** dev) {
+  hipPointerAttribute_t attr;
+  hipError_t e = hipPointerGetAttributes(&attr, records);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();  // not a pointer HIP knows: pageable host memory
+    return fail(FATHOM_ERESIDENCY, "records pointer is not HIP device or pinned host memory");
+  }
+  if (residency == FATHOM_HBM) {
+    if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged)
+      return fail(FATHOM_ERESIDENCY, "FATHOM_HBM records must be device memory");
+    *dev = static_cast<const uint8_t*>(records);
+    return FATHOM_OK;
+  }
+  if (residency == FATHOM_HOST_DIRECT) {
+    if (attr.type != hipMemoryTypeHost)
+      return fail(FATHOM_ERESIDENCY, "FATHOM_HOST_DIRECT records must be pinned host memory");
+    const uint8_t* p = static_cast<const uint8_t*>(attr.devicePointer);
+    if (!p) return fail(FATHOM_ERESIDENCY, "pinned host records have no device mapping");
+    *dev = p + (static_cast<const uint8_t*>(records) - static_cast<const uint8_t*>(attr.hostPointer));
+    return FATHOM_OK;
+  }
+  return fail(FATHOM_EINVAL, "unknown residency %d", residency);
+}
+
+int check_scan_args(const void* records, int residency, const float* q, const uint8_t* depth,
+                    const uint8_t* union_depth, int h_q, int h_kv, int64_t n, int d,
+                    const uint8_t** dev) {
+  int st = check_heads(h_q, h_kv, d);
+  if (st) return st;
+  if (n < 0 || n > (int64_t(1) << 34)) return fail(FATHOM_ESHAPE, "n=%lld out of range", (long long)n);
+  if (!q || !depth || !union_depth) return fail(FATHOM_EINVAL, "null q/depth/union_depth");
+  if (!aligned(q, 4)) return fail(FATHOM_EINVAL, "q must be 4-byte aligned");
+  if (n == 0) return FATHOM_OK;
+  if (!records) return fail(FATHOM_EINVAL, "null records");
+  if (!aligned(records, 16)) return fail(FATHOM_EINVAL, "records must be 16-byte aligned");
+  return resolve_records(records, residency, dev);
+}
+
+}  // namespace
+
+extern "C" {
+
+int fathom_version(void) { return 100; }
+
+const char* fathom_last_error(void) { return g_last_error.c_str(); }
+
+size_t fathom_scale_bytes(int64_t n) { return n <= 0 ? 0 : (size_t)fathom::make_layout(n).S; }
+size_t fathom_plane_bytes(int64_t n) { return n <= 0 ? 0 : (size_t)fathom::make_layout(n).P; }
+size_t fathom_record_bytes(int64_t n) { return n <= 0 ? 0 : (size_t)fathom::make_layout(n).R; }
+
+int pack_bitplanes(const float* k, int h_kv, int64_t n, int d, void* records, uint32_t* status,
+                   void* stream) {
+  if (h_kv < 1 || h_kv > 65535) return fail(FATHOM_ESHAPE, "h_kv=%d outside [1, 65535]", h_kv);
+  if (d < 1 || d > fathom::kMaxD) return fail(FATHOM_ESHAPE, "d=%d outside [1, %d]", d, fathom::kMaxD);
+  if (n < 0 || n > (int64_t(1) << 34)) return fail(FATHOM_ESHAPE, "n=%lld out of range", (long long)n);
+  if (n > 0 && (!k || !records)) return fail(FATHOM_EINVAL, "null k or records");
+  if (n > 0 && (!aligned(k, 4) || !aligned(records, 16)))
+    return fail(FATHOM_EINVAL, "k must be 4-byte and records 16-byte aligned");
+  if (fathom::make_layout(n).nb > 0x7fffffff) return fail(FATHOM_ESHAPE, "too many blocks");
+  hipError_t e = fathom::launch_pack(k, h_kv, fathom::make_layout(n), d, static_cast<uint8_t*>(records),
+                                     status, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "pack launch");
+  return ok();
+}
+
+int allocate_depths(const float* q, const float* sigma2, int h_q, int h_kv, int d, int mode,
+                    int budget, uint8_t* depth, uint8_t* union_depth, uint32_t* status,
+                    void* stream) {
+  int st = check_heads(h_q, h_kv, d);
+  if (st) return st;
+  if (!q || !sigma2 || !depth || !union_depth) return fail(FATHOM_EINVAL, "null pointer argument");
+  if (!aligned(q, 4) || !aligned(sigma2, 4)) return fail(FATHOM_EINVAL, "q/sigma2 must be 4-byte aligned");
+  if (mode != FATHOM_WATERFILL && mode != FATHOM_TOPQ) return fail(FATHOM_EINVAL, "unknown mode %d", mode);
+  if (budget < 0 || budget > fathom::kPlanes * d)
+    return fail(FATHOM_EBUDGET, "budget=%d outside [0, %d]", budget, fathom::kPlanes * d);
+  if (mode == FATHOM_TOPQ && budget % fathom::kPlanes != 0)
+    return fail(FATHOM_EBUDGET, "fixed-depth mode needs budget %% 4 == 0 (got %d)", budget);
+  hipError_t e = fathom::launch_allocate(q, sigma2, h_kv, h_q / h_kv, d, mode, budget, depth,
+                                         union_depth, status, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "allocate launch");
+  return ok();
+}
+
+size_t fathom_workspace_bytes(int h_q, int h_kv, int64_t n, int d, int k) {
+  (void)h_kv;
+  (void)d;
+  (void)k;
+  if (h_q <= 0 || n <= 0) return 0;
+  return al256((size_t)h_q * (size_t)score_ld(n) * 4) + fathom::select_workspace_bytes(h_q, n);
+}
+
+int fathom_scan_scores(const void* records, int residency, const float* q, const uint8_t* depth,
+                       const uint8_t* union_depth, int h_q, int h_kv, int64_t n, int d,
+                       float* scores, int64_t ld, void* stream) {
+  const uint8_t* dev = nullptr;
+  int st = check_scan_args(records, residency, q, depth, union_depth, h_q, h_kv, n, d, &dev);
+  if (st) return st;
+  if (n == 0) return ok();
+  if (!scores) return fail(FATHOM_EINVAL, "null scores");
+  if (ld < n) return fail(FATHOM_ESHAPE, "ld=%lld < n=%lld", (long long)ld, (long long)n);
+  hipError_t e = fathom::launch_scan(dev, q, depth, union_depth, h_kv, h_q / h_kv,
+                                     fathom::make_layout(n), d, scores, ld,
+                                     static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "scan launch");
+  return ok();
+}
+
+int scan_topk(const void* records, int residency, const float* q, const uint8_t* depth,
+              const uint8_t* union_depth, int h_q, int h_kv, int64_t n, int d, int k,
+              int32_t* topk_idx, float* topk_score, void* workspace, size_t workspace_bytes,
+              void* stream) {
+  const uint8_t* dev = nullptr;
+  int st = check_scan_args(records, residency, q, depth, union_depth, h_q, h_kv, n, d, &dev);
+  if (st) return st;
+  if (k < 0 || k > n) return fail(FATHOM_ESHAPE, "k=%d outside [0, n=%lld]", k, (long long)n);
+  if (k == 0) return ok();
+  if (!topk_idx) return fail(FATHOM_EINVAL, "null topk_idx");
+  const size_t need = fathom_workspace_bytes(h_q, h_kv, n, d, k);
+  if (!workspace || workspace_bytes < need)
+    return fail(FATHOM_EWORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, need);
+  if (!aligned(workspace, 256)) return fail(FATHOM_EINVAL, "workspace must be 256-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t ld = score_ld(n);
+  float* scores = static_cast<float*>(workspace);
+  uint8_t* sel_base = static_cast<uint8_t*>(workspace) + al256((size_t)h_q * (size_t)ld * 4);
+  hipError_t e = fathom::launch_scan(dev, q, depth, union_depth, h_kv, h_q / h_kv,
+                                     fathom::make_layout(n), d, scores, ld, s);
+  if (e != hipSuccess) return hip_fail(e, "scan launch");
+  e = fathom::launch_select(scores, ld, h_q, n, k, topk_idx, topk_score,
+                            fathom::carve_select(sel_base, h_q, n), s);
+  if (e != hipSuccess) return hip_fail(e, "select launch");
+  return ok();
+}
+
+}  // extern "C"

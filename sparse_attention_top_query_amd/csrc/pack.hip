@@ -1,0 +1,96 @@
+// pack_bitplanes kernel: 4-bit mid-rise codes under one fp16 scale per
+// (KV head, channel, 128-key block), stored channel-major as 4 bit planes.
+//
+// Fathom review (evolve.pub), "Strengths" (paper Sec 3.2) and FAQ: uniform
+// 4-bit codes, one shared block scale, planes contiguous per channel so that a
+// prefix of t planes is the channel's t-bit quantizer.  ai-feeds digest,
+// Method / key module 1: each channel is kept as 4 bit planes.
+//
+// One workgroup per (128-key block, KV head); one thread per channel.  Thread
+// c walks the block's 128 keys twice (max, then codes): both passes read
+// k[j][c] for consecutive c across the wave, i.e. coalesced rows of the
+// token-major K; the second pass hits L2.  Each thread then writes 16 bytes
+// per plane (the block's 128 bits) and its 2-byte scale.
+#include <hip/hip_fp16.h>
+
+#include "fathom_internal.h"
+
+namespace fathom {
+namespace {
+
+__global__ __launch_bounds__(256) void pack_kernel(const float* __restrict__ k, int64_t n, int d,
+                                                   int64_t nb, int64_t S, int64_t P, int64_t R,
+                                                   uint8_t* __restrict__ rec,
+                                                   uint32_t* __restrict__ status) {
+  const int c = threadIdx.x;
+  if (c >= d) return;  // no barriers below
+  const int64_t b = blockIdx.x;
+  const int64_t g = blockIdx.y;
+  const int64_t j0 = b * kBlock;
+  const int cnt = (int)min<int64_t>(kBlock, n - j0);
+  const float* col = k + (g * n + j0) * d + c;
+
+  float mx = 0.0f;
+  bool finite = true;
+  for (int j = 0; j < cnt; ++j) {
+    const float v = col[(int64_t)j * d];
+    finite &= isfinite(v);
+    mx = fmaxf(mx, fabsf(v));
+  }
+  // max|k| / 8: scaling by 2^-3 is exact in fp32 down to the subnormal range,
+  // where the fp16 result is 0 either way; fp32 -> fp16 rounds to nearest even.
+  const __half dh = __float2half_rn(mx * 0.125f);
+  const float dl = __half2float(dh);
+  uint32_t flags = 0;
+  if (!finite) flags |= 1u;                      // FATHOM_FLAG_KEY_NONFINITE
+  else if (!isfinite(dl)) flags |= 2u;           // FATHOM_FLAG_SCALE_OVERFLOW
+  if (flags && status) atomicOr(status, flags);
+
+  uint32_t w[kPlanes][4] = {};
+  for (int j = 0; j < cnt; ++j) {
+    const float v = col[(int64_t)j * d];
+    // code = #{i in 1..15 : v >= (i - 8) * Delta}: the thresholds are exact
+    // fp32 products (Delta has 11 significant bits), found by a 4-step search.
+    int code = 8;
+    if (dl != 0.0f) {
+      code = 0;
+#pragma unroll
+      for (int step = 8; step >= 1; step >>= 1) {
+        const int cand = code + step;
+        if (v >= (float)(cand - 8) * dl) code = cand;
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < kPlanes; ++p)
+      w[p][j >> 5] |= (uint32_t)((code >> (kPlanes - 1 - p)) & 1) << (j & 31);
+  }
+
+  uint8_t* r = rec + (g * d + c) * R;
+  reinterpret_cast<__half*>(r)[b] = dh;
+  if (b == nb - 1) {
+    for (int64_t x = 2 * nb; x < S; ++x) r[x] = 0;  // zero the scale padding
+  }
+#pragma unroll
+  for (int p = 0; p < kPlanes; ++p)
+    *reinterpret_cast<uint4*>(r + S + p * P + b * 16) = make_uint4(w[p][0], w[p][1], w[p][2], w[p][3]);
+}
+
+__global__ void clear_word(uint32_t* p) { *p = 0u; }
+
+}  // namespace
+
+hipError_t launch_pack(const float* k, int h_kv, const Layout& L, int d, uint8_t* rec,
+                       uint32_t* status, hipStream_t s) {
+  if (status) {
+    clear_word<<<1, 1, 0, s>>>(status);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (L.nb == 0) return hipSuccess;
+  const int threads = ((d + 63) / 64) * 64;
+  dim3 grid((unsigned)L.nb, (unsigned)h_kv);
+  pack_kernel<<<grid, threads, 0, s>>>(k, L.n, d, L.nb, L.S, L.P, L.R, rec, status);
+  return hipGetLastError();
+}
+
+}  // namespace fathom

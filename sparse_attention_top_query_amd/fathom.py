@@ -1,0 +1,211 @@
+"""Python binding of libfathom.so (ctypes): argument marshalling only.
+
+Every function takes torch tensors for device (or pinned host) memory, checks
+dtype, device and contiguity, and passes raw pointers plus the current HIP
+stream to the C ABI declared in include/fathom.h.  All compute runs in the
+library's HIP kernels; nothing here computes any part of the method.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfathom.so")
+
+HBM = 0
+HOST_DIRECT = 1
+WATERFILL = 0
+TOPQ = 1
+
+FLAG_KEY_NONFINITE = 1
+FLAG_SCALE_OVERFLOW = 2
+FLAG_Q_NONFINITE = 4
+FLAG_SIGMA2_INVALID = 8
+FLAG_IMPORTANCE_OVERFLOW = 16
+
+STATUS_NAMES = {0: "FATHOM_OK", -1: "FATHOM_EINVAL", -2: "FATHOM_ESHAPE", -3: "FATHOM_EBUDGET",
+                -5: "FATHOM_EWORKSPACE", -6: "FATHOM_EHIP", -7: "FATHOM_ERESIDENCY"}
+
+
+class FathomError(RuntimeError):
+    """A negative status from the library, with its message."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libfathom.so (built in-tree by sparse_attention_top_query_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m sparse_attention_top_query_amd.build` (there is no fallback)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, L, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    sig = {
+        "fathom_scale_bytes": (S, [L]),
+        "fathom_plane_bytes": (S, [L]),
+        "fathom_record_bytes": (S, [L]),
+        "pack_bitplanes": (I, [P, I, L, I, P, P, P]),
+        "allocate_depths": (I, [P, P, I, I, I, I, I, P, P, P, P]),
+        "fathom_workspace_bytes": (S, [I, I, L, I, I]),
+        "scan_topk": (I, [P, I, P, P, P, I, I, L, I, I, P, P, P, S, P]),
+        "fathom_scan_scores": (I, [P, I, P, P, P, I, I, L, I, P, L, P]),
+        "fathom_last_error": (ctypes.c_char_p, []),
+        "fathom_version": (I, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise FathomError(status, load().fathom_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need(t, name, dtype, ndim=None, device=True):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device and not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+
+
+def record_bytes(n: int) -> int:
+    return int(load().fathom_record_bytes(n))
+
+
+def scale_bytes(n: int) -> int:
+    return int(load().fathom_scale_bytes(n))
+
+
+def plane_bytes(n: int) -> int:
+    return int(load().fathom_plane_bytes(n))
+
+
+def workspace_bytes(h_q: int, h_kv: int, n: int, d: int, k: int) -> int:
+    return int(load().fathom_workspace_bytes(h_q, h_kv, n, d, k))
+
+
+def pack(k: torch.Tensor, records: torch.Tensor | None = None, status: torch.Tensor | None = None):
+    """pack_bitplanes: k float32 [h_kv, n, d] on device -> records uint8 [h_kv, d, R]."""
+    _need(k, "k", torch.float32, 3)
+    h_kv, n, d = k.shape
+    r = record_bytes(n)
+    if records is None:
+        records = torch.empty((h_kv, d, r), dtype=torch.uint8, device=k.device)
+    _need(records, "records", torch.uint8)
+    if records.numel() < h_kv * d * r:
+        raise ValueError("records buffer too small")
+    if status is not None:
+        _need(status, "status", torch.int32)
+    _check(load().pack_bitplanes(_ptr(k), h_kv, n, d, _ptr(records), _ptr(status), _stream(k)))
+    return records
+
+
+def allocate(q: torch.Tensor, sigma2: torch.Tensor, budget: int, mode: int = WATERFILL,
+             depth: torch.Tensor | None = None, union_depth: torch.Tensor | None = None,
+             status: torch.Tensor | None = None):
+    """allocate_depths: q [h_q, d], sigma2 [h_kv, d] -> (depth uint8 [h_q, d], union uint8 [h_kv, d])."""
+    _need(q, "q", torch.float32, 2)
+    _need(sigma2, "sigma2", torch.float32, 2)
+    h_q, d = q.shape
+    h_kv = sigma2.shape[0]
+    if sigma2.shape[1] != d:
+        raise ValueError("sigma2 and q disagree on d")
+    if depth is None:
+        depth = torch.empty((h_q, d), dtype=torch.uint8, device=q.device)
+    if union_depth is None:
+        union_depth = torch.empty((h_kv, d), dtype=torch.uint8, device=q.device)
+    _need(depth, "depth", torch.uint8)
+    _need(union_depth, "union_depth", torch.uint8)
+    if status is not None:
+        _need(status, "status", torch.int32)
+    _check(load().allocate_depths(_ptr(q), _ptr(sigma2), h_q, h_kv, d, mode, budget, _ptr(depth),
+                                  _ptr(union_depth), _ptr(status), _stream(q)))
+    return depth, union_depth
+
+
+def _residency_of(records: torch.Tensor) -> int:
+    return HBM if records.is_cuda else HOST_DIRECT
+
+
+def scan_topk(records: torch.Tensor, q: torch.Tensor, depth: torch.Tensor, union_depth: torch.Tensor,
+              n: int, k: int, residency: int | None = None, workspace: torch.Tensor | None = None,
+              idx: torch.Tensor | None = None, scores: torch.Tensor | None = None,
+              want_scores: bool = False):
+    """scan_topk: -> int32 [h_q, k] ascending key indices (and float32 scores if asked).
+
+    ``records`` may be a device tensor (HBM residency) or a pinned host tensor
+    (host-direct residency)."""
+    _need(q, "q", torch.float32, 2)
+    _need(depth, "depth", torch.uint8)
+    _need(union_depth, "union_depth", torch.uint8)
+    _need(records, "records", torch.uint8, device=False)
+    if residency is None:
+        residency = _residency_of(records)
+    h_q, d = q.shape
+    h_kv = union_depth.shape[0]
+    if records.numel() < h_kv * d * record_bytes(n):
+        raise ValueError("records buffer too small for (h_kv, d, n)")
+    wsb = workspace_bytes(h_q, h_kv, n, d, k)
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=q.device)
+    _need(workspace, "workspace", torch.uint8)
+    if idx is None:
+        idx = torch.empty((h_q, k), dtype=torch.int32, device=q.device)
+    _need(idx, "idx", torch.int32)
+    if want_scores and scores is None:
+        scores = torch.empty((h_q, k), dtype=torch.float32, device=q.device)
+    if scores is not None:
+        _need(scores, "scores", torch.float32)
+    _check(load().scan_topk(_ptr(records), residency, _ptr(q), _ptr(depth), _ptr(union_depth), h_q, h_kv,
+                            n, d, k, _ptr(idx), _ptr(scores), _ptr(workspace), workspace.numel(),
+                            _stream(q)))
+    return (idx, scores) if want_scores or scores is not None else idx
+
+
+def scan_scores(records: torch.Tensor, q: torch.Tensor, depth: torch.Tensor, union_depth: torch.Tensor,
+                n: int, residency: int | None = None, out: torch.Tensor | None = None):
+    """fathom_scan_scores: -> float32 [h_q, n] scores (the scan stage alone)."""
+    _need(q, "q", torch.float32, 2)
+    _need(depth, "depth", torch.uint8)
+    _need(union_depth, "union_depth", torch.uint8)
+    _need(records, "records", torch.uint8, device=False)
+    if residency is None:
+        residency = _residency_of(records)
+    h_q, d = q.shape
+    h_kv = union_depth.shape[0]
+    if out is None:
+        out = torch.empty((h_q, max(n, 1)), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, 2)
+    _check(load().fathom_scan_scores(_ptr(records), residency, _ptr(q), _ptr(depth), _ptr(union_depth),
+                                     h_q, h_kv, n, d, _ptr(out), out.shape[1], _stream(q)))
+    return out[:, :n]

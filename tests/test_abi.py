@@ -1,0 +1,101 @@
+"""The C-ABI library loads, exports every symbol include/fathom.h declares, and
+validates arguments on the host (no GPU needed: every call here fails
+validation before any HIP call)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from oracle import fathom_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "fathom.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from sparse_attention_top_query_amd import build, fathom
+    if not os.path.exists(fathom.LIB_PATH):
+        build.build()
+    return fathom.load()
+
+
+def test_header_declares_the_entry_points():
+    names = header_functions()
+    for fn in ("pack_bitplanes", "allocate_depths", "scan_topk", "fathom_workspace_bytes",
+               "fathom_scan_scores", "fathom_last_error", "fathom_record_bytes"):
+        assert fn in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_record_geometry_matches_layout_definition(lib):
+    for n in (0, 1, 127, 128, 129, 1000, 1024, 4096, 131072, 262144, 1 << 20, 3 * 1024 + 300):
+        s, p, r = O.record_layout(n)
+        assert lib.fathom_scale_bytes(n) == s
+        assert lib.fathom_plane_bytes(n) == p
+        assert lib.fathom_record_bytes(n) == r
+
+
+def test_workspace_bytes_monotone(lib):
+    a = lib.fathom_workspace_bytes(32, 8, 1 << 20, 128, 2048)
+    b = lib.fathom_workspace_bytes(32, 8, 1 << 17, 128, 2048)
+    assert a > b > 0
+    assert a >= 32 * (1 << 20) * 4       # holds the fp32 scores of every head
+    assert lib.fathom_workspace_bytes(32, 8, 0, 128, 0) == 0
+
+
+def _err(lib):
+    return lib.fathom_last_error().decode()
+
+
+def test_host_validation_errors(lib):
+    P = ctypes.c_void_p
+    fake = P(0x1000)   # never dereferenced: validation fails first
+    # pack: bad d / h_kv
+    assert lib.pack_bitplanes(fake, 1, 128, 0, fake, None, None) == -2
+    assert "d=0" in _err(lib)
+    assert lib.pack_bitplanes(fake, 0, 128, 4, fake, None, None) == -2
+    assert lib.pack_bitplanes(None, 1, 128, 4, fake, None, None) == -1
+    # allocate: budget, mode, group size
+    assert lib.allocate_depths(fake, fake, 4, 1, 8, 0, 33, fake, fake, None, None) == -3
+    assert lib.allocate_depths(fake, fake, 4, 1, 8, 1, 6, fake, fake, None, None) == -3
+    assert lib.allocate_depths(fake, fake, 4, 1, 8, 7, 6, fake, fake, None, None) == -1
+    assert lib.allocate_depths(fake, fake, 3, 1, 8, 0, 6, fake, fake, None, None) == -2
+    assert lib.allocate_depths(fake, fake, 6, 4, 8, 0, 6, fake, fake, None, None) == -2
+    assert lib.allocate_depths(fake, fake, 4, 1, 300, 0, 6, fake, fake, None, None) == -2
+    # scan: shape checks come before any pointer query
+    assert lib.scan_topk(fake, 0, fake, fake, fake, 4, 3, 128, 8, 4, fake, None, fake, 1 << 20, None) == -2
+    assert lib.scan_topk(fake, 0, fake, fake, fake, 4, 1, -1, 8, 4, fake, None, fake, 1 << 20, None) == -2
+    assert lib.fathom_scan_scores(fake, 0, None, fake, fake, 4, 1, 128, 8, fake, 128, None) == -1
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    import torch
+    from sparse_attention_top_query_amd import fathom
+    k = torch.zeros((1, 128, 8), dtype=torch.float32)
+    with pytest.raises(ValueError):
+        fathom.pack(k)
+    with pytest.raises(TypeError):
+        fathom.pack(k.double())
+
+
+def test_product_path_does_not_import_oracle():
+    pkg = os.path.join(ROOT, "sparse_attention_top_query_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text, f
