@@ -36,15 +36,21 @@ def parse():
     ap.add_argument("--workload", default="w3_host_1m_B92")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--kernel-reps", type=int, default=20)
+    ap.add_argument("--residency", choices=["staged", "direct"], default="staged",
+                    help="host-resident records: staged through HBM (default) or read in place")
+    ap.add_argument("--copies", type=int, default=8,
+                    help="HBM-resident workloads: distinct record copies cycled per step, so the "
+                         "256 MB Infinity Cache cannot hold them")
     return ap.parse_args()
 
 
 def algorithmic_bytes(union: np.ndarray, n: int) -> int:
     """Bytes the method must read per step: for every (KV head, channel) with a
-    nonzero union depth t, the block scales and t planes of its n keys."""
-    nb = (n + 127) // 128
+    nonzero union depth t, its contiguous prefix run -- the block scales and t
+    planes of its n keys (n/64 + t n/8 bytes for n a multiple of 1024)."""
+    units = -(-((n + 127) // 128) // 8)
     t = union.astype(np.int64)
-    return int(((t > 0) * 2 * nb + t * 16 * nb).sum())
+    return int(np.where(t > 0, 144 * units + (t - 1) * 128 * units, 0).sum())
 
 
 def measure_h2d_peak(torch, dev, mib=512, reps=5) -> float:
@@ -99,9 +105,10 @@ def build_records(torch, F, wl, dev, layer=0):
     return records, torch.from_numpy(q).to(dev), torch.from_numpy(s2).to(dev), q, s2
 
 
-def cpu_baseline(wl, q_np, s2_np, budget, seconds_hint=20.0):
+def cpu_baseline(wl, q_np, s2_np, budget, seconds=15.0):
     """The oracle timed on this host: allocation + fp64 scores + top-k for the
-    query heads of KV head 0 over all n keys (codes precomputed, not timed)."""
+    query heads of KV head 0 over all n keys (codes precomputed, not timed),
+    repeated over those heads until about `seconds` of CPU work is measured."""
     from threadpoolctl import threadpool_limits
 
     from oracle import fathom_oracle as O
@@ -113,17 +120,17 @@ def cpu_baseline(wl, q_np, s2_np, budget, seconds_hint=20.0):
     heads = 0
     t0 = time.perf_counter()
     with threadpool_limits(limits=1):
-        for h in range(wl.g):
+        while heads < wl.g or time.perf_counter() - t0 < seconds:
+            h = heads % wl.g
             t = O.waterfill_depths(O.importance(q_np[h], s2_np[0]), budget)
             s, _ = O.scores(q_np[h], kappa, delta, t)
             O.topk(s, wl.k)
             heads += 1
-            if time.perf_counter() - t0 > seconds_hint:
-                break
     dt = time.perf_counter() - t0
     return {"value": heads * wl.n / dt, "unit": "keys/s", "cores": 1, "kind": "oracle",
-            "sample": f"{heads} query heads of KV head 0 x {wl.n} keys (allocation + fp64 scores + "
-                      f"top-{wl.k}; codes precomputed), numpy single-threaded, {dt:.1f} s"}
+            "sample": f"{heads} query-head scans (the {wl.g} heads of KV head 0, cycled) x {wl.n} keys: "
+                      f"allocation + fp64 scores + top-{wl.k}, codes precomputed; numpy single-threaded, "
+                      f"{dt:.1f} s"}
 
 
 def main():
@@ -150,15 +157,23 @@ def main():
     setup_s = time.perf_counter() - t_setup
     hk, hq, n, d, k = wl.sessions * wl.h_kv, wl.sessions * wl.h_q, wl.n, wl.d, wl.k
 
+    host = wl.residency == "host"
+    residency = (F.HOST_STAGED if args.residency == "staged" else F.HOST_DIRECT) if host else F.HBM
+    copies = [records]
+    if not host:
+        copies += [records.clone() for _ in range(max(0, args.copies - 1))]
     depth = torch.empty((hq, d), dtype=torch.uint8, device=dev)
     uni = torch.empty((hk, d), dtype=torch.uint8, device=dev)
-    ws = torch.empty(F.workspace_bytes(hq, hk, n, d, k), dtype=torch.uint8, device=dev)
+    ws = torch.empty(F.workspace_bytes(hq, hk, n, d, k, residency), dtype=torch.uint8, device=dev)
     idx = torch.empty((hq, k), dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev)
+    it = [0]
 
     def step():
+        rec = copies[it[0] % len(copies)]
+        it[0] += 1
         F.allocate(q, s2, budget, mode=mode, depth=depth, union_depth=uni)
-        F.scan_topk(records, q, depth, uni, n, k, workspace=ws, idx=idx)
+        F.scan_topk(rec, q, depth, uni, n, k, residency=residency, workspace=ws, idx=idx)
 
     for _ in range(args.warmup):
         step()
@@ -173,15 +188,15 @@ def main():
     wall = time.perf_counter() - t0
     step_ms = ev0.elapsed_time(ev1) / args.steps
 
-    # the dominant kernel alone (same launch as inside scan_topk), timed with
+    # the scan stage alone (the same launches as inside scan_topk), timed with
     # events on the stream it is launched on
     scores = torch.empty((hq, n), dtype=torch.float32, device=dev)
-    F.scan_scores(records, q, depth, uni, n, out=scores)
+    F.scan_scores(records, q, depth, uni, n, residency=residency, out=scores, workspace=ws)
     torch.cuda.synchronize(dev)
     ka, kb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ka.record(stream)
-    for _ in range(args.kernel_reps):
-        F.scan_scores(records, q, depth, uni, n, out=scores)
+    for r in range(args.kernel_reps):
+        F.scan_scores(copies[r % len(copies)], q, depth, uni, n, residency=residency, out=scores, workspace=ws)
     kb.record(stream)
     torch.cuda.synchronize(dev)
     scan_ms = ka.elapsed_time(kb) / args.kernel_reps
@@ -190,17 +205,23 @@ def main():
     union_np = uni.cpu().numpy()
     alg_bytes = algorithmic_bytes(union_np, n)
     achieved = alg_bytes / (scan_ms * 1e-3) / 1e9
-    host = wl.residency == "host"
     keys_per_s = hq * n / (step_ms * 1e-3)
+    g = hq // hk
+    if host and residency == F.HOST_STAGED:
+        kname = f"stage_scan_kernel<{g}> ({-(-hk // max(1, min(hk, (64 << 20) // (d * F.record_bytes(n))))) + 1} launches per step)"
+    else:
+        kname = f"scan_kernel<{g}>"
     if host:
         roof = {"bound": "host_link", "achieved": round(achieved, 2), "peak": PCIE5_X16_GBPS, "unit": "GB/s",
                 "frac": round(achieved / PCIE5_X16_GBPS, 4), "traffic": None,
                 "measured_h2d_peak": round(h2d_peak, 2), "frac_of_measured_h2d": round(achieved / h2d_peak, 4),
-                "kernel": "scan_kernel<4>", "kernel_ms": round(scan_ms, 4), "bytes_per_launch": alg_bytes}
+                "kernel": kname, "kernel_ms": round(scan_ms, 4), "bytes_per_launch": alg_bytes,
+                "residency": args.residency}
     else:
         roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                "kernel": "scan_kernel<4>", "kernel_ms": round(scan_ms, 4), "bytes_per_launch": alg_bytes}
+                "kernel": kname, "kernel_ms": round(scan_ms, 4), "bytes_per_launch": alg_bytes,
+                "record_copies_cycled": len(copies)}
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(wl, q_np, s2_np, budget)
@@ -218,7 +239,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": wl.name, "h_kv": hk, "h_q": hq, "d": d, "n": n, "budget_bits": budget,
-                   "k": k, "residency": "pinned host, read over the host link" if host else "HBM",
+                   "k": k, "residency": (f"pinned host, {args.residency} over the host link" if host else "HBM"),
                    "mode": wl.mode},
         "roofline": roof,
         "cpu_baseline": cpu,

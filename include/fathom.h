@@ -50,9 +50,14 @@ typedef enum fathom_status {
 /* Where scan_topk finds the records. */
 enum fathom_residency {
   FATHOM_HBM = 0,          /* records in device memory                                  */
-  FATHOM_HOST_DIRECT = 1   /* records in pinned host memory (hipHostMalloc or torch
-                              pin_memory); the scan kernel reads only the budgeted plane
-                              prefixes straight over the host link, no staging copy     */
+  FATHOM_HOST_DIRECT = 1,  /* records in pinned host memory (hipHostMalloc or torch
+                              pin_memory); the scan kernel reads the budgeted plane
+                              prefixes of each tile straight over the host link          */
+  FATHOM_HOST_STAGED = 2   /* records in pinned host memory; each channel's budgeted prefix
+                              run is gathered into an HBM mirror in the workspace with long
+                              contiguous reads, and the copy of one KV head overlaps the
+                              scan of the previous one ([Review] Strengths, paper Sec 3.6:
+                              partial reads as contiguous host-link runs)                 */
 };
 
 /* How allocate_depths spends the budget. */
@@ -75,17 +80,21 @@ enum fathom_depth_mode {
  * contiguous, so the first t planes are the channel's t-bit quantizer;
  * [Review] Strengths (paper Sec 3.6): a partial read is one contiguous run.
  *
- * records = [h_kv][d] records of fathom_record_bytes(n) bytes each:
- *   bytes [0, S)        fp16 scale Delta of each 128-key block, little-endian,
- *                       zero padded to S = fathom_scale_bytes(n) (multiple of 16);
- *   bytes [S + p*P, S + (p+1)*P)   plane p (p = 0 is the most significant bit),
- *                       P = fathom_plane_bytes(n) = 16 * ceil(n / 128):
- *                       key j is bit (j % 8) of byte j / 8; bits past n are 0.
- * For n a multiple of 1024: S = n/64, P = n/8, R = n/64 + n/2.
+ * records = [h_kv][d] records of R = fathom_record_bytes(n) bytes each.  With
+ * U = ceil(n / 1024) units of 1024 keys (8 blocks of 128):
+ *   head, bytes [0, 144 U): unit u at 144 u holds the fp16 scales Delta of
+ *        blocks 8u..8u+7 (16 bytes, little-endian) followed by the plane-0 bits
+ *        of keys 1024u..1024u+1023 (128 bytes);
+ *   plane p in 1..3 at 144 U + (p-1) 128 U: 128 U bytes.
+ * Plane 0 is the most significant bit; key j is bit (j % 8) of byte (j % 1024)/8
+ * of its unit's plane-0 bits, and of byte j/8 of planes 1..3.  Padding is 0.
+ * The scales and the first t >= 1 planes form the single contiguous run of
+ * fathom_prefix_bytes(n, t) = 144 U + (t-1) 128 U bytes at the record start,
+ * and every key's scale is read together with its most significant plane.
+ * For n a multiple of 1024: R = n/64 + n/2 and the t-prefix is n/64 + t n/8.
  * ------------------------------------------------------------------------- */
-size_t fathom_scale_bytes(int64_t n);
-size_t fathom_plane_bytes(int64_t n);
 size_t fathom_record_bytes(int64_t n);
+size_t fathom_prefix_bytes(int64_t n, int t);
 
 /* pack_bitplanes -- quantise and pack the K cache (once per cache or layer).
  * [Review] Strengths (paper Sec 3.2) and FAQ: 4-bit uniform codes under one
@@ -125,8 +134,10 @@ int allocate_depths(const float* q, const float* sigma2, int h_q, int h_kv, int 
                     int mode, int budget, uint8_t* depth, uint8_t* union_depth,
                     uint32_t* status, void* stream);
 
-/* Bytes of device workspace scan_topk needs for this shape. */
-size_t fathom_workspace_bytes(int h_q, int h_kv, int64_t n, int d, int k);
+/* Bytes of device workspace scan_topk (and fathom_scan_scores) needs for this
+ * shape and residency: the fp32 scores and selection state, plus for
+ * FATHOM_HOST_STAGED an HBM mirror of the records (h_kv * d * R bytes). */
+size_t fathom_workspace_bytes(int h_q, int h_kv, int64_t n, int d, int k, int residency);
 
 /* scan_topk -- score every key from its read prefix and select the top k
  * ([Abstract]; [Digest] key modules 4-5 and Output: the scan pulls only the
@@ -152,12 +163,13 @@ int scan_topk(const void* records, int residency, const float* q, const uint8_t*
               size_t workspace_bytes, void* stream);
 
 /* fathom_scan_scores -- the scan stage alone (for tests and profiling): the same
- * scores scan_topk ranks, written to device float32 [h_q][ld] (ld >= n, only the
- * first n entries of each row are meaningful). */
+ * scores scan_topk ranks, written to device float32 [h_q][ld] (ld >= n; the
+ * first n entries of each row are written).  The workspace is used only by
+ * FATHOM_HOST_STAGED (for its HBM mirror) and may be NULL otherwise. */
 int fathom_scan_scores(const void* records, int residency, const float* q,
                        const uint8_t* depth, const uint8_t* union_depth, int h_q,
                        int h_kv, int64_t n, int d, float* scores, int64_t ld,
-                       void* stream);
+                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* Message for the last failing call on this thread ("" if none). */
 const char* fathom_last_error(void);

@@ -64,23 +64,42 @@ TOL_REL = 1e-4       # score tolerance factor applied to sum_c |q_c * k_hat_c|
 # Strengths citing paper Sec 3.6).
 # ---------------------------------------------------------------------------
 
+UNIT_BLOCKS = 8                      # 128-key blocks per interleave unit (1024 keys)
+UNIT_SCALE_BYTES = 2 * UNIT_BLOCKS   # 16: fp16 scales of one unit
+UNIT_PLANE_BYTES = 16 * UNIT_BLOCKS  # 128: one plane's bits of one unit
+
+
 def n_blocks(n: int) -> int:
     """Number of 128-token scale blocks covering n keys (last one may be partial)."""
     return (n + BLOCK - 1) // BLOCK
 
 
-def record_layout(n: int) -> tuple[int, int, int]:
-    """(scale_bytes S, plane_bytes P, record_bytes R) of one (KV head, channel) record.
+def n_units(n: int) -> int:
+    """Number of 1024-key units covering n keys."""
+    return (n_blocks(n) + UNIT_BLOCKS - 1) // UNIT_BLOCKS
 
-    A record is  [ S bytes: fp16 scale per block, zero padded to 16 bytes ]
-                 [ P bytes: plane 0 (MSB) ] [ plane 1 ] [ plane 2 ] [ plane 3 (LSB) ]
-    with P = 16 bytes per block (128 keys, one bit each), so that reading the
-    first t planes of a record is one contiguous run of S + t*P bytes.
+
+def record_layout(n: int) -> tuple[int, int, int, int]:
+    """(units U, head bytes H, plane bytes P, record bytes R) of one (KV head, channel) record.
+
+    A record is   [ head: U units of (16 B fp16 scales of the unit's 8 blocks,
+                                     128 B plane-0 bits of the unit's 1024 keys) ]
+                  [ plane 1: P = 128 U bytes ] [ plane 2 ] [ plane 3 ]
+    Plane 0 is the most significant bit.  Every key's scale travels with its
+    plane-0 bits, and reading the first t >= 1 planes is the single contiguous
+    run [0, H + (t - 1) P).  For n a multiple of 1024, R = n/64 + n/2.
+    Padding (blocks or keys past n) is zero.
     """
-    nb = n_blocks(n)
-    s = ((2 * nb + 15) // 16) * 16
-    p = 16 * nb
-    return s, p, s + PLANES * p
+    u = n_units(n)
+    h = u * (UNIT_SCALE_BYTES + UNIT_PLANE_BYTES)
+    p = u * UNIT_PLANE_BYTES
+    return u, h, p, h + (PLANES - 1) * p
+
+
+def prefix_bytes(n: int, t: int) -> int:
+    """Bytes of the contiguous run holding the scales and the first t planes."""
+    _, h, p, _ = record_layout(n)
+    return 0 if t == 0 else h + (t - 1) * p
 
 
 # ---------------------------------------------------------------------------
@@ -141,40 +160,58 @@ def quantize_codes(k: np.ndarray, delta: np.ndarray) -> np.ndarray:
     return cnt.reshape(-1, d)[:n].copy()
 
 
-def pack_records(kappa: np.ndarray, delta: np.ndarray) -> np.ndarray:
-    """Channel-major bit-plane records of one KV head: uint8 [d, R].
-
-    Plane p holds bit (3 - p) of every key's code; key j is bit (j mod 8) of
-    byte j // 8 of the plane (so bit j mod 32 of little-endian u32 word j // 32).
-    Bits of keys past n are zero.  Scales are little-endian fp16.
-    """
+def _plane_bits(kappa: np.ndarray, plane: int, units: int) -> np.ndarray:
+    """Bits of one plane packed per channel: uint8 [d, 128 * units]; key j is bit
+    (j mod 8) of byte j // 8; keys past n are 0."""
     n, d = kappa.shape
-    s, p, r = record_layout(n)
-    nb = n_blocks(n)
+    bits = ((kappa >> (PLANES - 1 - plane)) & 1).astype(np.uint8)       # [n, d]
+    padded = np.zeros((units * UNIT_BLOCKS * BLOCK, d), dtype=np.uint8)
+    padded[:n] = bits
+    return np.packbits(padded.T, axis=1, bitorder="little")
+
+
+def pack_records(kappa: np.ndarray, delta: np.ndarray) -> np.ndarray:
+    """Channel-major bit-plane records of one KV head: uint8 [d, R] (layout in
+    record_layout).  Plane p holds bit (3 - p) of every key's code; scales are
+    little-endian fp16."""
+    n, d = kappa.shape
+    u, h, p, r = record_layout(n)
     rec = np.zeros((d, r), dtype=np.uint8)
-    rec[:, : 2 * nb] = np.ascontiguousarray(delta.astype("<f2")).view(np.uint8).reshape(d, 2 * nb)
-    for plane in range(PLANES):
-        bits = ((kappa >> (PLANES - 1 - plane)) & 1).astype(np.uint8)    # [n, d]
-        padded = np.zeros((nb * BLOCK, d), dtype=np.uint8)
-        padded[:n] = bits
-        packed = np.packbits(padded.T, axis=1, bitorder="little")        # [d, P]
-        rec[:, s + plane * p: s + (plane + 1) * p] = packed
+    if u == 0:
+        return rec
+    sc = np.zeros((d, u * UNIT_BLOCKS), dtype="<f2")
+    sc[:, : delta.shape[1]] = delta
+    sc_bytes = sc.view(np.uint8).reshape(d, u, UNIT_SCALE_BYTES)
+    p0 = _plane_bits(kappa, 0, u).reshape(d, u, UNIT_PLANE_BYTES)
+    rec[:, :h] = np.concatenate([sc_bytes, p0], axis=2).reshape(d, h)
+    for plane in range(1, PLANES):
+        rec[:, h + (plane - 1) * p: h + plane * p] = _plane_bits(kappa, plane, u)
     return rec
 
 
 def unpack_codes(rec: np.ndarray, n: int, depth: int = PLANES) -> tuple[np.ndarray, np.ndarray]:
     """Read back (delta [d, nb] fp16, t-bit prefix codes [n, d]) from records.
 
-    Reads only the first ``depth`` planes of each record -- the contiguous
-    prefix the scan pulls -- and returns kappa >> (4 - depth).
+    Reads only bytes [0, prefix_bytes(n, depth)) of each record -- the run the
+    scan pulls -- and returns kappa >> (4 - depth) (the scales need depth >= 1;
+    with depth 0 they are returned as zeros, as nothing is read).
     """
     d = rec.shape[0]
-    s, p, _ = record_layout(n)
+    u, h, p, _ = record_layout(n)
     nb = n_blocks(n)
-    delta = np.ascontiguousarray(rec[:, : 2 * nb]).view("<f2").reshape(d, nb).astype(np.float16)
+    run = rec[:, : prefix_bytes(n, depth)]
     code = np.zeros((n, d), dtype=np.uint8)
-    for plane in range(depth):
-        bits = np.unpackbits(rec[:, s + plane * p: s + (plane + 1) * p], axis=1, bitorder="little")
+    delta = np.zeros((d, nb), dtype=np.float16)
+    if depth == 0 or u == 0:
+        return delta, code
+    head = np.ascontiguousarray(run[:, :h]).reshape(d, u, UNIT_SCALE_BYTES + UNIT_PLANE_BYTES)
+    delta = np.ascontiguousarray(head[:, :, :UNIT_SCALE_BYTES]).view("<f2").reshape(d, -1)[:, :nb]
+    delta = delta.astype(np.float16)
+    planes = [np.ascontiguousarray(head[:, :, UNIT_SCALE_BYTES:]).reshape(d, p)]
+    for plane in range(1, depth):
+        planes.append(run[:, h + (plane - 1) * p: h + plane * p])
+    for bits_packed in planes:
+        bits = np.unpackbits(bits_packed, axis=1, bitorder="little")
         code = (code << 1) | bits[:, :n].T
     return delta, code
 

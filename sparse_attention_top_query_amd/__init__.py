@@ -8,19 +8,19 @@ fallback: calls fail if the library has not been built.
 from .fathom import (  # noqa: F401
     HBM,
     HOST_DIRECT,
+    HOST_STAGED,
     TOPQ,
     WATERFILL,
     FathomError,
     allocate,
     load,
     pack,
-    plane_bytes,
+    prefix_bytes,
     record_bytes,
-    scale_bytes,
     scan_scores,
     scan_topk,
     workspace_bytes,
 )
 
-__all__ = ["HBM", "HOST_DIRECT", "TOPQ", "WATERFILL", "FathomError", "allocate", "load", "pack",
-           "plane_bytes", "record_bytes", "scale_bytes", "scan_scores", "scan_topk", "workspace_bytes"]
+__all__ = ["HBM", "HOST_DIRECT", "HOST_STAGED", "TOPQ", "WATERFILL", "FathomError", "allocate", "load", "pack",
+           "prefix_bytes", "record_bytes", "scan_scores", "scan_topk", "workspace_bytes"]

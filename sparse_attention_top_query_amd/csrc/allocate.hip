@@ -8,32 +8,53 @@
 // sum_c w_c 4^(-t_c) subject to sum_c t_c = B, t_c in {0..4}.
 //
 // One workgroup per KV head, one wavefront per query head of its group.  A
-// lane owns channels lane, lane+64, lane+128, lane+192.  Each of the B greedy
-// steps finds the channel of largest marginal gain w_c 4^(-t_c) with a
-// wave-wide max over a single 64-bit key:
-//   key = bits(double(w_c) * 4^(-t_c)) | (256 - c).
-// w_c is an fp32 value, so as a double its low 29 significand bits are zero
-// and scaling by 4^(-t) is exact: the key orders by exact gain first, then
-// by lowest channel, which is the tie rule.  Non-negative doubles order like
-// their bit patterns, and 256 - c >= 1 keeps every real candidate above 0.
+// lane owns channels lane, lane+64, lane+128, lane+192.
+//
+// The greedy is computed in closed form rather than step by step.  Plane t of
+// channel c (t = 0..3) is an item with marginal gain w_c 4^(-t); gains fall
+// with t, so the greedy takes items in the order (gain desc, channel asc,
+// plane asc) and after B steps holds exactly the B first items of that order.
+// Each item gets a distinct 64-bit key
+//   key = bits(double(w_c) * 4^(-t)) | (256 - c) << 2 | (3 - t),
+// which sorts in that order: w_c is an fp32 value, so as a double its low 29
+// significand bits are zero and scaling by 4^(-t) is exact; non-negative
+// doubles order like their bit patterns.  The B-th largest key K is found by a
+// 63-step bitwise search (each step counts the keys >= a candidate with one
+// compare per item and a wave-wide ballot count), and t_c is the number of
+// channel c's items with key >= K.  The fixed top-|q| mode selects m channels
+// the same way with key = bits(|q_c|) << 8 | (255 - c).
 #include "fathom_internal.h"
 
 namespace fathom {
 namespace {
 
-__device__ inline uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const uint64_t o = __shfl_xor(v, off, 64);
-    v = o > v ? o : v;
-  }
-  return v;
-}
-
 __device__ inline uint32_t wave_or(uint32_t v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v |= __shfl_xor(v, off, 64);
   return v;
+}
+
+// Wave-wide sum of per-lane counts in [0, 31], from one ballot per bit.
+__device__ __forceinline__ uint32_t wave_count(uint32_t cnt) {
+  uint32_t tot = 0;
+#pragma unroll
+  for (int b = 0; b < 5; ++b) tot += (uint32_t)__popcll(__ballot((cnt >> b) & 1u)) << b;
+  return tot;
+}
+
+// Largest K such that at least `want` of the wave's keys are >= K (the want-th
+// largest key when keys are distinct); `want` >= 1 and at most the key count.
+template <int N>
+__device__ __forceinline__ uint64_t wave_kth_key(const uint64_t (&key)[N], uint32_t want, int top_bit) {
+  uint64_t T = 0;
+  for (int bit = top_bit; bit >= 0; --bit) {
+    const uint64_t cand = T | (1ull << bit);
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i) cnt += key[i] >= cand;
+    if (wave_count(cnt) >= want) T = cand;
+  }
+  return T;
 }
 
 __global__ __launch_bounds__(1024) void allocate_kernel(const float* __restrict__ q,
@@ -43,7 +64,6 @@ __global__ __launch_bounds__(1024) void allocate_kernel(const float* __restrict_
                                                         uint8_t* __restrict__ uni,
                                                         uint32_t* __restrict__ status) {
   __shared__ uint8_t sdep[kMaxG][kMaxD];
-  __shared__ float sabs[kMaxG][kMaxD];
   __shared__ uint32_t sflag[kMaxG];
 
   const int kv = blockIdx.x;
@@ -74,48 +94,41 @@ __global__ __launch_bounds__(1024) void allocate_kernel(const float* __restrict_
   }
   flag = wave_or(flag);
 
-  // |q| of every channel, for the fixed-depth mode (written by all waves so the
-  // barrier below is reached uniformly)
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = lane + 64 * i;
-    if (c < d) sabs[wv][c] = aq[i];
-  }
-  __syncthreads();
-
-  if (flag == 0 && mode == 0) {
-    for (int step = 0; step < budget; ++step) {
-      uint64_t best = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c = lane + 64 * i;
-        if (c < d && t[i] < kPlanes) {
-          const double gain = ldexp((double)w[i], -2 * t[i]);
-          const uint64_t key = ((uint64_t)__double_as_longlong(gain)) | (uint64_t)(256 - c);
-          best = key > best ? key : best;
-        }
-      }
-      best = wave_max_u64(best);   // > 0: step < budget <= 4d leaves a channel with room
-      const int cw = 256 - (int)(best & 511u);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (lane + 64 * i == cw) t[i] += 1;
-    }
-  } else if (flag == 0) {
-    // fixed-depth comparison mode: 4 planes on the m channels of largest |q_c|
-    const int m = budget / kPlanes;
+  if (flag == 0 && mode == 0 && budget > 0) {
+    uint64_t key[16];   // item (channel lane + 64 i, plane t) at 4 i + t; 0 = no item
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int c = lane + 64 * i;
-      if (c < d) {
-        int rank = 0;
-        for (int c2 = 0; c2 < d; ++c2) {
-          const float a2 = sabs[wv][c2];
-          rank += (a2 > aq[i]) || (a2 == aq[i] && c2 < c);
-        }
-        t[i] = rank < m ? kPlanes : 0;
+#pragma unroll
+      for (int t = 0; t < kPlanes; ++t) {
+        const uint64_t gain = (uint64_t)__double_as_longlong(ldexp((double)w[i], -2 * t));
+        key[4 * i + t] = c < d ? (gain | (uint64_t)(256 - c) << 2 | (uint64_t)(3 - t)) : 0ull;
       }
     }
+    const uint64_t K = wave_kth_key(key, (uint32_t)budget, 62);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int tc = 0;
+#pragma unroll
+      for (int t = 0; t < kPlanes; ++t) tc += key[4 * i + t] >= K;
+      t[i] = lane + 64 * i < d ? tc : 0;
+    }
+  } else if (flag == 0 && mode == 1 && budget > 0) {
+    // fixed-depth comparison mode: 4 planes on the m channels of largest |q_c|
+    const uint32_t m = (uint32_t)(budget / kPlanes);
+    uint64_t key[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = lane + 64 * i;
+      key[i] = c < d ? ((uint64_t)__float_as_uint(aq[i]) << 8 | (uint64_t)(255 - c)) : 0ull;
+    }
+    // a channel with |q| = +0 and c = 255 has key 0: count it via the >= test only
+    // when something else is smaller, so search over keys + 1
+#pragma unroll
+    for (int i = 0; i < 4; ++i) key[i] = lane + 64 * i < d ? key[i] + 1 : 0ull;
+    const uint64_t K = wave_kth_key(key, m, 40);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t[i] = (lane + 64 * i < d && key[i] >= K) ? kPlanes : 0;
   }
 
 #pragma unroll

@@ -65,9 +65,9 @@ int resolve_records(const void* records, int residency, const uint8_t** dev) {
     *dev = static_cast<const uint8_t*>(records);
     return FATHOM_OK;
   }
-  if (residency == FATHOM_HOST_DIRECT) {
+  if (residency == FATHOM_HOST_DIRECT || residency == FATHOM_HOST_STAGED) {
     if (attr.type != hipMemoryTypeHost)
-      return fail(FATHOM_ERESIDENCY, "FATHOM_HOST_DIRECT records must be pinned host memory");
+      return fail(FATHOM_ERESIDENCY, "host-resident records must be pinned host memory");
     const uint8_t* p = static_cast<const uint8_t*>(attr.devicePointer);
     if (!p) return fail(FATHOM_ERESIDENCY, "pinned host records have no device mapping");
     *dev = p + (static_cast<const uint8_t*>(records) - static_cast<const uint8_t*>(attr.hostPointer));
@@ -98,9 +98,11 @@ int fathom_version(void) { return 100; }
 
 const char* fathom_last_error(void) { return g_last_error.c_str(); }
 
-size_t fathom_scale_bytes(int64_t n) { return n <= 0 ? 0 : (size_t)fathom::make_layout(n).S; }
-size_t fathom_plane_bytes(int64_t n) { return n <= 0 ? 0 : (size_t)fathom::make_layout(n).P; }
 size_t fathom_record_bytes(int64_t n) { return n <= 0 ? 0 : (size_t)fathom::make_layout(n).R; }
+size_t fathom_prefix_bytes(int64_t n, int t) {
+  if (n <= 0 || t <= 0) return 0;
+  return (size_t)fathom::prefix_bytes(fathom::make_layout(n), t > fathom::kPlanes ? fathom::kPlanes : t);
+}
 
 int pack_bitplanes(const float* k, int h_kv, int64_t n, int d, void* records, uint32_t* status,
                    void* stream) {
@@ -135,27 +137,62 @@ int allocate_depths(const float* q, const float* sigma2, int h_q, int h_kv, int 
   return ok();
 }
 
-size_t fathom_workspace_bytes(int h_q, int h_kv, int64_t n, int d, int k) {
-  (void)h_kv;
-  (void)d;
+size_t fathom_workspace_bytes(int h_q, int h_kv, int64_t n, int d, int k, int residency) {
   (void)k;
-  if (h_q <= 0 || n <= 0) return 0;
-  return al256((size_t)h_q * (size_t)score_ld(n) * 4) + fathom::select_workspace_bytes(h_q, n);
+  if (h_q <= 0 || h_kv <= 0 || d <= 0 || n <= 0) return 0;
+  size_t bytes = al256((size_t)h_q * (size_t)score_ld(n) * 4) + fathom::select_workspace_bytes(h_q, n, k > 0 ? k : 1);
+  if (residency == FATHOM_HOST_STAGED) bytes += al256((size_t)h_kv * (size_t)d * (size_t)fathom::make_layout(n).R);
+  return bytes;
 }
+
+}  // extern "C"
+
+namespace {
+
+// Scores of every key into `scores` [h_q][ld]; staging comes from the workspace.
+int run_scan(const uint8_t* dev, int residency, const float* q, const uint8_t* depth,
+             const uint8_t* union_depth, int h_q, int h_kv, int64_t n, int d, float* scores, int64_t ld,
+             uint8_t* staging, hipStream_t s) {
+  const fathom::Layout L = fathom::make_layout(n);
+  hipError_t e;
+  if (residency == FATHOM_HOST_STAGED)
+    e = fathom::launch_scan_staged(dev, staging, q, depth, union_depth, h_kv, h_q / h_kv, L, d, scores, ld, s);
+  else
+    e = fathom::launch_scan(dev, residency == FATHOM_HOST_DIRECT, q, depth, union_depth, h_kv, h_q / h_kv, L, d,
+                            scores, ld, s);
+  if (e != hipSuccess) return hip_fail(e, "scan launch");
+  return FATHOM_OK;
+}
+
+size_t staging_offset(int h_q, int64_t n, int k) {
+  return al256((size_t)h_q * (size_t)score_ld(n) * 4) + fathom::select_workspace_bytes(h_q, n, k > 0 ? k : 1);
+}
+
+}  // namespace
+
+extern "C" {
 
 int fathom_scan_scores(const void* records, int residency, const float* q, const uint8_t* depth,
                        const uint8_t* union_depth, int h_q, int h_kv, int64_t n, int d,
-                       float* scores, int64_t ld, void* stream) {
+                       float* scores, int64_t ld, void* workspace, size_t workspace_bytes,
+                       void* stream) {
   const uint8_t* dev = nullptr;
   int st = check_scan_args(records, residency, q, depth, union_depth, h_q, h_kv, n, d, &dev);
   if (st) return st;
   if (n == 0) return ok();
   if (!scores) return fail(FATHOM_EINVAL, "null scores");
   if (ld < n) return fail(FATHOM_ESHAPE, "ld=%lld < n=%lld", (long long)ld, (long long)n);
-  hipError_t e = fathom::launch_scan(dev, q, depth, union_depth, h_kv, h_q / h_kv,
-                                     fathom::make_layout(n), d, scores, ld,
-                                     static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "scan launch");
+  uint8_t* staging = nullptr;
+  if (residency == FATHOM_HOST_STAGED) {
+    const size_t need = fathom_workspace_bytes(h_q, h_kv, n, d, 1, residency);
+    if (!workspace || workspace_bytes < need)
+      return fail(FATHOM_EWORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, need);
+    if (!aligned(workspace, 256)) return fail(FATHOM_EINVAL, "workspace must be 256-byte aligned");
+    staging = static_cast<uint8_t*>(workspace) + staging_offset(h_q, n, 1);
+  }
+  st = run_scan(dev, residency, q, depth, union_depth, h_q, h_kv, n, d, scores, ld, staging,
+                static_cast<hipStream_t>(stream));
+  if (st) return st;
   return ok();
 }
 
@@ -169,7 +206,7 @@ int scan_topk(const void* records, int residency, const float* q, const uint8_t*
   if (k < 0 || k > n) return fail(FATHOM_ESHAPE, "k=%d outside [0, n=%lld]", k, (long long)n);
   if (k == 0) return ok();
   if (!topk_idx) return fail(FATHOM_EINVAL, "null topk_idx");
-  const size_t need = fathom_workspace_bytes(h_q, h_kv, n, d, k);
+  const size_t need = fathom_workspace_bytes(h_q, h_kv, n, d, k, residency);
   if (!workspace || workspace_bytes < need)
     return fail(FATHOM_EWORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, need);
   if (!aligned(workspace, 256)) return fail(FATHOM_EINVAL, "workspace must be 256-byte aligned");
@@ -177,11 +214,11 @@ int scan_topk(const void* records, int residency, const float* q, const uint8_t*
   const int64_t ld = score_ld(n);
   float* scores = static_cast<float*>(workspace);
   uint8_t* sel_base = static_cast<uint8_t*>(workspace) + al256((size_t)h_q * (size_t)ld * 4);
-  hipError_t e = fathom::launch_scan(dev, q, depth, union_depth, h_kv, h_q / h_kv,
-                                     fathom::make_layout(n), d, scores, ld, s);
-  if (e != hipSuccess) return hip_fail(e, "scan launch");
-  e = fathom::launch_select(scores, ld, h_q, n, k, topk_idx, topk_score,
-                            fathom::carve_select(sel_base, h_q, n), s);
+  uint8_t* staging = static_cast<uint8_t*>(workspace) + staging_offset(h_q, n, k);
+  st = run_scan(dev, residency, q, depth, union_depth, h_q, h_kv, n, d, scores, ld, staging, s);
+  if (st) return st;
+  hipError_t e = fathom::launch_select(scores, ld, h_q, n, k, topk_idx, topk_score,
+                                       fathom::carve_select(sel_base, h_q, n, k), s);
   if (e != hipSuccess) return hip_fail(e, "select launch");
   return ok();
 }

@@ -11,24 +11,35 @@ constexpr int kPlanes = 4;        // 4-bit codes
 constexpr int kMaxD = 256;        // channels supported (one wave covers 64, 4 per lane)
 constexpr int kMaxG = 16;         // query heads per KV head
 
-// Byte geometry of one (KV head, channel) record.
+constexpr int kUnitBlocks = 8;    // blocks per interleave unit (1024 keys)
+constexpr int kUnitHead = 144;    // head bytes per unit: 16 B scales + 128 B plane-0 bits
+
+// Byte geometry of one (KV head, channel) record:
+//   head [0, H): per 1024-key unit u, at 144u: 8 fp16 scales (16 B) then the
+//                unit's plane-0 bits (128 B);
+//   plane p in 1..3 at H + (p-1) P, one bit per key (key j: bit j%8 of byte j/8).
+// A prefix of t >= 1 planes is the single run [0, H + (t-1) P).
 struct Layout {
   int64_t n;     // keys
   int64_t nb;    // 128-key blocks
-  int64_t S;     // scale section bytes (multiple of 16)
-  int64_t P;     // bytes per plane (16 per block)
-  int64_t R;     // record bytes = S + 4P
+  int64_t U;     // 1024-key units
+  int64_t H;     // head bytes = 144 U
+  int64_t P;     // bytes of plane 1, 2 or 3 = 128 U
+  int64_t R;     // record bytes = H + 3P
 };
 
 inline Layout make_layout(int64_t n) {
   Layout L;
   L.n = n;
   L.nb = (n + kBlock - 1) / kBlock;
-  L.S = ((2 * L.nb + 15) / 16) * 16;
-  L.P = 16 * L.nb;
-  L.R = L.S + kPlanes * L.P;
+  L.U = (L.nb + kUnitBlocks - 1) / kUnitBlocks;
+  L.H = kUnitHead * L.U;
+  L.P = 16 * kUnitBlocks * L.U;
+  L.R = L.H + (kPlanes - 1) * L.P;
   return L;
 }
+
+inline int64_t prefix_bytes(const Layout& L, int t) { return t <= 0 ? 0 : L.H + (t - 1) * L.P; }
 
 // ---- launchers (each returns hipSuccess or the launch error) ----
 hipError_t launch_pack(const float* k, int h_kv, const Layout& L, int d, uint8_t* rec,
@@ -36,20 +47,29 @@ hipError_t launch_pack(const float* k, int h_kv, const Layout& L, int d, uint8_t
 hipError_t launch_allocate(const float* q, const float* sigma2, int h_kv, int g, int d,
                            int mode, int budget, uint8_t* depth, uint8_t* uni,
                            uint32_t* status, hipStream_t s);
-hipError_t launch_scan(const uint8_t* rec, const float* q, const uint8_t* depth,
+// Scores of every key from device memory (host = false) or read in place from
+// pinned host memory (host = true, larger tiles for long contiguous runs).
+hipError_t launch_scan(const uint8_t* rec, bool host, const float* q, const uint8_t* depth,
                        const uint8_t* uni, int h_kv, int g, const Layout& L, int d,
                        float* scores, int64_t ld, hipStream_t s);
+// Host-resident records: gather the union prefix runs into `staging` (an HBM
+// mirror of the records, h_kv * d * R bytes) and scan them there, the copy of
+// one KV head overlapped with the scan of the previous.
+hipError_t launch_scan_staged(const uint8_t* host, uint8_t* staging, const float* q,
+                              const uint8_t* depth, const uint8_t* uni, int h_kv, int g,
+                              const Layout& L, int d, float* scores, int64_t ld, hipStream_t s);
 
 // Top-k selection over scores [h_q][ld], first n entries per row.
 struct SelectWorkspace {
-  uint32_t* hist;     // [h_q][2048]
-  uint32_t* state;    // [h_q][4]: prefix, need, -, -
-  uint32_t* counts;   // [h_q][nchunks][2]: (greater, equal) per chunk
+  uint32_t* hist;     // [h_q][2048] histogram of the top 11 key bits
+  uint32_t* state;    // [h_q][4]: threshold bin, keys above it, overflow flag, -
+  uint32_t* counts;   // [h_q][nchunks] kept keys per 4096-key chunk
+  uint64_t* kept;     // [h_q][nchunks][512] (key, index) at or above the threshold bin
   int64_t nchunks;
 };
 int64_t select_chunks(int64_t n);
-size_t select_workspace_bytes(int h_q, int64_t n);
-SelectWorkspace carve_select(void* base, int h_q, int64_t n);
+size_t select_workspace_bytes(int h_q, int64_t n, int k);
+SelectWorkspace carve_select(void* base, int h_q, int64_t n, int k);
 hipError_t launch_select(const float* scores, int64_t ld, int h_q, int64_t n, int k,
                          int32_t* idx, float* val, const SelectWorkspace& ws, hipStream_t s);
 

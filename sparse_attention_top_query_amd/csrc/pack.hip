@@ -10,7 +10,9 @@
 // c walks the block's 128 keys twice (max, then codes): both passes read
 // k[j][c] for consecutive c across the wave, i.e. coalesced rows of the
 // token-major K; the second pass hits L2.  Each thread then writes 16 bytes
-// per plane (the block's 128 bits) and its 2-byte scale.
+// per plane (the block's 128 bits) and its 2-byte scale.  Record layout: the
+// scale and plane-0 bits of a block sit in its 1024-key unit's 144-byte head
+// slot (16 B of scales, then 128 B of plane-0 bits); planes 1-3 follow the head.
 #include <hip/hip_fp16.h>
 
 #include "fathom_internal.h"
@@ -19,7 +21,7 @@ namespace fathom {
 namespace {
 
 __global__ __launch_bounds__(256) void pack_kernel(const float* __restrict__ k, int64_t n, int d,
-                                                   int64_t nb, int64_t S, int64_t P, int64_t R,
+                                                   int64_t nb, int64_t U, int64_t H, int64_t P, int64_t R,
                                                    uint8_t* __restrict__ rec,
                                                    uint32_t* __restrict__ status) {
   const int c = threadIdx.x;
@@ -66,13 +68,22 @@ __global__ __launch_bounds__(256) void pack_kernel(const float* __restrict__ k, 
   }
 
   uint8_t* r = rec + (g * d + c) * R;
-  reinterpret_cast<__half*>(r)[b] = dh;
-  if (b == nb - 1) {
-    for (int64_t x = 2 * nb; x < S; ++x) r[x] = 0;  // zero the scale padding
-  }
+  uint8_t* unit = r + kUnitHead * (b / kUnitBlocks);
+  reinterpret_cast<__half*>(unit)[b % kUnitBlocks] = dh;
+  *reinterpret_cast<uint4*>(unit + 16 + 16 * (b % kUnitBlocks)) = make_uint4(w[0][0], w[0][1], w[0][2], w[0][3]);
 #pragma unroll
-  for (int p = 0; p < kPlanes; ++p)
-    *reinterpret_cast<uint4*>(r + S + p * P + b * 16) = make_uint4(w[p][0], w[p][1], w[p][2], w[p][3]);
+  for (int p = 1; p < kPlanes; ++p)
+    *reinterpret_cast<uint4*>(r + H + (p - 1) * P + b * 16) = make_uint4(w[p][0], w[p][1], w[p][2], w[p][3]);
+  if (b == nb - 1) {
+    // zero the blocks of the last unit that lie past n
+    for (int64_t bb = nb; bb < U * kUnitBlocks; ++bb) {
+      uint8_t* ub = r + kUnitHead * (bb / kUnitBlocks);
+      reinterpret_cast<__half*>(ub)[bb % kUnitBlocks] = __float2half_rn(0.0f);
+      *reinterpret_cast<uint4*>(ub + 16 + 16 * (bb % kUnitBlocks)) = make_uint4(0u, 0u, 0u, 0u);
+      for (int p = 1; p < kPlanes; ++p)
+        *reinterpret_cast<uint4*>(r + H + (p - 1) * P + bb * 16) = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
 }
 
 __global__ void clear_word(uint32_t* p) { *p = 0u; }
@@ -89,7 +100,7 @@ hipError_t launch_pack(const float* k, int h_kv, const Layout& L, int d, uint8_t
   if (L.nb == 0) return hipSuccess;
   const int threads = ((d + 63) / 64) * 64;
   dim3 grid((unsigned)L.nb, (unsigned)h_kv);
-  pack_kernel<<<grid, threads, 0, s>>>(k, L.n, d, L.nb, L.S, L.P, L.R, rec, status);
+  pack_kernel<<<grid, threads, 0, s>>>(k, L.n, d, L.nb, L.U, L.H, L.P, L.R, rec, status);
   return hipGetLastError();
 }
 

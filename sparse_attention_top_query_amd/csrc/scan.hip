@@ -1,4 +1,4 @@
-// Scan kernel: reconstruct every key from its budgeted plane prefixes and
+// Scan kernels: reconstruct every key from its budgeted plane prefixes and
 // accumulate q . k_hat for the query heads of one KV head.
 //
 // ai-feeds digest, Method / key modules 4-5: the scan reads only the planes
@@ -6,208 +6,232 @@
 // (the paper's Sec 3.5 rule; its formula is not in the text, the reading here
 // is the midpoint of the prefix's cell of the t-bit mid-rise quantizer).
 // Fathom abstract: the prefix of t planes is exactly the channel's t-bit
-// quantizer, so k_hat_t = Delta 2^(4-t) (r_t + 1/2) with
-// r_t = (code >> (4-t)) - 2^(t-1), a signed integer of t bits.
+// quantizer, so with r_t = (code >> (4-t)) - 2^(t-1), a signed t-bit integer,
+//   q * k_hat_t = q Delta 2^(4-t) (r_t + 1/2) = [q 2^(3-t) Delta] * (2 r_t + 1).
+// The bracket is one fp32 rounding, the odd integer 2 r_t + 1 is exact, so every
+// term is the centered product q k_hat up to one rounding and the fp32 sum stays
+// within about (m + 1) 2^-24 sum_c |q_c k_hat_c| for m channels.
 //
-// Work decomposition (one workgroup = 4 wavefronts = 2048 keys of one KV head):
-//  1. The union depths of the KV head give the list of channels to read; every
-//     query head of the group is scored from the one read of the longest prefix.
-//  2. Staging, channel group by channel group (at most 64 plane chunks, 16 KB):
-//     the tile's plane bytes (256 contiguous bytes per channel-plane, 16 per
-//     128-key block) and fp16 scales are loaded into registers with 16-byte
-//     loads, all issued before any LDS write so many requests are in flight,
-//     then stored to LDS.  The same code reads HBM or, for host-resident
-//     records, pinned host memory over the host link, where contiguous runs of
-//     >= 256 bytes are what keeps the link near its peak.
-//  3. Compute: lane = key.  A 64-key plane word is wave-uniform, so it lives in
-//     an SGPR pair and every lane takes its own bit from it.  The signed prefix
-//     integer is built MSB first: r_1 = b_0 - 1, r_{t+1} = 2 r_t + b_t, which
-//     yields every shorter prefix on the way, so heads reading fewer planes of
-//     the same channel reuse it.  Per head: s += c_h * float(r_t) with
-//     c_h = q_h * Delta * 2^(4-t) (one rounding), and the +1/2 term is summed
-//     per block into a wave-uniform bias c_h / 2.
-//     Error: |c r| <= 2 |c (r + 1/2)| for every integer r, so the fp32 sums stay
-//     within ~(3m + 3) 2^-24 sum_c |q_c k_hat_c| for m channels.
+// Work decomposition: one workgroup scores a tile of TB 128-key blocks of one KV
+// head for all of its G query heads; each wavefront owns 2 blocks (256 keys,
+// 4 sub-chunks of 64, lane = key).
+//  1. The union depths of the KV head list the channels to read; every query
+//     head of the group is scored from the one read of the longest prefix.
+//  2. Staging, channel group by channel group (about 64 channel-planes): the
+//     tile's slice of each channel's record head (its units' fp16 scales and
+//     plane-0 bits) and of planes 1..t-1 are loaded with 16-byte loads into
+//     registers -- all issued before any LDS write, and those of the next group
+//     while the current group is computed -- then stored to LDS, the most
+//     significant plane complemented.  The same code reads HBM, an HBM staging
+//     mirror, or pinned host memory over the host link; the tile size sets the
+//     contiguous run per channel-plane (16 B per block).
+//  3. Per (channel, block) the coefficients q_h 2^(3-t_h) Delta are formed once in
+//     LDS.  Per key, each lane reads its own plane words and builds the signed
+//     prefix MSB first: r_1 = -(complemented bit) = b_0 - 1, then
+//     r_{t+1} = 2 r_t + b_t, which yields every shorter prefix on the way for
+//     heads that read fewer planes; per head one fma with float(2 r_t + 1).
 #include <hip/hip_fp16.h>
+
+#include <algorithm>
 
 #include "fathom_internal.h"
 
 namespace fathom {
 namespace {
 
-#ifndef FATHOM_TILE_BLOCKS
-#define FATHOM_TILE_BLOCKS 16
-#endif
-constexpr int kTileBlocks = FATHOM_TILE_BLOCKS;   // 128-key blocks per tile
-#ifndef FATHOM_WAVE_BLOCKS
-#define FATHOM_WAVE_BLOCKS 4
-#endif
-constexpr int kWaveBlocks = FATHOM_WAVE_BLOCKS;   // blocks per wavefront
-constexpr int kThreads = 64 * kTileBlocks / kWaveBlocks;
-constexpr int kSub = kWaveBlocks * 2;          // 64-key sub-chunks per wavefront
-constexpr int kGroupChunks = 64;               // (entry, plane) chunks staged at once
-constexpr int kGroupEntries = 64;              // entries staged at once (scales)
-constexpr int kScalePieces = kTileBlocks * 2 / 16;   // 16-byte pieces of a tile's scales
-static_assert(kTileBlocks % 8 == 0 && kThreads >= kMaxD, "tile must hold whole 16-byte scale pieces and one thread per channel");
-constexpr int kMaxPieces = kGroupChunks * kTileBlocks + kGroupEntries * kScalePieces;
-constexpr int kPiecesPerThread = (kMaxPieces + kThreads - 1) / kThreads;
+constexpr int kGroupChunks = 64;               // channel-planes per staging group (+3 slack)
+constexpr int kSlackChunks = kPlanes - 1;      // an entry starting in a group ends in it
+constexpr int kStageChunks = kGroupChunks + kSlackChunks;
+constexpr int kStageEntries = kStageChunks;    // entries have >= 1 chunk
 constexpr int kMaxChunks = kPlanes * kMaxD;
+constexpr int kWaveBlocks = 2;                 // 128-key blocks per wavefront
+constexpr int kSub = 2 * kWaveBlocks;          // 64-key sub-chunks per wavefront
 
-template <int G>
+template <int G, int TB>
+struct Cfg {
+  static constexpr int threads = 64 * TB / kWaveBlocks;
+  static constexpr int units = TB / kUnitBlocks;      // 1024-key record units per tile
+  static constexpr int slots = TB + units;            // 16-byte pieces per chunk slot
+  static constexpr int ppt = (kStageChunks * slots + threads - 1) / threads;
+  static_assert(threads >= kMaxD && threads <= 1024, "one thread per channel in the list build");
+  static_assert(TB % kUnitBlocks == 0, "tiles hold whole 1024-key units");
+};
+
+template <int G, int TB>
 struct ScanSmem {
-  uint4 planes[kGroupChunks][kTileBlocks];     // staged plane bits (16 KB)
-  uint4 scales[kGroupEntries][kScalePieces];   // staged fp16 scales
-  float ent_q[kMaxD][G];                       // q of each query head
-  uint8_t ent_th[kMaxD][G];                    // depth of each query head
-  uint16_t ent_base[kMaxD + 1];                // first chunk of entry e (prefix sum)
-  uint8_t ent_c[kMaxD];                        // channel of list entry e
-  uint8_t ent_tb[kMaxD];                       // union depth of entry e
-  uint16_t grp[kMaxD + 1];                     // first entry of each channel group
+  uint4 planes[kStageChunks][TB];                  // staged plane bits (plane 0 complemented)
+  uint4 scales[kStageEntries][TB / kUnitBlocks];   // staged fp16 scales per entry of the group
+  float coef[kStageEntries][TB][G];                // q_h 2^(3-t_h) Delta_b per entry, block, head
+  float ent_q[kMaxD][G];                           // q_h 2^(3-t_h) of each list entry
+  uint64_t ent_word[kMaxD];                        // union depth | used depths | head depths
+  uint16_t ent_base[kMaxD + 1];                    // first chunk of entry e (prefix sum)
+  uint8_t ent_c[kMaxD];                            // channel of list entry e
+  uint16_t grp[kMaxChunks / kGroupChunks + 2];     // first entry of each staging group
   uint8_t chunk_e[kMaxChunks];
   uint8_t chunk_p[kMaxChunks];
-  int wsum[2][kThreads / 64];
+  int wsum[2][16];
   int n_grp;
 };
 
-__device__ __forceinline__ bool lane_bit(uint64_t m) { return __builtin_amdgcn_inverse_ballot_w64(m); }
+struct ScanArgs {
+  const uint8_t* rec;        // records, device-visible
+  const float* q;
+  const uint8_t* depth;
+  const uint8_t* uni;
+  int64_t n, nb, H, P, R;
+  int d;
+  float* scores;
+  int64_t ld;
+};
 
-template <int G>
-__global__ __launch_bounds__(kThreads) void scan_kernel(const uint8_t* __restrict__ rec,
-                                                        const float* __restrict__ q,
-                                                        const uint8_t* __restrict__ depth,
-                                                        const uint8_t* __restrict__ uni, int64_t n,
-                                                        int64_t nb, int64_t S, int64_t P, int64_t R,
-                                                        int d, float* __restrict__ scores,
-                                                        int64_t ld) {
-  __shared__ ScanSmem<G> sm;
+// Entry word: bits 0-2 union depth, bits 3-6 depths in use (bit 2+t: some head
+// reads exactly t planes), then 3 bits of depth per head from bit 8.
+__device__ __forceinline__ int word_tb(uint64_t w) { return (int)(w & 7); }
+__device__ __forceinline__ int word_th(uint64_t w, int h) { return (int)((w >> (8 + 3 * h)) & 7); }
+
+// Scores of tile `tile` (TB blocks) of KV head g, all its query heads.
+template <int G, int TB>
+__device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t tile, ScanSmem<G, TB>& sm) {
+  using C = Cfg<G, TB>;
+  constexpr int SLOTS = C::slots;
+  constexpr int NT = C::threads;
+  constexpr int PPT = C::ppt;
+  static_assert(8 + 3 * G <= 64, "head depths must fit the entry word");
+  const uint8_t* __restrict__ rec = a.rec;
+  const int64_t nb = a.nb, H = a.H, P = a.P, R = a.R;
+  const int d = a.d;
 
   const int tid = threadIdx.x;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int64_t g = blockIdx.y;
-  const int64_t blk0 = (int64_t)blockIdx.x * kTileBlocks;
-  const int nvalid = (int)min<int64_t>(kTileBlocks, nb - blk0);
+  const int64_t blk0 = tile * TB;
+  const int nvalid = (int)min<int64_t>(TB, nb - blk0);
 
-  // ---- 1. list of union channels, in channel order ----
-  const int c = tid;
-  const int u = (c < d) ? (int)uni[g * d + c] : 0;
-  const int act = u > 0;
-  int a_inc = act, t_inc = u;
+  // ---- 1. list of union channels, in channel order, and staging groups ----
+  {
+    const int c = tid;
+    const int u = (c < d) ? (int)a.uni[g * d + c] : 0;
+    const int act = u > 0;
+    int a_inc = act, t_inc = u;
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int xa = __shfl_up(a_inc, off, 64);
-    const int xt = __shfl_up(t_inc, off, 64);
-    if (lane >= off) {
-      a_inc += xa;
-      t_inc += xt;
-    }
-  }
-  if (lane == 63) {
-    sm.wsum[0][wv] = a_inc;
-    sm.wsum[1][wv] = t_inc;
-  }
-  __syncthreads();
-  int a_off = 0, t_off = 0, n_ent = 0, n_chunk = 0;
-#pragma unroll
-  for (int x = 0; x < kThreads / 64; ++x) {
-    if (x < wv) {
-      a_off += sm.wsum[0][x];
-      t_off += sm.wsum[1][x];
-    }
-    n_ent += sm.wsum[0][x];
-    n_chunk += sm.wsum[1][x];
-  }
-  if (act) {
-    const int e = a_off + a_inc - 1;
-    const int base = t_off + t_inc - u;
-    sm.ent_c[e] = (uint8_t)c;
-    sm.ent_tb[e] = (uint8_t)u;
-    sm.ent_base[e] = (uint16_t)base;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const int64_t row = (g * G + h) * d + c;
-      sm.ent_th[e][h] = depth[row];
-      sm.ent_q[e][h] = q[row];
-    }
-    for (int p = 0; p < u; ++p) {
-      sm.chunk_e[base + p] = (uint8_t)e;
-      sm.chunk_p[base + p] = (uint8_t)p;
-    }
-  }
-  if (tid == 0) sm.ent_base[n_ent] = (uint16_t)n_chunk;
-  __syncthreads();
-  if (tid == 0) {
-    // channel groups: consecutive entries with at most kGroupChunks chunks and
-    // kGroupEntries entries each (an entry has at most 4 chunks)
-    int ng = 0, e0 = 0;
-    sm.grp[0] = 0;
-    for (int e = 0; e < n_ent; ++e) {
-      if (sm.ent_base[e + 1] - sm.ent_base[e0] > kGroupChunks || e + 1 - e0 > kGroupEntries) {
-        sm.grp[++ng] = (uint16_t)e;
-        e0 = e;
+    for (int off = 1; off < 64; off <<= 1) {
+      const int xa = __shfl_up(a_inc, off, 64);
+      const int xt = __shfl_up(t_inc, off, 64);
+      if (lane >= off) {
+        a_inc += xa;
+        t_inc += xt;
       }
     }
-    if (n_ent > 0) sm.grp[++ng] = (uint16_t)n_ent;
-    sm.n_grp = ng;
+    if (lane == 63) {
+      sm.wsum[0][wv] = a_inc;
+      sm.wsum[1][wv] = t_inc;
+    }
+    __syncthreads();
+    int a_off = 0, t_off = 0, n_ent = 0;
+#pragma unroll
+    for (int x = 0; x < NT / 64; ++x) {
+      if (x < wv) {
+        a_off += sm.wsum[0][x];
+        t_off += sm.wsum[1][x];
+      }
+      n_ent += sm.wsum[0][x];
+    }
+    const int e = a_off + a_inc - 1;
+    const int base = t_off + t_inc - u;
+    if (act) {
+      uint64_t word = (uint64_t)u;
+      for (int h = 0; h < G; ++h) {
+        const int64_t row = (g * G + h) * d + c;
+        const int th = a.depth[row];
+        if (th > 0) word |= (uint64_t)1 << (2 + th);
+        word |= (uint64_t)th << (8 + 3 * h);
+        sm.ent_q[e][h] = ldexpf(a.q[row], 3 - th);   // exact power-of-two scaling
+      }
+      sm.ent_word[e] = word;
+      sm.ent_c[e] = (uint8_t)c;
+      sm.ent_base[e] = (uint16_t)base;
+      if (e == n_ent - 1) {
+        sm.ent_base[n_ent] = (uint16_t)(base + u);
+        // an entry joins the group holding its first chunk; first chunks are at
+        // most 4 apart, so groups 0 .. base/64 are all non-empty
+        sm.n_grp = base / kGroupChunks + 1;
+        sm.grp[base / kGroupChunks + 1] = (uint16_t)n_ent;
+      }
+      for (int p = 0; p < u; ++p) {
+        sm.chunk_e[base + p] = (uint8_t)e;
+        sm.chunk_p[base + p] = (uint8_t)p;
+      }
+    }
+    if (tid == 0 && n_ent == 0) sm.n_grp = 0;
+    __syncthreads();
+    if (act) {
+      const int gi = base / kGroupChunks;
+      if (e == 0 || sm.ent_base[e - 1] / kGroupChunks != gi) sm.grp[gi] = (uint16_t)e;
+    }
+    __syncthreads();
   }
-  __syncthreads();
 
   float acc[kSub][G];
-  float bias[kWaveBlocks][G];
 #pragma unroll
   for (int s = 0; s < kSub; ++s)
 #pragma unroll
     for (int h = 0; h < G; ++h) acc[s][h] = 0.0f;
-#pragma unroll
-  for (int x = 0; x < kWaveBlocks; ++x)
-#pragma unroll
-    for (int h = 0; h < G; ++h) bias[x][h] = 0.0f;
 
   const uint8_t* recg = rec + g * d * R;
+  const int64_t unit0 = blk0 / kUnitBlocks;
   const int n_grp = sm.n_grp;
 
-  // ---- 2. staging, software-pipelined: the loads of channel group gi+1 are in
-  // flight (in registers) while group gi is computed from LDS ----
-  uint4 v[kPiecesPerThread];
+  // ---- 2. staging.  Piece i of a group is slot i % SLOTS of chunk i / SLOTS.  A
+  // plane-0 chunk walks the tile's head slice in memory order (per unit: 1 scale
+  // piece, then 8 plane-0 pieces); a chunk of plane p >= 1 uses its first TB slots.
+  uint4 v[PPT];
   auto issue = [&](int gi) {
-    const int e_lo = sm.grp[gi], e_hi = sm.grp[gi + 1];
-    const int ch_lo = sm.ent_base[e_lo];
-    const int n_plane_pieces = (sm.ent_base[e_hi] - ch_lo) * kTileBlocks;
-    const int total = n_plane_pieces + (e_hi - e_lo) * kScalePieces;
+    const int ch_lo = sm.ent_base[sm.grp[gi]];
+    const int n_pieces = (sm.ent_base[sm.grp[gi + 1]] - ch_lo) * SLOTS;
 #pragma unroll
-    for (int r = 0; r < kPiecesPerThread; ++r) {
-      const int i = tid + r * kThreads;
+    for (int r = 0; r < PPT; ++r) {
+      const int i = tid + r * NT;
       const uint4* src = nullptr;
-      if (i < n_plane_pieces) {
-        const int ch = ch_lo + i / kTileBlocks;
-        const int b = i % kTileBlocks;
-        if (b < nvalid) {
-          const int e = sm.chunk_e[ch];
-          src = reinterpret_cast<const uint4*>(recg + (int64_t)sm.ent_c[e] * R + S +
-                                               sm.chunk_p[ch] * P + (blk0 + b) * 16);
+      if (i < n_pieces) {
+        const int ch = ch_lo + i / SLOTS;
+        const int k = i % SLOTS;
+        const int p = sm.chunk_p[ch];
+        const uint8_t* base = recg + (int64_t)sm.ent_c[sm.chunk_e[ch]] * R;
+        if (p == 0) {
+          const int un = k / (kUnitBlocks + 1);
+          const int w = k % (kUnitBlocks + 1);
+          if (un * kUnitBlocks + (w == 0 ? 0 : w - 1) < nvalid)
+            src = reinterpret_cast<const uint4*>(base + kUnitHead * (unit0 + un) + 16 * w);
+        } else if (k < nvalid) {   // also skips the unused slots k >= TB
+          src = reinterpret_cast<const uint4*>(base + H + (p - 1) * P + (blk0 + k) * 16);
         }
-      } else if (i < total) {
-        const int j = i - n_plane_pieces;
-        const int e = e_lo + j / kScalePieces;
-        const int piece = j % kScalePieces;          // blocks 8*piece .. 8*piece+7
-        if (piece * 8 < nvalid)
-          src = reinterpret_cast<const uint4*>(recg + (int64_t)sm.ent_c[e] * R + blk0 * 2 + piece * 16);
       }
       v[r] = src ? *src : make_uint4(0u, 0u, 0u, 0u);
     }
   };
   auto commit = [&](int gi) {
-    const int e_lo = sm.grp[gi], e_hi = sm.grp[gi + 1];
+    const int e_lo = sm.grp[gi];
     const int ch_lo = sm.ent_base[e_lo];
-    const int n_plane_pieces = (sm.ent_base[e_hi] - ch_lo) * kTileBlocks;
-    const int total = n_plane_pieces + (e_hi - e_lo) * kScalePieces;
-    uint4* const dst_planes = &sm.planes[0][0];
-    uint4* const dst_scales = &sm.scales[0][0];
+    const int n_pieces = (sm.ent_base[sm.grp[gi + 1]] - ch_lo) * SLOTS;
 #pragma unroll
-    for (int r = 0; r < kPiecesPerThread; ++r) {
-      const int i = tid + r * kThreads;
-      if (i < n_plane_pieces) dst_planes[i] = v[r];
-      else if (i < total) dst_scales[i - n_plane_pieces] = v[r];
+    for (int r = 0; r < PPT; ++r) {
+      const int i = tid + r * NT;
+      if (i < n_pieces) {
+        const int chl = i / SLOTS;
+        const int k = i % SLOTS;
+        if (sm.chunk_p[ch_lo + chl] == 0) {
+          const int un = k / (kUnitBlocks + 1);
+          const int w = k % (kUnitBlocks + 1);
+          if (w == 0) {
+            sm.scales[sm.chunk_e[ch_lo + chl] - e_lo][un] = v[r];
+          } else {
+            const uint4 x = v[r];
+            sm.planes[chl][un * kUnitBlocks + w - 1] = make_uint4(~x.x, ~x.y, ~x.z, ~x.w);
+          }
+        } else if (k < TB) {
+          sm.planes[chl][k] = v[r];
+        }
+      }
     }
   };
 
@@ -217,49 +241,96 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const uint8_t* __restric
     const int ch_lo = sm.ent_base[e_lo];
     commit(gi);
     __syncthreads();
+    // coefficients q_h 2^(3-t_h) Delta_b for every entry, block and head of the group
+    for (int i = tid; i < (e_hi - e_lo) * TB * G; i += NT) {
+      const int el = i / (TB * G);
+      const int b = (i / G) % TB;
+      const int h = i % G;
+      const __half dl = reinterpret_cast<const __half*>(&sm.scales[el][0])[b];
+      sm.coef[el][b][h] = sm.ent_q[e_lo + el][h] * __half2float(dl);
+    }
+    __syncthreads();
     if (gi + 1 < n_grp) issue(gi + 1);
 
-    // ---- 3. reconstruct and accumulate; wave wv owns kWaveBlocks blocks from kWaveBlocks*wv ----
+    // ---- 3. reconstruct and accumulate; wave wv owns blocks 2wv and 2wv+1 ----
     if (kWaveBlocks * wv < nvalid) {
+      const int pos = lane & 31;
       for (int e = e_lo; e < e_hi; ++e) {
-        const int tb = sm.ent_tb[e];
+        const uint64_t ew = sm.ent_word[e];
+        uint64_t word = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)ew);
+        if (8 + 3 * G > 32) word |= (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(ew >> 32)) << 32;
+        const int tb = word_tb(word);
         const int cb = sm.ent_base[e] - ch_lo;
-        const __half* sc = reinterpret_cast<const __half*>(&sm.scales[e - e_lo][0]);
-        int th[G];
-        float coef[kWaveBlocks][G];
-        int used = 0;
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          th[h] = sm.ent_th[e][h];
-          used |= 1 << th[h];
-          const float qs = ldexpf(sm.ent_q[e][h], kPlanes - th[h]);   // exact power-of-two scaling
-#pragma unroll
-          for (int x = 0; x < kWaveBlocks; ++x) {
-            coef[x][h] = qs * __half2float(sc[kWaveBlocks * wv + x]);
-            if (th[h] > 0) bias[x][h] += 0.5f * coef[x][h];
-          }
-        }
-        // plane p of sub-chunk s: 64-bit word pw[p * 2 * kTileBlocks + s]
-        const uint64_t* pw = reinterpret_cast<const uint64_t*>(&sm.planes[cb][kWaveBlocks * wv]);
+        // lane's plane word of sub-chunk s: block 2wv + s/2, u32 word 2(s%2) + lane/32
+        const uint32_t* pw = reinterpret_cast<const uint32_t*>(&sm.planes[cb][kWaveBlocks * wv]) + (lane >> 5);
+        int r1[kSub], r2[kSub], r3[kSub], r4[kSub];
 #pragma unroll
         for (int s = 0; s < kSub; ++s) {
-          const int r1 = lane_bit(pw[s]) ? 0 : -1;
-          int r2 = 0, r3 = 0, r4 = 0;
-          if (tb >= 2) r2 = 2 * r1 + (int)lane_bit(pw[2 * kTileBlocks + s]);
-          if (tb >= 3) r3 = 2 * r2 + (int)lane_bit(pw[4 * kTileBlocks + s]);
-          if (tb >= 4) r4 = 2 * r3 + (int)lane_bit(pw[6 * kTileBlocks + s]);
-          float f1 = 0.f, f2 = 0.f, f3 = 0.f, f4 = 0.f;
-          if (used & 2) f1 = (float)r1;
-          if (used & 4) f2 = (float)r2;
-          if (used & 8) f3 = (float)r3;
-          if (used & 16) f4 = (float)r4;
+          const int off = (s >> 1) * 4 + (s & 1) * 2;       // u32 offset of the sub-chunk
+          r1[s] = __builtin_amdgcn_sbfe((int)pw[off], pos, 1);   // complemented MSB: b0 - 1
+        }
+        if (tb >= 2) {
 #pragma unroll
-          for (int h = 0; h < G; ++h) {
-            const float cf = coef[s >> 1][h];
-            if (th[h] == 1) acc[s][h] = fmaf(cf, f1, acc[s][h]);
-            else if (th[h] == 2) acc[s][h] = fmaf(cf, f2, acc[s][h]);
-            else if (th[h] == 3) acc[s][h] = fmaf(cf, f3, acc[s][h]);
-            else if (th[h] == 4) acc[s][h] = fmaf(cf, f4, acc[s][h]);
+          for (int s = 0; s < kSub; ++s) {
+            const int off = (s >> 1) * 4 + (s & 1) * 2;
+            r2[s] = 2 * r1[s] + (int)__builtin_amdgcn_ubfe(pw[TB * 4 + off], pos, 1);
+          }
+        }
+        if (tb >= 3) {
+#pragma unroll
+          for (int s = 0; s < kSub; ++s) {
+            const int off = (s >> 1) * 4 + (s & 1) * 2;
+            r3[s] = 2 * r2[s] + (int)__builtin_amdgcn_ubfe(pw[2 * TB * 4 + off], pos, 1);
+          }
+        }
+        if (tb >= 4) {
+#pragma unroll
+          for (int s = 0; s < kSub; ++s) {
+            const int off = (s >> 1) * 4 + (s & 1) * 2;
+            r4[s] = 2 * r3[s] + (int)__builtin_amdgcn_ubfe(pw[3 * TB * 4 + off], pos, 1);
+          }
+        }
+        // odd integers 2 r_t + 1 as floats, for the depths some head uses
+        float f1[kSub], f2[kSub], f3[kSub], f4[kSub];
+        if (word & 8) {
+#pragma unroll
+          for (int s = 0; s < kSub; ++s) f1[s] = (float)(2 * r1[s] + 1);
+        }
+        if (word & 16) {
+#pragma unroll
+          for (int s = 0; s < kSub; ++s) f2[s] = (float)(2 * r2[s] + 1);
+        }
+        if (word & 32) {
+#pragma unroll
+          for (int s = 0; s < kSub; ++s) f3[s] = (float)(2 * r3[s] + 1);
+        }
+        if (word & 64) {
+#pragma unroll
+          for (int s = 0; s < kSub; ++s) f4[s] = (float)(2 * r4[s] + 1);
+        }
+        const float* cf = &sm.coef[e - e_lo][kWaveBlocks * wv][0];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float c0 = cf[h], c1 = cf[G + h];
+          switch (word_th(word, h)) {
+            case 1:
+#pragma unroll
+              for (int s = 0; s < kSub; ++s) acc[s][h] = fmaf(s < 2 ? c0 : c1, f1[s], acc[s][h]);
+              break;
+            case 2:
+#pragma unroll
+              for (int s = 0; s < kSub; ++s) acc[s][h] = fmaf(s < 2 ? c0 : c1, f2[s], acc[s][h]);
+              break;
+            case 3:
+#pragma unroll
+              for (int s = 0; s < kSub; ++s) acc[s][h] = fmaf(s < 2 ? c0 : c1, f3[s], acc[s][h]);
+              break;
+            case 4:
+#pragma unroll
+              for (int s = 0; s < kSub; ++s) acc[s][h] = fmaf(s < 2 ? c0 : c1, f4[s], acc[s][h]);
+              break;
+            default:
+              break;
           }
         }
       }
@@ -271,34 +342,183 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const uint8_t* __restric
 #pragma unroll
   for (int s = 0; s < kSub; ++s) {
     const int64_t j = (blk0 + kWaveBlocks * wv + (s >> 1)) * kBlock + (s & 1) * 64 + lane;
-    if (j < n) {
+    if (j < a.n) {
 #pragma unroll
-      for (int h = 0; h < G; ++h) scores[(g * G + h) * ld + j] = acc[s][h] + bias[s >> 1][h];
+      for (int h = 0; h < G; ++h) a.scores[(g * G + h) * a.ld + j] = acc[s][h];
     }
   }
 }
 
+// Tile size per residency: device memory likes many small tiles (occupancy);
+// reading pinned host memory in place wants long contiguous runs per
+// channel-plane (>= 512 bytes keeps the host link near its streaming rate).
+constexpr int kTileDevice = 8;    // 1024 keys, 256 threads
 template <int G>
+struct HostTile {
+  static constexpr int TB = G <= 4 ? 32 : 16;   // LDS for the coefficients bounds it for large G
+};
+
+template <int G, int TB>
+__global__ __launch_bounds__((Cfg<G, TB>::threads)) void scan_kernel(ScanArgs a) {
+  __shared__ ScanSmem<G, TB> sm;
+  scan_tile<G, TB>(a, blockIdx.y, blockIdx.x, sm);
+}
+
+// ---------------------------------------------------------------------------
+// Host-resident records, staged: the scan's input is first gathered from
+// pinned host memory into an HBM mirror of the records with long contiguous
+// reads (each channel's prefix run of the union depth, split into 32 KB
+// pieces), which keeps the host link at its streaming rate.  Launch i copies
+// KV heads [i*hb, (i+1)*hb) while the same launch's other workgroups scan the
+// heads staged by launch i-1, so the copy of one head overlaps the compute of
+// the previous one; kernel boundaries order the copy before its scan.
+// ---------------------------------------------------------------------------
+
+constexpr int64_t kCopyPiece = 32768;   // bytes per copy workgroup
+
+inline int64_t copy_pieces_per_head(const Layout& L, int d) {
+  return (int64_t)d * ((L.R + kCopyPiece - 1) / kCopyPiece);
+}
+
+template <int G, int TB>
+__device__ __forceinline__ void copy_piece(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                           const uint8_t* __restrict__ uni, int64_t g, int d,
+                                           int64_t H, int64_t P, int64_t R, int64_t piece,
+                                           ScanSmem<G, TB>& sm) {
+  constexpr int NT = Cfg<G, TB>::threads;
+  constexpr int PER = (int)(kCopyPiece / 16 / NT);
+  const int tid = threadIdx.x;
+  const int wv = tid >> 6;
+  const int lane = tid & 63;
+  // pieces of channel c's run [0, H + (t-1) P), t = union depth
+  const int c = tid;
+  const int t = c < d ? (int)uni[g * d + c] : 0;
+  const int64_t bytes = t > 0 ? H + (int64_t)(t - 1) * P : 0;
+  const int np = (int)((bytes + kCopyPiece - 1) / kCopyPiece);
+  int inc = np;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int x = __shfl_up(inc, off, 64);
+    if (lane >= off) inc += x;
+  }
+  if (lane == 63) sm.wsum[0][wv] = inc;
+  if (tid == 0) sm.n_grp = -1;
+  __syncthreads();
+  int base = 0;
+  for (int x = 0; x < wv; ++x) base += sm.wsum[0][x];
+  const int first = base + inc - np;
+  if (np > 0 && piece >= first && piece < first + np) {
+    sm.n_grp = c;                                    // owner channel of this piece
+    sm.wsum[1][0] = (int)(piece - first);            // piece index within the run
+    sm.wsum[1][1] = (int)((bytes + 15) / 16);        // run length in 16-byte units
+  }
+  __syncthreads();
+  const int owner = sm.n_grp;
+  if (owner < 0) return;                             // past the last piece of this head
+  const int64_t u0 = (int64_t)sm.wsum[1][0] * (kCopyPiece / 16);
+  const int64_t units = sm.wsum[1][1];
+  const uint4* s4 = reinterpret_cast<const uint4*>(src + (g * d + owner) * R);
+  uint4* d4 = reinterpret_cast<uint4*>(dst + (g * d + owner) * R);
+  uint4 v[PER];
+#pragma unroll
+  for (int r = 0; r < PER; ++r) {
+    const int64_t i = u0 + (int64_t)r * NT + tid;
+    v[r] = i < units ? s4[i] : make_uint4(0u, 0u, 0u, 0u);
+  }
+#pragma unroll
+  for (int r = 0; r < PER; ++r) {
+    const int64_t i = u0 + (int64_t)r * NT + tid;
+    if (i < units) d4[i] = v[r];
+  }
+}
+
+template <int G, int TB>
+__global__ __launch_bounds__((Cfg<G, TB>::threads)) void stage_scan_kernel(
+    ScanArgs a, const uint8_t* __restrict__ host, int64_t copy_g0, int copy_heads, int64_t ncopy,
+    int64_t scan_g0, int scan_heads, int64_t tiles) {
+  __shared__ ScanSmem<G, TB> sm;
+  const int64_t b = blockIdx.x;
+  const int64_t scan_blocks = tiles * scan_heads;
+  if (b < scan_blocks) {
+    scan_tile<G, TB>(a, scan_g0 + b / tiles, b % tiles, sm);
+  } else {
+    const int64_t cb = b - scan_blocks;
+    if (cb < ncopy * copy_heads)
+      copy_piece<G, TB>(host, const_cast<uint8_t*>(a.rec), a.uni, copy_g0 + cb / ncopy, a.d, a.H, a.P,
+                        a.R, cb % ncopy, sm);
+  }
+}
+
+template <int G, int TB>
 hipError_t launch_g(const uint8_t* rec, const float* q, const uint8_t* depth, const uint8_t* uni,
                     int h_kv, const Layout& L, int d, float* scores, int64_t ld, hipStream_t s) {
-  dim3 grid((unsigned)((L.nb + kTileBlocks - 1) / kTileBlocks), (unsigned)h_kv);
-  scan_kernel<G><<<grid, kThreads, 0, s>>>(rec, q, depth, uni, L.n, L.nb, L.S, L.P, L.R, d,
-                                           scores, ld);
+  const ScanArgs a{rec, q, depth, uni, L.n, L.nb, L.H, L.P, L.R, d, scores, ld};
+  dim3 grid((unsigned)((L.nb + TB - 1) / TB), (unsigned)h_kv);
+  scan_kernel<G, TB><<<grid, Cfg<G, TB>::threads, 0, s>>>(a);
   return hipGetLastError();
+}
+
+template <int G>
+hipError_t launch_staged_g(const uint8_t* host, uint8_t* staging, const float* q, const uint8_t* depth,
+                           const uint8_t* uni, int h_kv, const Layout& L, int d, float* scores,
+                           int64_t ld, hipStream_t s) {
+  constexpr int TB = kTileDevice;
+  const ScanArgs a{staging, q, depth, uni, L.n, L.nb, L.H, L.P, L.R, d, scores, ld};
+  const int64_t tiles = (L.nb + TB - 1) / TB;
+  const int64_t ncopy = copy_pieces_per_head(L, d);
+  // heads per launch: about 64 MB of records per launch
+  const int64_t head_bytes = (int64_t)d * L.R;
+  const int hb = (int)std::max<int64_t>(
+      1, std::min<int64_t>(h_kv, (int64_t(64) << 20) / std::max<int64_t>(head_bytes, 1)));
+  const int steps = (h_kv + hb - 1) / hb;
+  for (int i = 0; i <= steps; ++i) {
+    const int64_t cg0 = (int64_t)i * hb;
+    const int ch = i < steps ? (int)std::min<int64_t>(hb, h_kv - cg0) : 0;
+    const int64_t sg0 = (int64_t)(i - 1) * hb;
+    const int sh = i > 0 ? (int)std::min<int64_t>(hb, h_kv - sg0) : 0;
+    const int64_t blocks = ncopy * ch + tiles * sh;
+    stage_scan_kernel<G, TB><<<(unsigned)blocks, Cfg<G, TB>::threads, 0, s>>>(a, host, cg0, ch, ncopy, sg0,
+                                                                               sh, tiles);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <int G>
+hipError_t launch_any(const uint8_t* rec, bool host, const float* q, const uint8_t* depth,
+                      const uint8_t* uni, int h_kv, const Layout& L, int d, float* scores, int64_t ld,
+                      hipStream_t s) {
+  if (host) return launch_g<G, HostTile<G>::TB>(rec, q, depth, uni, h_kv, L, d, scores, ld, s);
+  return launch_g<G, kTileDevice>(rec, q, depth, uni, h_kv, L, d, scores, ld, s);
 }
 
 }  // namespace
 
-hipError_t launch_scan(const uint8_t* rec, const float* q, const uint8_t* depth,
+hipError_t launch_scan(const uint8_t* rec, bool host, const float* q, const uint8_t* depth,
                        const uint8_t* uni, int h_kv, int g, const Layout& L, int d,
                        float* scores, int64_t ld, hipStream_t s) {
   if (L.nb == 0) return hipSuccess;
   switch (g) {
-    case 1: return launch_g<1>(rec, q, depth, uni, h_kv, L, d, scores, ld, s);
-    case 2: return launch_g<2>(rec, q, depth, uni, h_kv, L, d, scores, ld, s);
-    case 4: return launch_g<4>(rec, q, depth, uni, h_kv, L, d, scores, ld, s);
-    case 8: return launch_g<8>(rec, q, depth, uni, h_kv, L, d, scores, ld, s);
-    case 16: return launch_g<16>(rec, q, depth, uni, h_kv, L, d, scores, ld, s);
+    case 1: return launch_any<1>(rec, host, q, depth, uni, h_kv, L, d, scores, ld, s);
+    case 2: return launch_any<2>(rec, host, q, depth, uni, h_kv, L, d, scores, ld, s);
+    case 4: return launch_any<4>(rec, host, q, depth, uni, h_kv, L, d, scores, ld, s);
+    case 8: return launch_any<8>(rec, host, q, depth, uni, h_kv, L, d, scores, ld, s);
+    case 16: return launch_any<16>(rec, host, q, depth, uni, h_kv, L, d, scores, ld, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_scan_staged(const uint8_t* host, uint8_t* staging, const float* q, const uint8_t* depth,
+                              const uint8_t* uni, int h_kv, int g, const Layout& L, int d, float* scores,
+                              int64_t ld, hipStream_t s) {
+  if (L.nb == 0) return hipSuccess;
+  switch (g) {
+    case 1: return launch_staged_g<1>(host, staging, q, depth, uni, h_kv, L, d, scores, ld, s);
+    case 2: return launch_staged_g<2>(host, staging, q, depth, uni, h_kv, L, d, scores, ld, s);
+    case 4: return launch_staged_g<4>(host, staging, q, depth, uni, h_kv, L, d, scores, ld, s);
+    case 8: return launch_staged_g<8>(host, staging, q, depth, uni, h_kv, L, d, scores, ld, s);
+    case 16: return launch_staged_g<16>(host, staging, q, depth, uni, h_kv, L, d, scores, ld, s);
     default: return hipErrorInvalidValue;
   }
 }

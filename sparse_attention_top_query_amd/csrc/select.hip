@@ -2,13 +2,25 @@
 // equal scores, returned in ascending index order (ai-feeds digest, Method /
 // key module 5 and Output: the scan outputs top-k key indices per query).
 //
-// Radix select on order-preserving 32-bit keys, integer-only, LDS histograms:
-//   key(f) = f >= +0 ? bits | 0x80000000 : ~bits   (-0 folded onto +0)
-//   passes over digits [31:21], [20:10], [9:0] narrow the k-th largest key T and
-//   the number `need` of keys equal to T that still belong to the top k;
-//   a count pass gives every chunk its (> T, == T) counts, and the write pass
-//   places the selected keys of each chunk after those of earlier chunks, so the
-//   output is in index order and ties at T go to the lowest indices.
+// Scores are mapped to order-preserving 32-bit keys
+//   key(f) = f >= +0 ? bits | 0x80000000 : ~bits      (-0 folded onto +0)
+// and everything after that is integer work, with two passes over the scores:
+//   1. hist     LDS histogram of the top 12 key bits per head;
+//   2. find     per head, the bin b holding the k-th largest key and the number
+//               of keys above it;
+//   3. collect  every key in bin b or above is written, as (key, index), to its
+//               4096-key chunk's slot in index order (ballot ranks per
+//               wavefront, no atomics), with the slot's count;
+//   4. resolve  one workgroup per head concatenates the slots in chunk order in
+//               LDS -- all kept keys, in index order -- radix-selects the exact
+//               k-th key T among them (10 + 10 more bits) and how many keys equal
+//               to T still belong to the top k, and compacts in order: keys above
+//               T and the lowest-index keys equal to T.  No sorting is needed.
+// A head whose kept keys overflow a chunk slot or the LDS buffer takes an exact
+// in-order fallback in the resolve kernel: three radix passes over its whole row
+// find T, then one ordered pass writes the selection.
+#include <algorithm>
+
 #include "fathom_internal.h"
 
 namespace fathom {
@@ -16,8 +28,13 @@ namespace {
 
 constexpr int kSelThreads = 256;
 constexpr int kPerThread = 16;
-constexpr int kChunk = kSelThreads * kPerThread;   // keys per workgroup
-constexpr int kBins = 2048;
+constexpr int kChunk = kSelThreads * kPerThread;   // keys per hist/collect workgroup
+constexpr int kBins = 4096;                        // first digit: top 12 key bits
+constexpr int kDigit0 = 20;                        // shift of the first digit
+constexpr int kResolveThreads = 1024;
+constexpr int kSlot = 512;                         // kept keys per 4096-key chunk
+constexpr int kKeep = 16384;                       // kept keys per head resolved in LDS (128 KB)
+constexpr int kKeepPer = kKeep / kResolveThreads;
 
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t b = __float_as_uint(f);
@@ -25,46 +42,25 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-struct Digit {
-  int shift;       // position of this digit
-  int bits;        // width of this digit
-  int hi_shift;    // keys must match the prefix in bits [31:hi_shift]; 32 = no filter
-};
-
-__device__ __forceinline__ Digit digit_of(int pass) {
-  if (pass == 0) return {21, 11, 32};
-  if (pass == 1) return {10, 11, 21};
-  return {0, 10, 10};
-}
-
-__global__ __launch_bounds__(kSelThreads) void select_init(uint32_t* hist, uint32_t* state, int k) {
+// state per head: [0] bin b, [1] keys above bin b, [2] overflow flag, [3] unused
+__global__ __launch_bounds__(kSelThreads) void sel_init(uint32_t* hist, uint32_t* state) {
   const int h = blockIdx.x;
   for (int b = threadIdx.x; b < kBins; b += kSelThreads) hist[(int64_t)h * kBins + b] = 0u;
-  if (threadIdx.x == 0) {
-    state[h * 4 + 0] = 0u;               // prefix
-    state[h * 4 + 1] = (uint32_t)k;      // need
-  }
+  if (threadIdx.x < 4) state[h * 4 + threadIdx.x] = 0u;
 }
 
-__global__ __launch_bounds__(kSelThreads) void select_hist(const float* __restrict__ scores, int64_t ld,
-                                                           int64_t n, int pass,
-                                                           uint32_t* __restrict__ hist,
-                                                           const uint32_t* __restrict__ state) {
+__global__ __launch_bounds__(kSelThreads) void sel_hist(const float* __restrict__ scores, int64_t ld,
+                                                        int64_t n, uint32_t* __restrict__ hist) {
   __shared__ uint32_t lh[kBins];
   const int h = blockIdx.y;
-  const Digit dg = digit_of(pass);
   for (int b = threadIdx.x; b < kBins; b += kSelThreads) lh[b] = 0u;
   __syncthreads();
-  const uint32_t prefix = state[h * 4 + 0];
-  const uint32_t mask = (1u << dg.bits) - 1u;
   const float* row = scores + (int64_t)h * ld;
   const int64_t j0 = (int64_t)blockIdx.x * kChunk;
+#pragma unroll 4
   for (int i = 0; i < kPerThread; ++i) {
     const int64_t j = j0 + (int64_t)i * kSelThreads + threadIdx.x;
-    if (j < n) {
-      const uint32_t key = order_key(row[j]);
-      if (dg.hi_shift == 32 || (key >> dg.hi_shift) == prefix) atomicAdd(&lh[(key >> dg.shift) & mask], 1u);
-    }
+    if (j < n) atomicAdd(&lh[order_key(row[j]) >> kDigit0], 1u);
   }
   __syncthreads();
   for (int b = threadIdx.x; b < kBins; b += kSelThreads) {
@@ -73,84 +69,28 @@ __global__ __launch_bounds__(kSelThreads) void select_hist(const float* __restri
   }
 }
 
-// One workgroup per head: find the bin holding the need-th largest key, extend
-// the prefix by it, reduce `need` by the keys in higher bins, clear the histogram.
-__global__ __launch_bounds__(kSelThreads) void select_find(uint32_t* __restrict__ hist,
-                                                           uint32_t* __restrict__ state, int pass) {
-  constexpr int kPer = kBins / kSelThreads;   // 8 bins per thread
-  __shared__ uint32_t tot[kSelThreads];
-  const int h = blockIdx.x;
-  const Digit dg = digit_of(pass);
-  const int nbins = 1 << dg.bits;
-  uint32_t* hh = hist + (int64_t)h * kBins;
-  uint32_t v[kPer];
-  uint32_t mine = 0;
+// inclusive suffix sum over the workgroup's threads (thread t gets sum over t' >= t)
+template <int NT>
+__device__ __forceinline__ uint32_t block_suffix_inclusive(uint32_t v, uint32_t* wsum) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  uint32_t s = v;
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int b = threadIdx.x * kPer + i;
-    v[i] = b < nbins ? hh[b] : 0u;
-    mine += v[i];
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t x = __shfl_down(s, off, 64);
+    if (lane + off < 64) s += x;
   }
-  tot[threadIdx.x] = mine;
   __syncthreads();
-  // keys in bins above this thread's range
+  if (lane == 0) wsum[w] = s;
+  __syncthreads();
   uint32_t above = 0;
-  for (int t = threadIdx.x + 1; t < kSelThreads; ++t) above += tot[t];
-  const uint32_t need = state[h * 4 + 1];
-  const uint32_t prefix = state[h * 4 + 0];
-  __syncthreads();
-#pragma unroll
-  for (int i = kPer - 1; i >= 0; --i) {
-    const int b = threadIdx.x * kPer + i;
-    if (b < nbins && above < need && above + v[i] >= need) {
-      state[h * 4 + 0] = (prefix << dg.bits) | (uint32_t)b;
-      state[h * 4 + 1] = need - above;
-    }
-    above += v[i];
-  }
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) hh[threadIdx.x * kPer + i] = 0u;
+  for (int x = w + 1; x < NT / 64; ++x) above += wsum[x];
+  return s + above;
 }
 
-__device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t* red) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  uint32_t s = 0;
-#pragma unroll
-  for (int w = 0; w < kSelThreads / 64; ++w) s += red[w];
-  return s;
-}
-
-__global__ __launch_bounds__(kSelThreads) void select_count(const float* __restrict__ scores, int64_t ld,
-                                                            int64_t n, const uint32_t* __restrict__ state,
-                                                            uint32_t* __restrict__ counts, int64_t nchunks) {
-  __shared__ uint32_t red[kSelThreads / 64];
-  const int h = blockIdx.y;
-  const uint32_t T = state[h * 4 + 0];
-  const float* row = scores + (int64_t)h * ld;
-  const int64_t j0 = (int64_t)blockIdx.x * kChunk;
-  uint32_t gt = 0, eq = 0;
-  for (int i = 0; i < kPerThread; ++i) {
-    const int64_t j = j0 + (int64_t)i * kSelThreads + threadIdx.x;
-    if (j < n) {
-      const uint32_t key = order_key(row[j]);
-      gt += key > T;
-      eq += key == T;
-    }
-  }
-  gt = block_sum(gt, red);
-  eq = block_sum(eq, red);
-  if (threadIdx.x == 0) {
-    counts[((int64_t)h * nchunks + blockIdx.x) * 2 + 0] = gt;
-    counts[((int64_t)h * nchunks + blockIdx.x) * 2 + 1] = eq;
-  }
-}
-
-// exclusive scan of one value per thread over the workgroup (thread order)
-__device__ __forceinline__ uint32_t block_exclusive(uint32_t v, uint32_t* wsum) {
+// exclusive prefix sum over the workgroup's threads, in thread order; *total = sum
+template <int NT>
+__device__ __forceinline__ uint32_t block_exclusive(uint32_t v, uint32_t* wsum, uint32_t* total) {
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   uint32_t inc = v;
@@ -162,110 +102,295 @@ __device__ __forceinline__ uint32_t block_exclusive(uint32_t v, uint32_t* wsum) 
   __syncthreads();
   if (lane == 63) wsum[w] = inc;
   __syncthreads();
-  uint32_t base = 0;
-  for (int x = 0; x < w; ++x) base += wsum[x];
+  uint32_t base = 0, all = 0;
+  for (int x = 0; x < NT / 64; ++x) {
+    if (x < w) base += wsum[x];
+    all += wsum[x];
+  }
+  *total = all;
   return base + inc - v;
 }
 
-__global__ __launch_bounds__(kSelThreads) void select_write(const float* __restrict__ scores, int64_t ld,
-                                                            int64_t n, int k,
-                                                            const uint32_t* __restrict__ state,
-                                                            const uint32_t* __restrict__ counts,
-                                                            int64_t nchunks, int32_t* __restrict__ idx,
-                                                            float* __restrict__ val) {
-  __shared__ uint32_t red[kSelThreads / 64];
+// Bin of the k-th largest key: the bin b with (keys above b) < k <= (keys at or above b).
+__global__ __launch_bounds__(kSelThreads) void sel_find(const uint32_t* __restrict__ hist,
+                                                        uint32_t* __restrict__ state, int k) {
+  constexpr int kPer = kBins / kSelThreads;   // 16 bins per thread
   __shared__ uint32_t wsum[kSelThreads / 64];
-  const int h = blockIdx.y;
-  const int64_t chunk = blockIdx.x;
-  const uint32_t T = state[h * 4 + 0];
-  const uint32_t need = state[h * 4 + 1];
-  const uint32_t* cnt = counts + (int64_t)h * nchunks * 2;
-  uint32_t gsum = 0, esum = 0;
-  for (int64_t x = threadIdx.x; x < chunk; x += kSelThreads) {
-    gsum += cnt[2 * x];
-    esum += cnt[2 * x + 1];
+  const int h = blockIdx.x;
+  const uint32_t* hh = hist + (int64_t)h * kBins;
+  uint32_t v[kPer];
+  uint32_t mine = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    v[i] = hh[threadIdx.x * kPer + i];
+    mine += v[i];
   }
-  const uint32_t Gb = block_sum(gsum, red);
-  const uint32_t Eb = block_sum(esum, red);
+  uint32_t above = block_suffix_inclusive<kSelThreads>(mine, wsum) - mine;   // keys in higher bins
+#pragma unroll
+  for (int i = kPer - 1; i >= 0; --i) {
+    if (above < (uint32_t)k && above + v[i] >= (uint32_t)k) {
+      state[h * 4 + 0] = threadIdx.x * kPer + i;
+      state[h * 4 + 1] = above;
+    }
+    above += v[i];
+  }
+}
 
-  // this thread's keys: kPerThread consecutive indices
+// One pass over the scores: the keys of a chunk in bin b or above, in index
+// order, go to the chunk's slot.  Iteration i of wavefront w covers keys
+// j0 + 256 i + 64 w + lane, so (i, w, lane) order is index order.
+__global__ __launch_bounds__(kSelThreads) void sel_collect(const float* __restrict__ scores, int64_t ld,
+                                                           int64_t n, uint32_t* __restrict__ state,
+                                                           uint64_t* __restrict__ kept,
+                                                           uint32_t* __restrict__ counts, int64_t nchunks) {
+  constexpr int NW = kSelThreads / 64;
+  __shared__ uint32_t cnt[kPerThread][NW];
+  const int h = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const uint32_t bin = state[h * 4 + 0];
   const float* row = scores + (int64_t)h * ld;
-  const int64_t j0 = chunk * kChunk + (int64_t)threadIdx.x * kPerThread;
-  uint32_t keys[kPerThread];
-  uint32_t gt = 0, eq = 0;
+  const int64_t j0 = (int64_t)blockIdx.x * kChunk;
+  uint32_t key[kPerThread];
+  uint64_t mask[kPerThread];
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
-    const int64_t j = j0 + i;
-    const bool valid = j < n;
-    keys[i] = valid ? order_key(row[j]) : 0u;
-    gt += valid && keys[i] > T;
-    eq += valid && keys[i] == T;
+    const int64_t j = j0 + (int64_t)i * kSelThreads + threadIdx.x;
+    key[i] = j < n ? order_key(row[j]) : 0u;
   }
-  const uint32_t gt_before = block_exclusive(gt, wsum);
-  const uint32_t eq_before = block_exclusive(eq, wsum);
-  const uint32_t room = need > Eb ? need - Eb : 0u;         // ties still to take in this chunk
-  const uint32_t ties_taken_before = min(room, eq_before);
-  uint32_t pos = Gb + min(Eb, need) + gt_before + ties_taken_before;
-  uint32_t tie_rank = Eb + eq_before;
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) {
+    const int64_t j = j0 + (int64_t)i * kSelThreads + threadIdx.x;
+    mask[i] = __ballot(j < n && (key[i] >> kDigit0) >= bin);
+    if (lane == 0) cnt[i][w] = (uint32_t)__popcll(mask[i]);
+  }
+  __syncthreads();
+  // slot offset of (i, w): keys kept by the (i', w') pairs before it
+  uint64_t* slot = kept + ((int64_t)h * nchunks + blockIdx.x) * kSlot;
+  uint32_t run = 0;
+  for (int i = 0; i < kPerThread; ++i) {
+    uint32_t off = run;
+    for (int x = 0; x < w; ++x) off += cnt[i][x];
+    const uint64_t m = mask[i];
+    if ((m >> lane) & 1ull) {
+      const uint32_t pos = off + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
+      const int64_t j = j0 + (int64_t)i * kSelThreads + threadIdx.x;
+      if (pos < (uint32_t)kSlot) slot[pos] = ((uint64_t)key[i] << 32) | (uint32_t)j;
+    }
+    for (int x = 0; x < NW; ++x) run += cnt[i][x];
+  }
+  if (threadIdx.x == 0) {
+    counts[(int64_t)h * nchunks + blockIdx.x] = run;
+    if (run > (uint32_t)kSlot) state[h * 4 + 2] = 1u;   // overflow: resolve from the row
+  }
+}
+
+// The bin of a kBins histogram holding the need-th largest key: sh[0] = bin,
+// sh[1] = keys in higher bins.  Called by every thread; needs 1 <= need <= total.
+template <int NT>
+__device__ __forceinline__ void find_bin(const uint32_t* lh, uint32_t need, uint32_t* wsum, uint32_t* sh) {
+  constexpr int kPer = kBins / NT;
+  uint32_t v[kPer];
+  uint32_t mine = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    v[i] = lh[threadIdx.x * kPer + i];
+    mine += v[i];
+  }
+  uint32_t above = block_suffix_inclusive<NT>(mine, wsum) - mine;
+#pragma unroll
+  for (int i = kPer - 1; i >= 0; --i) {
+    if (above < need && above + v[i] >= need) {
+      sh[0] = threadIdx.x * kPer + i;
+      sh[1] = above;
+    }
+    above += v[i];
+  }
+  __syncthreads();
+}
+
+// Exact in-order selection over the whole row by one workgroup (fallback).
+__device__ void resolve_row(const float* __restrict__ row, int64_t n, int k, int32_t* __restrict__ out,
+                            float* __restrict__ outv, uint32_t* lh, uint32_t* wsum, uint32_t* sh) {
+  constexpr int NT = kResolveThreads;
+  uint32_t prefix = 0, need = (uint32_t)k;
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? kDigit0 : (pass == 1 ? 10 : 0);
+    const int bits = pass == 0 ? 32 - kDigit0 : 10;
+    const int hi_shift = pass == 0 ? 32 : (pass == 1 ? kDigit0 : 10);
+    const uint32_t mask = (1u << bits) - 1u;
+    for (int b = threadIdx.x; b < kBins; b += NT) lh[b] = 0u;
+    __syncthreads();
+    for (int64_t j = threadIdx.x; j < n; j += NT) {
+      const uint32_t key = order_key(row[j]);
+      if (hi_shift == 32 || (key >> hi_shift) == prefix) atomicAdd(&lh[(key >> shift) & mask], 1u);
+    }
+    __syncthreads();
+    find_bin<NT>(lh, need, wsum, sh);
+    prefix = (prefix << bits) | sh[0];
+    need -= sh[1];
+    __syncthreads();
+  }
+  const uint32_t T = prefix;
+  // ordered pass: keys above T, then the first `need` keys equal to T
+  uint32_t written = 0, ties = 0;
+  for (int64_t j0 = 0; j0 < n; j0 += NT) {
+    const int64_t j = j0 + threadIdx.x;
+    const uint32_t key = j < n ? order_key(row[j]) : 0u;
+    const uint32_t gt = (j < n && key > T) ? 1u : 0u;
+    const uint32_t eq = (j < n && key == T) ? 1u : 0u;
+    uint32_t tot_eq = 0, tot_sel = 0;
+    const uint32_t eq_before = block_exclusive<NT>(eq, wsum, &tot_eq);
+    const uint32_t sel = (gt || (eq && ties + eq_before < need)) ? 1u : 0u;
+    const uint32_t pos = block_exclusive<NT>(sel, wsum, &tot_sel);
+    if (sel) {
+      out[written + pos] = (int32_t)j;
+      if (outv) outv[written + pos] = row[j];
+    }
+    written += tot_sel;
+    ties += tot_eq;
+  }
+}
+
+__device__ __forceinline__ float key_to_float(uint32_t key) {
+  const uint32_t b = (key & 0x80000000u) ? (key & 0x7fffffffu) : ~key;
+  return __uint_as_float(b);
+}
+
+__global__ __launch_bounds__(kResolveThreads) void sel_resolve(const float* __restrict__ scores, int64_t ld,
+                                                               int64_t n, int k,
+                                                               const uint32_t* __restrict__ state,
+                                                               const uint64_t* __restrict__ kept,
+                                                               const uint32_t* __restrict__ counts,
+                                                               int64_t nchunks, int32_t* __restrict__ idx,
+                                                               float* __restrict__ val) {
+  constexpr int NT = kResolveThreads;
+  __shared__ uint64_t buf[kKeep];          // kept (key, index) of the head, in index order
+  __shared__ uint32_t lh[kBins];
+  __shared__ uint32_t coff[kResolveThreads + 1];   // offsets of the chunk slots in buf
+  __shared__ uint32_t wsum[NT / 64];
+  __shared__ uint32_t sh[2];
+  const int h = blockIdx.x;
+  const float* row = scores + (int64_t)h * ld;
   int32_t* out = idx + (int64_t)h * k;
   float* outv = val ? val + (int64_t)h * k : nullptr;
+  const uint32_t bin = state[h * 4 + 0];
+  const uint32_t above = state[h * 4 + 1];
+  bool fallback = state[h * 4 + 2] != 0u || nchunks > NT;
+  uint32_t total = 0;
+  if (!fallback) {
+    const uint32_t c = threadIdx.x < nchunks ? counts[(int64_t)h * nchunks + threadIdx.x] : 0u;
+    const uint32_t off = block_exclusive<NT>(c, wsum, &total);
+    coff[threadIdx.x] = off;
+    if (threadIdx.x == 0) coff[nchunks] = total;
+    fallback = total > (uint32_t)kKeep;
+  }
+  if (fallback) {
+    resolve_row(row, n, k, out, outv, lh, wsum, sh);
+    return;
+  }
+  __syncthreads();
+  // gather the slots in chunk order (binary search of the chunk of item x)
+  for (uint32_t x = threadIdx.x; x < total; x += NT) {
+    int lo = 0, hi = (int)nchunks;            // coff[lo] <= x < coff[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (coff[mid] <= x) lo = mid;
+      else hi = mid;
+    }
+    buf[x] = kept[((int64_t)h * nchunks + lo) * kSlot + (x - coff[lo])];
+  }
+  // the k-th key among the kept ones: keys above bin b are all in; among the keys
+  // of bin b find the (k - above)-th largest by the next 11, then 10 bits
+  uint32_t prefix = bin, need = (uint32_t)k - above;
+  for (int pass = 0; pass < 2; ++pass) {
+    const int shift = pass == 0 ? 10 : 0;
+    const int hi_shift = pass == 0 ? kDigit0 : 10;
+    for (int b = threadIdx.x; b < kBins; b += NT) lh[b] = 0u;
+    __syncthreads();
+    for (uint32_t x = threadIdx.x; x < total; x += NT) {
+      const uint32_t key = (uint32_t)(buf[x] >> 32);
+      if ((key >> hi_shift) == prefix) atomicAdd(&lh[(key >> shift) & 1023u], 1u);
+    }
+    __syncthreads();
+    find_bin<NT>(lh, need, wsum, sh);
+    prefix = (prefix << 10) | sh[0];
+    need -= sh[1];
+    __syncthreads();
+  }
+  const uint32_t T = prefix;
+  // ordered compaction: thread t owns kept items [kKeepPer t, kKeepPer (t+1))
+  uint32_t gt = 0, eq = 0;
+  uint32_t kk[kKeepPer];
 #pragma unroll
-  for (int i = 0; i < kPerThread; ++i) {
-    const int64_t j = j0 + i;
-    if (j >= n) break;
-    bool take = false;
-    if (keys[i] > T) {
-      take = true;
-    } else if (keys[i] == T) {
-      take = tie_rank < need;
-      ++tie_rank;
+  for (int r = 0; r < kKeepPer; ++r) {
+    const uint32_t x = threadIdx.x * kKeepPer + r;
+    kk[r] = x < total ? (uint32_t)(buf[x] >> 32) : 0u;
+    gt += x < total && kk[r] > T;
+    eq += x < total && kk[r] == T;
+  }
+  uint32_t tot_eq = 0, tot_gt = 0;
+  const uint32_t eq_before = block_exclusive<NT>(eq, wsum, &tot_eq);
+  const uint32_t gt_before = block_exclusive<NT>(gt, wsum, &tot_gt);
+  uint32_t ties = eq_before;
+  uint32_t pos = gt_before + min(eq_before, need);
+#pragma unroll
+  for (int r = 0; r < kKeepPer; ++r) {
+    const uint32_t x = threadIdx.x * kKeepPer + r;
+    if (x >= total) break;
+    bool take = kk[r] > T;
+    if (kk[r] == T) {
+      take = ties < need;
+      ++ties;
     }
     if (take) {
-      if (pos < (uint32_t)k) {   // always true when the threshold search is right
-        out[pos] = (int32_t)j;
-        if (outv) outv[pos] = row[j];
+      if (pos < (uint32_t)k) {
+        out[pos] = (int32_t)(buf[x] & 0xffffffffu);
+        if (outv) outv[pos] = key_to_float(kk[r]);
       }
       ++pos;
     }
   }
 }
 
+size_t al256(size_t x) { return (x + 255) / 256 * 256; }
+
 }  // namespace
 
 int64_t select_chunks(int64_t n) { return (n + kChunk - 1) / kChunk; }
 
-size_t select_workspace_bytes(int h_q, int64_t n) {
-  const size_t hist = (size_t)h_q * kBins * 4;
-  const size_t state = (size_t)h_q * 4 * 4;
-  const size_t counts = (size_t)h_q * (size_t)select_chunks(n) * 2 * 4;
-  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
-  return al(hist) + al(state) + al(counts);
+size_t select_workspace_bytes(int h_q, int64_t n, int k) {
+  (void)k;
+  const size_t nc = (size_t)select_chunks(n);
+  return al256((size_t)h_q * kBins * 4) + al256((size_t)h_q * 4 * 4) + al256((size_t)h_q * nc * 4) +
+         al256((size_t)h_q * nc * kSlot * 8);
 }
 
-SelectWorkspace carve_select(void* base, int h_q, int64_t n) {
-  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+SelectWorkspace carve_select(void* base, int h_q, int64_t n, int k) {
+  (void)k;
   uint8_t* p = static_cast<uint8_t*>(base);
   SelectWorkspace ws;
   ws.nchunks = select_chunks(n);
   ws.hist = reinterpret_cast<uint32_t*>(p);
-  p += al((size_t)h_q * kBins * 4);
+  p += al256((size_t)h_q * kBins * 4);
   ws.state = reinterpret_cast<uint32_t*>(p);
-  p += al((size_t)h_q * 4 * 4);
+  p += al256((size_t)h_q * 4 * 4);
   ws.counts = reinterpret_cast<uint32_t*>(p);
+  p += al256((size_t)h_q * (size_t)ws.nchunks * 4);
+  ws.kept = reinterpret_cast<uint64_t*>(p);
   return ws;
 }
 
 hipError_t launch_select(const float* scores, int64_t ld, int h_q, int64_t n, int k, int32_t* idx,
                          float* val, const SelectWorkspace& ws, hipStream_t s) {
   if (k == 0 || n == 0 || h_q == 0) return hipSuccess;
-  select_init<<<h_q, kSelThreads, 0, s>>>(ws.hist, ws.state, k);
+  sel_init<<<h_q, kSelThreads, 0, s>>>(ws.hist, ws.state);
   dim3 grid((unsigned)ws.nchunks, (unsigned)h_q);
-  for (int pass = 0; pass < 3; ++pass) {
-    select_hist<<<grid, kSelThreads, 0, s>>>(scores, ld, n, pass, ws.hist, ws.state);
-    select_find<<<h_q, kSelThreads, 0, s>>>(ws.hist, ws.state, pass);
-  }
-  select_count<<<grid, kSelThreads, 0, s>>>(scores, ld, n, ws.state, ws.counts, ws.nchunks);
-  select_write<<<grid, kSelThreads, 0, s>>>(scores, ld, n, k, ws.state, ws.counts, ws.nchunks, idx, val);
+  sel_hist<<<grid, kSelThreads, 0, s>>>(scores, ld, n, ws.hist);
+  sel_find<<<h_q, kSelThreads, 0, s>>>(ws.hist, ws.state, k);
+  sel_collect<<<grid, kSelThreads, 0, s>>>(scores, ld, n, ws.state, ws.kept, ws.counts, ws.nchunks);
+  sel_resolve<<<h_q, kResolveThreads, 0, s>>>(scores, ld, n, k, ws.state, ws.kept, ws.counts, ws.nchunks, idx,
+                                              val);
   return hipGetLastError();
 }
 

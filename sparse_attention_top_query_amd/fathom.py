@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libfathom.so")
 
 HBM = 0
 HOST_DIRECT = 1
+HOST_STAGED = 2
 WATERFILL = 0
 TOPQ = 1
 
@@ -53,14 +54,13 @@ def load() -> ctypes.CDLL:
     lib = ctypes.CDLL(LIB_PATH)
     P, I, L, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
     sig = {
-        "fathom_scale_bytes": (S, [L]),
-        "fathom_plane_bytes": (S, [L]),
         "fathom_record_bytes": (S, [L]),
+        "fathom_prefix_bytes": (S, [L, I]),
         "pack_bitplanes": (I, [P, I, L, I, P, P, P]),
         "allocate_depths": (I, [P, P, I, I, I, I, I, P, P, P, P]),
-        "fathom_workspace_bytes": (S, [I, I, L, I, I]),
+        "fathom_workspace_bytes": (S, [I, I, L, I, I, I]),
         "scan_topk": (I, [P, I, P, P, P, I, I, L, I, I, P, P, P, S, P]),
-        "fathom_scan_scores": (I, [P, I, P, P, P, I, I, L, I, P, L, P]),
+        "fathom_scan_scores": (I, [P, I, P, P, P, I, I, L, I, P, L, P, S, P]),
         "fathom_last_error": (ctypes.c_char_p, []),
         "fathom_version": (I, []),
     }
@@ -102,16 +102,13 @@ def record_bytes(n: int) -> int:
     return int(load().fathom_record_bytes(n))
 
 
-def scale_bytes(n: int) -> int:
-    return int(load().fathom_scale_bytes(n))
+def prefix_bytes(n: int, t: int) -> int:
+    """Bytes of the contiguous run holding the scales and the first t planes."""
+    return int(load().fathom_prefix_bytes(n, t))
 
 
-def plane_bytes(n: int) -> int:
-    return int(load().fathom_plane_bytes(n))
-
-
-def workspace_bytes(h_q: int, h_kv: int, n: int, d: int, k: int) -> int:
-    return int(load().fathom_workspace_bytes(h_q, h_kv, n, d, k))
+def workspace_bytes(h_q: int, h_kv: int, n: int, d: int, k: int, residency: int = HBM) -> int:
+    return int(load().fathom_workspace_bytes(h_q, h_kv, n, d, k, residency))
 
 
 def pack(k: torch.Tensor, records: torch.Tensor | None = None, status: torch.Tensor | None = None):
@@ -154,7 +151,7 @@ def allocate(q: torch.Tensor, sigma2: torch.Tensor, budget: int, mode: int = WAT
 
 
 def _residency_of(records: torch.Tensor) -> int:
-    return HBM if records.is_cuda else HOST_DIRECT
+    return HBM if records.is_cuda else HOST_STAGED
 
 
 def scan_topk(records: torch.Tensor, q: torch.Tensor, depth: torch.Tensor, union_depth: torch.Tensor,
@@ -164,7 +161,7 @@ def scan_topk(records: torch.Tensor, q: torch.Tensor, depth: torch.Tensor, union
     """scan_topk: -> int32 [h_q, k] ascending key indices (and float32 scores if asked).
 
     ``records`` may be a device tensor (HBM residency) or a pinned host tensor
-    (host-direct residency)."""
+    (staged host residency by default; HOST_DIRECT reads it in place)."""
     _need(q, "q", torch.float32, 2)
     _need(depth, "depth", torch.uint8)
     _need(union_depth, "union_depth", torch.uint8)
@@ -175,7 +172,7 @@ def scan_topk(records: torch.Tensor, q: torch.Tensor, depth: torch.Tensor, union
     h_kv = union_depth.shape[0]
     if records.numel() < h_kv * d * record_bytes(n):
         raise ValueError("records buffer too small for (h_kv, d, n)")
-    wsb = workspace_bytes(h_q, h_kv, n, d, k)
+    wsb = workspace_bytes(h_q, h_kv, n, d, k, residency)
     if workspace is None:
         workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=q.device)
     _need(workspace, "workspace", torch.uint8)
@@ -193,7 +190,8 @@ def scan_topk(records: torch.Tensor, q: torch.Tensor, depth: torch.Tensor, union
 
 
 def scan_scores(records: torch.Tensor, q: torch.Tensor, depth: torch.Tensor, union_depth: torch.Tensor,
-                n: int, residency: int | None = None, out: torch.Tensor | None = None):
+                n: int, residency: int | None = None, out: torch.Tensor | None = None,
+                workspace: torch.Tensor | None = None):
     """fathom_scan_scores: -> float32 [h_q, n] scores (the scan stage alone)."""
     _need(q, "q", torch.float32, 2)
     _need(depth, "depth", torch.uint8)
@@ -206,6 +204,11 @@ def scan_scores(records: torch.Tensor, q: torch.Tensor, depth: torch.Tensor, uni
     if out is None:
         out = torch.empty((h_q, max(n, 1)), dtype=torch.float32, device=q.device)
     _need(out, "out", torch.float32, 2)
+    if workspace is None and residency == HOST_STAGED:
+        workspace = torch.empty(max(workspace_bytes(h_q, h_kv, n, d, 1, residency), 1), dtype=torch.uint8,
+                                device=q.device)
+    wsn = 0 if workspace is None else workspace.numel()
     _check(load().fathom_scan_scores(_ptr(records), residency, _ptr(q), _ptr(depth), _ptr(union_depth),
-                                     h_q, h_kv, n, d, _ptr(out), out.shape[1], _stream(q)))
+                                     h_q, h_kv, n, d, _ptr(out), out.shape[1], _ptr(workspace), wsn,
+                                     _stream(q)))
     return out[:, :n]

@@ -43,18 +43,20 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_record_geometry_matches_layout_definition(lib):
     for n in (0, 1, 127, 128, 129, 1000, 1024, 4096, 131072, 262144, 1 << 20, 3 * 1024 + 300):
-        s, p, r = O.record_layout(n)
-        assert lib.fathom_scale_bytes(n) == s
-        assert lib.fathom_plane_bytes(n) == p
+        _, _, _, r = O.record_layout(n)
         assert lib.fathom_record_bytes(n) == r
+        for t in range(5):
+            assert lib.fathom_prefix_bytes(n, t) == O.prefix_bytes(n, t)
 
 
 def test_workspace_bytes_monotone(lib):
-    a = lib.fathom_workspace_bytes(32, 8, 1 << 20, 128, 2048)
-    b = lib.fathom_workspace_bytes(32, 8, 1 << 17, 128, 2048)
+    a = lib.fathom_workspace_bytes(32, 8, 1 << 20, 128, 2048, 0)
+    b = lib.fathom_workspace_bytes(32, 8, 1 << 17, 128, 2048, 0)
     assert a > b > 0
     assert a >= 32 * (1 << 20) * 4       # holds the fp32 scores of every head
-    assert lib.fathom_workspace_bytes(32, 8, 0, 128, 0) == 0
+    staged = lib.fathom_workspace_bytes(32, 8, 1 << 20, 128, 2048, 2)
+    assert staged - a >= 8 * 128 * O.record_layout(1 << 20)[3]   # plus an HBM mirror of the records
+    assert lib.fathom_workspace_bytes(32, 8, 0, 128, 0, 0) == 0
 
 
 def _err(lib):
@@ -79,7 +81,7 @@ def test_host_validation_errors(lib):
     # scan: shape checks come before any pointer query
     assert lib.scan_topk(fake, 0, fake, fake, fake, 4, 3, 128, 8, 4, fake, None, fake, 1 << 20, None) == -2
     assert lib.scan_topk(fake, 0, fake, fake, fake, 4, 1, -1, 8, 4, fake, None, fake, 1 << 20, None) == -2
-    assert lib.fathom_scan_scores(fake, 0, None, fake, fake, 4, 1, 128, 8, fake, 128, None) == -1
+    assert lib.fathom_scan_scores(fake, 0, None, fake, fake, 4, 1, 128, 8, fake, 128, None, 0, None) == -1
 
 
 def test_binding_refuses_cpu_tensors(lib):

@@ -223,6 +223,16 @@ def test_budget_zero_selects_lowest_indices(F):
     assert np.array_equal(idx, np.tile(np.arange(100), (4, 1)))
 
 
+def test_budget_zero_large_n_takes_row_fallback(F):
+    """All scores equal (B = 0): every key is a candidate, more than the LDS sort
+    holds, so selection runs the exact in-order fallback; lowest indices win."""
+    case = (1, 4, 40000, 16, 0)
+    *_, rec, dq, dep, uni, sg = run_case(F, case)
+    for kk in (1, 2048, 9000, 40000):
+        idx = F.scan_topk(rec, dq, dep, uni, 40000, kk).cpu().numpy()
+        assert np.array_equal(idx, np.tile(np.arange(kk), (4, 1))), kk
+
+
 def test_select_many_ties(F):
     """Exact selection among massive score ties (a one-channel cache whose keys take
     three values), across several select chunks."""
@@ -245,16 +255,31 @@ def test_select_many_ties(F):
         assert np.array_equal(idx, O.topk(s, kk))
 
 
-@pytest.mark.parametrize("case", [SCAN_CASES[0], SCAN_CASES[2]])
-def test_host_direct_matches_hbm_bit_for_bit(F, case):
+@pytest.mark.parametrize("case", [SCAN_CASES[0], SCAN_CASES[2], SCAN_CASES[3], SCAN_CASES[5]])
+def test_host_residencies_match_hbm_bit_for_bit(F, case):
+    """The same scan over pinned host records, read in place or staged through
+    HBM, gives bit-identical scores and indices to the HBM-resident scan."""
     h_kv, g, n, d, budget = case
     k, q, s2, rec, dq, dep, uni, sg = run_case(F, case)
     host = rec.cpu().pin_memory()
-    sh = F.scan_scores(host, dq, dep, uni, n).cpu().numpy()
-    assert np.array_equal(sh.view(np.uint32), sg.view(np.uint32))
+    for res in (F.HOST_DIRECT, F.HOST_STAGED):
+        sh = F.scan_scores(host, dq, dep, uni, n, residency=res).cpu().numpy()
+        assert np.array_equal(sh.view(np.uint32), sg.view(np.uint32)), res
     a = F.scan_topk(rec, dq, dep, uni, n, 64).cpu().numpy()
-    b = F.scan_topk(host, dq, dep, uni, n, 64).cpu().numpy()
-    assert np.array_equal(a, b)
+    for res in (F.HOST_DIRECT, F.HOST_STAGED):
+        b = F.scan_topk(host, dq, dep, uni, n, 64, residency=res).cpu().numpy()
+        assert np.array_equal(a, b), res
+
+
+def test_staged_many_heads_per_launch(F):
+    """Records of ~10 MB per KV head put 6 KV heads in each copy/scan launch, with a
+    ragged last launch (13 = 6 + 6 + 1): staged must still equal HBM-resident."""
+    case = (13, 4, 160000, 128, 68)
+    h_kv, g, n, d, budget = case
+    k, q, s2, rec, dq, dep, uni, sg = run_case(F, case)
+    host = rec.cpu().pin_memory()
+    sh = F.scan_scores(host, dq, dep, uni, n, residency=F.HOST_STAGED).cpu().numpy()
+    assert np.array_equal(sh.view(np.uint32), sg.view(np.uint32))
 
 
 def test_topq_scan_parity(F):
@@ -274,13 +299,19 @@ def test_topq_scan_parity(F):
 def test_scan_rejects_bad_residency_and_workspace(F):
     case = (1, 4, 1024, 32, 20)
     *_, rec, dq, dep, uni, sg = run_case(F, case)
-    with pytest.raises(F.FathomError) as e:
-        F.scan_topk(rec, dq, dep, uni, 1024, 8, residency=F.HOST_DIRECT)
-    assert e.value.status == -7
-    pageable = rec.cpu()
-    with pytest.raises(F.FathomError) as e:
-        F.scan_topk(pageable, dq, dep, uni, 1024, 8, residency=F.HOST_DIRECT)
-    assert e.value.status == -7
+    for res in (F.HOST_DIRECT, F.HOST_STAGED):
+        with pytest.raises(F.FathomError) as e:
+            F.scan_topk(rec, dq, dep, uni, 1024, 8, residency=res)
+        assert e.value.status == -7
+        pageable = rec.cpu()
+        with pytest.raises(F.FathomError) as e:
+            F.scan_topk(pageable, dq, dep, uni, 1024, 8, residency=res)
+        assert e.value.status == -7
+    host = rec.cpu().pin_memory()
+    small = torch.empty(1024, dtype=torch.uint8, device="cuda:0")
+    with pytest.raises(F.FathomError) as e:       # no room for the staging mirror
+        F.scan_scores(host, dq, dep, uni, 1024, residency=F.HOST_STAGED, workspace=small)
+    assert e.value.status == -5
     small = torch.empty(16, dtype=torch.uint8, device="cuda:0")
     with pytest.raises(F.FathomError) as e:
         F.scan_topk(rec, dq, dep, uni, 1024, 8, workspace=small)

@@ -39,7 +39,7 @@ def test_six_keys_hand_values():
     assert g["delta"] == [1.0, 0.25]
     assert g["kappa"] == [[15, 4, 10, 7, 8, 14], [9, 0, 12, 14, 5, 8]]
     r0 = bytes.fromhex(g["records_hex"][0])
-    assert r0[0:2] == b"\x00\x3c" and r0[16] == 0x35 and r0[32] == 0x2B
+    assert r0[0:2] == b"\x00\x3c" and r0[16] == 0x35 and r0[144] == 0x2B
     depths = [g["budgets"][str(b)]["depth"] for b in range(1, 9)]
     assert depths == [[0, 1], [1, 1], [1, 2], [2, 2], [2, 3], [3, 3], [3, 4], [4, 4]]
     assert g["budgets"]["2"]["scores"] == [6.0, -6.0, 6.0, -2.0, 2.0, 6.0]

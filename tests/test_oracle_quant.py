@@ -137,34 +137,43 @@ def test_four_plane_prefix_is_full_dequant():
 
 
 def test_record_layout_bit_by_bit():
-    """Decode records byte by byte from the layout definition (no numpy bit helpers)."""
+    """Decode records byte by byte from the layout definition (no numpy bit helpers):
+    unit u of the head holds the fp16 scales of blocks 8u..8u+7 then the plane-0
+    bits of keys 1024u..1024u+1023; planes 1-3 follow, one bit per key."""
     k = crafted_keys()
     n, d = k.shape
     delta, kappa, rec = O.pack_head(k)
-    s, p, r = O.record_layout(n)
+    u, h, p, r = O.record_layout(n)
     nb = O.n_blocks(n)
-    assert rec.shape == (d, r) and s % 16 == 0 and p == 16 * nb
+    assert rec.shape == (d, r) and h == 144 * u and p == 128 * u and r == h + 3 * p
     for c in range(d):
         raw = bytes(rec[c])
-        for b in range(nb):
-            (v,) = struct.unpack_from("<e", raw, 2 * b)
-            assert v == float(delta[c, b]) or (v == 0 and float(delta[c, b]) == 0)
-        assert all(x == 0 for x in raw[2 * nb: s])
+        for b in range(8 * u):
+            (v,) = struct.unpack_from("<e", raw, 144 * (b // 8) + 2 * (b % 8))
+            if b < nb:
+                assert v == float(delta[c, b]) or (v == 0 and float(delta[c, b]) == 0)
+            else:
+                assert raw[144 * (b // 8) + 2 * (b % 8)] == 0 and raw[144 * (b // 8) + 2 * (b % 8) + 1] == 0
         for plane in range(4):
-            base = s + plane * p
-            for j in range(nb * 128):
-                bit = (raw[base + j // 8] >> (j % 8)) & 1
+            for j in range(u * 1024):
+                if plane == 0:
+                    off = 144 * (j // 1024) + 16 + (j % 1024) // 8
+                else:
+                    off = h + (plane - 1) * p + j // 8
+                bit = (raw[off] >> (j % 8)) & 1
                 want = ((int(kappa[j, c]) >> (3 - plane)) & 1) if j < n else 0
                 assert bit == want, (c, plane, j)
 
 
-def test_record_sizes():
-    # n a multiple of 1024: R = n/64 + n/2 (scales then four n/8-byte planes)
+def test_record_sizes_and_prefix_runs():
+    # n a multiple of 1024: R = n/64 + n/2 (scales, then four n/8-byte planes)
     for n in (4096, 131072, 262144, 1 << 20):
-        s, p, r = O.record_layout(n)
-        assert (s, p, r) == (n // 64, n // 8, n // 64 + n // 2)
-    assert O.record_layout(1) == (16, 16, 80)
-    assert O.record_layout(0) == (0, 0, 0)
+        u, h, p, r = O.record_layout(n)
+        assert r == n // 64 + n // 2 and h == n // 64 + n // 8 and p == n // 8
+        for t in range(5):
+            assert O.prefix_bytes(n, t) == (0 if t == 0 else n // 64 + t * n // 8)
+    assert O.record_layout(1) == (1, 144, 128, 528)
+    assert O.record_layout(0) == (0, 0, 0, 0)
 
 
 def test_unpack_roundtrip_and_prefix_read():
@@ -172,8 +181,12 @@ def test_unpack_roundtrip_and_prefix_read():
     k = rng.standard_normal((777, 5)).astype(np.float32)
     delta, kappa, rec = O.pack_head(k)
     for t in range(0, 5):
-        d2, code = O.unpack_codes(rec, 777, t)
-        assert np.array_equal(d2.view(np.uint16), delta.view(np.uint16))
+        # only the prefix run is needed: clobber everything after it
+        cut = rec.copy()
+        cut[:, O.prefix_bytes(777, t):] = 0xA5
+        d2, code = O.unpack_codes(cut, 777, t)
+        if t:
+            assert np.array_equal(d2.view(np.uint16), delta.view(np.uint16))
         assert np.array_equal(code, kappa >> (4 - t))
 
 
