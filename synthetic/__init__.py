@@ -97,23 +97,29 @@ def queries(wl_key: int, layer: int, session: int, g: int, count: int, d: int) -
     return _rng(wl_key, layer, session, g, 1).standard_normal((count, d), dtype=np.float32)
 
 
-def layer_inputs(wl: Workload, layer: int = 0, n: int | None = None):
+def layer_inputs(wl: Workload, layer: int = 0, n: int | None = None, threads: int = 8):
     """All inputs of one layer: K [S*h_kv, n, d], q [S*h_q, d], sigma2 [S*h_kv, d].
 
     Sessions are laid out as extra KV heads (session-major), since sessions
     never mix: session s, KV head g is virtual KV head s*h_kv + g.
     ``n`` may shrink the key count for a cheaper variant of the same recipe.
+    KV heads are drawn in parallel threads (each from its own seeded stream,
+    so the result does not depend on the thread count).
     """
+    from concurrent.futures import ThreadPoolExecutor
     n = wl.n if n is None else n
     hk = wl.sessions * wl.h_kv
     k = np.empty((hk, n, wl.d), dtype=np.float32)
     s2 = np.empty((hk, wl.d), dtype=np.float32)
     q = np.empty((hk * wl.g, wl.d), dtype=np.float32)
-    for s in range(wl.sessions):
-        for g in range(wl.h_kv):
-            v = s * wl.h_kv + g
-            k[v], s2[v] = kv_head(wl.key, layer, s, g, n, wl.d, wl.outliers)
-            q[v * wl.g:(v + 1) * wl.g] = queries(wl.key, layer, s, g, wl.g, wl.d)
+
+    def one(v):
+        s, g = divmod(v, wl.h_kv)
+        k[v], s2[v] = kv_head(wl.key, layer, s, g, n, wl.d, wl.outliers)
+        q[v * wl.g:(v + 1) * wl.g] = queries(wl.key, layer, s, g, wl.g, wl.d)
+
+    with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
+        list(ex.map(one, range(hk)))
     return k, q, s2
 
 
