@@ -36,8 +36,11 @@ def parse():
     ap.add_argument("--workload", default="w3_host_1m_B92")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--kernel-reps", type=int, default=20)
-    ap.add_argument("--residency", choices=["staged", "direct"], default="staged",
-                    help="host-resident records: staged through HBM (default) or read in place")
+    ap.add_argument("--residency", choices=["staged", "direct"], default="direct",
+                    help="host-resident records: read in place by the scan (default) or staged through HBM")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="only run a 1 GiB device-to-device copy (the known-size kernel used to scale the "
+                         "FETCH_SIZE / WRITE_SIZE counters) and exit")
     ap.add_argument("--copies", type=int, default=8,
                     help="HBM-resident workloads: distinct record copies cycled per step, so the "
                          "256 MB Infinity Cache cannot hold them")
@@ -145,6 +148,14 @@ def main():
     from synthetic import workloads
     F.load()
     dev = torch.device("cuda:0")
+    if args.calibrate:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize(dev)
+        print(json.dumps({"calibration": "device-to-device copy", "bytes_per_copy": 1 << 30, "copies": 3}))
+        return
     wl = workloads()[args.workload]
     if wl.layers != 1:
         raise SystemExit("bench.py times single-layer workloads; multi-layer decode runs through the tests")
