@@ -26,6 +26,16 @@ sys.path.insert(0, ROOT)
 
 PCIE5_X16_GBPS = 64.0      # published host-link rate per direction (PCIe 5.0 x16)
 HBM_PEAK_GBPS = 8000.0     # MI355X HBM3E
+# VALU lane-operations per second: 256 CUs x 64 lanes x 2.4 GHz (packed FP32 is
+# not used, so one lane-op per lane and clock)
+VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
+
+# rocprofv3 summaries whose FETCH_SIZE / WRITE_SIZE figures give the measured
+# traffic of the dominant kernel, keyed by (workload, residency)
+PROFILES = {
+    ("w3_host_1m_B92", "direct"): "scan_host_1m_B92_direct.md",
+    ("w2_hbm_131k_B92", "hbm"): "scan_hbm_131k_B92.md",
+}
 
 
 def parse():
@@ -54,6 +64,48 @@ def algorithmic_bytes(union: np.ndarray, n: int) -> int:
     units = -(-((n + 127) // 128) // 8)
     t = union.astype(np.int64)
     return int(np.where(t > 0, 144 * units + (t - 1) * 128 * units, 0).sum())
+
+
+def algorithmic_ops(depth: np.ndarray, union: np.ndarray, n: int) -> int:
+    """VALU lane-operations of the reconstruction for all keys: per KV head and
+    union channel with depth u > 0, 2u - 1 integer ops build the signed prefixes,
+    2 ops per distinct depth read by some head form float(2r + 1), and 1 FMA per
+    query head that reads the channel.  Counted per KV-head key."""
+    hk, d = union.shape
+    g = depth.shape[0] // hk
+    dep = depth.reshape(hk, g, d).astype(np.int64)
+    u = union.astype(np.int64)
+    chain = np.where(u > 0, 2 * u - 1, 0).sum()
+    levels = sum(((dep == t).any(axis=1)).sum() for t in range(1, 5))
+    fmas = (dep > 0).sum()
+    return int((chain + 2 * levels + fmas) * n)
+
+
+def measured_traffic(workload: str, residency: str, kernel: str):
+    """Scaled FETCH_SIZE + WRITE_SIZE bytes per launch from the committed
+    rocprofv3 summary of this workload, or None when there is none or the scan
+    sources have changed since the counters were taken."""
+    import hashlib
+    name = PROFILES.get((workload, residency))
+    path = os.path.join(ROOT, "profiles", name) if name else None
+    if not path or not os.path.exists(path):
+        return None
+    text = open(path).read()
+    if "```figures" not in text:
+        return None
+    fig = {}
+    for line in text.split("```figures", 1)[1].split("```", 1)[0].strip().splitlines():
+        key, _, val = line.partition(":")
+        fig[key.strip()] = val.strip()
+    h = hashlib.sha256()
+    for f in ("scan.hip", "fathom_internal.h"):
+        h.update(open(os.path.join(ROOT, "sparse_attention_top_query_amd", "csrc", f), "rb").read())
+    if fig.get("kernel_source_sha256") != h.hexdigest() or "fetch_bytes_per_dispatch" not in fig:
+        return None
+    if not kernel.startswith(fig.get("kernel", "?").split("<")[0]):
+        return None
+    fetch, write = int(fig["fetch_bytes_per_dispatch"]), int(fig["write_bytes_per_dispatch"])
+    return {"total": fetch + write, "fetch": fetch, "write": write, "source": f"profiles/{name}"}
 
 
 def measure_h2d_peak(torch, dev, mib=512, reps=5) -> float:
@@ -219,20 +271,29 @@ def main():
     keys_per_s = hq * n / (step_ms * 1e-3)
     g = hq // hk
     if host and residency == F.HOST_STAGED:
-        kname = f"stage_scan_kernel<{g}> ({-(-hk // max(1, min(hk, (64 << 20) // (d * F.record_bytes(n))))) + 1} launches per step)"
+        kname = f"stage_scan_kernel<{g}, 8>"
     else:
-        kname = f"scan_kernel<{g}>"
+        kname = f"scan_kernel<{g}, {32 if g <= 4 else 16}>" if host else f"scan_kernel<{g}, 8>"
+    res_key = args.residency if host else "hbm"
+    traffic = measured_traffic(args.workload, res_key, kname)
+    common = {"traffic": traffic["total"] if traffic else None,
+              "traffic_fetch": traffic["fetch"] if traffic else None,
+              "traffic_write": traffic["write"] if traffic else None,
+              "traffic_source": traffic["source"] if traffic else None,
+              "kernel": kname, "kernel_ms": round(scan_ms, 4), "bytes_per_launch": alg_bytes}
     if host:
         roof = {"bound": "host_link", "achieved": round(achieved, 2), "peak": PCIE5_X16_GBPS, "unit": "GB/s",
-                "frac": round(achieved / PCIE5_X16_GBPS, 4), "traffic": None,
+                "frac": round(achieved / PCIE5_X16_GBPS, 4), **common,
                 "measured_h2d_peak": round(h2d_peak, 2), "frac_of_measured_h2d": round(achieved / h2d_peak, 4),
-                "kernel": kname, "kernel_ms": round(scan_ms, 4), "bytes_per_launch": alg_bytes,
                 "residency": args.residency}
     else:
-        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                "kernel": kname, "kernel_ms": round(scan_ms, 4), "bytes_per_launch": alg_bytes,
-                "record_copies_cycled": len(copies)}
+        # records in HBM: the reconstruction's VALU work bounds the scan, not HBM
+        ops = algorithmic_ops(depth.cpu().numpy(), union_np, n)
+        tops = ops / (scan_ms * 1e-3) / 1e12
+        roof = {"bound": "alu", "achieved": round(tops, 3), "peak": round(VALU_PEAK_TOPS, 2),
+                "unit": "T lane-op/s", "frac": round(tops / VALU_PEAK_TOPS, 4), **common,
+                "ops_per_launch": ops, "hbm_achieved_gbps": round(achieved, 2),
+                "hbm_frac": round(achieved / HBM_PEAK_GBPS, 4), "record_copies_cycled": len(copies)}
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(wl, q_np, s2_np, budget)
