@@ -13,8 +13,9 @@
 // within about (m + 1) 2^-24 sum_c |q_c k_hat_c| for m channels.
 //
 // Work decomposition: one workgroup scores a tile of TB 128-key blocks of one KV
-// head for all of its G query heads; each wavefront owns 2 blocks (256 keys,
-// 4 sub-chunks of 64, lane = key).
+// head for all of its G query heads; each wavefront owns 2 blocks (256 keys):
+// lanes 0-31 one block, lanes 32-63 the other, and lane l scores key l%32 of
+// each of its block's four 32-key words.
 //  1. The union depths of the KV head list the channels to read; every query
 //     head of the group is scored from the one read of the longest prefix.
 //  2. Staging, channel group by channel group (about 64 channel-planes): the
@@ -45,7 +46,7 @@ constexpr int kStageChunks = kGroupChunks + kSlackChunks;
 constexpr int kStageEntries = kStageChunks;    // entries have >= 1 chunk
 constexpr int kMaxChunks = kPlanes * kMaxD;
 constexpr int kWaveBlocks = 2;                 // 128-key blocks per wavefront
-constexpr int kSub = 2 * kWaveBlocks;          // 64-key sub-chunks per wavefront
+constexpr int kSub = kBlock / 32;              // 32-key words per block; a lane scores one key of each
 
 template <int G, int TB>
 struct Cfg {
@@ -63,7 +64,7 @@ struct ScanSmem {
   uint4 scales[kStageEntries][TB / kUnitBlocks];   // staged fp16 scales per entry of the group
   float coef[kStageEntries][TB][G];                // q_h 2^(3-t_h) Delta_b per entry, block, head
   float ent_q[kMaxD][G];                           // q_h 2^(3-t_h) of each list entry
-  uint64_t ent_word[kMaxD];                        // union depth | used depths | head depths
+  uint64_t ent_word[kMaxD + 1];                    // union depth | used depths | head depths
   uint16_t ent_base[kMaxD + 1];                    // first chunk of entry e (prefix sum)
   uint8_t ent_c[kMaxD];                            // channel of list entry e
   uint16_t grp[kMaxChunks / kGroupChunks + 2];     // first entry of each staging group
@@ -88,6 +89,7 @@ struct ScanArgs {
 // reads exactly t planes), then 3 bits of depth per head from bit 8.
 __device__ __forceinline__ int word_tb(uint64_t w) { return (int)(w & 7); }
 __device__ __forceinline__ int word_th(uint64_t w, int h) { return (int)((w >> (8 + 3 * h)) & 7); }
+__device__ __forceinline__ uint32_t u4(const uint4& v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
 
 // Scores of tile `tile` (TB blocks) of KV head g, all its query heads.
 template <int G, int TB>
@@ -105,6 +107,7 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t 
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int64_t blk0 = tile * TB;
+  const int bl = kWaveBlocks * wv + (lane >> 5);   // block of this lane within the tile
   const int nvalid = (int)min<int64_t>(TB, nb - blk0);
 
   // ---- 1. list of union channels, in channel order, and staging groups ----
@@ -252,85 +255,60 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t 
     __syncthreads();
     if (gi + 1 < n_grp) issue(gi + 1);
 
-    // ---- 3. reconstruct and accumulate; wave wv owns blocks 2wv and 2wv+1 ----
+    // ---- 3. reconstruct and accumulate.  Lane l owns block bl = 2wv + l/32 and,
+    // in it, key l%32 of each of the block's four 32-key words (sub-chunks s).
     if (kWaveBlocks * wv < nvalid) {
       const int pos = lane & 31;
+      uint64_t nword = sm.ent_word[e_lo];
+      int nbase = sm.ent_base[e_lo];
       for (int e = e_lo; e < e_hi; ++e) {
-        const uint64_t ew = sm.ent_word[e];
-        uint64_t word = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)ew);
-        if (8 + 3 * G > 32) word |= (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(ew >> 32)) << 32;
+        uint64_t word = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)nword);
+        if (8 + 3 * G > 32)
+          word |= (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(nword >> 32)) << 32;
+        const int cb = __builtin_amdgcn_readfirstlane(nbase) - ch_lo;
+        nword = sm.ent_word[e + 1];     // next entry's word, read ahead (array has kMaxD + 1 slots)
+        nbase = sm.ent_base[e + 1];
         const int tb = word_tb(word);
-        const int cb = sm.ent_base[e] - ch_lo;
-        // lane's plane word of sub-chunk s: block 2wv + s/2, u32 word 2(s%2) + lane/32
-        const uint32_t* pw = reinterpret_cast<const uint32_t*>(&sm.planes[cb][kWaveBlocks * wv]) + (lane >> 5);
-        int r1[kSub], r2[kSub], r3[kSub], r4[kSub];
+        const uint4* pp = &sm.planes[cb][bl];
+        // plane words of the prefix (only the planes the union depth reads)
+        uint4 w0 = pp[0], w1, w2, w3;
+        if (tb > 1) w1 = pp[TB];
+        if (tb > 2) w2 = pp[2 * TB];
+        if (tb > 3) w3 = pp[3 * TB];
+        float cf[G];
 #pragma unroll
-        for (int s = 0; s < kSub; ++s) {
-          const int off = (s >> 1) * 4 + (s & 1) * 2;       // u32 offset of the sub-chunk
-          r1[s] = __builtin_amdgcn_sbfe((int)pw[off], pos, 1);   // complemented MSB: b0 - 1
-        }
-        if (tb >= 2) {
+        for (int h = 0; h < G; ++h) cf[h] = sm.coef[e - e_lo][bl][h];
+        int r[kSub];
+        // one depth t: float(2 r_t + 1) once, then every head that reads exactly t planes
+        auto level = [&](int t) {
+          float f[kSub];
 #pragma unroll
-          for (int s = 0; s < kSub; ++s) {
-            const int off = (s >> 1) * 4 + (s & 1) * 2;
-            r2[s] = 2 * r1[s] + (int)__builtin_amdgcn_ubfe(pw[TB * 4 + off], pos, 1);
+          for (int s2 = 0; s2 < kSub; ++s2) f[s2] = (float)(2 * r[s2] + 1);
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            if (word_th(word, h) != t) continue;
+#pragma unroll
+            for (int s2 = 0; s2 < kSub; ++s2) acc[s2][h] = fmaf(cf[h], f[s2], acc[s2][h]);
           }
-        }
-        if (tb >= 3) {
+        };
+        // signed prefixes MSB first (plane 0 is stored complemented): r_1 = b_0 - 1,
+        // r_{t+1} = 2 r_t + b_t
 #pragma unroll
-          for (int s = 0; s < kSub; ++s) {
-            const int off = (s >> 1) * 4 + (s & 1) * 2;
-            r3[s] = 2 * r2[s] + (int)__builtin_amdgcn_ubfe(pw[2 * TB * 4 + off], pos, 1);
-          }
-        }
-        if (tb >= 4) {
+        for (int s2 = 0; s2 < kSub; ++s2) r[s2] = __builtin_amdgcn_sbfe((int)u4(w0, s2), pos, 1);
+        if (word & (8u << 0)) level(1);
+        if (tb > 1) {
 #pragma unroll
-          for (int s = 0; s < kSub; ++s) {
-            const int off = (s >> 1) * 4 + (s & 1) * 2;
-            r4[s] = 2 * r3[s] + (int)__builtin_amdgcn_ubfe(pw[3 * TB * 4 + off], pos, 1);
-          }
-        }
-        // odd integers 2 r_t + 1 as floats, for the depths some head uses
-        float f1[kSub], f2[kSub], f3[kSub], f4[kSub];
-        if (word & 8) {
+          for (int s2 = 0; s2 < kSub; ++s2) r[s2] = 2 * r[s2] + (int)__builtin_amdgcn_ubfe(u4(w1, s2), pos, 1);
+          if (word & (8u << 1)) level(2);
+          if (tb > 2) {
 #pragma unroll
-          for (int s = 0; s < kSub; ++s) f1[s] = (float)(2 * r1[s] + 1);
-        }
-        if (word & 16) {
+            for (int s2 = 0; s2 < kSub; ++s2) r[s2] = 2 * r[s2] + (int)__builtin_amdgcn_ubfe(u4(w2, s2), pos, 1);
+            if (word & (8u << 2)) level(3);
+            if (tb > 3) {
 #pragma unroll
-          for (int s = 0; s < kSub; ++s) f2[s] = (float)(2 * r2[s] + 1);
-        }
-        if (word & 32) {
-#pragma unroll
-          for (int s = 0; s < kSub; ++s) f3[s] = (float)(2 * r3[s] + 1);
-        }
-        if (word & 64) {
-#pragma unroll
-          for (int s = 0; s < kSub; ++s) f4[s] = (float)(2 * r4[s] + 1);
-        }
-        const float* cf = &sm.coef[e - e_lo][kWaveBlocks * wv][0];
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float c0 = cf[h], c1 = cf[G + h];
-          switch (word_th(word, h)) {
-            case 1:
-#pragma unroll
-              for (int s = 0; s < kSub; ++s) acc[s][h] = fmaf(s < 2 ? c0 : c1, f1[s], acc[s][h]);
-              break;
-            case 2:
-#pragma unroll
-              for (int s = 0; s < kSub; ++s) acc[s][h] = fmaf(s < 2 ? c0 : c1, f2[s], acc[s][h]);
-              break;
-            case 3:
-#pragma unroll
-              for (int s = 0; s < kSub; ++s) acc[s][h] = fmaf(s < 2 ? c0 : c1, f3[s], acc[s][h]);
-              break;
-            case 4:
-#pragma unroll
-              for (int s = 0; s < kSub; ++s) acc[s][h] = fmaf(s < 2 ? c0 : c1, f4[s], acc[s][h]);
-              break;
-            default:
-              break;
+              for (int s2 = 0; s2 < kSub; ++s2) r[s2] = 2 * r[s2] + (int)__builtin_amdgcn_ubfe(u4(w3, s2), pos, 1);
+              level(4);
+            }
           }
         }
       }
@@ -339,12 +317,14 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t 
   }
 
   // ---- 4. scores ----
+  if (bl < nvalid) {
 #pragma unroll
-  for (int s = 0; s < kSub; ++s) {
-    const int64_t j = (blk0 + kWaveBlocks * wv + (s >> 1)) * kBlock + (s & 1) * 64 + lane;
-    if (j < a.n) {
+    for (int s2 = 0; s2 < kSub; ++s2) {
+      const int64_t j = (blk0 + bl) * kBlock + s2 * 32 + (lane & 31);
+      if (j < a.n) {
 #pragma unroll
-      for (int h = 0; h < G; ++h) a.scores[(g * G + h) * a.ld + j] = acc[s][h];
+        for (int h = 0; h < G; ++h) a.scores[(g * G + h) * a.ld + j] = acc[s2][h];
+      }
     }
   }
 }
