@@ -8,21 +8,22 @@
 // sum_c w_c 4^(-t_c) subject to sum_c t_c = B, t_c in {0..4}.
 //
 // One workgroup per KV head, one wavefront per query head of its group.  A
-// lane owns channels lane, lane+64, lane+128, lane+192.
+// lane owns channels lane + 64 i, i < CPL (2 for d <= 128, else 4).
 //
 // The greedy is computed in closed form rather than step by step.  Plane t of
 // channel c (t = 0..3) is an item with marginal gain w_c 4^(-t); gains fall
 // with t, so the greedy takes items in the order (gain desc, channel asc,
 // plane asc) and after B steps holds exactly the B first items of that order.
-// Each item gets a distinct 64-bit key
-//   key = bits(double(w_c) * 4^(-t)) | (256 - c) << 2 | (3 - t),
-// which sorts in that order: w_c is an fp32 value, so as a double its low 29
-// significand bits are zero and scaling by 4^(-t) is exact; non-negative
-// doubles order like their bit patterns.  The B-th largest key K is found by a
-// 63-step bitwise search (each step counts the keys >= a candidate with one
-// compare per item and a wave-wide ballot count), and t_c is the number of
-// channel c's items with key >= K.  The fixed top-|q| mode selects m channels
-// the same way with key = bits(|q_c|) << 8 | (255 - c).
+// Each item gets a distinct integer key that sorts in that order:
+//   key = bits(double(w_c) * 4^(-t)) >> 29 << 11 | (256 - c) << 2 | (3 - t).
+// w_c is an fp32 value, so as a double its low 29 significand bits are zero and
+// scaling by 4^(-t) is exact (no double underflow for t <= 3); non-negative
+// doubles order like their bit patterns, and dropping the 29 zero bits keeps
+// the key within 45 bits.  The B-th largest key K is found by a bitwise search
+// from bit 44 down (each step counts the keys >= a candidate, one wave ballot
+// per item), and t_c is the number of channel c's items with key >= K.  The
+// fixed top-|q| mode selects m channels the same way with
+// key = bits(|q_c|) << 8 | (255 - c).
 #include "fathom_internal.h"
 
 namespace fathom {
@@ -34,14 +35,6 @@ __device__ inline uint32_t wave_or(uint32_t v) {
   return v;
 }
 
-// Wave-wide sum of per-lane counts in [0, 31], from one ballot per bit.
-__device__ __forceinline__ uint32_t wave_count(uint32_t cnt) {
-  uint32_t tot = 0;
-#pragma unroll
-  for (int b = 0; b < 5; ++b) tot += (uint32_t)__popcll(__ballot((cnt >> b) & 1u)) << b;
-  return tot;
-}
-
 // Largest K such that at least `want` of the wave's keys are >= K (the want-th
 // largest key when keys are distinct); `want` >= 1 and at most the key count.
 template <int N>
@@ -51,12 +44,13 @@ __device__ __forceinline__ uint64_t wave_kth_key(const uint64_t (&key)[N], uint3
     const uint64_t cand = T | (1ull << bit);
     uint32_t cnt = 0;
 #pragma unroll
-    for (int i = 0; i < N; ++i) cnt += key[i] >= cand;
-    if (wave_count(cnt) >= want) T = cand;
+    for (int i = 0; i < N; ++i) cnt += (uint32_t)__popcll(__ballot(key[i] >= cand));
+    if (cnt >= want) T = cand;
   }
   return T;
 }
 
+template <int CPL>
 __global__ __launch_bounds__(1024) void allocate_kernel(const float* __restrict__ q,
                                                         const float* __restrict__ sigma2, int g,
                                                         int d, int mode, int budget,
@@ -71,12 +65,12 @@ __global__ __launch_bounds__(1024) void allocate_kernel(const float* __restrict_
   const int lane = threadIdx.x & 63;
   const int h = kv * g + wv;
 
-  float w[4];
-  float aq[4];
-  int t[4];
+  float w[CPL];
+  float aq[CPL];
+  int t[CPL];
   uint32_t flag = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < CPL; ++i) {
     const int c = lane + 64 * i;
     t[i] = 0;
     w[i] = 0.0f;
@@ -95,19 +89,19 @@ __global__ __launch_bounds__(1024) void allocate_kernel(const float* __restrict_
   flag = wave_or(flag);
 
   if (flag == 0 && mode == 0 && budget > 0) {
-    uint64_t key[16];   // item (channel lane + 64 i, plane t) at 4 i + t; 0 = no item
+    uint64_t key[kPlanes * CPL];   // item (channel lane + 64 i, plane t) at 4 i + t; 0 = no item
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < CPL; ++i) {
       const int c = lane + 64 * i;
 #pragma unroll
       for (int t = 0; t < kPlanes; ++t) {
-        const uint64_t gain = (uint64_t)__double_as_longlong(ldexp((double)w[i], -2 * t));
-        key[4 * i + t] = c < d ? (gain | (uint64_t)(256 - c) << 2 | (uint64_t)(3 - t)) : 0ull;
+        const uint64_t gain = (uint64_t)__double_as_longlong(ldexp((double)w[i], -2 * t)) >> 29;
+        key[4 * i + t] = c < d ? (gain << 11 | (uint64_t)(256 - c) << 2 | (uint64_t)(3 - t)) : 0ull;
       }
     }
-    const uint64_t K = wave_kth_key(key, (uint32_t)budget, 62);
+    const uint64_t K = wave_kth_key(key, (uint32_t)budget, 44);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < CPL; ++i) {
       int tc = 0;
 #pragma unroll
       for (int t = 0; t < kPlanes; ++t) tc += key[4 * i + t] >= K;
@@ -116,23 +110,23 @@ __global__ __launch_bounds__(1024) void allocate_kernel(const float* __restrict_
   } else if (flag == 0 && mode == 1 && budget > 0) {
     // fixed-depth comparison mode: 4 planes on the m channels of largest |q_c|
     const uint32_t m = (uint32_t)(budget / kPlanes);
-    uint64_t key[4];
+    uint64_t key[CPL];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < CPL; ++i) {
       const int c = lane + 64 * i;
       key[i] = c < d ? ((uint64_t)__float_as_uint(aq[i]) << 8 | (uint64_t)(255 - c)) : 0ull;
     }
     // a channel with |q| = +0 and c = 255 has key 0: count it via the >= test only
     // when something else is smaller, so search over keys + 1
 #pragma unroll
-    for (int i = 0; i < 4; ++i) key[i] = lane + 64 * i < d ? key[i] + 1 : 0ull;
+    for (int i = 0; i < CPL; ++i) key[i] = lane + 64 * i < d ? key[i] + 1 : 0ull;
     const uint64_t K = wave_kth_key(key, m, 40);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) t[i] = (lane + 64 * i < d && key[i] >= K) ? kPlanes : 0;
+    for (int i = 0; i < CPL; ++i) t[i] = (lane + 64 * i < d && key[i] >= K) ? kPlanes : 0;
   }
 
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < CPL; ++i) {
     const int c = lane + 64 * i;
     if (c < d) {
       depth[(int64_t)h * d + c] = (uint8_t)t[i];
@@ -158,7 +152,10 @@ __global__ __launch_bounds__(1024) void allocate_kernel(const float* __restrict_
 hipError_t launch_allocate(const float* q, const float* sigma2, int h_kv, int g, int d,
                            int mode, int budget, uint8_t* depth, uint8_t* uni,
                            uint32_t* status, hipStream_t s) {
-  allocate_kernel<<<h_kv, 64 * g, 0, s>>>(q, sigma2, g, d, mode, budget, depth, uni, status);
+  if (d <= 128)
+    allocate_kernel<2><<<h_kv, 64 * g, 0, s>>>(q, sigma2, g, d, mode, budget, depth, uni, status);
+  else
+    allocate_kernel<4><<<h_kv, 64 * g, 0, s>>>(q, sigma2, g, d, mode, budget, depth, uni, status);
   return hipGetLastError();
 }
 

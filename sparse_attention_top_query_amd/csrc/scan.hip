@@ -338,10 +338,20 @@ struct HostTile {
   static constexpr int TB = G <= 4 ? 32 : 16;   // LDS for the coefficients bounds it for large G
 };
 
+// Workgroup ids are dealt round-robin to the 8 XCDs, each with its own L2.  The
+// kernel maps id w to logical tile (w % 8) * per + w / 8 so that every XCD scans
+// one contiguous range of (KV head, tile) pairs: neighbouring tiles, whose head
+// runs can share a cache line at their boundary, then meet in the same L2.
+constexpr int kXcds = 8;
+
 template <int G, int TB>
-__global__ __launch_bounds__((Cfg<G, TB>::threads)) void scan_kernel(ScanArgs a) {
+__global__ __launch_bounds__((Cfg<G, TB>::threads)) void scan_kernel(ScanArgs a, int64_t tiles, int64_t total) {
   __shared__ ScanSmem<G, TB> sm;
-  scan_tile<G, TB>(a, blockIdx.y, blockIdx.x, sm);
+  const int64_t w = blockIdx.x;
+  const int64_t per = (total + kXcds - 1) / kXcds;
+  const int64_t L = (w % kXcds) * per + w / kXcds;
+  if (L >= total) return;
+  scan_tile<G, TB>(a, L / tiles, L % tiles, sm);
 }
 
 // ---------------------------------------------------------------------------
@@ -433,8 +443,10 @@ template <int G, int TB>
 hipError_t launch_g(const uint8_t* rec, const float* q, const uint8_t* depth, const uint8_t* uni,
                     int h_kv, const Layout& L, int d, float* scores, int64_t ld, hipStream_t s) {
   const ScanArgs a{rec, q, depth, uni, L.n, L.nb, L.H, L.P, L.R, d, scores, ld};
-  dim3 grid((unsigned)((L.nb + TB - 1) / TB), (unsigned)h_kv);
-  scan_kernel<G, TB><<<grid, Cfg<G, TB>::threads, 0, s>>>(a);
+  const int64_t tiles = (L.nb + TB - 1) / TB;
+  const int64_t total = tiles * h_kv;
+  const int64_t per = (total + kXcds - 1) / kXcds;
+  scan_kernel<G, TB><<<(unsigned)(per * kXcds), Cfg<G, TB>::threads, 0, s>>>(a, tiles, total);
   return hipGetLastError();
 }
 
