@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="w3_host_1m_B92")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing leg")
+    ap.add_argument("--no-compare", action="store_true",
+                    help="skip the fixed-depth (136-bit, 68-bit) comparison scans")
     ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--residency", choices=["staged", "direct"], default="direct",
                     help="host-resident records: read in place by the scan (default) or staged through HBM")
@@ -182,7 +184,14 @@ def cpu_baseline(wl, q_np, s2_np, budget, seconds=15.0):
             O.topk(s, wl.k)
             heads += 1
     dt = time.perf_counter() - t0
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next(line.split(":", 1)[1].strip() for line in f if line.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
     return {"value": heads * wl.n / dt, "unit": "keys/s", "cores": 1, "kind": "oracle",
+            "host": f"{model}, {os.cpu_count()} logical CPUs visible, numpy {np.__version__}",
             "sample": f"{heads} query-head scans (the {wl.g} heads of KV head 0, cycled) x {wl.n} keys: "
                       f"allocation + fp64 scores + top-{wl.k}, codes precomputed; numpy single-threaded, "
                       f"{dt:.1f} s"}
@@ -294,6 +303,34 @@ def main():
                 "unit": "T lane-op/s", "frac": round(tops / VALU_PEAK_TOPS, 4), **common,
                 "ops_per_launch": ops, "hbm_achieved_gbps": round(achieved, 2),
                 "hbm_frac": round(achieved / HBM_PEAK_GBPS, 4), "record_copies_cycled": len(copies)}
+    # The pages compare the method against fixed-depth scans: 136 bits (34
+    # channels x 4 planes) and 68 bits (17 x 4), channels by largest |q_c|.
+    # Same records, queries and stream, timed the same way.
+    comparison = None
+    if not args.no_compare:
+        def timed(b, m, steps):
+            def one():
+                F.allocate(q, s2, b, mode=m, depth=depth, union_depth=uni)
+                F.scan_topk(records, q, depth, uni, n, k, residency=residency, workspace=ws, idx=idx)
+            for _ in range(2):
+                one()
+            torch.cuda.synchronize(dev)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(steps):
+                one()
+            e1.record(stream)
+            torch.cuda.synchronize(dev)
+            ms = e0.elapsed_time(e1) / steps
+            return {"ms_per_step": round(ms, 4),
+                    "bytes_per_key": round(algorithmic_bytes(uni.cpu().numpy(), n) / (hk * n), 3)}
+        csteps = max(3, min(args.steps, 20))
+        comparison = {"method_B": budget, "method_ms_per_step": round(step_ms, 4)}
+        for name, b, m in (("fixed_136", 136, F.TOPQ), ("fixed_68", 68, F.TOPQ), ("method_B68", 68, F.WATERFILL)):
+            comparison[name] = timed(b, m, csteps)
+        comparison["speedup_vs_fixed_136"] = round(comparison["fixed_136"]["ms_per_step"] / step_ms, 3)
+        comparison["bytes_method_B68_vs_fixed_68"] = round(
+            comparison["method_B68"]["bytes_per_key"] / comparison["fixed_68"]["bytes_per_key"], 3)
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(wl, q_np, s2_np, budget)
@@ -315,6 +352,7 @@ def main():
                    "mode": wl.mode},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "comparison": comparison,
         "bytes_per_key": round(alg_bytes / (hk * n), 3),
         "link_frac_of_measured_h2d_per_step": round(alg_bytes / (step_ms * 1e-3) / 1e9 / h2d_peak, 4)
         if host else None,
