@@ -1,0 +1,105 @@
+"""Plain CPU oracle for sparse attention over the selected keys.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module.  The product path
+never imports, calls or links it, and it imports nothing from the product path.
+
+What it follows.  On the pages about "Fathom: Per-Query Read Depth for Sparse
+Decoding over Offloaded KV Caches" (arXiv 2609.17652), the scan produces the
+top-k key indices of each query and real attention is then computed over those
+keys only ([Digest] Output; [Review] "Frequently asked questions": the scan
+picks the top-k for sparse attention).  The pages give no formula for that
+attention, so the reading taken is the standard one:
+
+    s_j = scale * (q . K_j)                   for j in the query's index set S
+    M   = max_j s_j
+    o   = sum_j exp(s_j - M) V_j / sum_j exp(s_j - M)
+    lse = M + log sum_j exp(s_j - M)          (= log sum_j exp(s_j))
+
+with K and V the cache rows as the serving stack holds them (bf16, token-major
+[n][d]), one query head at a time; a query head of a GQA group uses the rows of
+its KV head.  Index entries outside [0, n) are skipped; with none left, o = 0
+and lse = -inf.
+
+Precision: bf16 values and fp32 q are exact in fp64, every product q_c K_jc is
+exact (24 + 8 significant bits), and the rest is fp64.
+
+Parity status (what pins it, in tests/test_oracle_attention.py):
+  bf16_to_f64           pinned: hand-decoded bit patterns (normal, negative,
+                        largest finite, subnormal, signed zero).
+  sparse_attention      pinned: the full index set equals dense softmax
+                        attention from scipy.special.softmax and a matmul;
+                        one key gives V_j and lse = s_j exactly; q = 0 gives
+                        the mean of the rows (exact rationals) and lse = log k;
+                        two keys follow the logistic closed form; invariance
+                        to the order of the index set; huge common logits do
+                        not overflow; skipped indices equal the valid subset.
+  attention_tolerance   derived from the fp32 arithmetic of the GPU kernel
+                        (see its docstring); not a pin.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Decode bf16 bit patterns (uint16): a bf16 value is the fp32 value whose
+    upper 16 bits are the pattern and whose lower 16 bits are zero."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def logits(q: np.ndarray, k_rows: np.ndarray, idx: np.ndarray, scale: float) -> np.ndarray:
+    """s_j = scale * (q . K_j) in fp64 for the entries of idx (already valid)."""
+    kk = bf16_to_f64(k_rows[idx])                       # [m, d]
+    return np.float64(np.float32(scale)) * (kk @ np.asarray(q, np.float32).astype(np.float64))
+
+
+def sparse_attention(q: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray, idx: np.ndarray,
+                     scale: float):
+    """Attention of one query over the keys idx of one KV head.
+
+    q float32 [d]; k_rows, v_rows uint16 (bf16) [n, d]; idx integer [k].
+    Returns (o float64 [d], lse float64, p float64 [m] weights of the valid
+    entries, valid int64 [m] their indices in idx order)."""
+    n, d = k_rows.shape
+    idx = np.asarray(idx, dtype=np.int64)
+    valid = idx[(idx >= 0) & (idx < n)]
+    if valid.size == 0:
+        return np.zeros(d), -np.inf, np.zeros(0), valid
+    s = logits(q, k_rows, valid, scale)
+    m = s.max()
+    w = np.exp(s - m)
+    total = w.sum()
+    p = w / total
+    o = p @ bf16_to_f64(v_rows[valid])
+    return o, m + np.log(total), p, valid
+
+
+def attention_tolerance(q, k_rows, v_rows, idx, scale, chain: int = 128):
+    """Bound on |o_gpu - o| per channel and on |lse_gpu - lse| for an fp32
+    kernel that forms each logit as scale * (a sum of d products with a
+    reduction chain of at most 24 roundings for d <= 256), exponentiates
+    s_j - M, and accumulates numerator and denominator along chains of at most
+    `chain` additions.  With u = 2^-24, A_j = |scale| sum_c |q_c K_jc|:
+      |ds_j| <= 26 u A_j =: e_s                      (logit)
+      relative error of each weight <= 2 e_s + u |s_j - M| + 4 u =: eta
+      |do_c| <= (2 eta + 2 chain u) sum_j p_j |V_jc|
+      |dlse| <= e_s + eta + chain u + 2 u |lse|.
+    The u |s_j - M| term is weighted by p_j <= e^-(M - s_j) in the sum, so it
+    is taken at its maximum over j of (M - s_j) e^-(M - s_j) <= 1/e per unit of
+    p.  A safety factor of 4 covers the expf error (a few ulp)."""
+    n, d = k_rows.shape
+    o, lse, p, valid = sparse_attention(q, k_rows, v_rows, idx, scale)
+    if valid.size == 0:
+        return np.zeros(d), 0.0
+    u = 2.0 ** -24
+    kk = bf16_to_f64(k_rows[valid])
+    a = abs(float(np.float32(scale))) * (np.abs(kk) @ np.abs(np.asarray(q, np.float32).astype(np.float64)))
+    e_s = 26 * u * a.max()
+    eta = 2 * e_s + u + 4 * u
+    pv = p @ np.abs(bf16_to_f64(v_rows[valid]))
+    tau_o = 4 * (2 * eta + 2 * chain * u) * pv
+    tau_lse = 4 * (e_s + eta + chain * u + 2 * u * abs(lse))
+    return tau_o, tau_lse

@@ -123,6 +123,23 @@ def layer_inputs(wl: Workload, layer: int = 0, n: int | None = None, threads: in
     return k, q, s2
 
 
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Storage format of a bf16 cache: the fp32 values rounded to bf16 (round to
+    nearest, ties to even) and returned as uint16 bit patterns.  Inputs are
+    finite."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = ((b >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((b + r) >> np.uint32(16)).astype(np.uint16)
+
+
+def kv_rows_bf16(wl_key: int, layer: int, session: int, g: int, n: int, d: int, outliers: int):
+    """(K bf16 [n, d], V bf16 [n, d]) cache rows of one KV head: K is the same
+    draw as kv_head() rounded to bf16; V = N(0, 1) from the stream [..., 2]."""
+    k, _ = kv_head(wl_key, layer, session, g, n, d, outliers)
+    v = _rng(wl_key, layer, session, g, 2).standard_normal((n, d), dtype=np.float32)
+    return to_bf16_bits(k), to_bf16_bits(v)
+
+
 def small_case(seed: int, h_kv: int, g: int, n: int, d: int, outliers: int = 0):
     """A small seeded case with the same recipe, for parity tests at odd shapes."""
     rng = _rng(1000 + seed)
