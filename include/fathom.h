@@ -12,6 +12,8 @@
  *   pack_bitplanes   once per cache: 4-bit codes as channel-major bit planes;
  *   allocate_depths  per query step: read depth t_c of every channel per query head;
  *   scan_topk        per query step: score every key from its read prefix, return top-k.
+ * and the attention that consumes the selection is a fourth:
+ *   attend_topk      per query step: attention of each query head over its top-k keys.
  *
  * Conventions shared by every call:
  *   - Device pointers are HIP device memory unless stated; every call is
@@ -73,6 +75,7 @@ enum fathom_depth_mode {
 #define FATHOM_FLAG_Q_NONFINITE 4u          /* allocate: q is NaN or +-Inf              */
 #define FATHOM_FLAG_SIGMA2_INVALID 8u       /* allocate: sigma2 negative or non-finite  */
 #define FATHOM_FLAG_IMPORTANCE_OVERFLOW 16u /* allocate: q^2 sigma2 overflows fp32      */
+#define FATHOM_FLAG_INDEX_RANGE 32u         /* attend: an index outside [0, n), skipped */
 
 /* ---------------------------------------------------------------------------
  * Record layout.  [Digest] Inputs and key module 1, [Review] FAQ: the 4-bit K
@@ -170,6 +173,43 @@ int fathom_scan_scores(const void* records, int residency, const float* q,
                        const uint8_t* depth, const uint8_t* union_depth, int h_q,
                        int h_kv, int64_t n, int d, float* scores, int64_t ld,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace attend_topk needs: per query head and split of its
+ * k keys, a partial output (d + 2 floats) and a flag word. */
+size_t fathom_attend_workspace_bytes(int h_q, int d, int k);
+
+/* attend_topk -- attention of every query head over its selected keys
+ * ([Digest] Output: top-k key indices per query, then real attention over those
+ * keys; [Review] FAQ: the scan picks the top-k for sparse attention).  The pages
+ * give no formula; the reading is the standard softmax attention:
+ *   s_j = scale * (q_h . K_j) for j in topk_idx[h],
+ *   out[h] = sum_j exp(s_j - M) V_j / sum_j exp(s_j - M),  M = max_j s_j,
+ *   lse[h] = M + log sum_j exp(s_j - M),
+ * with K, V the rows of KV head h / G.
+ *   k_cache, v_cache  bf16 (uint16 bit patterns) [h_kv][n][d], token-major, as the
+ *                     serving stack holds its cache; device memory (FATHOM_HBM) or
+ *                     pinned host memory read in place (FATHOM_HOST_DIRECT); both
+ *                     in the same residency; 16-byte aligned; read-only.
+ *   q                 device, float32 [h_q][d], 16-byte aligned.
+ *   topk_idx          device, int32 [h_q][k] (scan_topk's output, or any list;
+ *                     order does not matter, repeats count repeatedly).  Entries
+ *                     outside [0, n) are skipped and flagged.
+ *   d                 8, 16, 32, 64, 128 or 256.
+ *   out               device, float32 [h_q][d].
+ *   lse               device, float32 [h_q] or NULL.  A head with no valid entry
+ *                     gets out = 0 and lse = -inf.
+ *   status            device, uint32 [h_q] or NULL, written (not OR-ed):
+ *                     FATHOM_FLAG_INDEX_RANGE if the head's list held an entry
+ *                     outside [0, n).
+ *   workspace         device, >= fathom_attend_workspace_bytes(h_q, d, k) bytes,
+ *                     256-byte aligned.
+ * fp32 arithmetic: logits as fused multiply-adds reduced across lanes, expf of
+ * s_j - M, sums along chains of at most 16 + 6 + 4 + S additions, S = ceil(k / 256)
+ * (ceil(k / 128) for d = 256) splits of the list. */
+int attend_topk(const void* k_cache, const void* v_cache, int residency, const float* q,
+                const int32_t* topk_idx, int h_q, int h_kv, int64_t n, int d, int k,
+                float scale, float* out, float* lse, uint32_t* status, void* workspace,
+                size_t workspace_bytes, void* stream);
 
 /* Message for the last failing call on this thread ("" if none). */
 const char* fathom_last_error(void);

@@ -13,6 +13,8 @@ from .fathom import (  # noqa: F401
     WATERFILL,
     FathomError,
     allocate,
+    attend,
+    attend_workspace_bytes,
     load,
     pack,
     prefix_bytes,
@@ -22,5 +24,5 @@ from .fathom import (  # noqa: F401
     workspace_bytes,
 )
 
-__all__ = ["HBM", "HOST_DIRECT", "HOST_STAGED", "TOPQ", "WATERFILL", "FathomError", "allocate", "load", "pack",
+__all__ = ["HBM", "HOST_DIRECT", "HOST_STAGED", "TOPQ", "WATERFILL", "FathomError", "allocate", "attend", "attend_workspace_bytes", "load", "pack",
            "prefix_bytes", "record_bytes", "scan_scores", "scan_topk", "workspace_bytes"]

@@ -4,10 +4,12 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
 
+#include "attend.h"
 #include "fathom_internal.h"
 
 namespace {
@@ -51,29 +53,34 @@ int64_t score_ld(int64_t n) { return (n + 63) / 64 * 64; }
 
 size_t al256(size_t x) { return (x + 255) / 256 * 256; }
 
-// Resolve the device-visible address of the records for the claimed residency.
-int resolve_records(const void* records, int residency, const uint8_t** dev) {
+// Resolve the device-visible address of a buffer (`what`: records, k_cache, ...)
+// for the claimed residency.
+int resolve_view(const void* buf, int residency, const char* what, const uint8_t** dev) {
   hipPointerAttribute_t attr;
-  hipError_t e = hipPointerGetAttributes(&attr, records);
+  hipError_t e = hipPointerGetAttributes(&attr, buf);
   if (e != hipSuccess) {
     (void)hipGetLastError();  // not a pointer HIP knows: pageable host memory
-    return fail(FATHOM_ERESIDENCY, "records pointer is not HIP device or pinned host memory");
+    return fail(FATHOM_ERESIDENCY, "%s pointer is not HIP device or pinned host memory", what);
   }
   if (residency == FATHOM_HBM) {
     if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged)
-      return fail(FATHOM_ERESIDENCY, "FATHOM_HBM records must be device memory");
-    *dev = static_cast<const uint8_t*>(records);
+      return fail(FATHOM_ERESIDENCY, "FATHOM_HBM %s must be device memory", what);
+    *dev = static_cast<const uint8_t*>(buf);
     return FATHOM_OK;
   }
   if (residency == FATHOM_HOST_DIRECT || residency == FATHOM_HOST_STAGED) {
     if (attr.type != hipMemoryTypeHost)
-      return fail(FATHOM_ERESIDENCY, "host-resident records must be pinned host memory");
+      return fail(FATHOM_ERESIDENCY, "host-resident %s must be pinned host memory", what);
     const uint8_t* p = static_cast<const uint8_t*>(attr.devicePointer);
-    if (!p) return fail(FATHOM_ERESIDENCY, "pinned host records have no device mapping");
-    *dev = p + (static_cast<const uint8_t*>(records) - static_cast<const uint8_t*>(attr.hostPointer));
+    if (!p) return fail(FATHOM_ERESIDENCY, "pinned host %s has no device mapping", what);
+    *dev = p + (static_cast<const uint8_t*>(buf) - static_cast<const uint8_t*>(attr.hostPointer));
     return FATHOM_OK;
   }
   return fail(FATHOM_EINVAL, "unknown residency %d", residency);
+}
+
+int resolve_records(const void* records, int residency, const uint8_t** dev) {
+  return resolve_view(records, residency, "records", dev);
 }
 
 int check_scan_args(const void* records, int residency, const float* q, const uint8_t* depth,
@@ -220,6 +227,47 @@ int scan_topk(const void* records, int residency, const float* q, const uint8_t*
   hipError_t e = fathom::launch_select(scores, ld, h_q, n, k, topk_idx, topk_score,
                                        fathom::carve_select(sel_base, h_q, n, k), s);
   if (e != hipSuccess) return hip_fail(e, "select launch");
+  return ok();
+}
+
+size_t fathom_attend_workspace_bytes(int h_q, int d, int k) {
+  if (h_q <= 0 || d <= 0 || k <= 0) return 0;
+  return fathom::attend_workspace_bytes(h_q, d, k);
+}
+
+int attend_topk(const void* k_cache, const void* v_cache, int residency, const float* q,
+                const int32_t* topk_idx, int h_q, int h_kv, int64_t n, int d, int k, float scale,
+                float* out, float* lse, uint32_t* status, void* workspace, size_t workspace_bytes,
+                void* stream) {
+  if (h_kv < 1 || h_kv > 65535) return fail(FATHOM_ESHAPE, "h_kv=%d outside [1, 65535]", h_kv);
+  if (h_q < h_kv || h_q % h_kv != 0)
+    return fail(FATHOM_ESHAPE, "h_q=%d is not a multiple of h_kv=%d", h_q, h_kv);
+  if (d != 8 && d != 16 && d != 32 && d != 64 && d != 128 && d != 256)
+    return fail(FATHOM_ESHAPE, "attend_topk needs d in {8, 16, 32, 64, 128, 256} (got %d)", d);
+  if (n < 1 || n > (int64_t(1) << 34)) return fail(FATHOM_ESHAPE, "n=%lld out of range", (long long)n);
+  if (k < 1 || k > (1 << 28)) return fail(FATHOM_ESHAPE, "k=%d outside [1, 2^28]", k);
+  if (!std::isfinite(scale)) return fail(FATHOM_EINVAL, "scale must be finite");
+  if (!k_cache || !v_cache || !q || !topk_idx || !out) return fail(FATHOM_EINVAL, "null pointer argument");
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(q, 16))
+    return fail(FATHOM_EINVAL, "k_cache, v_cache and q must be 16-byte aligned");
+  if (!aligned(topk_idx, 4) || !aligned(out, 4) || (lse && !aligned(lse, 4)) || (status && !aligned(status, 4)))
+    return fail(FATHOM_EINVAL, "topk_idx/out/lse/status must be 4-byte aligned");
+  if (residency != FATHOM_HBM && residency != FATHOM_HOST_DIRECT)
+    return fail(FATHOM_ERESIDENCY, "attend_topk reads its caches from HBM or in place from pinned host memory");
+  const size_t need = fathom::attend_workspace_bytes(h_q, d, k);
+  if (!workspace || workspace_bytes < need)
+    return fail(FATHOM_EWORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, need);
+  if (!aligned(workspace, 256)) return fail(FATHOM_EINVAL, "workspace must be 256-byte aligned");
+  const uint8_t* kd = nullptr;
+  const uint8_t* vd = nullptr;
+  int st = resolve_view(k_cache, residency, "k_cache", &kd);
+  if (st) return st;
+  st = resolve_view(v_cache, residency, "v_cache", &vd);
+  if (st) return st;
+  hipError_t e = fathom::launch_attend(reinterpret_cast<const uint16_t*>(kd), reinterpret_cast<const uint16_t*>(vd),
+                                       q, topk_idx, h_q, h_kv, n, d, k, scale, out, lse, status, workspace,
+                                       static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "attend launch");
   return ok();
 }
 

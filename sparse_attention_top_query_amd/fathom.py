@@ -27,6 +27,7 @@ FLAG_SCALE_OVERFLOW = 2
 FLAG_Q_NONFINITE = 4
 FLAG_SIGMA2_INVALID = 8
 FLAG_IMPORTANCE_OVERFLOW = 16
+FLAG_INDEX_RANGE = 32
 
 STATUS_NAMES = {0: "FATHOM_OK", -1: "FATHOM_EINVAL", -2: "FATHOM_ESHAPE", -3: "FATHOM_EBUDGET",
                 -5: "FATHOM_EWORKSPACE", -6: "FATHOM_EHIP", -7: "FATHOM_ERESIDENCY"}
@@ -61,6 +62,8 @@ def load() -> ctypes.CDLL:
         "fathom_workspace_bytes": (S, [I, I, L, I, I, I]),
         "scan_topk": (I, [P, I, P, P, P, I, I, L, I, I, P, P, P, S, P]),
         "fathom_scan_scores": (I, [P, I, P, P, P, I, I, L, I, P, L, P, S, P]),
+        "fathom_attend_workspace_bytes": (S, [I, I, I]),
+        "attend_topk": (I, [P, P, I, P, P, I, I, L, I, I, ctypes.c_float, P, P, P, P, S, P]),
         "fathom_last_error": (ctypes.c_char_p, []),
         "fathom_version": (I, []),
     }
@@ -212,3 +215,47 @@ def scan_scores(records: torch.Tensor, q: torch.Tensor, depth: torch.Tensor, uni
                                      h_q, h_kv, n, d, _ptr(out), out.shape[1], _ptr(workspace), wsn,
                                      _stream(q)))
     return out[:, :n]
+
+
+def attend_workspace_bytes(h_q: int, d: int, k: int) -> int:
+    return int(load().fathom_attend_workspace_bytes(h_q, d, k))
+
+
+def attend(k_cache: torch.Tensor, v_cache: torch.Tensor, q: torch.Tensor, idx: torch.Tensor, scale: float,
+           residency: int | None = None, out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+           status: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """attend_topk: -> (float32 out [h_q, d], float32 lse [h_q]) attention over the selected keys.
+
+    ``k_cache``/``v_cache``: bf16 [h_kv, n, d] (torch.bfloat16, or their bit
+    patterns as int16/uint16), both device tensors (HBM) or both pinned host
+    tensors (read in place).  ``idx``: int32 [h_q, k]."""
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        if not isinstance(t, torch.Tensor) or t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+            raise TypeError(f"{name} must be a bfloat16 (or 16-bit pattern) tensor")
+        if not t.is_contiguous() or t.dim() != 3:
+            raise ValueError(f"{name} must be a contiguous [h_kv, n, d] tensor")
+    if k_cache.shape != v_cache.shape or k_cache.is_cuda != v_cache.is_cuda:
+        raise ValueError("k_cache and v_cache must have one shape and one residency")
+    _need(q, "q", torch.float32, 2)
+    _need(idx, "idx", torch.int32, 2)
+    h_kv, n, d = k_cache.shape
+    h_q, k = idx.shape
+    if q.shape != (h_q, d):
+        raise ValueError("q must be [h_q, d] with h_q = idx.shape[0] and d = k_cache.shape[2]")
+    if residency is None:
+        residency = HBM if k_cache.is_cuda else HOST_DIRECT
+    if out is None:
+        out = torch.empty((h_q, d), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, 2)
+    if lse is None:
+        lse = torch.empty(h_q, dtype=torch.float32, device=q.device)
+    _need(lse, "lse", torch.float32, 1)
+    if status is not None:
+        _need(status, "status", torch.int32)
+    if workspace is None:
+        workspace = torch.empty(max(attend_workspace_bytes(h_q, d, k), 1), dtype=torch.uint8, device=q.device)
+    _need(workspace, "workspace", torch.uint8)
+    _check(load().attend_topk(_ptr(k_cache), _ptr(v_cache), residency, _ptr(q), _ptr(idx), h_q, h_kv, n, d, k,
+                              ctypes.c_float(scale), _ptr(out), _ptr(lse), _ptr(status), _ptr(workspace),
+                              workspace.numel(), _stream(q)))
+    return out, lse

@@ -31,7 +31,8 @@ def lib():
 def test_header_declares_the_entry_points():
     names = header_functions()
     for fn in ("pack_bitplanes", "allocate_depths", "scan_topk", "fathom_workspace_bytes",
-               "fathom_scan_scores", "fathom_last_error", "fathom_record_bytes"):
+               "fathom_scan_scores", "fathom_last_error", "fathom_record_bytes", "attend_topk",
+               "fathom_attend_workspace_bytes"):
         assert fn in names
 
 
@@ -82,6 +83,32 @@ def test_host_validation_errors(lib):
     assert lib.scan_topk(fake, 0, fake, fake, fake, 4, 3, 128, 8, 4, fake, None, fake, 1 << 20, None) == -2
     assert lib.scan_topk(fake, 0, fake, fake, fake, 4, 1, -1, 8, 4, fake, None, fake, 1 << 20, None) == -2
     assert lib.fathom_scan_scores(fake, 0, None, fake, fake, 4, 1, 128, 8, fake, 128, None, 0, None) == -1
+
+
+def test_attend_workspace_and_validation(lib):
+    P = ctypes.c_void_p
+    f = ctypes.c_float
+    fake = P(0x1000)
+    # one split of 256 keys per query head at d = 128: (d + 2) floats + a flag word, 256-byte padded
+    assert lib.fathom_attend_workspace_bytes(32, 128, 256) == 32 * 130 * 4 + 256   # 16640 is 65 x 256
+    assert lib.fathom_attend_workspace_bytes(32, 128, 2048) > lib.fathom_attend_workspace_bytes(32, 128, 256)
+    assert lib.fathom_attend_workspace_bytes(0, 128, 64) == 0
+    ws = 1 << 20
+
+    def call(kc=fake, vc=fake, res=0, q=fake, idx=fake, h_q=4, h_kv=1, n=1000, d=128, k=64, scale=0.1,
+             out=fake, wsp=fake, wsb=ws):
+        return lib.attend_topk(kc, vc, res, q, idx, h_q, h_kv, n, d, k, f(scale), out, None, None, wsp, wsb, None)
+    assert call(d=100) == -2 and "d in" in _err(lib)
+    assert call(d=512) == -2
+    assert call(h_q=6, h_kv=4) == -2
+    assert call(k=0) == -2
+    assert call(n=0) == -2
+    assert call(scale=float("nan")) == -1
+    assert call(kc=None) == -1
+    assert call(out=None) == -1
+    assert call(q=P(0x1004)) == -1 and "aligned" in _err(lib)
+    assert call(res=2) == -7
+    assert call(wsb=16) == -5
 
 
 def test_binding_refuses_cpu_tensors(lib):

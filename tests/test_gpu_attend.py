@@ -1,0 +1,196 @@
+"""GPU parity of attend_topk (attention over the selected keys) against the
+oracle, through the C ABI: every supported d, one and several splits of the
+index list, HBM and pinned-host caches, out-of-range and repeated entries, and
+the whole path pack -> allocate -> scan_topk -> attend_topk."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention_oracle as A
+from oracle import fathom_oracle as O
+from synthetic import small_case, to_bf16_bits
+from tests.parity import dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def F():
+    from sparse_attention_top_query_amd import fathom
+    fathom.load()
+    assert torch.cuda.is_available()
+    return fathom
+
+
+def cache(rng, h_kv, n, d, kscale=1.0):
+    k = to_bf16_bits((rng.standard_normal((h_kv, n, d)) * kscale).astype(np.float32))
+    v = to_bf16_bits(rng.standard_normal((h_kv, n, d)).astype(np.float32))
+    return k, v
+
+
+def to_torch(a, pinned=False):
+    t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16))
+    if pinned:
+        p = torch.empty(t.shape, dtype=torch.int16, pin_memory=True)
+        p.copy_(t)
+        return p
+    return t.to("cuda:0")
+
+
+def splits(d, k):
+    kw = min(256, 4096 // (d // 8))
+    return -(-k // kw)
+
+
+def check(out, lse, q, kc, vc, idx, scale, g, where=""):
+    h_q, d = q.shape
+    worst = 0.0
+    for h in range(h_q):
+        o, l, _, valid = A.sparse_attention(q[h], kc[h // g], vc[h // g], idx[h], scale)
+        tau_o, tau_l = A.attention_tolerance(q[h], kc[h // g], vc[h // g], idx[h], scale,
+                                             chain=30 + splits(d, idx.shape[1]))
+        if valid.size == 0:
+            assert np.all(out[h] == 0) and lse[h] == -np.inf, f"{where} head {h}: empty set"
+            continue
+        err = np.abs(out[h].astype(np.float64) - o)
+        assert np.all(err <= tau_o), (f"{where} head {h}: worst excess {float(np.max(err - tau_o)):.3e} "
+                                      f"at channel {int(np.argmax(err - tau_o))}")
+        assert abs(float(lse[h]) - l) <= tau_l, f"{where} head {h}: lse {lse[h]} vs {l} (tol {tau_l:.2e})"
+        worst = max(worst, float(np.max(err / np.maximum(tau_o, 1e-300))))
+    return worst
+
+
+def run(F, kc, vc, q, idx, scale, pinned=False, status=False):
+    st = torch.full((q.shape[0],), -1, dtype=torch.int32, device="cuda:0") if status else None
+    out, lse = F.attend(to_torch(kc, pinned), to_torch(vc, pinned), dev(q), dev(idx.astype(np.int32)), scale,
+                        status=st)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), lse.cpu().numpy(), (st.cpu().numpy() if status else None)
+
+
+CASES = [  # (h_kv, g, n, d, k)
+    (2, 4, 3000, 128, 300),
+    (1, 1, 500, 128, 1),
+    (1, 2, 700, 128, 256),
+    (1, 2, 700, 128, 257),
+    (3, 1, 4096, 64, 1000),
+    (1, 8, 2000, 256, 129),
+    (2, 2, 300, 32, 77),
+    (1, 4, 1000, 16, 600),
+    (1, 1, 5000, 8, 2048),
+    (1, 16, 1024, 128, 64),
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_attend_matches_oracle(F, case):
+    h_kv, g, n, d, k = case
+    print(f"attend case={case}", flush=True)
+    rng = np.random.default_rng(hash(case) % 1000)
+    kc, vc = cache(rng, h_kv, n, d, kscale=2.0)
+    q = rng.standard_normal((h_kv * g, d)).astype(np.float32)
+    idx = np.stack([np.sort(rng.choice(n, k, replace=False)) for _ in range(h_kv * g)])
+    scale = float(1 / np.sqrt(d))
+    out, lse, _ = run(F, kc, vc, q, idx, scale)
+    check(out, lse, q, kc, vc, idx, scale, g, where=str(case))
+
+
+def test_pinned_host_caches_are_bit_identical_to_hbm(F):
+    rng = np.random.default_rng(11)
+    h_kv, g, n, d, k = 2, 4, 6000, 128, 700
+    kc, vc = cache(rng, h_kv, n, d)
+    q = rng.standard_normal((h_kv * g, d)).astype(np.float32)
+    idx = np.stack([np.sort(rng.choice(n, k, replace=False)) for _ in range(h_kv * g)])
+    a = run(F, kc, vc, q, idx, 0.09)
+    b = run(F, kc, vc, q, idx, 0.09, pinned=True)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    check(b[0], b[1], q, kc, vc, idx, 0.09, g, where="pinned")
+
+
+def test_out_of_range_entries_are_skipped_and_flagged(F):
+    rng = np.random.default_rng(12)
+    h_kv, g, n, d = 1, 4, 900, 64
+    kc, vc = cache(rng, h_kv, n, d)
+    q = rng.standard_normal((4, d)).astype(np.float32)
+    idx = np.stack([np.sort(rng.choice(n, 300, replace=False)) for _ in range(4)]).astype(np.int64)
+    idx[1, 5] = -1
+    idx[1, 200] = n
+    idx[2, :] = -7                                      # nothing valid: out 0, lse -inf
+    idx[3, 299] = 2 ** 31 - 1
+    out, lse, st = run(F, kc, vc, q, idx, 0.125, status=True)
+    assert list(st) == [0, 32, 32, 32]
+    check(out, lse, q, kc, vc, idx, 0.125, g, where="invalid entries")
+
+
+def test_repeated_entries_count_repeatedly(F):
+    rng = np.random.default_rng(13)
+    kc, vc = cache(rng, 1, 400, 128)
+    q = rng.standard_normal((1, 128)).astype(np.float32)
+    idx = np.array([[3, 3, 3, 10, 50, 50]])
+    out, lse, _ = run(F, kc, vc, q, idx, 0.2)
+    check(out, lse, q, kc, vc, idx, 0.2, 1, where="repeats")
+
+
+def test_large_logits_do_not_overflow(F):
+    rng = np.random.default_rng(14)
+    kc, vc = cache(rng, 1, 1000, 128, kscale=30.0)
+    q = (rng.standard_normal((2, 128)) * 30).astype(np.float32)
+    idx = np.stack([np.arange(0, 1000, 2), np.arange(1, 1000, 2)])
+    out, lse, _ = run(F, kc, vc, q, idx, 1.0)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    check(out, lse, q, kc, vc, idx, 1.0, 2, where="large logits")
+
+
+def test_repeat_calls_are_deterministic(F):
+    rng = np.random.default_rng(15)
+    kc, vc = cache(rng, 2, 5000, 128)
+    q = rng.standard_normal((8, 128)).astype(np.float32)
+    idx = np.stack([np.sort(rng.choice(5000, 2048, replace=False)) for _ in range(8)])
+    a = run(F, kc, vc, q, idx, 0.088)
+    b = run(F, kc, vc, q, idx, 0.088)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_residency_mismatch_is_rejected(F):
+    rng = np.random.default_rng(16)
+    kc, vc = cache(rng, 1, 100, 64)
+    q = dev(rng.standard_normal((1, 64)).astype(np.float32))
+    idx = dev(np.arange(10, dtype=np.int32)[None])
+    with pytest.raises(F.FathomError) as e:
+        F.attend(to_torch(kc, pinned=True), to_torch(vc, pinned=True), q, idx, 0.1, residency=F.HBM)
+    assert e.value.status == -7
+
+
+@pytest.mark.parametrize("residency", ["hbm", "host"])
+def test_whole_path_pack_allocate_scan_attend(F, residency):
+    # the top-k of the GPU scan feeds the attention; the oracle attends over the
+    # same index lists (which themselves are checked against the oracle scan in
+    # the scan parity tests)
+    h_kv, g, n, d, budget, k = 2, 4, 6000, 128, 92, 512
+    print(f"whole path residency={residency}", flush=True)
+    kf, q, s2 = small_case(77, h_kv, g, n, d, outliers=4)
+    rec = F.pack(dev(kf))
+    if residency == "host":
+        pinned = torch.empty(rec.shape, dtype=torch.uint8, pin_memory=True)
+        pinned.copy_(rec)
+        rec = pinned
+    depth, uni = F.allocate(dev(q), dev(s2), budget)
+    idx = F.scan_topk(rec, dev(q), depth, uni, n, k,
+                      residency=F.HBM if residency == "hbm" else F.HOST_DIRECT)
+    kc = to_bf16_bits(kf)
+    vc = to_bf16_bits(np.random.default_rng(78).standard_normal((h_kv, n, d)).astype(np.float32))
+    out, lse = F.attend(to_torch(kc, residency == "host"), to_torch(vc, residency == "host"), dev(q), idx,
+                        float(1 / np.sqrt(d)))
+    torch.cuda.synchronize()
+    idx_np = idx.cpu().numpy()
+    assert np.all(np.diff(idx_np, axis=1) > 0)
+    check(out.cpu().numpy(), lse.cpu().numpy(), q, kc, vc, idx_np, float(1 / np.sqrt(d)), g, where="whole path")
+    # and the index lists are the oracle's top-k up to boundary ties
+    from tests.parity import check_topk
+    for h in range(h_kv * g):
+        dep = O.waterfill_depths(O.importance(q[h], s2[h // g]), budget)
+        delta = O.block_scales(kf[h // g])
+        kappa = O.quantize_codes(kf[h // g], delta)
+        s_or, a_or = O.scores(q[h], kappa, delta, dep)
+        check_topk(idx_np[h], s_or, a_or, k, where=f"whole path head {h}")
