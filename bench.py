@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="w3_host_1m_B92")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing leg")
+    ap.add_argument("--no-attend", action="store_true",
+                    help="skip the attention over the selected keys (bf16 K/V caches are not built)")
     ap.add_argument("--no-compare", action="store_true",
                     help="skip the fixed-depth (136-bit, 68-bit) comparison scans")
     ap.add_argument("--kernel-reps", type=int, default=20)
@@ -127,10 +129,12 @@ def measure_h2d_peak(torch, dev, mib=512, reps=5) -> float:
     return (mib << 20) / (best * 1e-3) / 1e9
 
 
-def build_records(torch, F, wl, dev, layer=0):
+def build_records(torch, F, wl, dev, layer=0, caches=False):
     """Generate K per KV head (numpy, threaded), pack on the GPU, return records
-    resident where the workload puts them, plus q and sigma2 on the device."""
-    from synthetic import kv_head, queries
+    resident where the workload puts them, plus q and sigma2 on the device.
+    With `caches`, also the bf16 K and V cache rows [h_kv, n, d] (as int16 bit
+    patterns) in the same residency, for the attention over the selection."""
+    from synthetic import kv_head, queries, to_bf16_bits, values
     hk = wl.sessions * wl.h_kv
     r = F.record_bytes(wl.n)
     host = wl.residency == "host"
@@ -142,14 +146,26 @@ def build_records(torch, F, wl, dev, layer=0):
     q = np.empty((hk * wl.g, wl.d), np.float32)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     stage = torch.empty((1, wl.d, r), dtype=torch.uint8, device=dev)
+    kc = vc = None
+    if caches:
+        kc = torch.empty((hk, wl.n, wl.d), dtype=torch.int16, pin_memory=host, device=None if host else dev)
+        vc = torch.empty((hk, wl.n, wl.d), dtype=torch.int16, pin_memory=host, device=None if host else dev)
 
     def gen(v):
         s, g = divmod(v, wl.h_kv)
-        return v, kv_head(wl.key, layer, s, g, wl.n, wl.d, wl.outliers)
+        k, sig2 = kv_head(wl.key, layer, s, g, wl.n, wl.d, wl.outliers)
+        kb = vb = None
+        if caches:
+            kb = torch.from_numpy(to_bf16_bits(k).view(np.int16))
+            vb = torch.from_numpy(to_bf16_bits(values(wl.key, layer, s, g, wl.n, wl.d)).view(np.int16))
+        return v, (k, sig2), kb, vb
 
     with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
-        for v, (k, sig2) in ex.map(gen, range(hk)):
+        for v, (k, sig2), kb, vb in ex.map(gen, range(hk)):
             s, g = divmod(v, wl.h_kv)
+            if caches:
+                kc[v].copy_(kb)
+                vc[v].copy_(vb)
             s2[v] = sig2
             q[v * wl.g:(v + 1) * wl.g] = queries(wl.key, layer, s, g, wl.g, wl.d)
             kd = torch.from_numpy(k).to(dev)[None]
@@ -159,7 +175,7 @@ def build_records(torch, F, wl, dev, layer=0):
             del kd
     torch.cuda.synchronize(dev)
     assert int(status.item()) == 0, "pack reported non-finite keys or scale overflow"
-    return records, torch.from_numpy(q).to(dev), torch.from_numpy(s2).to(dev), q, s2
+    return records, torch.from_numpy(q).to(dev), torch.from_numpy(s2).to(dev), q, s2, kc, vc
 
 
 def cpu_baseline(wl, q_np, s2_np, budget, seconds=15.0):
@@ -225,7 +241,7 @@ def main():
     h2d_peak = measure_h2d_peak(torch, dev)
 
     t_setup = time.perf_counter()
-    records, q, s2, q_np, s2_np = build_records(torch, F, wl, dev)
+    records, q, s2, q_np, s2_np, kc, vc = build_records(torch, F, wl, dev, caches=not args.no_attend)
     setup_s = time.perf_counter() - t_setup
     hk, hq, n, d, k = wl.sessions * wl.h_kv, wl.sessions * wl.h_q, wl.n, wl.d, wl.k
 
@@ -331,6 +347,43 @@ def main():
         comparison["speedup_vs_fixed_136"] = round(comparison["fixed_136"]["ms_per_step"] / step_ms, 3)
         comparison["bytes_method_B68_vs_fixed_68"] = round(
             comparison["method_B68"]["bytes_per_key"] / comparison["fixed_68"]["bytes_per_key"], 3)
+    # Attention over the selected keys (the step after the scan): the bf16 K and
+    # V rows of every query head's top-k, gathered from the same residency.
+    attention = None
+    if not args.no_attend:
+        step()   # idx of the method's own selection at this budget
+        scale = float(1.0 / np.sqrt(d))
+        aws = torch.empty(F.attend_workspace_bytes(hq, d, k), dtype=torch.uint8, device=dev)
+        aout = torch.empty((hq, d), dtype=torch.float32, device=dev)
+        alse = torch.empty(hq, dtype=torch.float32, device=dev)
+        for _ in range(3):
+            F.attend(kc, vc, q, idx, scale, out=aout, lse=alse, workspace=aws)
+        torch.cuda.synchronize(dev)
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = max(5, args.kernel_reps)
+        a0.record(stream)
+        for _ in range(reps):
+            F.attend(kc, vc, q, idx, scale, out=aout, lse=alse, workspace=aws)
+        a1.record(stream)
+        torch.cuda.synchronize(dev)
+        att_ms = a0.elapsed_time(a1) / reps
+        att_bytes = hq * k * d * 2 * 2
+        att_gbps = att_bytes / (att_ms * 1e-3) / 1e9
+        # rows selected by several query heads of a KV head need crossing the
+        # link (or leaving HBM) only once: the distinct rows per KV head
+        sel = idx.cpu().numpy().reshape(hk, hq // hk, k)
+        uniq = sum(int(np.unique(sel[v]).size) for v in range(hk))
+        uniq_bytes = uniq * d * 2 * 2
+        uniq_gbps = uniq_bytes / (att_ms * 1e-3) / 1e9
+        peak = h2d_peak if host else HBM_PEAK_GBPS
+        attention = {"ms": round(att_ms, 4), "bytes_per_call": att_bytes,
+                     "achieved_gbps": round(att_gbps, 2),
+                     "distinct_row_bytes": uniq_bytes, "distinct_row_gbps": round(uniq_gbps, 2),
+                     "frac": round(uniq_gbps / peak, 4),
+                     "of": "measured H2D peak, distinct rows" if host else "8 TB/s HBM, distinct rows",
+                     "kernel": "attend_kernel<16> + attend_merge" if d == 128 else "attend_kernel + attend_merge",
+                     "rows": f"{hq} query heads x {k} selected keys x (K + V) bf16 rows of {d}",
+                     "step_plus_attention_ms": round(step_ms + att_ms, 4)}
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(wl, q_np, s2_np, budget)
@@ -353,6 +406,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "comparison": comparison,
+        "attention": attention,
         "bytes_per_key": round(alg_bytes / (hk * n), 3),
         "link_frac_of_measured_h2d_per_step": round(alg_bytes / (step_ms * 1e-3) / 1e9 / h2d_peak, 4)
         if host else None,

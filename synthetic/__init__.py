@@ -132,12 +132,16 @@ def to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return ((b + r) >> np.uint32(16)).astype(np.uint16)
 
 
+def values(wl_key: int, layer: int, session: int, g: int, n: int, d: int) -> np.ndarray:
+    """float32 [n, d] value rows of one KV head: N(0, 1) from the stream [..., 2]."""
+    return _rng(wl_key, layer, session, g, 2).standard_normal((n, d), dtype=np.float32)
+
+
 def kv_rows_bf16(wl_key: int, layer: int, session: int, g: int, n: int, d: int, outliers: int):
     """(K bf16 [n, d], V bf16 [n, d]) cache rows of one KV head: K is the same
-    draw as kv_head() rounded to bf16; V = N(0, 1) from the stream [..., 2]."""
+    draw as kv_head() rounded to bf16, V is values() rounded to bf16."""
     k, _ = kv_head(wl_key, layer, session, g, n, d, outliers)
-    v = _rng(wl_key, layer, session, g, 2).standard_normal((n, d), dtype=np.float32)
-    return to_bf16_bits(k), to_bf16_bits(v)
+    return to_bf16_bits(k), to_bf16_bits(values(wl_key, layer, session, g, n, d))
 
 
 def small_case(seed: int, h_kv: int, g: int, n: int, d: int, outliers: int = 0):
