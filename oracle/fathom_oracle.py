@@ -36,6 +36,11 @@ Parity status of each function (what pins it, in tests/test_oracle_*.py):
                                  (KKT) certificate at d=128, sum t = B,
                                  monotone in B.
   topq_depths                    pinned: independent sort by (-|q|, c).
+  group_importance               pinned: one head equals importance; the
+                                 shared allocation equals brute force over all
+                                 depth vectors of sum_h sum_c w_hc 4^-t_c
+                                 (exact rationals, d=4, B<=16); sequential
+                                 fp32 summation checked with Fractions.
   union_depths                   pinned: prefix nesting (union prefix contains
                                  every head's prefix).
   reconstruct, scores            pinned: B=4d equals full 4-bit dequant
@@ -265,6 +270,23 @@ def waterfill_depths(w: np.ndarray, budget: int) -> np.ndarray:
     return t
 
 
+def group_importance(qs: np.ndarray, sigma2: np.ndarray) -> np.ndarray:
+    """Group-shared importance of a GQA group (a variant the pages leave open:
+    the review's FAQ on GQA and the group's shared K): one allocation per KV
+    head on w_c = sum_h q_h,c^2 sigma_c^2, so every query head of the group
+    reads the same B bits per key.  Reading of the arithmetic: each term is
+    ``importance`` of one head, and the terms are added in fp32 in head order,
+    w = fl32(...fl32(fl32(w_0 + w_1) + w_2)... + w_{G-1})."""
+    qs = np.asarray(qs, dtype=np.float32)
+    acc = np.zeros(qs.shape[1], dtype=np.float32)
+    for h in range(qs.shape[0]):
+        with np.errstate(over="ignore"):
+            acc = (acc + importance(qs[h], sigma2)).astype(np.float32)
+    if not np.all(np.isfinite(acc)):
+        raise ValueError("group importance overflows fp32")
+    return acc
+
+
 def topq_depths(q: np.ndarray, m: int) -> np.ndarray:
     """Fixed-depth comparison mode: all 4 planes of the m channels with the largest |q_c|.
 
@@ -352,7 +374,8 @@ def step(k_heads, q, sigma2, budget, k, mode="waterfill", packed=None):
 
     k_heads: float32 [h_kv, n, d]; q: float32 [h_q, d]; sigma2: float32 [h_kv, d].
     mode "waterfill": reverse water-filling with ``budget`` bits per key;
-    mode "topq": 4 planes on budget // 4 channels of largest |q_c|.
+    mode "topq": 4 planes on budget // 4 channels of largest |q_c|;
+    mode "group": one water-filling per KV head on the group importance.
     ``packed`` may hold precomputed (delta, kappa) per KV head.
     Returns dict with depth [h_q, d], union [h_kv, d], idx [h_q, k], and the
     fp64 scores/sums per query head.
@@ -364,6 +387,9 @@ def step(k_heads, q, sigma2, budget, k, mode="waterfill", packed=None):
     for h in range(h_q):
         if mode == "waterfill":
             depth[h] = waterfill_depths(importance(q[h], sigma2[h // g]), budget)
+        elif mode == "group":
+            kv = h // g
+            depth[h] = waterfill_depths(group_importance(q[kv * g:(kv + 1) * g], sigma2[kv]), budget)
         else:
             if budget % PLANES:
                 raise ValueError("fixed mode needs budget % 4 == 0")

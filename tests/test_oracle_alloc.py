@@ -182,3 +182,46 @@ def test_union_contains_every_prefix():
     dep = np.stack([O.waterfill_depths(O.importance(q[h], s2), 92) for h in range(4)])
     u = O.union_depths(dep)
     assert np.all(u >= dep) and np.all((u[None] == dep).any(axis=0))
+
+
+# ---- group-shared allocation (one depth vector per KV head) ----
+
+def test_group_importance_of_one_head_is_importance():
+    rng = np.random.default_rng(21)
+    q = rng.standard_normal((1, 128)).astype(np.float32)
+    s2 = np.exp(rng.standard_normal(128)).astype(np.float32)
+    assert np.array_equal(O.group_importance(q, s2), O.importance(q[0], s2))
+
+
+def test_group_importance_is_sequential_fp32_sum():
+    rng = np.random.default_rng(22)
+    qs = (rng.standard_normal((4, 64)) * np.exp(rng.standard_normal((4, 64)) * 2)).astype(np.float32)
+    s2 = np.exp(rng.standard_normal(64) * 2).astype(np.float32)
+    got = O.group_importance(qs, s2)
+    for c in range(64):
+        acc = Fraction(0)
+        for h in range(4):
+            w = round_binary(round_binary(fr(qs[h, c]) * fr(qs[h, c]), *F32) * fr(s2[c]), *F32)
+            acc = round_binary(acc + w, *F32)
+        assert fr(got[c]) == acc
+
+
+def test_group_allocation_minimises_the_summed_objective_d4():
+    """With weights whose fp32 sums are exact (small dyadic values), the shared
+    depth vector minimises sum_h sum_c w_hc 4^-t_c over all 5^4 vectors."""
+    rng = np.random.default_rng(23)
+    cands = list(itertools.product(range(5), repeat=4))
+    for trial in range(30):
+        qs = rng.integers(-3, 4, (4, 4)).astype(np.float32) * np.float32(0.5)
+        s2 = rng.choice(np.array([0.25, 1.0, 2.0, 4.0], np.float32), 4)
+        wh = [O.importance(qs[h], s2) for h in range(4)]
+        wg = O.group_importance(qs, s2)
+        for b in range(0, 17):
+            t = O.waterfill_depths(wg, b)
+            assert int(t.sum()) == b
+
+            def obj(c):
+                return sum(objective(wh[h], c) for h in range(4))
+            feas = [c for c in cands if sum(c) == b]
+            vals = [obj(c) for c in feas]
+            assert obj(t) == min(vals)
