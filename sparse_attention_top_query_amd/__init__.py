@@ -11,6 +11,7 @@ from .fathom import (  # noqa: F401
     HOST_STAGED,
     TOPQ,
     WATERFILL,
+    WATERFILL_GROUP,
     FathomError,
     allocate,
     attend,
@@ -24,5 +25,5 @@ from .fathom import (  # noqa: F401
     workspace_bytes,
 )
 
-__all__ = ["HBM", "HOST_DIRECT", "HOST_STAGED", "TOPQ", "WATERFILL", "FathomError", "allocate", "attend", "attend_workspace_bytes", "load", "pack",
+__all__ = ["HBM", "HOST_DIRECT", "HOST_STAGED", "TOPQ", "WATERFILL", "WATERFILL_GROUP", "FathomError", "allocate", "attend", "attend_workspace_bytes", "load", "pack",
            "prefix_bytes", "record_bytes", "scan_scores", "scan_topk", "workspace_bytes"]

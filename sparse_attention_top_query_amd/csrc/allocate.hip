@@ -24,6 +24,10 @@
 // per item), and t_c is the number of channel c's items with key >= K.  The
 // fixed top-|q| mode selects m channels the same way with
 // key = bits(|q_c|) << 8 | (255 - c).
+//
+// Group-shared mode (mode 2): one allocation per KV head on the fp32 sum, in
+// head order, of the group's importances w_h,c; all query heads of the group
+// get the same depths, so the scan reads exactly B bits per KV-head key.
 #include "fathom_internal.h"
 
 namespace fathom {
@@ -69,6 +73,10 @@ __global__ __launch_bounds__(1024) void allocate_kernel(const float* __restrict_
   float aq[CPL];
   int t[CPL];
   uint32_t flag = 0;
+  // the group-shared mode sums the importances of all g query heads of the KV
+  // head, in head order; every wavefront of the group forms the same sum
+  const int h_lo = mode == 2 ? kv * g : h;
+  const int h_hi = mode == 2 ? kv * g + g : h + 1;
 #pragma unroll
   for (int i = 0; i < CPL; ++i) {
     const int c = lane + 64 * i;
@@ -76,19 +84,21 @@ __global__ __launch_bounds__(1024) void allocate_kernel(const float* __restrict_
     w[i] = 0.0f;
     aq[i] = 0.0f;
     if (c < d) {
-      const float qv = q[(int64_t)h * d + c];
       const float sv = sigma2[(int64_t)kv * d + c];
-      if (!isfinite(qv)) flag |= 4u;                         // FATHOM_FLAG_Q_NONFINITE
       if (!(isfinite(sv) && sv >= 0.0f)) flag |= 8u;         // FATHOM_FLAG_SIGMA2_INVALID
-      // two fp32 round-to-nearest products, never fused
-      w[i] = __fmul_rn(__fmul_rn(qv, qv), sv);
+      for (int x = h_lo; x < h_hi; ++x) {
+        const float qv = q[(int64_t)x * d + c];
+        if (!isfinite(qv)) flag |= 4u;                       // FATHOM_FLAG_Q_NONFINITE
+        // two fp32 round-to-nearest products, never fused; sums in fp32, in order
+        w[i] = __fadd_rn(w[i], __fmul_rn(__fmul_rn(qv, qv), sv));
+        if (x == h) aq[i] = fabsf(qv);
+      }
       if (!flag && !isfinite(w[i])) flag |= 16u;             // FATHOM_FLAG_IMPORTANCE_OVERFLOW
-      aq[i] = fabsf(qv);
     }
   }
   flag = wave_or(flag);
 
-  if (flag == 0 && mode == 0 && budget > 0) {
+  if (flag == 0 && (mode == 0 || mode == 2) && budget > 0) {
     uint64_t key[kPlanes * CPL];   // item (channel lane + 64 i, plane t) at 4 i + t; 0 = no item
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {

@@ -21,6 +21,7 @@ HOST_DIRECT = 1
 HOST_STAGED = 2
 WATERFILL = 0
 TOPQ = 1
+WATERFILL_GROUP = 2
 
 FLAG_KEY_NONFINITE = 1
 FLAG_SCALE_OVERFLOW = 2

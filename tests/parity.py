@@ -42,6 +42,9 @@ def oracle_depths(q, s2, budget, mode="waterfill"):
     for h in range(h_q):
         if mode == "waterfill":
             dep[h] = O.waterfill_depths(O.importance(q[h], s2[h // g]), budget)
+        elif mode == "group":
+            kv = h // g
+            dep[h] = O.waterfill_depths(O.group_importance(q[kv * g:(kv + 1) * g], s2[kv]), budget)
         else:
             dep[h] = O.topq_depths(q[h], budget // 4)
     uni = np.stack([O.union_depths(dep[v * g:(v + 1) * g]) for v in range(s2.shape[0])])

@@ -145,6 +145,32 @@ def test_allocate_status_flags(F):
     assert dep[0].sum() == 40 and dep[4].sum() == 40
 
 
+@pytest.mark.parametrize("shape", ALLOC_SHAPES)
+@pytest.mark.parametrize("budget_frac", [0.0, 0.09, 0.18, 0.5, 1.0])
+def test_allocate_group_shared_bit_exact(F, shape, budget_frac):
+    h_kv, g, d = shape
+    budget = int(round(budget_frac * 4 * d))
+    _, q, s2 = small_case(17, h_kv, g, 1, d, outliers=min(4, d))
+    dep, uni = F.allocate(dev(q), dev(s2), budget, mode=F.WATERFILL_GROUP)
+    rd, ru = oracle_depths(q, s2, budget, mode="group")
+    dep, uni = dep.cpu().numpy(), uni.cpu().numpy()
+    assert np.array_equal(dep, rd)
+    assert np.array_equal(uni, ru)
+    for v in range(h_kv):   # one shared vector per group, exactly B bits
+        assert np.all(dep[v * g:(v + 1) * g] == uni[v])
+        assert int(uni[v].sum()) == budget
+
+
+def test_allocate_group_status_zeroes_the_group(F):
+    _, q, s2 = small_case(18, 2, 4, 1, 64)
+    q[6, 3] = np.inf           # KV head 1, query head 2
+    st = torch.full((2,), -1, dtype=torch.int32, device="cuda:0")
+    dep, uni = F.allocate(dev(q), dev(s2), 50, mode=F.WATERFILL_GROUP, status=st)
+    assert list(st.cpu().numpy()) == [0, 4]
+    dep = dep.cpu().numpy()
+    assert np.all(dep[4:] == 0) and np.all(dep[:4].sum(axis=1) == 50)
+
+
 def test_allocate_rejects_bad_budget(F):
     _, q, s2 = small_case(13, 1, 4, 1, 16)
     with pytest.raises(F.FathomError):
@@ -175,7 +201,8 @@ def run_case(F, case, residency="hbm", mode="waterfill"):
     if residency == "host":
         rec = rec.cpu().pin_memory()
     dq = dev(q)
-    dep, uni = F.allocate(dq, dev(s2), budget, mode=F.WATERFILL if mode == "waterfill" else F.TOPQ)
+    modes = {"waterfill": F.WATERFILL, "topq": F.TOPQ, "group": F.WATERFILL_GROUP}
+    dep, uni = F.allocate(dq, dev(s2), budget, mode=modes[mode])
     scores = F.scan_scores(rec, dq, dep, uni, n)
     torch.cuda.synchronize()
     return k, q, s2, rec, dq, dep, uni, scores.cpu().numpy()
@@ -294,6 +321,20 @@ def test_topq_scan_parity(F):
         s, a = O.scores(q[h], kappa, delta, rd[h])
         check_scores(sg[h], s, a)
         check_topk(idx[h], s, a, 256, s_gpu=sg[h])
+
+
+def test_group_shared_scan_parity(F):
+    case = (2, 4, 5000, 128, 92)
+    k, q, s2, rec, dq, dep, uni, sg = run_case(F, case, mode="group")
+    packed = oracle_pack(k)
+    rd, _ = oracle_depths(q, s2, 92, mode="group")
+    assert np.array_equal(dep.cpu().numpy(), rd)
+    idx = F.scan_topk(rec, dq, dep, uni, 5000, 300).cpu().numpy()
+    for h in range(8):
+        delta, kappa, _ = packed[h // 4]
+        s, a = O.scores(q[h], kappa, delta, rd[h])
+        check_scores(sg[h], s, a)
+        check_topk(idx[h], s, a, 300, s_gpu=sg[h])
 
 
 def test_scan_rejects_bad_residency_and_workspace(F):
