@@ -342,7 +342,8 @@ def main():
                     "bytes_per_key": round(algorithmic_bytes(uni.cpu().numpy(), n) / (hk * n), 3)}
         csteps = max(3, min(args.steps, 20))
         comparison = {"method_B": budget, "method_ms_per_step": round(step_ms, 4)}
-        for name, b, m in (("fixed_136", 136, F.TOPQ), ("fixed_68", 68, F.TOPQ), ("method_B68", 68, F.WATERFILL)):
+        for name, b, m in (("fixed_136", 136, F.TOPQ), ("fixed_68", 68, F.TOPQ), ("method_B68", 68, F.WATERFILL),
+                           (f"group_shared_B{budget}", budget, F.WATERFILL_GROUP)):
             comparison[name] = timed(b, m, csteps)
         comparison["speedup_vs_fixed_136"] = round(comparison["fixed_136"]["ms_per_step"] / step_ms, 3)
         comparison["bytes_method_B68_vs_fixed_68"] = round(
