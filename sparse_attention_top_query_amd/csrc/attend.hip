@@ -211,26 +211,46 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttArgs a, int64_t 
 }
 
 // One workgroup per query head: o = sum_s o_s e^(M_s - M) / sum_s l_s e^(M_s - M).
+// The factors e^(M_s - M) are formed once per split in LDS; sums run in split
+// order.
+constexpr int kMergeSplits = 1024;   // splits merged per pass through LDS
+
 __global__ __launch_bounds__(kAttThreads) void attend_merge(AttArgs a) {
+  __shared__ float fac[kMergeSplits];
+  __shared__ float red[kAttThreads];
   const int h = blockIdx.x;
   const int d = a.d;
+  const int tid = threadIdx.x;
   const float* pp = a.part + (int64_t)h * a.splits * (d + 2);
-  float M = -INFINITY;
-  for (int sp = 0; sp < a.splits; ++sp) M = fmaxf(M, pp[(int64_t)sp * (d + 2) + d]);
-  float l = 0.0f;
-  for (int sp = 0; sp < a.splits; ++sp) {
-    const float ls = pp[(int64_t)sp * (d + 2) + d + 1];
-    if (ls > 0.0f) l += ls * expf(pp[(int64_t)sp * (d + 2) + d] - M);
+  // M = max over splits (threads stride the splits, then a tree in LDS)
+  float m = -INFINITY;
+  for (int sp = tid; sp < a.splits; sp += kAttThreads) m = fmaxf(m, pp[(int64_t)sp * (d + 2) + d]);
+  red[tid] = m;
+  __syncthreads();
+  for (int w = kAttThreads / 2; w > 0; w >>= 1) {
+    if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
+    __syncthreads();
   }
-  for (int c = threadIdx.x; c < d; c += blockDim.x) {
-    float o = 0.0f;
-    for (int sp = 0; sp < a.splits; ++sp) {
-      const float ls = pp[(int64_t)sp * (d + 2) + d + 1];
-      if (ls > 0.0f) o += pp[(int64_t)sp * (d + 2) + c] * expf(pp[(int64_t)sp * (d + 2) + d] - M);
+  const float M = red[0];
+  __syncthreads();
+  float o = 0.0f, l = 0.0f;
+  for (int base = 0; base < a.splits; base += kMergeSplits) {
+    const int cnt = min(kMergeSplits, a.splits - base);
+    for (int x = tid; x < cnt; x += kAttThreads) {
+      const float* q = pp + (int64_t)(base + x) * (d + 2);
+      fac[x] = q[d + 1] > 0.0f ? expf(q[d] - M) : 0.0f;
     }
-    a.out[(int64_t)h * d + c] = l > 0.0f ? o / l : 0.0f;
+    __syncthreads();
+    for (int x = 0; x < cnt; ++x) {
+      const float f = fac[x];
+      const float* q = pp + (int64_t)(base + x) * (d + 2);
+      if (tid < d) o = fmaf(q[tid], f, o);
+      l = fmaf(q[d + 1], f, l);
+    }
+    __syncthreads();
   }
-  if (threadIdx.x == 0) {
+  if (tid < d) a.out[(int64_t)h * d + tid] = l > 0.0f ? o / l : 0.0f;
+  if (tid == 0) {
     if (a.lse) a.lse[h] = l > 0.0f ? M + logf(l) : -INFINITY;
     if (a.status) {
       uint32_t f = 0;
