@@ -48,6 +48,10 @@ Parity status of each function (what pins it, in tests/test_oracle_*.py):
                                  the t-bit quantizer identity, the
                                  4x-per-bit error bound.
   topk                           pinned: brute-force sort on small n.
+  tail_scores, step_append       pinned: tail scores equal exact rational
+                                 sums; an empty tail reduces to step(); an
+                                 all-tail cache gives the brute-force top-k of
+                                 the exact q . k.
 The pages' own six-key worked example (the review's App. A) is referenced
 but its values are not in the text we have, so it cannot serve as a pin.
 """
@@ -363,6 +367,52 @@ def topk(s: np.ndarray, k: int) -> np.ndarray:
         raise ValueError("k out of range")
     order = np.lexsort((np.arange(n), -np.asarray(s, dtype=np.float64)))
     return np.sort(order[:k])
+
+
+# ---------------------------------------------------------------------------
+# Appending keys during decoding.  The pages fix the block scale over a whole
+# 128-key block ([Review] Strengths, paper Sec 3.2), so a block can only be
+# quantised once it is full; they say nothing about the newest keys.  Reading:
+# full blocks are sealed (scaled and packed) as they fill, and the open tail
+# block, fewer than 128 keys, is kept exact in fp32 and scored exactly.
+# ---------------------------------------------------------------------------
+
+def tail_scores(q: np.ndarray, tail_k: np.ndarray):
+    """Exact scores of unquantised tail keys: s_j = sum_c q_c k_jc in fp64 (each
+    product of two fp32 values is exact in fp64), and A_j = sum_c |q_c k_jc|.
+    tail_k float32 [m, d]."""
+    qq = np.asarray(q, dtype=np.float32).astype(np.float64)
+    kk = np.asarray(tail_k, dtype=np.float32).astype(np.float64)
+    return kk @ qq, np.abs(kk) @ np.abs(qq)
+
+
+def step_append(k_sealed, tail_k, q, sigma2, budget, k, mode="waterfill"):
+    """One top-k step over n_sealed quantised keys plus an exact open tail.
+
+    k_sealed float32 [h_kv, n_sealed, d] (the keys of the sealed blocks);
+    tail_k float32 [h_kv, m, d] (keys n_sealed .. n_sealed + m - 1).  Scores of
+    sealed keys are the scan's (``scores``), of tail keys ``tail_scores``; the
+    top k over all n_sealed + m keys as in ``topk``."""
+    h_kv, n_s, d = k_sealed.shape
+    m = tail_k.shape[1]
+    h_q = q.shape[0]
+    g = h_q // h_kv
+    base = step(k_sealed, q, sigma2, budget, min(k, n_s), mode=mode) if n_s > 0 else None
+    idx = np.zeros((h_q, k), dtype=np.int64)
+    s_all, a_all = [], []
+    for h in range(h_q):
+        st, at = tail_scores(q[h], tail_k[h // g])
+        if base is not None:
+            s = np.concatenate([base["scores"][h], st])
+            a = np.concatenate([base["sums"][h], at])
+        else:
+            s, a = st, at
+        idx[h] = topk(s, k)
+        s_all.append(s)
+        a_all.append(a)
+    depth = base["depth"] if base is not None else None
+    union = base["union"] if base is not None else None
+    return {"depth": depth, "union": union, "idx": idx, "scores": s_all, "sums": a_all}
 
 
 # ---------------------------------------------------------------------------

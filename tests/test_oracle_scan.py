@@ -154,3 +154,50 @@ def test_step_matches_pure_python_pipeline():
             want = sorted(sorted(range(n), key=lambda j: (-sc[j], j))[:kk])
             assert list(res["idx"][h]) == want
         assert list(res["union"][kv]) == [max(res["depth"][h][c] for h in range(kv * g, kv * g + g)) for c in range(d)]
+
+
+# ---- appending keys: sealed blocks plus an exact open tail ----
+
+def test_tail_scores_are_exact_rational_sums():
+    from fractions import Fraction
+    rng = np.random.default_rng(31)
+    q = (rng.standard_normal(16) * 3).astype(np.float32)
+    tk = (rng.standard_normal((5, 16)) * np.exp(rng.standard_normal((5, 16)))).astype(np.float32)
+    s, a = O.tail_scores(q, tk)
+    for j in range(5):
+        exact = sum(Fraction(float(q[c])) * Fraction(float(tk[j, c])) for c in range(16))
+        asum = sum(abs(Fraction(float(q[c])) * Fraction(float(tk[j, c]))) for c in range(16))
+        assert abs(Fraction(s[j]) - exact) <= asum * Fraction(1, 2 ** 48)
+        assert abs(Fraction(a[j]) - asum) <= asum * Fraction(1, 2 ** 48)
+
+
+def test_step_append_with_empty_tail_is_step():
+    rng = np.random.default_rng(32)
+    kk = rng.standard_normal((2, 384, 32)).astype(np.float32)
+    q = rng.standard_normal((4, 32)).astype(np.float32)
+    s2 = np.exp(rng.standard_normal((2, 32))).astype(np.float32)
+    a = O.step(kk, q, s2, 40, 50)
+    b = O.step_append(kk, np.zeros((2, 0, 32), np.float32), q, s2, 40, 50)
+    assert np.array_equal(a["idx"], b["idx"]) and np.array_equal(a["depth"], b["depth"])
+    for h in range(4):
+        assert np.array_equal(a["scores"][h], b["scores"][h])
+
+
+def test_step_append_all_tail_is_exact_topk():
+    rng = np.random.default_rng(33)
+    tk = rng.standard_normal((1, 100, 16)).astype(np.float32)
+    q = rng.standard_normal((2, 16)).astype(np.float32)
+    r = O.step_append(np.zeros((1, 0, 16), np.float32), tk, q, np.ones((1, 16), np.float32), 20, 10)
+    for h in range(2):
+        s = [sum(float(q[h, c]) * float(tk[0, j, c]) for c in range(16)) for j in range(100)]
+        want = sorted(sorted(range(100), key=lambda j: (-s[j], j))[:10])
+        assert list(r["idx"][h]) == want
+
+
+def test_step_append_tail_indices_follow_the_sealed_keys():
+    rng = np.random.default_rng(34)
+    kk = rng.standard_normal((1, 256, 8)).astype(np.float32) * np.float32(0.01)
+    tk = np.full((1, 3, 8), 50.0, np.float32)           # tail keys dominate every score
+    q = np.ones((1, 8), np.float32)
+    r = O.step_append(kk, tk, q, np.ones((1, 8), np.float32), 32, 3)
+    assert list(r["idx"][0]) == [256, 257, 258]
