@@ -14,6 +14,7 @@
  *   scan_topk        per query step: score every key from its read prefix, return top-k.
  * and the attention that consumes the selection is a fourth:
  *   attend_topk      per query step: attention of each query head over its top-k keys.
+ * A cache that grows during decoding uses pack_blocks and scan_topk_append.
  *
  * Conventions shared by every call:
  *   - Device pointers are HIP device memory unless stated; every call is
@@ -181,6 +182,41 @@ int fathom_scan_scores(const void* records, int residency, const float* q,
                        const uint8_t* depth, const uint8_t* union_depth, int h_q,
                        int h_kv, int64_t n, int d, float* scores, int64_t ld,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Appending keys during decoding.  The block scale is shared by a whole
+ * 128-key block ([Review] Strengths, paper Sec 3.2), so a key can only be
+ * quantised once its block is full.  Records are allocated for a capacity
+ * n_cap (fathom_record_bytes(n_cap) bytes per (KV head, channel)); full blocks
+ * are sealed into them with pack_blocks, and the newest keys -- the open tail
+ * block -- stay in fp32 and are scored exactly by scan_topk_append (a reading:
+ * the pages say nothing of the newest keys).
+ * ------------------------------------------------------------------------- */
+
+/* pack_blocks -- seal blocks [block0, block0 + nblocks) of records with capacity
+ * n_cap: the same quantisation and layout as pack_bitplanes applied to the
+ * whole cache, for those blocks only (other blocks are not touched, except that
+ * sealing the last block of the capacity zeroes the padding after it).
+ *   k        device, float32 [h_kv][rows][d], the rows of those blocks:
+ *            rows = min(128 nblocks, n_cap - 128 block0).
+ *   records  device, [h_kv][d][fathom_record_bytes(n_cap)] bytes.
+ *   status   as for pack_bitplanes (cleared, then flags OR-ed in); may be NULL.
+ * Sealing blocks one call at a time or all at once gives identical bytes. */
+int pack_blocks(const float* k, int h_kv, int64_t n_cap, int64_t block0, int64_t nblocks, int d,
+                void* records, uint32_t* status, void* stream);
+
+/* scan_topk_append -- scan_topk over a growing cache: keys 0 .. n_sealed - 1 are
+ * the sealed blocks of records with capacity n_cap (n_sealed a multiple of 128,
+ * or n_cap), keys n_sealed .. n_sealed + n_tail - 1 are the open tail, scored
+ * exactly in fp32 as sum_c q_c k_c from tail_k (device float32
+ * [h_kv][n_tail][d]).  The top k over all n_sealed + n_tail keys follow the
+ * scan_topk rules.  Residency FATHOM_HBM or FATHOM_HOST_DIRECT.  Workspace:
+ * fathom_workspace_bytes(h_q, h_kv, n_sealed + n_tail, d, k, FATHOM_HBM). */
+int scan_topk_append(const void* records, int residency, int64_t n_cap, int64_t n_sealed,
+                     const float* tail_k, int64_t n_tail, const float* q, const uint8_t* depth,
+                     const uint8_t* union_depth, int h_q, int h_kv, int d, int k,
+                     int32_t* topk_idx, float* topk_score, void* workspace,
+                     size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace attend_topk needs: per query head and split of its
  * k keys, a partial output (d + 2 floats) and a flag word. */

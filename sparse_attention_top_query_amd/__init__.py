@@ -18,12 +18,14 @@ from .fathom import (  # noqa: F401
     attend_workspace_bytes,
     load,
     pack,
+    pack_blocks,
     prefix_bytes,
     record_bytes,
     scan_scores,
     scan_topk,
+    scan_topk_append,
     workspace_bytes,
 )
 
-__all__ = ["HBM", "HOST_DIRECT", "HOST_STAGED", "TOPQ", "WATERFILL", "WATERFILL_GROUP", "FathomError", "allocate", "attend", "attend_workspace_bytes", "load", "pack",
-           "prefix_bytes", "record_bytes", "scan_scores", "scan_topk", "workspace_bytes"]
+__all__ = ["HBM", "HOST_DIRECT", "HOST_STAGED", "TOPQ", "WATERFILL", "WATERFILL_GROUP", "FathomError", "allocate", "attend", "attend_workspace_bytes", "load", "pack", "pack_blocks",
+           "prefix_bytes", "record_bytes", "scan_scores", "scan_topk", "scan_topk_append", "workspace_bytes"]

@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <string>
 
+#include "append.h"
 #include "attend.h"
 #include "fathom_internal.h"
 
@@ -269,6 +270,77 @@ int attend_topk(const void* k_cache, const void* v_cache, int residency, const f
                                        q, topk_idx, h_q, h_kv, n, d, k, scale, out, lse, status, workspace,
                                        static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "attend launch");
+  return ok();
+}
+
+int pack_blocks(const float* k, int h_kv, int64_t n_cap, int64_t block0, int64_t nblocks, int d,
+                void* records, uint32_t* status, void* stream) {
+  if (h_kv < 1 || h_kv > 65535) return fail(FATHOM_ESHAPE, "h_kv=%d outside [1, 65535]", h_kv);
+  if (d < 1 || d > fathom::kMaxD) return fail(FATHOM_ESHAPE, "d=%d outside [1, %d]", d, fathom::kMaxD);
+  if (n_cap < 1 || n_cap > (int64_t(1) << 34)) return fail(FATHOM_ESHAPE, "n_cap=%lld out of range", (long long)n_cap);
+  const fathom::Layout cap = fathom::make_layout(n_cap);
+  if (block0 < 0 || nblocks < 0 || block0 + nblocks > cap.nb)
+    return fail(FATHOM_ESHAPE, "blocks [%lld, %lld) outside the %lld blocks of capacity %lld", (long long)block0,
+                (long long)(block0 + nblocks), (long long)cap.nb, (long long)n_cap);
+  if (nblocks > 0x7fffffff) return fail(FATHOM_ESHAPE, "too many blocks");
+  if (nblocks > 0 && (!k || !records)) return fail(FATHOM_EINVAL, "null k or records");
+  if (nblocks > 0 && (!aligned(k, 4) || !aligned(records, 16)))
+    return fail(FATHOM_EINVAL, "k must be 4-byte and records 16-byte aligned");
+  hipError_t e = fathom::launch_pack_blocks(k, h_kv, cap, block0, nblocks, d, static_cast<uint8_t*>(records),
+                                            status, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "pack launch");
+  return ok();
+}
+
+int scan_topk_append(const void* records, int residency, int64_t n_cap, int64_t n_sealed, const float* tail_k,
+                     int64_t n_tail, const float* q, const uint8_t* depth, const uint8_t* union_depth, int h_q,
+                     int h_kv, int d, int k, int32_t* topk_idx, float* topk_score, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  int st = check_heads(h_q, h_kv, d);
+  if (st) return st;
+  if (n_cap < 0 || n_cap > (int64_t(1) << 34)) return fail(FATHOM_ESHAPE, "n_cap=%lld out of range", (long long)n_cap);
+  if (n_sealed < 0 || n_sealed > n_cap || (n_sealed % fathom::kBlock != 0 && n_sealed != n_cap))
+    return fail(FATHOM_ESHAPE, "n_sealed=%lld must be a multiple of 128 (or n_cap) within [0, n_cap=%lld]",
+                (long long)n_sealed, (long long)n_cap);
+  if (n_tail < 0 || n_tail > (int64_t(1) << 30)) return fail(FATHOM_ESHAPE, "n_tail=%lld out of range", (long long)n_tail);
+  const int64_t n = n_sealed + n_tail;
+  if (k < 0 || k > n) return fail(FATHOM_ESHAPE, "k=%d outside [0, n_sealed + n_tail = %lld]", k, (long long)n);
+  if (residency != FATHOM_HBM && residency != FATHOM_HOST_DIRECT)
+    return fail(FATHOM_ERESIDENCY, "scan_topk_append reads records from HBM or in place from pinned host memory");
+  if (!q || !depth || !union_depth) return fail(FATHOM_EINVAL, "null q/depth/union_depth");
+  if (!aligned(q, 4)) return fail(FATHOM_EINVAL, "q must be 4-byte aligned");
+  if (n_tail > 0 && (!tail_k || !aligned(tail_k, 4))) return fail(FATHOM_EINVAL, "tail_k must be non-null, 4-byte aligned");
+  if (k == 0) return ok();
+  if (!topk_idx) return fail(FATHOM_EINVAL, "null topk_idx");
+  const uint8_t* dev = nullptr;
+  if (n_sealed > 0) {
+    if (!records) return fail(FATHOM_EINVAL, "null records");
+    if (!aligned(records, 16)) return fail(FATHOM_EINVAL, "records must be 16-byte aligned");
+    st = resolve_records(records, residency, &dev);
+    if (st) return st;
+  }
+  const size_t need = fathom_workspace_bytes(h_q, h_kv, n, d, k, FATHOM_HBM);
+  if (!workspace || workspace_bytes < need)
+    return fail(FATHOM_EWORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, need);
+  if (!aligned(workspace, 256)) return fail(FATHOM_EINVAL, "workspace must be 256-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t ld = score_ld(n);
+  float* scores = static_cast<float*>(workspace);
+  uint8_t* sel_base = static_cast<uint8_t*>(workspace) + al256((size_t)h_q * (size_t)ld * 4);
+  hipError_t e;
+  if (n_sealed > 0) {
+    // the capacity's geometry, cut to the sealed blocks
+    fathom::Layout L = fathom::make_layout(n_cap);
+    L.n = n_sealed;
+    L.nb = (n_sealed + fathom::kBlock - 1) / fathom::kBlock;
+    e = fathom::launch_scan(dev, residency == FATHOM_HOST_DIRECT, q, depth, union_depth, h_kv, h_q / h_kv, L, d,
+                            scores, ld, s);
+    if (e != hipSuccess) return hip_fail(e, "scan launch");
+  }
+  e = fathom::launch_tail_scores(tail_k, q, h_kv, h_q / h_kv, n_tail, d, scores, ld, n_sealed, s);
+  if (e != hipSuccess) return hip_fail(e, "tail launch");
+  e = fathom::launch_select(scores, ld, h_q, n, k, topk_idx, topk_score, fathom::carve_select(sel_base, h_q, n, k), s);
+  if (e != hipSuccess) return hip_fail(e, "select launch");
   return ok();
 }
 

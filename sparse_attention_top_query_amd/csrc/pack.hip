@@ -15,22 +15,27 @@
 // slot (16 B of scales, then 128 B of plane-0 bits); planes 1-3 follow the head.
 #include <hip/hip_fp16.h>
 
+#include <algorithm>
+
+#include "append.h"
 #include "fathom_internal.h"
 
 namespace fathom {
 namespace {
 
-__global__ __launch_bounds__(256) void pack_kernel(const float* __restrict__ k, int64_t n, int d,
-                                                   int64_t nb, int64_t U, int64_t H, int64_t P, int64_t R,
-                                                   uint8_t* __restrict__ rec,
+// Blocks block0 + blockIdx.x of records laid out for nb 128-key blocks; `k`
+// holds `rows` token-major rows per KV head, starting at key 128 block0.
+__global__ __launch_bounds__(256) void pack_kernel(const float* __restrict__ k, int64_t rows, int d,
+                                                   int64_t block0, int64_t nb, int64_t U, int64_t H,
+                                                   int64_t P, int64_t R, uint8_t* __restrict__ rec,
                                                    uint32_t* __restrict__ status) {
   const int c = threadIdx.x;
   if (c >= d) return;  // no barriers below
-  const int64_t b = blockIdx.x;
+  const int64_t b = block0 + blockIdx.x;
   const int64_t g = blockIdx.y;
-  const int64_t j0 = b * kBlock;
-  const int cnt = (int)min<int64_t>(kBlock, n - j0);
-  const float* col = k + (g * n + j0) * d + c;
+  const int64_t j0 = (int64_t)blockIdx.x * kBlock;   // first row of the block in `k`
+  const int cnt = (int)min<int64_t>(kBlock, rows - j0);
+  const float* col = k + (g * rows + j0) * d + c;
 
   float mx = 0.0f;
   bool finite = true;
@@ -75,7 +80,7 @@ __global__ __launch_bounds__(256) void pack_kernel(const float* __restrict__ k, 
   for (int p = 1; p < kPlanes; ++p)
     *reinterpret_cast<uint4*>(r + H + (p - 1) * P + b * 16) = make_uint4(w[p][0], w[p][1], w[p][2], w[p][3]);
   if (b == nb - 1) {
-    // zero the blocks of the last unit that lie past n
+    // zero the blocks of the last unit that lie past the last block
     for (int64_t bb = nb; bb < U * kUnitBlocks; ++bb) {
       uint8_t* ub = r + kUnitHead * (bb / kUnitBlocks);
       reinterpret_cast<__half*>(ub)[bb % kUnitBlocks] = __float2half_rn(0.0f);
@@ -100,7 +105,22 @@ hipError_t launch_pack(const float* k, int h_kv, const Layout& L, int d, uint8_t
   if (L.nb == 0) return hipSuccess;
   const int threads = ((d + 63) / 64) * 64;
   dim3 grid((unsigned)L.nb, (unsigned)h_kv);
-  pack_kernel<<<grid, threads, 0, s>>>(k, L.n, d, L.nb, L.U, L.H, L.P, L.R, rec, status);
+  pack_kernel<<<grid, threads, 0, s>>>(k, L.n, d, 0, L.nb, L.U, L.H, L.P, L.R, rec, status);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_blocks(const float* k, int h_kv, const Layout& cap, int64_t block0, int64_t nblocks,
+                              int d, uint8_t* rec, uint32_t* status, hipStream_t s) {
+  if (status) {
+    clear_word<<<1, 1, 0, s>>>(status);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (nblocks == 0) return hipSuccess;
+  const int64_t rows = std::min<int64_t>(nblocks * kBlock, cap.n - block0 * kBlock);
+  const int threads = ((d + 63) / 64) * 64;
+  dim3 grid((unsigned)nblocks, (unsigned)h_kv);
+  pack_kernel<<<grid, threads, 0, s>>>(k, rows, d, block0, cap.nb, cap.U, cap.H, cap.P, cap.R, rec, status);
   return hipGetLastError();
 }
 

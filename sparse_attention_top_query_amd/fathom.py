@@ -64,6 +64,8 @@ def load() -> ctypes.CDLL:
         "scan_topk": (I, [P, I, P, P, P, I, I, L, I, I, P, P, P, S, P]),
         "fathom_scan_scores": (I, [P, I, P, P, P, I, I, L, I, P, L, P, S, P]),
         "fathom_attend_workspace_bytes": (S, [I, I, I]),
+        "pack_blocks": (I, [P, I, L, L, L, I, P, P, P]),
+        "scan_topk_append": (I, [P, I, L, L, P, L, P, P, P, I, I, I, I, P, P, P, S, P]),
         "attend_topk": (I, [P, P, I, P, P, I, I, L, I, I, ctypes.c_float, P, P, P, P, S, P]),
         "fathom_last_error": (ctypes.c_char_p, []),
         "fathom_version": (I, []),
@@ -260,3 +262,60 @@ def attend(k_cache: torch.Tensor, v_cache: torch.Tensor, q: torch.Tensor, idx: t
                               ctypes.c_float(scale), _ptr(out), _ptr(lse), _ptr(status), _ptr(workspace),
                               workspace.numel(), _stream(q)))
     return out, lse
+
+
+def pack_blocks(k: torch.Tensor, records: torch.Tensor, n_cap: int, block0: int,
+                status: torch.Tensor | None = None):
+    """pack_blocks: seal the blocks whose rows ``k`` float32 [h_kv, rows, d] holds,
+    starting at block ``block0``, into ``records`` of capacity ``n_cap``."""
+    _need(k, "k", torch.float32, 3)
+    _need(records, "records", torch.uint8)
+    h_kv, rows, d = k.shape
+    nblocks = -(-rows // 128)
+    if records.numel() < h_kv * d * record_bytes(n_cap):
+        raise ValueError("records buffer too small for (h_kv, d, n_cap)")
+    if rows != min(128 * nblocks, n_cap - 128 * block0):
+        raise ValueError("k must hold whole blocks (or the capacity's last, shorter block)")
+    if status is not None:
+        _need(status, "status", torch.int32)
+    _check(load().pack_blocks(_ptr(k), h_kv, n_cap, block0, nblocks, d, _ptr(records), _ptr(status), _stream(k)))
+    return records
+
+
+def scan_topk_append(records: torch.Tensor | None, n_cap: int, n_sealed: int, tail_k: torch.Tensor | None,
+                     q: torch.Tensor, depth: torch.Tensor, union_depth: torch.Tensor, k: int,
+                     residency: int | None = None, workspace: torch.Tensor | None = None,
+                     idx: torch.Tensor | None = None, scores: torch.Tensor | None = None,
+                     want_scores: bool = False):
+    """scan_topk_append: top k over n_sealed sealed keys plus the exact open tail."""
+    _need(q, "q", torch.float32, 2)
+    _need(depth, "depth", torch.uint8)
+    _need(union_depth, "union_depth", torch.uint8)
+    h_q, d = q.shape
+    h_kv = union_depth.shape[0]
+    n_tail = 0
+    if tail_k is not None:
+        _need(tail_k, "tail_k", torch.float32, 3)
+        n_tail = tail_k.shape[1]
+    if records is not None:
+        _need(records, "records", torch.uint8, device=False)
+        if records.numel() < h_kv * d * record_bytes(n_cap):
+            raise ValueError("records buffer too small for (h_kv, d, n_cap)")
+    if residency is None:
+        residency = HBM if records is None or records.is_cuda else HOST_DIRECT
+    n = n_sealed + n_tail
+    if workspace is None:
+        workspace = torch.empty(max(workspace_bytes(h_q, h_kv, n, d, k, HBM), 1), dtype=torch.uint8,
+                                device=q.device)
+    _need(workspace, "workspace", torch.uint8)
+    if idx is None:
+        idx = torch.empty((h_q, k), dtype=torch.int32, device=q.device)
+    _need(idx, "idx", torch.int32)
+    if want_scores and scores is None:
+        scores = torch.empty((h_q, k), dtype=torch.float32, device=q.device)
+    if scores is not None:
+        _need(scores, "scores", torch.float32)
+    _check(load().scan_topk_append(_ptr(records), residency, n_cap, n_sealed, _ptr(tail_k), n_tail, _ptr(q),
+                                   _ptr(depth), _ptr(union_depth), h_q, h_kv, d, k, _ptr(idx), _ptr(scores),
+                                   _ptr(workspace), workspace.numel(), _stream(q)))
+    return (idx, scores) if want_scores or scores is not None else idx

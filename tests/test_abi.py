@@ -32,7 +32,7 @@ def test_header_declares_the_entry_points():
     names = header_functions()
     for fn in ("pack_bitplanes", "allocate_depths", "scan_topk", "fathom_workspace_bytes",
                "fathom_scan_scores", "fathom_last_error", "fathom_record_bytes", "attend_topk",
-               "fathom_attend_workspace_bytes"):
+               "fathom_attend_workspace_bytes", "pack_blocks", "scan_topk_append"):
         assert fn in names
 
 
@@ -109,6 +109,28 @@ def test_attend_workspace_and_validation(lib):
     assert call(q=P(0x1004)) == -1 and "aligned" in _err(lib)
     assert call(res=2) == -7
     assert call(wsb=16) == -5
+
+
+def test_append_validation(lib):
+    P = ctypes.c_void_p
+    fake = P(0x1000)
+    # pack_blocks: the range must lie inside the capacity's blocks (5000 keys -> 40 blocks)
+    assert lib.pack_blocks(fake, 2, 5000, 39, 2, 64, fake, None, None) == -2
+    assert lib.pack_blocks(fake, 2, 5000, -1, 1, 64, fake, None, None) == -2
+    assert lib.pack_blocks(fake, 2, 0, 0, 0, 64, fake, None, None) == -2
+    assert lib.pack_blocks(None, 2, 5000, 0, 3, 64, fake, None, None) == -1
+    assert lib.pack_blocks(fake, 2, 5000, 0, 3, 300, fake, None, None) == -2
+
+    def app(n_cap=8192, n_sealed=4096, tail=fake, n_tail=10, k=64, res=0, h_q=8, h_kv=2, ws=1 << 30):
+        return lib.scan_topk_append(fake, res, n_cap, n_sealed, tail, n_tail, fake, fake, fake, h_q, h_kv, 128, k,
+                                    fake, None, fake, ws, None)
+    assert app(n_sealed=4000) == -2 and "multiple of 128" in _err(lib)
+    assert app(n_sealed=9000) == -2
+    assert app(n_tail=-1) == -2
+    assert app(k=4096 + 11) == -2
+    assert app(res=2) == -7
+    assert app(tail=None) == -1
+    assert app(h_q=6, h_kv=4) == -2
 
 
 def test_binding_refuses_cpu_tensors(lib):
