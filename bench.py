@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--no-attend", action="store_true",
                     help="skip the attention over the selected keys (bf16 K/V caches are not built)")
+    ap.add_argument("--no-append", action="store_true",
+                    help="skip the growing-cache measurement (open tail block, sealing one block)")
     ap.add_argument("--no-compare", action="store_true",
                     help="skip the fixed-depth (136-bit, 68-bit) comparison scans")
     ap.add_argument("--kernel-reps", type=int, default=20)
@@ -338,13 +340,29 @@ def main():
             e1.record(stream)
             torch.cuda.synchronize(dev)
             ms = e0.elapsed_time(e1) / steps
+            picks[name_of[(b, m)]] = idx[:hq // hk].cpu().numpy()
             return {"ms_per_step": round(ms, 4),
                     "bytes_per_key": round(algorithmic_bytes(uni.cpu().numpy(), n) / (hk * n), 3)}
         csteps = max(3, min(args.steps, 20))
         comparison = {"method_B": budget, "method_ms_per_step": round(step_ms, 4)}
-        for name, b, m in (("fixed_136", 136, F.TOPQ), ("fixed_68", 68, F.TOPQ), ("method_B68", 68, F.WATERFILL),
-                           (f"group_shared_B{budget}", budget, F.WATERFILL_GROUP)):
-            comparison[name] = timed(b, m, csteps)
+        modes = [(f"method_B{budget}", budget, F.WATERFILL), ("fixed_136", 136, F.TOPQ), ("fixed_68", 68, F.TOPQ),
+                 ("method_B68", 68, F.WATERFILL), ("method_B46", 46, F.WATERFILL),
+                 (f"group_shared_B{budget}", budget, F.WATERFILL_GROUP)]
+        picks, name_of = {}, {(b, m): name for name, b, m in modes}
+        for name, b, m in modes:
+            r = timed(b, m, csteps)
+            if name != f"method_B{budget}":
+                comparison[name] = r
+        # informational: recall@k against the exact fp32 top-k of q . K on the
+        # unquantised keys, for the query heads of KV head 0
+        from synthetic import kv_head
+        k0, _ = kv_head(wl.key, 0, 0, 0, n, d, wl.outliers)
+        exact = [set(np.argpartition(-(k0 @ q_np[h]), k - 1)[:k].tolist()) for h in range(hq // hk)]
+        del k0
+        comparison["recall_at_k_vs_exact_fp32"] = {
+            name: round(float(np.mean([len(exact[h] & set(sel[h].tolist())) / k for h in range(len(exact))])), 4)
+            for name, sel in picks.items()}
+        comparison["recall_sample"] = f"the {hq // hk} query heads of KV head 0, top-{k} of {n} keys"
         comparison["speedup_vs_fixed_136"] = round(comparison["fixed_136"]["ms_per_step"] / step_ms, 3)
         comparison["bytes_method_B68_vs_fixed_68"] = round(
             comparison["method_B68"]["bytes_per_key"] / comparison["fixed_68"]["bytes_per_key"], 3)
@@ -385,6 +403,52 @@ def main():
                      "kernel": "attend_kernel<16> + attend_merge" if d == 128 else "attend_kernel + attend_merge",
                      "rows": f"{hq} query heads x {k} selected keys x (K + V) bf16 rows of {d}",
                      "step_plus_attention_ms": round(step_ms + att_ms, 4)}
+    # A growing cache: the last block left open (127 exact fp32 keys scored by
+    # the tail kernel, the rest scanned as sealed blocks), and the cost of
+    # sealing one 128-key block of every KV head.
+    append = None
+    if not args.no_append and n >= 256:
+        from synthetic import kv_head
+        n_sealed = (n - 1) // 128 * 128
+        n_tail = n - 1 - n_sealed
+        # rows n_sealed - 128 .. n - 2 of every KV head: the block to seal, then the tail
+        with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+            rows = np.stack(list(ex.map(
+                lambda v: kv_head(wl.key, 0, v // wl.h_kv, v % wl.h_kv, n, d, wl.outliers)[0][n_sealed - 128:n - 1],
+                range(hk))))
+        tail = torch.from_numpy(np.ascontiguousarray(rows[:, 128:])).to(dev)
+        blk = torch.from_numpy(np.ascontiguousarray(rows[:, :128])).to(dev)
+        aws2 = torch.empty(F.workspace_bytes(hq, hk, n_sealed + n_tail, d, k, F.HBM), dtype=torch.uint8, device=dev)
+
+        def step_tail():
+            F.allocate(q, s2, budget, mode=mode, depth=depth, union_depth=uni)
+            F.scan_topk_append(records, n, n_sealed, tail, q, depth, uni, k,
+                               residency=F.HOST_DIRECT if host else F.HBM, workspace=aws2, idx=idx)
+        for _ in range(2):
+            step_tail()
+        torch.cuda.synchronize(dev)
+        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        tsteps = max(3, min(args.steps, 20))
+        b0.record(stream)
+        for _ in range(tsteps):
+            step_tail()
+        b1.record(stream)
+        torch.cuda.synchronize(dev)
+        # sealing: one block of every KV head into device records of the same capacity
+        seal_rec = torch.empty((hk, d, F.record_bytes(n)), dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            F.pack_blocks(blk, seal_rec, n, n_sealed // 128 - 1)
+        torch.cuda.synchronize(dev)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        for _ in range(20):
+            F.pack_blocks(blk, seal_rec, n, n_sealed // 128 - 1)
+        c1.record(stream)
+        torch.cuda.synchronize(dev)
+        append = {"open_tail_keys": n_tail, "sealed_keys": n_sealed,
+                  "step_with_open_tail_ms": round(b0.elapsed_time(b1) / tsteps, 4),
+                  "seal_one_block_all_kv_heads_us": round(c0.elapsed_time(c1) / 20 * 1e3, 2)}
+        del seal_rec, blk, tail, aws2
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(wl, q_np, s2_np, budget)
@@ -408,6 +472,7 @@ def main():
         "cpu_baseline": cpu,
         "comparison": comparison,
         "attention": attention,
+        "append": append,
         "bytes_per_key": round(alg_bytes / (hk * n), 3),
         "link_frac_of_measured_h2d_per_step": round(alg_bytes / (step_ms * 1e-3) / 1e9 / h2d_peak, 4)
         if host else None,
