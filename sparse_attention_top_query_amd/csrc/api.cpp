@@ -159,16 +159,21 @@ size_t fathom_workspace_bytes(int h_q, int h_kv, int64_t n, int d, int k, int re
 namespace {
 
 // Scores of every key into `scores` [h_q][ld]; staging comes from the workspace.
+// The direct scans also zero `zero_words` words at `zero` (the selection's
+// counters); *cleared says whether that happened.
 int run_scan(const uint8_t* dev, int residency, const float* q, const uint8_t* depth,
              const uint8_t* union_depth, int h_q, int h_kv, int64_t n, int d, float* scores, int64_t ld,
-             uint8_t* staging, hipStream_t s) {
+             uint8_t* staging, uint32_t* zero, int64_t zero_words, bool* cleared, hipStream_t s) {
   const fathom::Layout L = fathom::make_layout(n);
   hipError_t e;
-  if (residency == FATHOM_HOST_STAGED)
+  *cleared = false;
+  if (residency == FATHOM_HOST_STAGED) {
     e = fathom::launch_scan_staged(dev, staging, q, depth, union_depth, h_kv, h_q / h_kv, L, d, scores, ld, s);
-  else
+  } else {
     e = fathom::launch_scan(dev, residency == FATHOM_HOST_DIRECT, q, depth, union_depth, h_kv, h_q / h_kv, L, d,
-                            scores, ld, s);
+                            scores, ld, zero, zero_words, s);
+    *cleared = zero != nullptr && L.nb > 0;
+  }
   if (e != hipSuccess) return hip_fail(e, "scan launch");
   return FATHOM_OK;
 }
@@ -199,8 +204,9 @@ int fathom_scan_scores(const void* records, int residency, const float* q, const
     if (!aligned(workspace, 256)) return fail(FATHOM_EINVAL, "workspace must be 256-byte aligned");
     staging = static_cast<uint8_t*>(workspace) + staging_offset(h_q, n, 1);
   }
-  st = run_scan(dev, residency, q, depth, union_depth, h_q, h_kv, n, d, scores, ld, staging,
-                static_cast<hipStream_t>(stream));
+  bool cleared = false;
+  st = run_scan(dev, residency, q, depth, union_depth, h_q, h_kv, n, d, scores, ld, staging, nullptr, 0,
+                &cleared, static_cast<hipStream_t>(stream));
   if (st) return st;
   return ok();
 }
@@ -224,10 +230,12 @@ int scan_topk(const void* records, int residency, const float* q, const uint8_t*
   float* scores = static_cast<float*>(workspace);
   uint8_t* sel_base = static_cast<uint8_t*>(workspace) + al256((size_t)h_q * (size_t)ld * 4);
   uint8_t* staging = static_cast<uint8_t*>(workspace) + staging_offset(h_q, n, k);
-  st = run_scan(dev, residency, q, depth, union_depth, h_q, h_kv, n, d, scores, ld, staging, s);
+  const fathom::SelectWorkspace sel = fathom::carve_select(sel_base, h_q, n, k);
+  bool cleared = false;
+  st = run_scan(dev, residency, q, depth, union_depth, h_q, h_kv, n, d, scores, ld, staging, sel.hist,
+                (int64_t)fathom::select_clear_words(h_q), &cleared, s);
   if (st) return st;
-  hipError_t e = fathom::launch_select(scores, ld, h_q, n, k, topk_idx, topk_score,
-                                       fathom::carve_select(sel_base, h_q, n, k), s);
+  hipError_t e = fathom::launch_select(scores, ld, h_q, n, k, topk_idx, topk_score, sel, cleared, s);
   if (e != hipSuccess) return hip_fail(e, "select launch");
   return ok();
 }
@@ -327,19 +335,22 @@ int scan_topk_append(const void* records, int residency, int64_t n_cap, int64_t 
   const int64_t ld = score_ld(n);
   float* scores = static_cast<float*>(workspace);
   uint8_t* sel_base = static_cast<uint8_t*>(workspace) + al256((size_t)h_q * (size_t)ld * 4);
+  const fathom::SelectWorkspace sel = fathom::carve_select(sel_base, h_q, n, k);
   hipError_t e;
+  bool cleared = false;
   if (n_sealed > 0) {
     // the capacity's geometry, cut to the sealed blocks
     fathom::Layout L = fathom::make_layout(n_cap);
     L.n = n_sealed;
     L.nb = (n_sealed + fathom::kBlock - 1) / fathom::kBlock;
     e = fathom::launch_scan(dev, residency == FATHOM_HOST_DIRECT, q, depth, union_depth, h_kv, h_q / h_kv, L, d,
-                            scores, ld, s);
+                            scores, ld, sel.hist, (int64_t)fathom::select_clear_words(h_q), s);
     if (e != hipSuccess) return hip_fail(e, "scan launch");
+    cleared = true;
   }
   e = fathom::launch_tail_scores(tail_k, q, h_kv, h_q / h_kv, n_tail, d, scores, ld, n_sealed, s);
   if (e != hipSuccess) return hip_fail(e, "tail launch");
-  e = fathom::launch_select(scores, ld, h_q, n, k, topk_idx, topk_score, fathom::carve_select(sel_base, h_q, n, k), s);
+  e = fathom::launch_select(scores, ld, h_q, n, k, topk_idx, topk_score, sel, cleared, s);
   if (e != hipSuccess) return hip_fail(e, "select launch");
   return ok();
 }

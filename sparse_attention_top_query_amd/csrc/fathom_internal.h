@@ -49,9 +49,11 @@ hipError_t launch_allocate(const float* q, const float* sigma2, int h_kv, int g,
                            uint32_t* status, hipStream_t s);
 // Scores of every key from device memory (host = false) or read in place from
 // pinned host memory (host = true, larger tiles for long contiguous runs).
+// The kernel also zeroes `zero_words` words at `zero` (the selection's
+// histograms and state; may be null).
 hipError_t launch_scan(const uint8_t* rec, bool host, const float* q, const uint8_t* depth,
                        const uint8_t* uni, int h_kv, int g, const Layout& L, int d,
-                       float* scores, int64_t ld, hipStream_t s);
+                       float* scores, int64_t ld, uint32_t* zero, int64_t zero_words, hipStream_t s);
 // Host-resident records: gather the union prefix runs into `staging` (an HBM
 // mirror of the records, h_kv * d * R bytes) and scan them there, the copy of
 // one KV head overlapped with the scan of the previous.
@@ -61,7 +63,7 @@ hipError_t launch_scan_staged(const uint8_t* host, uint8_t* staging, const float
 
 // Top-k selection over scores [h_q][ld], first n entries per row.
 struct SelectWorkspace {
-  uint32_t* hist;     // [h_q][2048] histogram of the top 11 key bits
+  uint32_t* hist;     // [h_q][4096] histogram of the top 12 key bits
   uint32_t* state;    // [h_q][4]: threshold bin, keys above it, overflow flag, -
   uint32_t* counts;   // [h_q][nchunks] kept keys per 4096-key chunk
   uint64_t* kept;     // [h_q][nchunks][512] (key, index) at or above the threshold bin
@@ -70,7 +72,10 @@ struct SelectWorkspace {
 int64_t select_chunks(int64_t n);
 size_t select_workspace_bytes(int h_q, int64_t n, int k);
 SelectWorkspace carve_select(void* base, int h_q, int64_t n, int k);
+// Words from ws.hist that must be zero when the selection starts (histograms
+// and state); `cleared` says a previous kernel on the stream zeroed them.
+size_t select_clear_words(int h_q);
 hipError_t launch_select(const float* scores, int64_t ld, int h_q, int64_t n, int k,
-                         int32_t* idx, float* val, const SelectWorkspace& ws, hipStream_t s);
+                         int32_t* idx, float* val, const SelectWorkspace& ws, bool cleared, hipStream_t s);
 
 }  // namespace fathom

@@ -83,6 +83,8 @@ struct ScanArgs {
   int d;
   float* scores;
   int64_t ld;
+  uint32_t* zero;            // words to clear on the way (may be null)
+  int64_t zero_words;
 };
 
 // Entry word: bits 0-2 union depth, bits 3-6 depths in use (bit 2+t: some head
@@ -351,6 +353,11 @@ __global__ __launch_bounds__((Cfg<G, TB>::threads)) void scan_kernel(ScanArgs a,
   const int64_t per = (total + kXcds - 1) / kXcds;
   const int64_t L = (w % kXcds) * per + w / kXcds;
   if (L >= total) return;
+  if (a.zero) {   // the selection's counters: one slice per workgroup
+    const int64_t slice = (a.zero_words + total - 1) / total;
+    const int64_t z1 = min((L + 1) * slice, a.zero_words);
+    for (int64_t i = L * slice + threadIdx.x; i < z1; i += Cfg<G, TB>::threads) a.zero[i] = 0u;
+  }
   scan_tile<G, TB>(a, L / tiles, L % tiles, sm);
 }
 
@@ -441,8 +448,9 @@ __global__ __launch_bounds__((Cfg<G, TB>::threads)) void stage_scan_kernel(
 
 template <int G, int TB>
 hipError_t launch_g(const uint8_t* rec, const float* q, const uint8_t* depth, const uint8_t* uni,
-                    int h_kv, const Layout& L, int d, float* scores, int64_t ld, hipStream_t s) {
-  const ScanArgs a{rec, q, depth, uni, L.n, L.nb, L.H, L.P, L.R, d, scores, ld};
+                    int h_kv, const Layout& L, int d, float* scores, int64_t ld, uint32_t* zero,
+                    int64_t zero_words, hipStream_t s) {
+  const ScanArgs a{rec, q, depth, uni, L.n, L.nb, L.H, L.P, L.R, d, scores, ld, zero, zero_words};
   const int64_t tiles = (L.nb + TB - 1) / TB;
   const int64_t total = tiles * h_kv;
   const int64_t per = (total + kXcds - 1) / kXcds;
@@ -455,7 +463,7 @@ hipError_t launch_staged_g(const uint8_t* host, uint8_t* staging, const float* q
                            const uint8_t* uni, int h_kv, const Layout& L, int d, float* scores,
                            int64_t ld, hipStream_t s) {
   constexpr int TB = kTileDevice;
-  const ScanArgs a{staging, q, depth, uni, L.n, L.nb, L.H, L.P, L.R, d, scores, ld};
+  const ScanArgs a{staging, q, depth, uni, L.n, L.nb, L.H, L.P, L.R, d, scores, ld, nullptr, 0};
   const int64_t tiles = (L.nb + TB - 1) / TB;
   const int64_t ncopy = copy_pieces_per_head(L, d);
   // heads per launch: about 64 MB of records per launch
@@ -480,23 +488,23 @@ hipError_t launch_staged_g(const uint8_t* host, uint8_t* staging, const float* q
 template <int G>
 hipError_t launch_any(const uint8_t* rec, bool host, const float* q, const uint8_t* depth,
                       const uint8_t* uni, int h_kv, const Layout& L, int d, float* scores, int64_t ld,
-                      hipStream_t s) {
-  if (host) return launch_g<G, HostTile<G>::TB>(rec, q, depth, uni, h_kv, L, d, scores, ld, s);
-  return launch_g<G, kTileDevice>(rec, q, depth, uni, h_kv, L, d, scores, ld, s);
+                      uint32_t* zero, int64_t zero_words, hipStream_t s) {
+  if (host) return launch_g<G, HostTile<G>::TB>(rec, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words, s);
+  return launch_g<G, kTileDevice>(rec, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words, s);
 }
 
 }  // namespace
 
 hipError_t launch_scan(const uint8_t* rec, bool host, const float* q, const uint8_t* depth,
                        const uint8_t* uni, int h_kv, int g, const Layout& L, int d,
-                       float* scores, int64_t ld, hipStream_t s) {
+                       float* scores, int64_t ld, uint32_t* zero, int64_t zero_words, hipStream_t s) {
   if (L.nb == 0) return hipSuccess;
   switch (g) {
-    case 1: return launch_any<1>(rec, host, q, depth, uni, h_kv, L, d, scores, ld, s);
-    case 2: return launch_any<2>(rec, host, q, depth, uni, h_kv, L, d, scores, ld, s);
-    case 4: return launch_any<4>(rec, host, q, depth, uni, h_kv, L, d, scores, ld, s);
-    case 8: return launch_any<8>(rec, host, q, depth, uni, h_kv, L, d, scores, ld, s);
-    case 16: return launch_any<16>(rec, host, q, depth, uni, h_kv, L, d, scores, ld, s);
+    case 1: return launch_any<1>(rec, host, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words, s);
+    case 2: return launch_any<2>(rec, host, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words, s);
+    case 4: return launch_any<4>(rec, host, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words, s);
+    case 8: return launch_any<8>(rec, host, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words, s);
+    case 16: return launch_any<16>(rec, host, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words, s);
     default: return hipErrorInvalidValue;
   }
 }

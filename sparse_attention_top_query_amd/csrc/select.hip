@@ -4,8 +4,11 @@
 //
 // Scores are mapped to order-preserving 32-bit keys
 //   key(f) = f >= +0 ? bits | 0x80000000 : ~bits      (-0 folded onto +0)
-// and everything after that is integer work, with two passes over the scores:
-//   1. hist     LDS histogram of the top 12 key bits per head;
+// and everything after that is integer work, with two passes over the scores.
+// The head histograms and the per-head state start at zero: cleared by the
+// scan that writes the scores, or by sel_init.
+//   1. hist     LDS histogram of the top 12 key bits per 4096-key chunk, added
+//               to the head's histogram;
 //   2. find     per head, the bin b holding the k-th largest key and the number
 //               of keys above it;
 //   3. collect  every key in bin b or above is written, as (key, index), to its
@@ -47,26 +50,6 @@ __global__ __launch_bounds__(kSelThreads) void sel_init(uint32_t* hist, uint32_t
   const int h = blockIdx.x;
   for (int b = threadIdx.x; b < kBins; b += kSelThreads) hist[(int64_t)h * kBins + b] = 0u;
   if (threadIdx.x < 4) state[h * 4 + threadIdx.x] = 0u;
-}
-
-__global__ __launch_bounds__(kSelThreads) void sel_hist(const float* __restrict__ scores, int64_t ld,
-                                                        int64_t n, uint32_t* __restrict__ hist) {
-  __shared__ uint32_t lh[kBins];
-  const int h = blockIdx.y;
-  for (int b = threadIdx.x; b < kBins; b += kSelThreads) lh[b] = 0u;
-  __syncthreads();
-  const float* row = scores + (int64_t)h * ld;
-  const int64_t j0 = (int64_t)blockIdx.x * kChunk;
-#pragma unroll 4
-  for (int i = 0; i < kPerThread; ++i) {
-    const int64_t j = j0 + (int64_t)i * kSelThreads + threadIdx.x;
-    if (j < n) atomicAdd(&lh[order_key(row[j]) >> kDigit0], 1u);
-  }
-  __syncthreads();
-  for (int b = threadIdx.x; b < kBins; b += kSelThreads) {
-    const uint32_t v = lh[b];
-    if (v) atomicAdd(&hist[(int64_t)h * kBins + b], v);
-  }
 }
 
 // inclusive suffix sum over the workgroup's threads (thread t gets sum over t' >= t)
@@ -111,7 +94,30 @@ __device__ __forceinline__ uint32_t block_exclusive(uint32_t v, uint32_t* wsum, 
   return base + inc - v;
 }
 
+__global__ __launch_bounds__(kSelThreads) void sel_hist(const float* __restrict__ scores, int64_t ld,
+                                                        int64_t n, uint32_t* __restrict__ hist) {
+  __shared__ uint32_t lh[kBins];
+  const int h = blockIdx.y;
+  for (int b = threadIdx.x; b < kBins; b += kSelThreads) lh[b] = 0u;
+  __syncthreads();
+  const float* row = scores + (int64_t)h * ld;
+  const int64_t j0 = (int64_t)blockIdx.x * kChunk;
+#pragma unroll 4
+  for (int i = 0; i < kPerThread; ++i) {
+    const int64_t j = j0 + (int64_t)i * kSelThreads + threadIdx.x;
+    if (j < n) atomicAdd(&lh[order_key(row[j]) >> kDigit0], 1u);
+  }
+  __syncthreads();
+  for (int b = threadIdx.x; b < kBins; b += kSelThreads) {
+    const uint32_t v = lh[b];
+    if (v) atomicAdd(&hist[(int64_t)h * kBins + b], v);
+  }
+}
+
 // Bin of the k-th largest key: the bin b with (keys above b) < k <= (keys at or above b).
+// A kernel of its own: the launch boundary orders it after every chunk's
+// histogram atomics (a device-scope fence per chunk instead would write back
+// the XCD's L2 once per workgroup).
 __global__ __launch_bounds__(kSelThreads) void sel_find(const uint32_t* __restrict__ hist,
                                                         uint32_t* __restrict__ state, int k) {
   constexpr int kPer = kBins / kSelThreads;   // 16 bins per thread
@@ -381,10 +387,14 @@ SelectWorkspace carve_select(void* base, int h_q, int64_t n, int k) {
   return ws;
 }
 
+size_t select_clear_words(int h_q) {
+  return (al256((size_t)h_q * kBins * 4) + al256((size_t)h_q * 4 * 4)) / 4;
+}
+
 hipError_t launch_select(const float* scores, int64_t ld, int h_q, int64_t n, int k, int32_t* idx,
-                         float* val, const SelectWorkspace& ws, hipStream_t s) {
+                         float* val, const SelectWorkspace& ws, bool cleared, hipStream_t s) {
   if (k == 0 || n == 0 || h_q == 0) return hipSuccess;
-  sel_init<<<h_q, kSelThreads, 0, s>>>(ws.hist, ws.state);
+  if (!cleared) sel_init<<<h_q, kSelThreads, 0, s>>>(ws.hist, ws.state);
   dim3 grid((unsigned)ws.nchunks, (unsigned)h_q);
   sel_hist<<<grid, kSelThreads, 0, s>>>(scores, ld, n, ws.hist);
   sel_find<<<h_q, kSelThreads, 0, s>>>(ws.hist, ws.state, k);
