@@ -36,6 +36,8 @@ Parity status of each function (what pins it, in tests/test_oracle_*.py):
                                  (KKT) certificate at d=128, sum t = B,
                                  monotone in B.
   topq_depths                    pinned: independent sort by (-|q|, c).
+  static_depths                  pinned: selection loop over (-sigma2, c),
+                                 ties and zeros.
   group_importance               pinned: one head equals importance; the
                                  shared allocation equals brute force over all
                                  depth vectors of sum_h sum_c w_hc 4^-t_c
@@ -307,6 +309,24 @@ def topq_depths(q: np.ndarray, m: int) -> np.ndarray:
     return t
 
 
+def static_depths(sigma2: np.ndarray, m: int) -> np.ndarray:
+    """Static fixed-depth comparison mode: all 4 planes of the m channels with the
+    largest offline variance sigma2_c, the same for every query of the KV head.
+
+    Stands for Double Sparsity's offline-calibrated channels ([Abstract] lists
+    it among the 136-bit scans); choosing by sigma2 with lowest index on ties is
+    the reading, sigma2 being the offline statistic the method itself uses.
+    """
+    s2 = np.asarray(sigma2, dtype=np.float32)
+    d = s2.shape[0]
+    if not 0 <= m <= d:
+        raise ValueError("m out of range")
+    order = sorted(range(d), key=lambda c: (-float(s2[c]), c))
+    t = np.zeros(d, dtype=np.int64)
+    t[order[:m]] = PLANES
+    return t
+
+
 def union_depths(depths: np.ndarray) -> np.ndarray:
     """Union prefix of a GQA group: max over the group's query heads.
 
@@ -425,7 +445,8 @@ def step(k_heads, q, sigma2, budget, k, mode="waterfill", packed=None):
     k_heads: float32 [h_kv, n, d]; q: float32 [h_q, d]; sigma2: float32 [h_kv, d].
     mode "waterfill": reverse water-filling with ``budget`` bits per key;
     mode "topq": 4 planes on budget // 4 channels of largest |q_c|;
-    mode "group": one water-filling per KV head on the group importance.
+    mode "group": one water-filling per KV head on the group importance;
+    mode "static": 4 planes on budget // 4 channels of largest sigma2.
     ``packed`` may hold precomputed (delta, kappa) per KV head.
     Returns dict with depth [h_q, d], union [h_kv, d], idx [h_q, k], and the
     fp64 scores/sums per query head.
@@ -440,6 +461,10 @@ def step(k_heads, q, sigma2, budget, k, mode="waterfill", packed=None):
         elif mode == "group":
             kv = h // g
             depth[h] = waterfill_depths(group_importance(q[kv * g:(kv + 1) * g], sigma2[kv]), budget)
+        elif mode == "static":
+            if budget % PLANES:
+                raise ValueError("fixed mode needs budget % 4 == 0")
+            depth[h] = static_depths(sigma2[h // g], budget // PLANES)
         else:
             if budget % PLANES:
                 raise ValueError("fixed mode needs budget % 4 == 0")

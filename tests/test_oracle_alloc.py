@@ -225,3 +225,23 @@ def test_group_allocation_minimises_the_summed_objective_d4():
             feas = [c for c in cands if sum(c) == b]
             vals = [obj(c) for c in feas]
             assert obj(t) == min(vals)
+
+
+def test_static_matches_selection_loop():
+    rng = np.random.default_rng(41)
+    for trial in range(20):
+        s2 = np.exp(rng.standard_normal(128)).astype(np.float32)
+        if trial % 3 == 0:
+            s2[rng.choice(128, 20)] = np.float32(2.0)      # ties
+            s2[rng.choice(128, 10)] = np.float32(0.0)      # zero variance
+        for m in (0, 1, 17, 34, 128):
+            chosen, left = [], list(range(128))
+            for _ in range(m):
+                best = left[0]
+                for c in left:
+                    if fr(s2[c]) > fr(s2[best]):
+                        best = c
+                chosen.append(best)
+                left.remove(best)
+            want = [4 if c in chosen else 0 for c in range(128)]
+            assert list(O.static_depths(s2, m)) == want
