@@ -346,6 +346,7 @@ def main():
         csteps = max(3, min(args.steps, 20))
         comparison = {"method_B": budget, "method_ms_per_step": round(step_ms, 4)}
         modes = [(f"method_B{budget}", budget, F.WATERFILL), ("fixed_136", 136, F.TOPQ), ("fixed_68", 68, F.TOPQ),
+                 ("static_136", 136, F.STATIC), ("static_68", 68, F.STATIC),
                  ("method_B68", 68, F.WATERFILL), ("method_B46", 46, F.WATERFILL),
                  (f"group_shared_B{budget}", budget, F.WATERFILL_GROUP)]
         picks, name_of = {}, {(b, m): name for name, b, m in modes}

@@ -68,10 +68,14 @@ enum fathom_depth_mode {
   FATHOM_WATERFILL = 0,    /* reverse water-filling (the method)                         */
   FATHOM_TOPQ = 1,         /* fixed-depth comparison scan: 4 planes on the budget/4
                               channels of largest |q_c| (ties: lowest channel)           */
-  FATHOM_WATERFILL_GROUP = 2 /* one reverse water-filling per KV head on the group's summed
+  FATHOM_WATERFILL_GROUP = 2, /* one reverse water-filling per KV head on the group's summed
                               importance; every query head of the group gets the same
                               depths, so the scan reads exactly `budget` bits per
                               KV-head key (a GQA variant the pages leave open)           */
+  FATHOM_STATIC = 3        /* fixed-depth comparison scan with static channels: 4 planes on
+                              the budget/4 channels of largest sigma2_c (offline statistics,
+                              as Double Sparsity calibrates its channels offline; ties:
+                              lowest channel), the same for every query of a KV head     */
 };
 
 /* Flags OR-ed into the device status words. */
@@ -130,11 +134,12 @@ int pack_bitplanes(const float* k, int h_kv, int64_t n, int d, void* records,
  *                largest w_c * 4^-t_c (compared exactly), lowest channel on ties --
  *                the minimiser of sum_c w_c 4^-t_c with sum_c t_c = budget.
  *                FATHOM_TOPQ: t_c = 4 on the budget/4 channels of largest |q_c|.
+ *                FATHOM_STATIC: t_c = 4 on the budget/4 channels of largest sigma2_c.
  *                FATHOM_WATERFILL_GROUP: the same greedy once per KV head on
  *                W_c = fl32(... fl32(w_0,c + w_1,c) ... + w_G-1,c), the fp32 sum in
  *                head order of the group's w_h,c; all G query heads get its depths
  *                (a non-finite q in the group zeroes the whole group's depths).
- *   budget       bits per key and query head, 0..4d (multiple of 4 for TOPQ).
+ *   budget       bits per key and query head, 0..4d (multiple of 4 for TOPQ, STATIC).
  *   depth        device, uint8 [h_q][d] output.
  *   union_depth  device, uint8 [h_kv][d] output: max over the KV head's query heads
  *                (the longest prefix, which contains every head's prefix).

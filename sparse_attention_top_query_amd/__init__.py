@@ -9,6 +9,7 @@ from .fathom import (  # noqa: F401
     HBM,
     HOST_DIRECT,
     HOST_STAGED,
+    STATIC,
     TOPQ,
     WATERFILL,
     WATERFILL_GROUP,
@@ -27,5 +28,5 @@ from .fathom import (  # noqa: F401
     workspace_bytes,
 )
 
-__all__ = ["HBM", "HOST_DIRECT", "HOST_STAGED", "TOPQ", "WATERFILL", "WATERFILL_GROUP", "FathomError", "allocate", "attend", "attend_workspace_bytes", "load", "pack", "pack_blocks",
+__all__ = ["HBM", "HOST_DIRECT", "HOST_STAGED", "STATIC", "TOPQ", "WATERFILL", "WATERFILL_GROUP", "FathomError", "allocate", "attend", "attend_workspace_bytes", "load", "pack", "pack_blocks",
            "prefix_bytes", "record_bytes", "scan_scores", "scan_topk", "scan_topk_append", "workspace_bytes"]

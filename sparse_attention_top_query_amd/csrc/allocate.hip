@@ -25,6 +25,9 @@
 // fixed top-|q| mode selects m channels the same way with
 // key = bits(|q_c|) << 8 | (255 - c).
 //
+// Static mode (mode 3) selects the same way with key = bits(sigma2_c) << 8 |
+// (255 - c); sigma2 >= 0, so its bits order like its values.
+//
 // Group-shared mode (mode 2): one allocation per KV head on the fp32 sum, in
 // head order, of the group's importances w_h,c; all query heads of the group
 // get the same depths, so the scan reads exactly B bits per KV-head key.
@@ -117,14 +120,17 @@ __global__ __launch_bounds__(1024) void allocate_kernel(const float* __restrict_
       for (int t = 0; t < kPlanes; ++t) tc += key[4 * i + t] >= K;
       t[i] = lane + 64 * i < d ? tc : 0;
     }
-  } else if (flag == 0 && mode == 1 && budget > 0) {
-    // fixed-depth comparison mode: 4 planes on the m channels of largest |q_c|
+  } else if (flag == 0 && (mode == 1 || mode == 3) && budget > 0) {
+    // fixed-depth comparison modes: 4 planes on the m channels of largest |q_c|
+    // (mode 1) or of largest offline variance sigma2_c (mode 3, the same for
+    // every query head of the KV head)
     const uint32_t m = (uint32_t)(budget / kPlanes);
     uint64_t key[CPL];
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
       const int c = lane + 64 * i;
-      key[i] = c < d ? ((uint64_t)__float_as_uint(aq[i]) << 8 | (uint64_t)(255 - c)) : 0ull;
+      const float v = mode == 1 ? aq[i] : (c < d ? sigma2[(int64_t)kv * d + c] : 0.0f);
+      key[i] = c < d ? ((uint64_t)__float_as_uint(v) << 8 | (uint64_t)(255 - c)) : 0ull;
     }
     // a channel with |q| = +0 and c = 255 has key 0: count it via the >= test only
     // when something else is smaller, so search over keys + 1

@@ -134,11 +134,11 @@ int allocate_depths(const float* q, const float* sigma2, int h_q, int h_kv, int 
   if (st) return st;
   if (!q || !sigma2 || !depth || !union_depth) return fail(FATHOM_EINVAL, "null pointer argument");
   if (!aligned(q, 4) || !aligned(sigma2, 4)) return fail(FATHOM_EINVAL, "q/sigma2 must be 4-byte aligned");
-  if (mode != FATHOM_WATERFILL && mode != FATHOM_TOPQ && mode != FATHOM_WATERFILL_GROUP)
+  if (mode != FATHOM_WATERFILL && mode != FATHOM_TOPQ && mode != FATHOM_WATERFILL_GROUP && mode != FATHOM_STATIC)
     return fail(FATHOM_EINVAL, "unknown mode %d", mode);
   if (budget < 0 || budget > fathom::kPlanes * d)
     return fail(FATHOM_EBUDGET, "budget=%d outside [0, %d]", budget, fathom::kPlanes * d);
-  if (mode == FATHOM_TOPQ && budget % fathom::kPlanes != 0)
+  if ((mode == FATHOM_TOPQ || mode == FATHOM_STATIC) && budget % fathom::kPlanes != 0)
     return fail(FATHOM_EBUDGET, "fixed-depth mode needs budget %% 4 == 0 (got %d)", budget);
   hipError_t e = fathom::launch_allocate(q, sigma2, h_kv, h_q / h_kv, d, mode, budget, depth,
                                          union_depth, status, static_cast<hipStream_t>(stream));

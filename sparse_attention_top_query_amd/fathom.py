@@ -22,6 +22,7 @@ HOST_STAGED = 2
 WATERFILL = 0
 TOPQ = 1
 WATERFILL_GROUP = 2
+STATIC = 3
 
 FLAG_KEY_NONFINITE = 1
 FLAG_SCALE_OVERFLOW = 2

@@ -45,6 +45,8 @@ def oracle_depths(q, s2, budget, mode="waterfill"):
         elif mode == "group":
             kv = h // g
             dep[h] = O.waterfill_depths(O.group_importance(q[kv * g:(kv + 1) * g], s2[kv]), budget)
+        elif mode == "static":
+            dep[h] = O.static_depths(s2[h // g], budget // 4)
         else:
             dep[h] = O.topq_depths(q[h], budget // 4)
     uni = np.stack([O.union_depths(dep[v * g:(v + 1) * g]) for v in range(s2.shape[0])])

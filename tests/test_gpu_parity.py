@@ -131,6 +131,17 @@ def test_allocate_topq_bit_exact(F, budget):
     assert np.array_equal(uni.cpu().numpy(), ru)
 
 
+@pytest.mark.parametrize("budget", [0, 68, 136, 512])
+def test_allocate_static_bit_exact(F, budget):
+    _, q, s2 = small_case(19, 8, 4, 1, 128, outliers=4)
+    s2[1, ::5] = np.float32(2.0)                 # variance ties, resolved by lowest channel
+    s2[2, :40] = 0.0
+    dep, uni = F.allocate(dev(q), dev(s2), budget, mode=F.STATIC)
+    rd, ru = oracle_depths(q, s2, budget, mode="static")
+    assert np.array_equal(dep.cpu().numpy(), rd)
+    assert np.array_equal(uni.cpu().numpy(), ru)
+
+
 def test_allocate_status_flags(F):
     _, q, s2 = small_case(12, 3, 2, 1, 32)
     q[1, 5] = np.nan          # KV head 0, query head 1
@@ -201,7 +212,7 @@ def run_case(F, case, residency="hbm", mode="waterfill"):
     if residency == "host":
         rec = rec.cpu().pin_memory()
     dq = dev(q)
-    modes = {"waterfill": F.WATERFILL, "topq": F.TOPQ, "group": F.WATERFILL_GROUP}
+    modes = {"waterfill": F.WATERFILL, "topq": F.TOPQ, "group": F.WATERFILL_GROUP, "static": F.STATIC}
     dep, uni = F.allocate(dq, dev(s2), budget, mode=modes[mode])
     scores = F.scan_scores(rec, dq, dep, uni, n)
     torch.cuda.synchronize()
@@ -335,6 +346,20 @@ def test_group_shared_scan_parity(F):
         s, a = O.scores(q[h], kappa, delta, rd[h])
         check_scores(sg[h], s, a)
         check_topk(idx[h], s, a, 300, s_gpu=sg[h])
+
+
+def test_static_scan_parity(F):
+    case = (2, 4, 4096, 128, 136)
+    k, q, s2, rec, dq, dep, uni, sg = run_case(F, case, mode="static")
+    packed = oracle_pack(k)
+    rd, _ = oracle_depths(q, s2, 136, mode="static")
+    assert np.array_equal(dep.cpu().numpy(), rd)
+    idx = F.scan_topk(rec, dq, dep, uni, 4096, 256).cpu().numpy()
+    for h in range(8):
+        delta, kappa, _ = packed[h // 4]
+        s, a = O.scores(q[h], kappa, delta, rd[h])
+        check_scores(sg[h], s, a)
+        check_topk(idx[h], s, a, 256, s_gpu=sg[h])
 
 
 def test_scan_rejects_bad_residency_and_workspace(F):
