@@ -159,19 +159,31 @@ size_t fathom_workspace_bytes(int h_q, int h_kv, int64_t n, int d, int k, int re
 namespace {
 
 // Scores of every key into `scores` [h_q][ld]; staging comes from the workspace.
-// The direct scans also zero `zero_words` words at `zero` (the selection's
-// counters); *cleared says whether that happened.
+// With a selection to follow (`sel`), the direct scans also prepare it: the
+// HBM scan zeroes its counters on the way (*cleared), and the link-bound
+// host-direct scan, where it fits, also builds its first-digit histograms
+// (*hist_done) after a clearing launch.
 int run_scan(const uint8_t* dev, int residency, const float* q, const uint8_t* depth,
              const uint8_t* union_depth, int h_q, int h_kv, int64_t n, int d, float* scores, int64_t ld,
-             uint8_t* staging, uint32_t* zero, int64_t zero_words, bool* cleared, hipStream_t s) {
+             uint8_t* staging, const fathom::SelectWorkspace* sel, bool* cleared, bool* hist_done,
+             hipStream_t s) {
   const fathom::Layout L = fathom::make_layout(n);
+  const int g = h_q / h_kv;
   hipError_t e;
   *cleared = false;
+  *hist_done = false;
   if (residency == FATHOM_HOST_STAGED) {
-    e = fathom::launch_scan_staged(dev, staging, q, depth, union_depth, h_kv, h_q / h_kv, L, d, scores, ld, s);
+    e = fathom::launch_scan_staged(dev, staging, q, depth, union_depth, h_kv, g, L, d, scores, ld, s);
+  } else if (sel && L.nb > 0 && residency == FATHOM_HOST_DIRECT && fathom::scan_fuses_hist(g)) {
+    e = fathom::launch_select_clear(*sel, h_q, s);
+    if (e == hipSuccess)
+      e = fathom::launch_scan(dev, true, q, depth, union_depth, h_kv, g, L, d, scores, ld, nullptr, 0, sel->hist, s);
+    *cleared = *hist_done = e == hipSuccess;
   } else {
-    e = fathom::launch_scan(dev, residency == FATHOM_HOST_DIRECT, q, depth, union_depth, h_kv, h_q / h_kv, L, d,
-                            scores, ld, zero, zero_words, s);
+    uint32_t* zero = sel ? sel->hist : nullptr;
+    const int64_t zero_words = sel ? (int64_t)fathom::select_clear_words(h_q) : 0;
+    e = fathom::launch_scan(dev, residency == FATHOM_HOST_DIRECT, q, depth, union_depth, h_kv, g, L, d, scores, ld,
+                            zero, zero_words, nullptr, s);
     *cleared = zero != nullptr && L.nb > 0;
   }
   if (e != hipSuccess) return hip_fail(e, "scan launch");
@@ -204,9 +216,9 @@ int fathom_scan_scores(const void* records, int residency, const float* q, const
     if (!aligned(workspace, 256)) return fail(FATHOM_EINVAL, "workspace must be 256-byte aligned");
     staging = static_cast<uint8_t*>(workspace) + staging_offset(h_q, n, 1);
   }
-  bool cleared = false;
-  st = run_scan(dev, residency, q, depth, union_depth, h_q, h_kv, n, d, scores, ld, staging, nullptr, 0,
-                &cleared, static_cast<hipStream_t>(stream));
+  bool cleared = false, hist_done = false;
+  st = run_scan(dev, residency, q, depth, union_depth, h_q, h_kv, n, d, scores, ld, staging, nullptr, &cleared,
+                &hist_done, static_cast<hipStream_t>(stream));
   if (st) return st;
   return ok();
 }
@@ -231,11 +243,11 @@ int scan_topk(const void* records, int residency, const float* q, const uint8_t*
   uint8_t* sel_base = static_cast<uint8_t*>(workspace) + al256((size_t)h_q * (size_t)ld * 4);
   uint8_t* staging = static_cast<uint8_t*>(workspace) + staging_offset(h_q, n, k);
   const fathom::SelectWorkspace sel = fathom::carve_select(sel_base, h_q, n, k);
-  bool cleared = false;
-  st = run_scan(dev, residency, q, depth, union_depth, h_q, h_kv, n, d, scores, ld, staging, sel.hist,
-                (int64_t)fathom::select_clear_words(h_q), &cleared, s);
+  bool cleared = false, hist_done = false;
+  st = run_scan(dev, residency, q, depth, union_depth, h_q, h_kv, n, d, scores, ld, staging, &sel, &cleared,
+                &hist_done, s);
   if (st) return st;
-  hipError_t e = fathom::launch_select(scores, ld, h_q, n, k, topk_idx, topk_score, sel, cleared, s);
+  hipError_t e = fathom::launch_select(scores, ld, h_q, n, k, topk_idx, topk_score, sel, cleared, hist_done, s);
   if (e != hipSuccess) return hip_fail(e, "select launch");
   return ok();
 }
@@ -344,13 +356,13 @@ int scan_topk_append(const void* records, int residency, int64_t n_cap, int64_t 
     L.n = n_sealed;
     L.nb = (n_sealed + fathom::kBlock - 1) / fathom::kBlock;
     e = fathom::launch_scan(dev, residency == FATHOM_HOST_DIRECT, q, depth, union_depth, h_kv, h_q / h_kv, L, d,
-                            scores, ld, sel.hist, (int64_t)fathom::select_clear_words(h_q), s);
+                            scores, ld, sel.hist, (int64_t)fathom::select_clear_words(h_q), nullptr, s);
     if (e != hipSuccess) return hip_fail(e, "scan launch");
     cleared = true;
   }
   e = fathom::launch_tail_scores(tail_k, q, h_kv, h_q / h_kv, n_tail, d, scores, ld, n_sealed, s);
   if (e != hipSuccess) return hip_fail(e, "tail launch");
-  e = fathom::launch_select(scores, ld, h_q, n, k, topk_idx, topk_score, sel, cleared, s);
+  e = fathom::launch_select(scores, ld, h_q, n, k, topk_idx, topk_score, sel, cleared, false, s);
   if (e != hipSuccess) return hip_fail(e, "select launch");
   return ok();
 }

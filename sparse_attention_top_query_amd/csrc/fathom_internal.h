@@ -41,6 +41,16 @@ inline Layout make_layout(int64_t n) {
 
 inline int64_t prefix_bytes(const Layout& L, int t) { return t <= 0 ? 0 : L.H + (t - 1) * L.P; }
 
+// Selection keys: an order-preserving map of fp32 scores to uint32 (-0 folded
+// onto +0), and the first digit of the selection's histogram (its top 12 bits).
+constexpr int kSelBins = 4096;
+constexpr int kSelDigit0 = 20;
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t b = __float_as_uint(f);
+  if (b == 0x80000000u) b = 0u;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
 // ---- launchers (each returns hipSuccess or the launch error) ----
 hipError_t launch_pack(const float* k, int h_kv, const Layout& L, int d, uint8_t* rec,
                        uint32_t* status, hipStream_t s);
@@ -50,10 +60,14 @@ hipError_t launch_allocate(const float* q, const float* sigma2, int h_kv, int g,
 // Scores of every key from device memory (host = false) or read in place from
 // pinned host memory (host = true, larger tiles for long contiguous runs).
 // The kernel also zeroes `zero_words` words at `zero` (the selection's
-// histograms and state; may be null).
+// histograms and state; may be null).  With `hist` (host = true only, and only
+// where scan_fuses_hist(g)), it also adds every score's first selection digit
+// to hist[h][kSelBins], which must be zero beforehand.
 hipError_t launch_scan(const uint8_t* rec, bool host, const float* q, const uint8_t* depth,
                        const uint8_t* uni, int h_kv, int g, const Layout& L, int d,
-                       float* scores, int64_t ld, uint32_t* zero, int64_t zero_words, hipStream_t s);
+                       float* scores, int64_t ld, uint32_t* zero, int64_t zero_words, uint32_t* hist,
+                       hipStream_t s);
+bool scan_fuses_hist(int g);
 // Host-resident records: gather the union prefix runs into `staging` (an HBM
 // mirror of the records, h_kv * d * R bytes) and scan them there, the copy of
 // one KV head overlapped with the scan of the previous.
@@ -75,7 +89,10 @@ SelectWorkspace carve_select(void* base, int h_q, int64_t n, int k);
 // Words from ws.hist that must be zero when the selection starts (histograms
 // and state); `cleared` says a previous kernel on the stream zeroed them.
 size_t select_clear_words(int h_q);
+// `hist_done`: the scan already built the histograms (implies cleared).
 hipError_t launch_select(const float* scores, int64_t ld, int h_q, int64_t n, int k,
-                         int32_t* idx, float* val, const SelectWorkspace& ws, bool cleared, hipStream_t s);
+                         int32_t* idx, float* val, const SelectWorkspace& ws, bool cleared, bool hist_done,
+                         hipStream_t s);
+hipError_t launch_select_clear(const SelectWorkspace& ws, int h_q, hipStream_t s);
 
 }  // namespace fathom

@@ -85,6 +85,7 @@ struct ScanArgs {
   int64_t ld;
   uint32_t* zero;            // words to clear on the way (may be null)
   int64_t zero_words;
+  uint32_t* hist;            // selection histograms [h_q][kSelBins] to add to (fused scans)
 };
 
 // Entry word: bits 0-2 union depth, bits 3-6 depths in use (bit 2+t: some head
@@ -93,8 +94,16 @@ __device__ __forceinline__ int word_tb(uint64_t w) { return (int)(w & 7); }
 __device__ __forceinline__ int word_th(uint64_t w, int h) { return (int)((w >> (8 + 3 * h)) & 7); }
 __device__ __forceinline__ uint32_t u4(const uint4& v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
 
-// Scores of tile `tile` (TB blocks) of KV head g, all its query heads.
+// Whether the selection's first-digit histograms of all G heads fit in the
+// tile's staging memory, which is dead once the last group is scored.
 template <int G, int TB>
+constexpr bool kFusable = sizeof(ScanSmem<G, TB>) >= (size_t)G * kSelBins * 4;
+
+// Scores of tile `tile` (TB blocks) of KV head g, all its query heads.  With
+// FUSE, the tile's scores are also counted into a.hist by their first
+// selection digit (an LDS histogram in the staging memory, then one global
+// atomic per non-empty bin).
+template <int G, int TB, bool FUSE = false>
 __device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t tile, ScanSmem<G, TB>& sm) {
   using C = Cfg<G, TB>;
   constexpr int SLOTS = C::slots;
@@ -329,6 +338,30 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t 
       }
     }
   }
+
+  // ---- 5. fused first-digit histogram of the selection ----
+  if constexpr (FUSE) {
+    static_assert(kFusable<G, TB>, "histograms must fit in the staging memory");
+    uint32_t* lh = reinterpret_cast<uint32_t*>(&sm);
+    __syncthreads();   // every wave is past its last read of the staging memory
+    for (int i = tid; i < G * kSelBins; i += NT) lh[i] = 0u;
+    __syncthreads();
+    if (bl < nvalid) {
+#pragma unroll
+      for (int s2 = 0; s2 < kSub; ++s2) {
+        const int64_t j = (blk0 + bl) * kBlock + s2 * 32 + (lane & 31);
+        if (j < a.n) {
+#pragma unroll
+          for (int h = 0; h < G; ++h) atomicAdd(&lh[h * kSelBins + (order_key(acc[s2][h]) >> kSelDigit0)], 1u);
+        }
+      }
+    }
+    __syncthreads();
+    for (int i = tid; i < G * kSelBins; i += NT) {
+      const uint32_t v = lh[i];
+      if (v) atomicAdd(&a.hist[(g * G + i / kSelBins) * kSelBins + i % kSelBins], v);
+    }
+  }
 }
 
 // Tile size per residency: device memory likes many small tiles (occupancy);
@@ -346,7 +379,7 @@ struct HostTile {
 // runs can share a cache line at their boundary, then meet in the same L2.
 constexpr int kXcds = 8;
 
-template <int G, int TB>
+template <int G, int TB, bool FUSE>
 __global__ __launch_bounds__((Cfg<G, TB>::threads)) void scan_kernel(ScanArgs a, int64_t tiles, int64_t total) {
   __shared__ ScanSmem<G, TB> sm;
   const int64_t w = blockIdx.x;
@@ -358,7 +391,7 @@ __global__ __launch_bounds__((Cfg<G, TB>::threads)) void scan_kernel(ScanArgs a,
     const int64_t z1 = min((L + 1) * slice, a.zero_words);
     for (int64_t i = L * slice + threadIdx.x; i < z1; i += Cfg<G, TB>::threads) a.zero[i] = 0u;
   }
-  scan_tile<G, TB>(a, L / tiles, L % tiles, sm);
+  scan_tile<G, TB, FUSE>(a, L / tiles, L % tiles, sm);
 }
 
 // ---------------------------------------------------------------------------
@@ -449,12 +482,19 @@ __global__ __launch_bounds__((Cfg<G, TB>::threads)) void stage_scan_kernel(
 template <int G, int TB>
 hipError_t launch_g(const uint8_t* rec, const float* q, const uint8_t* depth, const uint8_t* uni,
                     int h_kv, const Layout& L, int d, float* scores, int64_t ld, uint32_t* zero,
-                    int64_t zero_words, hipStream_t s) {
-  const ScanArgs a{rec, q, depth, uni, L.n, L.nb, L.H, L.P, L.R, d, scores, ld, zero, zero_words};
+                    int64_t zero_words, uint32_t* hist, hipStream_t s) {
+  const ScanArgs a{rec, q, depth, uni, L.n, L.nb, L.H, L.P, L.R, d, scores, ld, zero, zero_words, hist};
   const int64_t tiles = (L.nb + TB - 1) / TB;
   const int64_t total = tiles * h_kv;
   const int64_t per = (total + kXcds - 1) / kXcds;
-  scan_kernel<G, TB><<<(unsigned)(per * kXcds), Cfg<G, TB>::threads, 0, s>>>(a, tiles, total);
+  if constexpr (kFusable<G, TB>) {
+    if (hist) {
+      scan_kernel<G, TB, true><<<(unsigned)(per * kXcds), Cfg<G, TB>::threads, 0, s>>>(a, tiles, total);
+      return hipGetLastError();
+    }
+  }
+  if (hist) return hipErrorInvalidValue;
+  scan_kernel<G, TB, false><<<(unsigned)(per * kXcds), Cfg<G, TB>::threads, 0, s>>>(a, tiles, total);
   return hipGetLastError();
 }
 
@@ -463,7 +503,7 @@ hipError_t launch_staged_g(const uint8_t* host, uint8_t* staging, const float* q
                            const uint8_t* uni, int h_kv, const Layout& L, int d, float* scores,
                            int64_t ld, hipStream_t s) {
   constexpr int TB = kTileDevice;
-  const ScanArgs a{staging, q, depth, uni, L.n, L.nb, L.H, L.P, L.R, d, scores, ld, nullptr, 0};
+  const ScanArgs a{staging, q, depth, uni, L.n, L.nb, L.H, L.P, L.R, d, scores, ld, nullptr, 0, nullptr};
   const int64_t tiles = (L.nb + TB - 1) / TB;
   const int64_t ncopy = copy_pieces_per_head(L, d);
   // heads per launch: about 64 MB of records per launch
@@ -488,23 +528,37 @@ hipError_t launch_staged_g(const uint8_t* host, uint8_t* staging, const float* q
 template <int G>
 hipError_t launch_any(const uint8_t* rec, bool host, const float* q, const uint8_t* depth,
                       const uint8_t* uni, int h_kv, const Layout& L, int d, float* scores, int64_t ld,
-                      uint32_t* zero, int64_t zero_words, hipStream_t s) {
-  if (host) return launch_g<G, HostTile<G>::TB>(rec, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words, s);
-  return launch_g<G, kTileDevice>(rec, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words, s);
+                      uint32_t* zero, int64_t zero_words, uint32_t* hist, hipStream_t s) {
+  if (host)
+    return launch_g<G, HostTile<G>::TB>(rec, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words, hist, s);
+  if (hist) return hipErrorInvalidValue;
+  return launch_g<G, kTileDevice>(rec, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words, nullptr, s);
 }
 
 }  // namespace
 
+bool scan_fuses_hist(int g) {
+  switch (g) {
+    case 1: return kFusable<1, HostTile<1>::TB>;
+    case 2: return kFusable<2, HostTile<2>::TB>;
+    case 4: return kFusable<4, HostTile<4>::TB>;
+    case 8: return kFusable<8, HostTile<8>::TB>;
+    case 16: return kFusable<16, HostTile<16>::TB>;
+    default: return false;
+  }
+}
+
 hipError_t launch_scan(const uint8_t* rec, bool host, const float* q, const uint8_t* depth,
                        const uint8_t* uni, int h_kv, int g, const Layout& L, int d,
-                       float* scores, int64_t ld, uint32_t* zero, int64_t zero_words, hipStream_t s) {
+                       float* scores, int64_t ld, uint32_t* zero, int64_t zero_words, uint32_t* hist,
+                       hipStream_t s) {
   if (L.nb == 0) return hipSuccess;
   switch (g) {
-    case 1: return launch_any<1>(rec, host, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words, s);
-    case 2: return launch_any<2>(rec, host, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words, s);
-    case 4: return launch_any<4>(rec, host, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words, s);
-    case 8: return launch_any<8>(rec, host, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words, s);
-    case 16: return launch_any<16>(rec, host, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words, s);
+    case 1: return launch_any<1>(rec, host, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words, hist, s);
+    case 2: return launch_any<2>(rec, host, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words, hist, s);
+    case 4: return launch_any<4>(rec, host, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words, hist, s);
+    case 8: return launch_any<8>(rec, host, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words, hist, s);
+    case 16: return launch_any<16>(rec, host, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words, hist, s);
     default: return hipErrorInvalidValue;
   }
 }

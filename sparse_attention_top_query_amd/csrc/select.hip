@@ -32,18 +32,12 @@ namespace {
 constexpr int kSelThreads = 256;
 constexpr int kPerThread = 16;
 constexpr int kChunk = kSelThreads * kPerThread;   // keys per hist/collect workgroup
-constexpr int kBins = 4096;                        // first digit: top 12 key bits
-constexpr int kDigit0 = 20;                        // shift of the first digit
+constexpr int kBins = kSelBins;                    // first digit: top 12 key bits
+constexpr int kDigit0 = kSelDigit0;                // shift of the first digit
 constexpr int kResolveThreads = 1024;
 constexpr int kSlot = 512;                         // kept keys per 4096-key chunk
 constexpr int kKeep = 16384;                       // kept keys per head resolved in LDS (128 KB)
 constexpr int kKeepPer = kKeep / kResolveThreads;
-
-__device__ __forceinline__ uint32_t order_key(float f) {
-  uint32_t b = __float_as_uint(f);
-  if (b == 0x80000000u) b = 0u;
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
 
 // state per head: [0] bin b, [1] keys above bin b, [2] overflow flag, [3] unused
 __global__ __launch_bounds__(kSelThreads) void sel_init(uint32_t* hist, uint32_t* state) {
@@ -391,12 +385,17 @@ size_t select_clear_words(int h_q) {
   return (al256((size_t)h_q * kBins * 4) + al256((size_t)h_q * 4 * 4)) / 4;
 }
 
+hipError_t launch_select_clear(const SelectWorkspace& ws, int h_q, hipStream_t s) {
+  sel_init<<<h_q, kSelThreads, 0, s>>>(ws.hist, ws.state);
+  return hipGetLastError();
+}
+
 hipError_t launch_select(const float* scores, int64_t ld, int h_q, int64_t n, int k, int32_t* idx,
-                         float* val, const SelectWorkspace& ws, bool cleared, hipStream_t s) {
+                         float* val, const SelectWorkspace& ws, bool cleared, bool hist_done, hipStream_t s) {
   if (k == 0 || n == 0 || h_q == 0) return hipSuccess;
-  if (!cleared) sel_init<<<h_q, kSelThreads, 0, s>>>(ws.hist, ws.state);
+  if (!cleared && !hist_done) sel_init<<<h_q, kSelThreads, 0, s>>>(ws.hist, ws.state);
   dim3 grid((unsigned)ws.nchunks, (unsigned)h_q);
-  sel_hist<<<grid, kSelThreads, 0, s>>>(scores, ld, n, ws.hist);
+  if (!hist_done) sel_hist<<<grid, kSelThreads, 0, s>>>(scores, ld, n, ws.hist);
   sel_find<<<h_q, kSelThreads, 0, s>>>(ws.hist, ws.state, k);
   sel_collect<<<grid, kSelThreads, 0, s>>>(scores, ld, n, ws.state, ws.kept, ws.counts, ws.nchunks);
   sel_resolve<<<h_q, kResolveThreads, 0, s>>>(scores, ld, n, k, ws.state, ws.kept, ws.counts, ws.nchunks, idx,

@@ -309,6 +309,24 @@ def test_host_residencies_match_hbm_bit_for_bit(F, case):
         assert np.array_equal(a, b), res
 
 
+@pytest.mark.parametrize("case", [(2, 4, 3 * 1024 + 300, 128, 92), (1, 1, 4096, 128, 64), (3, 2, 9000, 64, 40),
+                                  (1, 8, 5000, 128, 100), (2, 4, 2048, 128, 0), (1, 4, 300, 16, 20)])
+def test_host_direct_topk_equals_hbm(F, case):
+    # host-direct scans build the selection's histogram inside the scan where it
+    # fits (G <= 4); the selection must come out exactly as from HBM records
+    h_kv, g, n, d, budget = case
+    k_np, q, s2, rec, dq, dep, uni, sg = run_case(F, case)
+    k = min(n, 333)
+    ih, sh = F.scan_topk(rec, dq, dep, uni, n, k, residency=F.HBM, want_scores=True)
+    host = rec.cpu().pin_memory()
+    idd, sd = F.scan_topk(host, dq, dep, uni, n, k, residency=F.HOST_DIRECT, want_scores=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(ih.cpu().numpy(), idd.cpu().numpy())
+    assert np.array_equal(sh.cpu().numpy().view(np.uint32), sd.cpu().numpy().view(np.uint32))
+    for h in range(h_kv * g):
+        assert np.array_equal(idd.cpu().numpy()[h], O.topk(sg[h].astype(np.float64), k))
+
+
 def test_staged_many_heads_per_launch(F):
     """Records of ~10 MB per KV head put 6 KV heads in each copy/scan launch, with a
     ragged last launch (13 = 6 + 6 + 1): staged must still equal HBM-resident."""
