@@ -26,7 +26,8 @@
  *     status nothing was enqueued and no output was written;
  *     fathom_last_error() gives a message (per calling thread).
  *   - Shapes: h_kv KV heads, G = h_q / h_kv query heads per KV head
- *     (G in {1, 2, 4, 8, 16}), d channels (1..256), n keys (n >= 0).
+ *     (G in {1, 2, 4, 8, 16}), d channels (1..256), n keys (0 <= n <= 2^30,
+ *     n * h_kv <= 2^33; these keep every launch grid within 2^32 work-items).
  *     Query head h belongs to KV head h / G.  Independent sessions are passed
  *     as extra KV heads (session-major), since sessions never mix.
  */

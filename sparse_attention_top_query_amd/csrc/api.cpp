@@ -52,6 +52,20 @@ int check_heads(int h_q, int h_kv, int d) {
 
 int64_t score_ld(int64_t n) { return (n + 63) / 64 * 64; }
 
+// Size limits that keep every launch grid within 2^32 work-items per dimension:
+// keys per head, keys times KV heads (the scan's threads are n h_kv / 4), and
+// the open tail.
+constexpr int64_t kMaxN = int64_t(1) << 30;
+constexpr int64_t kMaxKeyHeads = int64_t(1) << 33;
+constexpr int64_t kMaxTail = int64_t(1) << 20;
+
+int check_n(int64_t n, int h_kv, const char* what) {
+  if (n < 0 || n > kMaxN) return fail(FATHOM_ESHAPE, "%s=%lld outside [0, 2^30]", what, (long long)n);
+  if (n * h_kv > kMaxKeyHeads)
+    return fail(FATHOM_ESHAPE, "%s * h_kv = %lld exceeds 2^33", what, (long long)(n * h_kv));
+  return FATHOM_OK;
+}
+
 size_t al256(size_t x) { return (x + 255) / 256 * 256; }
 
 // Resolve the device-visible address of a buffer (`what`: records, k_cache, ...)
@@ -89,7 +103,8 @@ int check_scan_args(const void* records, int residency, const float* q, const ui
                     const uint8_t** dev) {
   int st = check_heads(h_q, h_kv, d);
   if (st) return st;
-  if (n < 0 || n > (int64_t(1) << 34)) return fail(FATHOM_ESHAPE, "n=%lld out of range", (long long)n);
+  st = check_n(n, h_kv, "n");
+  if (st) return st;
   if (!q || !depth || !union_depth) return fail(FATHOM_EINVAL, "null q/depth/union_depth");
   if (!aligned(q, 4)) return fail(FATHOM_EINVAL, "q must be 4-byte aligned");
   if (n == 0) return FATHOM_OK;
@@ -116,7 +131,8 @@ int pack_bitplanes(const float* k, int h_kv, int64_t n, int d, void* records, ui
                    void* stream) {
   if (h_kv < 1 || h_kv > 65535) return fail(FATHOM_ESHAPE, "h_kv=%d outside [1, 65535]", h_kv);
   if (d < 1 || d > fathom::kMaxD) return fail(FATHOM_ESHAPE, "d=%d outside [1, %d]", d, fathom::kMaxD);
-  if (n < 0 || n > (int64_t(1) << 34)) return fail(FATHOM_ESHAPE, "n=%lld out of range", (long long)n);
+  int st = check_n(n, h_kv, "n");
+  if (st) return st;
   if (n > 0 && (!k || !records)) return fail(FATHOM_EINVAL, "null k or records");
   if (n > 0 && (!aligned(k, 4) || !aligned(records, 16)))
     return fail(FATHOM_EINVAL, "k must be 4-byte and records 16-byte aligned");
@@ -266,8 +282,10 @@ int attend_topk(const void* k_cache, const void* v_cache, int residency, const f
     return fail(FATHOM_ESHAPE, "h_q=%d is not a multiple of h_kv=%d", h_q, h_kv);
   if (d != 8 && d != 16 && d != 32 && d != 64 && d != 128 && d != 256)
     return fail(FATHOM_ESHAPE, "attend_topk needs d in {8, 16, 32, 64, 128, 256} (got %d)", d);
-  if (n < 1 || n > (int64_t(1) << 34)) return fail(FATHOM_ESHAPE, "n=%lld out of range", (long long)n);
+  if (n < 1 || n > kMaxN) return fail(FATHOM_ESHAPE, "n=%lld outside [1, 2^30]", (long long)n);
   if (k < 1 || k > (1 << 28)) return fail(FATHOM_ESHAPE, "k=%d outside [1, 2^28]", k);
+  if ((int64_t)h_q * fathom::attend_splits(d, k) > (int64_t(1) << 23))
+    return fail(FATHOM_ESHAPE, "h_q * ceil(k / %d) exceeds 2^23 workgroups", fathom::attend_keys_per_group(d));
   if (!std::isfinite(scale)) return fail(FATHOM_EINVAL, "scale must be finite");
   if (!k_cache || !v_cache || !q || !topk_idx || !out) return fail(FATHOM_EINVAL, "null pointer argument");
   if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(q, 16))
@@ -297,7 +315,9 @@ int pack_blocks(const float* k, int h_kv, int64_t n_cap, int64_t block0, int64_t
                 void* records, uint32_t* status, void* stream) {
   if (h_kv < 1 || h_kv > 65535) return fail(FATHOM_ESHAPE, "h_kv=%d outside [1, 65535]", h_kv);
   if (d < 1 || d > fathom::kMaxD) return fail(FATHOM_ESHAPE, "d=%d outside [1, %d]", d, fathom::kMaxD);
-  if (n_cap < 1 || n_cap > (int64_t(1) << 34)) return fail(FATHOM_ESHAPE, "n_cap=%lld out of range", (long long)n_cap);
+  if (n_cap < 1) return fail(FATHOM_ESHAPE, "n_cap=%lld must be positive", (long long)n_cap);
+  int st = check_n(n_cap, h_kv, "n_cap");
+  if (st) return st;
   const fathom::Layout cap = fathom::make_layout(n_cap);
   if (block0 < 0 || nblocks < 0 || block0 + nblocks > cap.nb)
     return fail(FATHOM_ESHAPE, "blocks [%lld, %lld) outside the %lld blocks of capacity %lld", (long long)block0,
@@ -318,11 +338,12 @@ int scan_topk_append(const void* records, int residency, int64_t n_cap, int64_t 
                      size_t workspace_bytes, void* stream) {
   int st = check_heads(h_q, h_kv, d);
   if (st) return st;
-  if (n_cap < 0 || n_cap > (int64_t(1) << 34)) return fail(FATHOM_ESHAPE, "n_cap=%lld out of range", (long long)n_cap);
+  st = check_n(n_cap, h_kv, "n_cap");
+  if (st) return st;
   if (n_sealed < 0 || n_sealed > n_cap || (n_sealed % fathom::kBlock != 0 && n_sealed != n_cap))
     return fail(FATHOM_ESHAPE, "n_sealed=%lld must be a multiple of 128 (or n_cap) within [0, n_cap=%lld]",
                 (long long)n_sealed, (long long)n_cap);
-  if (n_tail < 0 || n_tail > (int64_t(1) << 30)) return fail(FATHOM_ESHAPE, "n_tail=%lld out of range", (long long)n_tail);
+  if (n_tail < 0 || n_tail > kMaxTail) return fail(FATHOM_ESHAPE, "n_tail=%lld outside [0, 2^20]", (long long)n_tail);
   const int64_t n = n_sealed + n_tail;
   if (k < 0 || k > n) return fail(FATHOM_ESHAPE, "k=%d outside [0, n_sealed + n_tail = %lld]", k, (long long)n);
   if (residency != FATHOM_HBM && residency != FATHOM_HOST_DIRECT)

@@ -158,7 +158,7 @@ def allocate(q: torch.Tensor, sigma2: torch.Tensor, budget: int, mode: int = WAT
 
 
 def _residency_of(records: torch.Tensor) -> int:
-    return HBM if records.is_cuda else HOST_STAGED
+    return HBM if records.is_cuda else HOST_DIRECT
 
 
 def scan_topk(records: torch.Tensor, q: torch.Tensor, depth: torch.Tensor, union_depth: torch.Tensor,
@@ -168,7 +168,8 @@ def scan_topk(records: torch.Tensor, q: torch.Tensor, depth: torch.Tensor, union
     """scan_topk: -> int32 [h_q, k] ascending key indices (and float32 scores if asked).
 
     ``records`` may be a device tensor (HBM residency) or a pinned host tensor
-    (staged host residency by default; HOST_DIRECT reads it in place)."""
+    (read in place over the host link by default; HOST_STAGED gathers the
+    prefix runs into an HBM mirror first)."""
     _need(q, "q", torch.float32, 2)
     _need(depth, "depth", torch.uint8)
     _need(union_depth, "union_depth", torch.uint8)

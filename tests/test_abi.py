@@ -133,6 +133,21 @@ def test_append_validation(lib):
     assert app(h_q=6, h_kv=4) == -2
 
 
+def test_size_limits_keep_grids_valid(lib):
+    P = ctypes.c_void_p
+    fake = P(0x1000)
+    f = ctypes.c_float
+    assert lib.pack_bitplanes(fake, 1, (1 << 30) + 1, 8, fake, None, None) == -2
+    assert lib.pack_bitplanes(fake, 16, 1 << 30, 8, fake, None, None) == -2          # n * h_kv > 2^33
+    assert lib.scan_topk(fake, 0, fake, fake, fake, 64, 16, 1 << 30, 8, 4, fake, None, fake, 1 << 20, None) == -2
+    assert "2^33" in _err(lib)
+    assert lib.scan_topk_append(fake, 0, 4096, 4096, fake, (1 << 20) + 1, fake, fake, fake, 4, 1, 128, 8, fake, None,
+                                fake, 1 << 30, None) == -2
+    # attention: h_q * ceil(k / 256) workgroups at most 2^23
+    assert lib.attend_topk(fake, fake, 0, fake, fake, 65536, 1, 1 << 20, 128, 1 << 16, f(0.1), fake, None, None,
+                           fake, 1 << 40, None) == -2
+
+
 def test_binding_refuses_cpu_tensors(lib):
     import torch
     from sparse_attention_top_query_amd import fathom
