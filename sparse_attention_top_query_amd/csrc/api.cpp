@@ -369,21 +369,31 @@ int scan_topk_append(const void* records, int residency, int64_t n_cap, int64_t 
   float* scores = static_cast<float*>(workspace);
   uint8_t* sel_base = static_cast<uint8_t*>(workspace) + al256((size_t)h_q * (size_t)ld * 4);
   const fathom::SelectWorkspace sel = fathom::carve_select(sel_base, h_q, n, k);
+  const int g = h_q / h_kv;
   hipError_t e;
-  bool cleared = false;
+  bool cleared = false, hist_done = false;
   if (n_sealed > 0) {
     // the capacity's geometry, cut to the sealed blocks
     fathom::Layout L = fathom::make_layout(n_cap);
     L.n = n_sealed;
     L.nb = (n_sealed + fathom::kBlock - 1) / fathom::kBlock;
-    e = fathom::launch_scan(dev, residency == FATHOM_HOST_DIRECT, q, depth, union_depth, h_kv, h_q / h_kv, L, d,
-                            scores, ld, sel.hist, (int64_t)fathom::select_clear_words(h_q), nullptr, s);
+    if (residency == FATHOM_HOST_DIRECT && fathom::scan_fuses_hist(g)) {
+      // the link-bound scan builds the histograms; the tail kernel adds its keys
+      e = fathom::launch_select_clear(sel, h_q, s);
+      if (e == hipSuccess)
+        e = fathom::launch_scan(dev, true, q, depth, union_depth, h_kv, g, L, d, scores, ld, nullptr, 0, sel.hist, s);
+      hist_done = true;
+    } else {
+      e = fathom::launch_scan(dev, residency == FATHOM_HOST_DIRECT, q, depth, union_depth, h_kv, g, L, d, scores,
+                              ld, sel.hist, (int64_t)fathom::select_clear_words(h_q), nullptr, s);
+    }
     if (e != hipSuccess) return hip_fail(e, "scan launch");
     cleared = true;
   }
-  e = fathom::launch_tail_scores(tail_k, q, h_kv, h_q / h_kv, n_tail, d, scores, ld, n_sealed, s);
+  e = fathom::launch_tail_scores(tail_k, q, h_kv, g, n_tail, d, scores, ld, n_sealed, hist_done ? sel.hist : nullptr,
+                                 s);
   if (e != hipSuccess) return hip_fail(e, "tail launch");
-  e = fathom::launch_select(scores, ld, h_q, n, k, topk_idx, topk_score, sel, cleared, false, s);
+  e = fathom::launch_select(scores, ld, h_q, n, k, topk_idx, topk_score, sel, cleared, hist_done, s);
   if (e != hipSuccess) return hip_fail(e, "select launch");
   return ok();
 }

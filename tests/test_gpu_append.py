@@ -123,3 +123,24 @@ def test_decode_loop_appends_and_seals(F):
         print(f"decode step {step_no}: n={n} sealed={sealed}", flush=True)
         for h in range(h_kv * g):
             check_topk(idx[h], ref["scores"][h], ref["sums"][h], k, where=f"step {step_no} head {h}")
+
+
+@pytest.mark.parametrize("case", APPEND_CASES)
+def test_append_host_direct_equals_hbm(F, case):
+    # the host-direct path counts scan and tail scores into the selection's
+    # histograms inside its kernels (G <= 4); the selection must equal HBM's
+    h_kv, g, n_cap, n_s, n_t, d, budget, k = case
+    kk, q, s2 = small_case(sum(case) + 1, h_kv, g, n_cap, d, outliers=min(4, d))
+    rec = empty_records(F, h_kv, d, n_cap)
+    if n_s > 0:
+        F.pack_blocks(dev(np.ascontiguousarray(kk[:, :n_s])), rec, n_cap, 0)
+    pinned = torch.empty(rec.shape, dtype=torch.uint8, pin_memory=True)
+    pinned.copy_(rec)
+    tail = dev(np.ascontiguousarray(kk[:, n_s:n_s + n_t])) if n_t else None
+    dq = dev(q)
+    dep, uni = F.allocate(dq, dev(s2), budget)
+    a = F.scan_topk_append(rec, n_cap, n_s, tail, dq, dep, uni, k, residency=F.HBM, want_scores=True)
+    b = F.scan_topk_append(pinned, n_cap, n_s, tail, dq, dep, uni, k, residency=F.HOST_DIRECT, want_scores=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(a[0].cpu().numpy(), b[0].cpu().numpy())
+    assert np.array_equal(a[1].cpu().numpy().view(np.uint32), b[1].cpu().numpy().view(np.uint32))
