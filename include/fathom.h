@@ -14,7 +14,8 @@
  *   scan_topk        per query step: score every key from its read prefix, return top-k.
  * and the attention that consumes the selection is a fourth:
  *   attend_topk      per query step: attention of each query head over its top-k keys.
- * A cache that grows during decoding uses pack_blocks and scan_topk_append.
+ * A cache that grows during decoding uses pack_blocks and scan_topk_append, or
+ * paged records and scan_topk_paged.
  *
  * Conventions shared by every call:
  *   - Device pointers are HIP device memory unless stated; every call is
@@ -223,6 +224,36 @@ int scan_topk_append(const void* records, int residency, int64_t n_cap, int64_t 
                      const uint8_t* union_depth, int h_q, int h_kv, int d, int k,
                      int32_t* topk_idx, float* topk_score, void* workspace,
                      size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Paged records: a cache that grows without reallocating or copying.  A page
+ * holds page_keys keys (a multiple of 4096) of one KV head, laid out exactly as
+ * the records of a page_keys-key cache: [d][fathom_record_bytes(page_keys)]
+ * bytes, so pack_bitplanes or pack_blocks (h_kv = 1, n = n_cap = page_keys)
+ * write it, and any t-prefix of a channel is one contiguous run inside it.
+ * Page p of KV head g holds keys p page_keys .. (p + 1) page_keys - 1.
+ * ------------------------------------------------------------------------- */
+
+/* fathom_device_address -- the address a kernel uses for `p`: `p` itself for
+ * device memory (FATHOM_HBM), the mapped device address of pinned host memory
+ * (FATHOM_HOST_DIRECT).  For building page tables.  Synchronous, no GPU work. */
+int fathom_device_address(const void* p, int residency, void** out);
+
+/* scan_topk_paged -- scan_topk_append over paged records.
+ *   page_table   device, [h_kv][ceil(n_sealed / page_keys)] device addresses
+ *                (fathom_device_address) of the pages, all in `residency`
+ *                (FATHOM_HBM or FATHOM_HOST_DIRECT); 8-byte aligned.
+ *   n_sealed     sealed keys, a multiple of 128; the blocks past n_sealed in the
+ *                last page are not read.
+ *   tail_k, n_tail, q, depth, union_depth, k, topk_idx, topk_score, workspace
+ *                as for scan_topk_append (workspace: fathom_workspace_bytes(h_q,
+ *                h_kv, n_sealed + n_tail, d, k, FATHOM_HBM)).
+ * The scores, and so the selection, are bit-identical to those of the same
+ * keys in contiguous records. */
+int scan_topk_paged(const void* const* page_table, int residency, int64_t page_keys, int64_t n_sealed,
+                    const float* tail_k, int64_t n_tail, const float* q, const uint8_t* depth,
+                    const uint8_t* union_depth, int h_q, int h_kv, int d, int k, int32_t* topk_idx,
+                    float* topk_score, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace attend_topk needs: per query head and split of its
  * k keys, a partial output (d + 2 floats) and a flag word. */

@@ -17,16 +17,19 @@ from .fathom import (  # noqa: F401
     allocate,
     attend,
     attend_workspace_bytes,
+    device_address,
     load,
     pack,
     pack_blocks,
+    page_table,
     prefix_bytes,
     record_bytes,
     scan_scores,
     scan_topk,
     scan_topk_append,
+    scan_topk_paged,
     workspace_bytes,
 )
 
-__all__ = ["HBM", "HOST_DIRECT", "HOST_STAGED", "STATIC", "TOPQ", "WATERFILL", "WATERFILL_GROUP", "FathomError", "allocate", "attend", "attend_workspace_bytes", "load", "pack", "pack_blocks",
-           "prefix_bytes", "record_bytes", "scan_scores", "scan_topk", "scan_topk_append", "workspace_bytes"]
+__all__ = ["HBM", "HOST_DIRECT", "HOST_STAGED", "STATIC", "TOPQ", "WATERFILL", "WATERFILL_GROUP", "FathomError", "allocate", "attend", "attend_workspace_bytes", "device_address", "load", "pack", "pack_blocks", "page_table",
+           "prefix_bytes", "record_bytes", "scan_scores", "scan_topk", "scan_topk_append", "scan_topk_paged", "workspace_bytes"]

@@ -398,4 +398,77 @@ int scan_topk_append(const void* records, int residency, int64_t n_cap, int64_t 
   return ok();
 }
 
+int fathom_device_address(const void* p, int residency, void** out) {
+  if (!p || !out) return fail(FATHOM_EINVAL, "null pointer argument");
+  if (residency != FATHOM_HBM && residency != FATHOM_HOST_DIRECT)
+    return fail(FATHOM_ERESIDENCY, "addresses are resolved for FATHOM_HBM or FATHOM_HOST_DIRECT memory");
+  const uint8_t* dev = nullptr;
+  int st = resolve_view(p, residency, "buffer", &dev);
+  if (st) return st;
+  *out = const_cast<uint8_t*>(dev);
+  return ok();
+}
+
+int scan_topk_paged(const void* const* page_table, int residency, int64_t page_keys, int64_t n_sealed,
+                    const float* tail_k, int64_t n_tail, const float* q, const uint8_t* depth,
+                    const uint8_t* union_depth, int h_q, int h_kv, int d, int k, int32_t* topk_idx,
+                    float* topk_score, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_heads(h_q, h_kv, d);
+  if (st) return st;
+  if (page_keys < 4096 || page_keys % 4096 != 0 || page_keys > kMaxN)
+    return fail(FATHOM_ESHAPE, "page_keys=%lld must be a positive multiple of 4096 up to 2^30", (long long)page_keys);
+  st = check_n(n_sealed, h_kv, "n_sealed");
+  if (st) return st;
+  if (n_sealed % fathom::kBlock != 0)
+    return fail(FATHOM_ESHAPE, "n_sealed=%lld must be a multiple of 128", (long long)n_sealed);
+  if (n_tail < 0 || n_tail > kMaxTail) return fail(FATHOM_ESHAPE, "n_tail=%lld outside [0, 2^20]", (long long)n_tail);
+  const int64_t n = n_sealed + n_tail;
+  if (k < 0 || k > n) return fail(FATHOM_ESHAPE, "k=%d outside [0, n_sealed + n_tail = %lld]", k, (long long)n);
+  if (residency != FATHOM_HBM && residency != FATHOM_HOST_DIRECT)
+    return fail(FATHOM_ERESIDENCY, "scan_topk_paged reads pages from HBM or in place from pinned host memory");
+  if (!q || !depth || !union_depth) return fail(FATHOM_EINVAL, "null q/depth/union_depth");
+  if (!aligned(q, 4)) return fail(FATHOM_EINVAL, "q must be 4-byte aligned");
+  if (n_tail > 0 && (!tail_k || !aligned(tail_k, 4))) return fail(FATHOM_EINVAL, "tail_k must be non-null, 4-byte aligned");
+  if (n_sealed > 0 && (!page_table || !aligned(page_table, 8)))
+    return fail(FATHOM_EINVAL, "page_table must be non-null and 8-byte aligned");
+  if (k == 0) return ok();
+  if (!topk_idx) return fail(FATHOM_EINVAL, "null topk_idx");
+  const size_t need = fathom_workspace_bytes(h_q, h_kv, n, d, k, FATHOM_HBM);
+  if (!workspace || workspace_bytes < need)
+    return fail(FATHOM_EWORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, need);
+  if (!aligned(workspace, 256)) return fail(FATHOM_EINVAL, "workspace must be 256-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t ld = score_ld(n);
+  float* scores = static_cast<float*>(workspace);
+  uint8_t* sel_base = static_cast<uint8_t*>(workspace) + al256((size_t)h_q * (size_t)ld * 4);
+  const fathom::SelectWorkspace sel = fathom::carve_select(sel_base, h_q, n, k);
+  const int g = h_q / h_kv;
+  const bool host = residency == FATHOM_HOST_DIRECT;
+  hipError_t e = hipSuccess;
+  bool cleared = false, hist_done = false;
+  if (n_sealed > 0) {
+    fathom::Layout L = fathom::make_layout(n_sealed);
+    const int64_t npages = (n_sealed + page_keys - 1) / page_keys;
+    const auto* table = reinterpret_cast<const uint8_t* const*>(page_table);
+    if (host && fathom::scan_fuses_hist(g)) {
+      e = fathom::launch_select_clear(sel, h_q, s);
+      if (e == hipSuccess)
+        e = fathom::launch_scan_paged(nullptr, table, npages, page_keys, true, q, depth, union_depth, h_kv, g, L, d,
+                                      scores, ld, nullptr, 0, sel.hist, s);
+      hist_done = true;
+    } else {
+      e = fathom::launch_scan_paged(nullptr, table, npages, page_keys, host, q, depth, union_depth, h_kv, g, L, d,
+                                    scores, ld, sel.hist, (int64_t)fathom::select_clear_words(h_q), nullptr, s);
+    }
+    if (e != hipSuccess) return hip_fail(e, "scan launch");
+    cleared = true;
+  }
+  e = fathom::launch_tail_scores(tail_k, q, h_kv, g, n_tail, d, scores, ld, n_sealed, hist_done ? sel.hist : nullptr,
+                                 s);
+  if (e != hipSuccess) return hip_fail(e, "tail launch");
+  e = fathom::launch_select(scores, ld, h_q, n, k, topk_idx, topk_score, sel, cleared, hist_done, s);
+  if (e != hipSuccess) return hip_fail(e, "select launch");
+  return ok();
+}
+
 }  // extern "C"

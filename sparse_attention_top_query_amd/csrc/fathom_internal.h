@@ -68,6 +68,13 @@ hipError_t launch_scan(const uint8_t* rec, bool host, const float* q, const uint
                        float* scores, int64_t ld, uint32_t* zero, int64_t zero_words, uint32_t* hist,
                        hipStream_t s);
 bool scan_fuses_hist(int g);
+// The same over paged records: table[g * npages + p] is the device-visible base
+// of page p of KV head g, [d][R(page_keys)] bytes laid out as whole records of
+// the page's page_keys keys (a multiple of 4096); L describes the keys scanned.
+hipError_t launch_scan_paged(const uint8_t* rec, const uint8_t* const* table, int64_t npages, int64_t page_keys,
+                             bool host, const float* q, const uint8_t* depth, const uint8_t* uni, int h_kv, int g,
+                             const Layout& L, int d, float* scores, int64_t ld, uint32_t* zero, int64_t zero_words,
+                             uint32_t* hist, hipStream_t s);
 // Host-resident records: gather the union prefix runs into `staging` (an HBM
 // mirror of the records, h_kv * d * R bytes) and scan them there, the copy of
 // one KV head overlapped with the scan of the previous.

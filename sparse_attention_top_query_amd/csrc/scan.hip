@@ -86,6 +86,12 @@ struct ScanArgs {
   uint32_t* zero;            // words to clear on the way (may be null)
   int64_t zero_words;
   uint32_t* hist;            // selection histograms [h_q][kSelBins] to add to (fused scans)
+  // paged records (may be null): pages[g * npages + p] is the device-visible
+  // base of page p of KV head g, [d][R] bytes for page_tiles tiles of keys,
+  // laid out as whole records of those keys (H, P, R are the page's)
+  const uint8_t* const* pages;
+  int64_t npages;
+  int64_t page_tiles;
 };
 
 // Entry word: bits 0-2 union depth, bits 3-6 depths in use (bit 2+t: some head
@@ -191,8 +197,17 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t 
 #pragma unroll
     for (int h = 0; h < G; ++h) acc[s][h] = 0.0f;
 
-  const uint8_t* recg = rec + g * d * R;
-  const int64_t unit0 = blk0 / kUnitBlocks;
+  // the tile's records: the KV head's own, or its page (addressed page-locally)
+  const uint8_t* recg;
+  int64_t ablk0;   // first block of the tile within those records
+  if (a.pages) {
+    recg = a.pages[g * a.npages + tile / a.page_tiles];
+    ablk0 = (tile % a.page_tiles) * TB;
+  } else {
+    recg = rec + g * d * R;
+    ablk0 = blk0;
+  }
+  const int64_t unit0 = ablk0 / kUnitBlocks;
   const int n_grp = sm.n_grp;
 
   // ---- 2. staging.  Piece i of a group is slot i % SLOTS of chunk i / SLOTS.  A
@@ -217,7 +232,7 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t 
           if (un * kUnitBlocks + (w == 0 ? 0 : w - 1) < nvalid)
             src = reinterpret_cast<const uint4*>(base + kUnitHead * (unit0 + un) + 16 * w);
         } else if (k < nvalid) {   // also skips the unused slots k >= TB
-          src = reinterpret_cast<const uint4*>(base + H + (p - 1) * P + (blk0 + k) * 16);
+          src = reinterpret_cast<const uint4*>(base + H + (p - 1) * P + (ablk0 + k) * 16);
         }
       }
       v[r] = src ? *src : make_uint4(0u, 0u, 0u, 0u);
@@ -479,11 +494,30 @@ __global__ __launch_bounds__((Cfg<G, TB>::threads)) void stage_scan_kernel(
   }
 }
 
+// Paging of a scan: the page table and the keys per page (0: contiguous records).
+struct Paging {
+  const uint8_t* const* table;
+  int64_t npages;
+  int64_t page_keys;
+};
+
 template <int G, int TB>
 hipError_t launch_g(const uint8_t* rec, const float* q, const uint8_t* depth, const uint8_t* uni,
                     int h_kv, const Layout& L, int d, float* scores, int64_t ld, uint32_t* zero,
-                    int64_t zero_words, uint32_t* hist, hipStream_t s) {
-  const ScanArgs a{rec, q, depth, uni, L.n, L.nb, L.H, L.P, L.R, d, scores, ld, zero, zero_words, hist};
+                    int64_t zero_words, uint32_t* hist, const Paging& pg, hipStream_t s) {
+  ScanArgs a{rec, q, depth, uni, L.n, L.nb, L.H, L.P, L.R, d, scores, ld, zero, zero_words, hist,
+             nullptr, 0, 1};
+  if (pg.table) {
+    // page records are laid out for page_keys keys; tiles never straddle pages
+    const Layout P = make_layout(pg.page_keys);
+    if (pg.page_keys % (TB * kBlock) != 0) return hipErrorInvalidValue;
+    a.H = P.H;
+    a.P = P.P;
+    a.R = P.R;
+    a.pages = pg.table;
+    a.npages = pg.npages;
+    a.page_tiles = pg.page_keys / (TB * kBlock);
+  }
   const int64_t tiles = (L.nb + TB - 1) / TB;
   const int64_t total = tiles * h_kv;
   const int64_t per = (total + kXcds - 1) / kXcds;
@@ -503,7 +537,8 @@ hipError_t launch_staged_g(const uint8_t* host, uint8_t* staging, const float* q
                            const uint8_t* uni, int h_kv, const Layout& L, int d, float* scores,
                            int64_t ld, hipStream_t s) {
   constexpr int TB = kTileDevice;
-  const ScanArgs a{staging, q, depth, uni, L.n, L.nb, L.H, L.P, L.R, d, scores, ld, nullptr, 0, nullptr};
+  const ScanArgs a{staging, q, depth, uni, L.n, L.nb, L.H, L.P, L.R, d, scores, ld, nullptr, 0, nullptr,
+                   nullptr, 0, 1};
   const int64_t tiles = (L.nb + TB - 1) / TB;
   const int64_t ncopy = copy_pieces_per_head(L, d);
   // heads per launch: about 64 MB of records per launch
@@ -528,11 +563,11 @@ hipError_t launch_staged_g(const uint8_t* host, uint8_t* staging, const float* q
 template <int G>
 hipError_t launch_any(const uint8_t* rec, bool host, const float* q, const uint8_t* depth,
                       const uint8_t* uni, int h_kv, const Layout& L, int d, float* scores, int64_t ld,
-                      uint32_t* zero, int64_t zero_words, uint32_t* hist, hipStream_t s) {
+                      uint32_t* zero, int64_t zero_words, uint32_t* hist, const Paging& pg, hipStream_t s) {
   if (host)
-    return launch_g<G, HostTile<G>::TB>(rec, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words, hist, s);
+    return launch_g<G, HostTile<G>::TB>(rec, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words, hist, pg, s);
   if (hist) return hipErrorInvalidValue;
-  return launch_g<G, kTileDevice>(rec, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words, nullptr, s);
+  return launch_g<G, kTileDevice>(rec, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words, nullptr, pg, s);
 }
 
 }  // namespace
@@ -552,13 +587,22 @@ hipError_t launch_scan(const uint8_t* rec, bool host, const float* q, const uint
                        const uint8_t* uni, int h_kv, int g, const Layout& L, int d,
                        float* scores, int64_t ld, uint32_t* zero, int64_t zero_words, uint32_t* hist,
                        hipStream_t s) {
+  return launch_scan_paged(rec, nullptr, 0, 0, host, q, depth, uni, h_kv, g, L, d, scores, ld, zero, zero_words,
+                           hist, s);
+}
+
+hipError_t launch_scan_paged(const uint8_t* rec, const uint8_t* const* table, int64_t npages, int64_t page_keys,
+                             bool host, const float* q, const uint8_t* depth, const uint8_t* uni, int h_kv, int g,
+                             const Layout& L, int d, float* scores, int64_t ld, uint32_t* zero, int64_t zero_words,
+                             uint32_t* hist, hipStream_t s) {
   if (L.nb == 0) return hipSuccess;
+  const Paging pg{table, npages, page_keys};
   switch (g) {
-    case 1: return launch_any<1>(rec, host, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words, hist, s);
-    case 2: return launch_any<2>(rec, host, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words, hist, s);
-    case 4: return launch_any<4>(rec, host, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words, hist, s);
-    case 8: return launch_any<8>(rec, host, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words, hist, s);
-    case 16: return launch_any<16>(rec, host, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words, hist, s);
+    case 1: return launch_any<1>(rec, host, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words, hist, pg, s);
+    case 2: return launch_any<2>(rec, host, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words, hist, pg, s);
+    case 4: return launch_any<4>(rec, host, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words, hist, pg, s);
+    case 8: return launch_any<8>(rec, host, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words, hist, pg, s);
+    case 16: return launch_any<16>(rec, host, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words, hist, pg, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -66,6 +66,8 @@ def load() -> ctypes.CDLL:
         "fathom_scan_scores": (I, [P, I, P, P, P, I, I, L, I, P, L, P, S, P]),
         "fathom_attend_workspace_bytes": (S, [I, I, I]),
         "pack_blocks": (I, [P, I, L, L, L, I, P, P, P]),
+        "fathom_device_address": (I, [P, I, ctypes.POINTER(ctypes.c_void_p)]),
+        "scan_topk_paged": (I, [P, I, L, L, P, L, P, P, P, I, I, I, I, P, P, P, S, P]),
         "scan_topk_append": (I, [P, I, L, L, P, L, P, P, P, I, I, I, I, P, P, P, S, P]),
         "attend_topk": (I, [P, P, I, P, P, I, I, L, I, I, ctypes.c_float, P, P, P, P, S, P]),
         "fathom_last_error": (ctypes.c_char_p, []),
@@ -320,4 +322,62 @@ def scan_topk_append(records: torch.Tensor | None, n_cap: int, n_sealed: int, ta
     _check(load().scan_topk_append(_ptr(records), residency, n_cap, n_sealed, _ptr(tail_k), n_tail, _ptr(q),
                                    _ptr(depth), _ptr(union_depth), h_q, h_kv, d, k, _ptr(idx), _ptr(scores),
                                    _ptr(workspace), workspace.numel(), _stream(q)))
+    return (idx, scores) if want_scores or scores is not None else idx
+
+
+def device_address(t: torch.Tensor, residency: int | None = None) -> int:
+    """fathom_device_address: the address kernels use for tensor ``t`` (device
+    memory, or pinned host memory read in place)."""
+    if residency is None:
+        residency = HBM if t.is_cuda else HOST_DIRECT
+    out = ctypes.c_void_p()
+    _check(load().fathom_device_address(_ptr(t), residency, ctypes.byref(out)))
+    return int(out.value)
+
+
+def page_table(pages, device="cuda:0", residency: int | None = None) -> torch.Tensor:
+    """int64 [h_kv, npages] device tensor of page addresses from ``pages[g][p]``,
+    uint8 tensors of [d, record_bytes(page_keys)] bytes each."""
+    rows = [[device_address(pg, residency) for pg in head] for head in pages]
+    if len({len(r) for r in rows}) != 1:
+        raise ValueError("every KV head needs the same number of pages")
+    return torch.tensor(rows, dtype=torch.int64, device=device)
+
+
+def scan_topk_paged(table: torch.Tensor | None, page_keys: int, n_sealed: int, tail_k: torch.Tensor | None,
+                    q: torch.Tensor, depth: torch.Tensor, union_depth: torch.Tensor, k: int,
+                    residency: int = HOST_DIRECT, workspace: torch.Tensor | None = None,
+                    idx: torch.Tensor | None = None, scores: torch.Tensor | None = None,
+                    want_scores: bool = False):
+    """scan_topk_paged: top k over n_sealed keys in paged records plus the exact open tail."""
+    _need(q, "q", torch.float32, 2)
+    _need(depth, "depth", torch.uint8)
+    _need(union_depth, "union_depth", torch.uint8)
+    h_q, d = q.shape
+    h_kv = union_depth.shape[0]
+    if table is not None:
+        _need(table, "table", torch.int64, 2)
+        if table.shape[0] != h_kv or table.shape[1] < -(-n_sealed // page_keys):
+            raise ValueError("page table must be [h_kv, >= ceil(n_sealed / page_keys)]")
+        if table.shape[1] != -(-n_sealed // page_keys):
+            table = table[:, :-(-n_sealed // page_keys)].contiguous()
+    n_tail = 0
+    if tail_k is not None:
+        _need(tail_k, "tail_k", torch.float32, 3)
+        n_tail = tail_k.shape[1]
+    n = n_sealed + n_tail
+    if workspace is None:
+        workspace = torch.empty(max(workspace_bytes(h_q, h_kv, n, d, k, HBM), 1), dtype=torch.uint8,
+                                device=q.device)
+    _need(workspace, "workspace", torch.uint8)
+    if idx is None:
+        idx = torch.empty((h_q, k), dtype=torch.int32, device=q.device)
+    _need(idx, "idx", torch.int32)
+    if want_scores and scores is None:
+        scores = torch.empty((h_q, k), dtype=torch.float32, device=q.device)
+    if scores is not None:
+        _need(scores, "scores", torch.float32)
+    _check(load().scan_topk_paged(_ptr(table), residency, page_keys, n_sealed, _ptr(tail_k), n_tail, _ptr(q),
+                                  _ptr(depth), _ptr(union_depth), h_q, h_kv, d, k, _ptr(idx), _ptr(scores),
+                                  _ptr(workspace), workspace.numel(), _stream(q)))
     return (idx, scores) if want_scores or scores is not None else idx
