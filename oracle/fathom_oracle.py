@@ -50,6 +50,8 @@ Parity status of each function (what pins it, in tests/test_oracle_*.py):
                                  the t-bit quantizer identity, the
                                  4x-per-bit error bound.
   topk                           pinned: brute-force sort on small n.
+  pack_nibbles, unpack_nibbles   pinned: hand-decoded bytes, round trip, sizes
+                                 (the free path's scores are ``scores``).
   tail_scores, step_append       pinned: tail scores equal exact rational
                                  sums; an empty tail reduces to step(); an
                                  all-tail cache gives the brute-force top-k of
@@ -225,6 +227,34 @@ def unpack_codes(rec: np.ndarray, n: int, depth: int = PLANES) -> tuple[np.ndarr
         bits = np.unpackbits(bits_packed, axis=1, bitorder="little")
         code = (code << 1) | bits[:, :n].T
     return delta, code
+
+
+def pack_nibbles(kappa: np.ndarray, delta: np.ndarray):
+    """The same 4-bit copy, token-major as a quantized serving stack holds it (the
+    "free path" the review's weaknesses name: scanning that copy directly, with
+    no bit-plane index; [Abstract]: the store is the serving stack's 4-bit K).
+
+    Reading of the layout (the pages give none; KIVI-style per-channel scales
+    over 128-token groups): codes [n][ceil(d/2)] bytes, channel 2i in the low
+    nibble of byte i and channel 2i+1 in the high nibble (0 past d); scales
+    [n_blocks][d] fp16, little-endian, the same Delta as the records.
+    Returns (codes uint8 [n, ceil(d/2)], scales uint8 [n_blocks, 2d])."""
+    kappa = np.asarray(kappa, dtype=np.int64)
+    n, d = kappa.shape
+    nib = np.zeros((n, 2 * ((d + 1) // 2)), dtype=np.int64)
+    nib[:, :d] = kappa
+    codes = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    scales = np.ascontiguousarray(np.asarray(delta).astype("<f2")).view(np.uint8).reshape(delta.shape[0], 2 * d)
+    return codes, scales
+
+
+def unpack_nibbles(codes: np.ndarray, d: int) -> np.ndarray:
+    """Codes [n, d] back from the token-major nibbles."""
+    c = np.asarray(codes, dtype=np.int64)
+    out = np.empty((c.shape[0], 2 * c.shape[1]), dtype=np.int64)
+    out[:, 0::2] = c & 15
+    out[:, 1::2] = c >> 4
+    return out[:, :d]
 
 
 def pack_head(k: np.ndarray):

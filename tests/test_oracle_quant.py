@@ -198,3 +198,26 @@ def test_invalid_keys_raise():
     k[3, 1] = np.float32(1e6)      # 1e6 / 8 = 125000 > fp16 max
     with pytest.raises(ValueError):
         O.block_scales(k)
+
+
+# ---- the token-major 4-bit copy (the free path) ----
+
+def test_nibbles_hand_example():
+    kappa = np.array([[0, 15, 8, 3, 9], [1, 2, 14, 7, 12]])
+    delta = np.array([[0.5, 1.0, 2.0, 0.25, 4.0]], np.float16)
+    codes, scales = O.pack_nibbles(kappa, delta)
+    # channel 0 low nibble, channel 1 high nibble of byte 0; the fifth channel
+    # alone in byte 2 (high nibble 0)
+    assert codes.tolist() == [[0xF0, 0x38, 0x09], [0x21, 0x7E, 0x0C]]
+    assert codes.shape == (2, 3) and scales.shape == (1, 10)
+    assert scales[0, :2].tolist() == [0x00, 0x38]        # fp16 0.5 = 0x3800, little-endian
+    assert scales[0, 8:10].tolist() == [0x00, 0x44]      # fp16 4.0 = 0x4400
+
+
+def test_nibbles_round_trip():
+    rng = np.random.default_rng(51)
+    for d in (1, 7, 64, 128):
+        kappa = rng.integers(0, 16, (300, d))
+        codes, _ = O.pack_nibbles(kappa, np.ones((3, d), np.float16))
+        assert codes.shape == (300, (d + 1) // 2)
+        assert np.array_equal(O.unpack_nibbles(codes, d), kappa)
