@@ -238,13 +238,15 @@ def pack_nibbles(kappa: np.ndarray, delta: np.ndarray):
     over 128-token groups): codes [n][ceil(d/2)] bytes, channel 2i in the low
     nibble of byte i and channel 2i+1 in the high nibble (0 past d); scales
     [n_blocks][d] fp16, little-endian, the same Delta as the records.
+    ``delta`` is block_scales' [d, n_blocks].
     Returns (codes uint8 [n, ceil(d/2)], scales uint8 [n_blocks, 2d])."""
     kappa = np.asarray(kappa, dtype=np.int64)
     n, d = kappa.shape
     nib = np.zeros((n, 2 * ((d + 1) // 2)), dtype=np.int64)
     nib[:, :d] = kappa
     codes = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
-    scales = np.ascontiguousarray(np.asarray(delta).astype("<f2")).view(np.uint8).reshape(delta.shape[0], 2 * d)
+    dt = np.asarray(delta).T                                   # [n_blocks, d]
+    scales = np.ascontiguousarray(dt.astype("<f2")).view(np.uint8).reshape(dt.shape[0], 2 * d)
     return codes, scales
 
 

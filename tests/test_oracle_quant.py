@@ -204,7 +204,7 @@ def test_invalid_keys_raise():
 
 def test_nibbles_hand_example():
     kappa = np.array([[0, 15, 8, 3, 9], [1, 2, 14, 7, 12]])
-    delta = np.array([[0.5, 1.0, 2.0, 0.25, 4.0]], np.float16)
+    delta = np.array([[0.5], [1.0], [2.0], [0.25], [4.0]], np.float16)   # [d, n_blocks], as block_scales
     codes, scales = O.pack_nibbles(kappa, delta)
     # channel 0 low nibble, channel 1 high nibble of byte 0; the fifth channel
     # alone in byte 2 (high nibble 0)
@@ -214,10 +214,19 @@ def test_nibbles_hand_example():
     assert scales[0, 8:10].tolist() == [0x00, 0x44]      # fp16 4.0 = 0x4400
 
 
+def test_nibbles_scales_follow_block_scales():
+    rng = np.random.default_rng(52)
+    k = (rng.standard_normal((300, 6)) * [1, 2, 4, 8, 16, 32]).astype(np.float32)
+    delta = O.block_scales(k)                                     # [d, n_blocks] = [6, 3]
+    _, scales = O.pack_nibbles(O.quantize_codes(k, delta), delta)
+    got = scales.view("<f2").reshape(3, 6)                        # [n_blocks, d]
+    assert np.array_equal(got.T.astype(np.float32), delta.astype(np.float32))
+
+
 def test_nibbles_round_trip():
     rng = np.random.default_rng(51)
     for d in (1, 7, 64, 128):
         kappa = rng.integers(0, 16, (300, d))
-        codes, _ = O.pack_nibbles(kappa, np.ones((3, d), np.float16))
+        codes, _ = O.pack_nibbles(kappa, np.ones((d, 3), np.float16))
         assert codes.shape == (300, (d + 1) // 2)
         assert np.array_equal(O.unpack_nibbles(codes, d), kappa)
