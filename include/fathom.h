@@ -255,6 +255,32 @@ int scan_topk_paged(const void* const* page_table, int residency, int64_t page_k
                     const uint8_t* union_depth, int h_q, int h_kv, int d, int k, int32_t* topk_idx,
                     float* topk_score, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * The "free path": the same scan over the token-major 4-bit K copy a quantized
+ * serving stack holds, with no bit-plane index ([Abstract]: the store is the
+ * serving stack's 4-bit K copy; [Review] weaknesses: the free path is unbuilt).
+ * Layout (a reading; the pages give none), d in {32, 64, 96, 128}:
+ *   codes   [h_kv][n][d/2] bytes: channel 2i in the low nibble of byte i,
+ *           2i+1 in the high nibble;
+ *   scales  [h_kv][ceil(n/128)][d] fp16, one per (128-key block, channel).
+ * Codes and scales are those of pack_bitplanes.  A key's codes are one row, so
+ * the scan reads every row whole: d/2 + d/64 bytes per key whatever the budget.
+ * ------------------------------------------------------------------------- */
+
+/* pack_nibbles -- the token-major 4-bit copy of K (device float32 [h_kv][n][d])
+ * into codes and scales (device memory); status as for pack_bitplanes. */
+int pack_nibbles(const float* k, int h_kv, int64_t n, int d, void* codes, void* scales, uint32_t* status,
+                 void* stream);
+
+/* scan_topk_nibbles -- scan_topk over the token-major copy: the same depths,
+ * the same scores bit for bit, the same selection.  codes and scales in device
+ * memory (FATHOM_HBM) or pinned host memory read in place (FATHOM_HOST_DIRECT);
+ * codes 16-byte aligned.  Workspace: fathom_workspace_bytes(h_q, h_kv, n, d, k,
+ * FATHOM_HBM). */
+int scan_topk_nibbles(const void* codes, const void* scales, int residency, const float* q, const uint8_t* depth,
+                      const uint8_t* union_depth, int h_q, int h_kv, int64_t n, int d, int k, int32_t* topk_idx,
+                      float* topk_score, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of device workspace attend_topk needs: per query head and split of its
  * k keys, a partial output (d + 2 floats) and a flag word. */
 size_t fathom_attend_workspace_bytes(int h_q, int d, int k);

@@ -21,15 +21,17 @@ from .fathom import (  # noqa: F401
     load,
     pack,
     pack_blocks,
+    pack_nibbles,
     page_table,
     prefix_bytes,
     record_bytes,
     scan_scores,
     scan_topk,
     scan_topk_append,
+    scan_topk_nibbles,
     scan_topk_paged,
     workspace_bytes,
 )
 
-__all__ = ["HBM", "HOST_DIRECT", "HOST_STAGED", "STATIC", "TOPQ", "WATERFILL", "WATERFILL_GROUP", "FathomError", "allocate", "attend", "attend_workspace_bytes", "device_address", "load", "pack", "pack_blocks", "page_table",
-           "prefix_bytes", "record_bytes", "scan_scores", "scan_topk", "scan_topk_append", "scan_topk_paged", "workspace_bytes"]
+__all__ = ["HBM", "HOST_DIRECT", "HOST_STAGED", "STATIC", "TOPQ", "WATERFILL", "WATERFILL_GROUP", "FathomError", "allocate", "attend", "attend_workspace_bytes", "device_address", "load", "pack", "pack_blocks", "pack_nibbles", "page_table",
+           "prefix_bytes", "record_bytes", "scan_scores", "scan_topk", "scan_topk_append", "scan_topk_nibbles", "scan_topk_paged", "workspace_bytes"]

@@ -12,6 +12,7 @@
 #include "append.h"
 #include "attend.h"
 #include "fathom_internal.h"
+#include "freepath.h"
 
 namespace {
 
@@ -467,6 +468,61 @@ int scan_topk_paged(const void* const* page_table, int residency, int64_t page_k
                                  s);
   if (e != hipSuccess) return hip_fail(e, "tail launch");
   e = fathom::launch_select(scores, ld, h_q, n, k, topk_idx, topk_score, sel, cleared, hist_done, s);
+  if (e != hipSuccess) return hip_fail(e, "select launch");
+  return ok();
+}
+
+int pack_nibbles(const float* k, int h_kv, int64_t n, int d, void* codes, void* scales, uint32_t* status,
+                 void* stream) {
+  if (h_kv < 1 || h_kv > 65535) return fail(FATHOM_ESHAPE, "h_kv=%d outside [1, 65535]", h_kv);
+  if (d < 32 || d > 128 || d % 32 != 0) return fail(FATHOM_ESHAPE, "the 4-bit token-major copy needs d in {32, 64, 96, 128} (got %d)", d);
+  int st = check_n(n, h_kv, "n");
+  if (st) return st;
+  if (n > 0 && (!k || !codes || !scales)) return fail(FATHOM_EINVAL, "null k, codes or scales");
+  if (n > 0 && (!aligned(k, 4) || !aligned(codes, 16) || !aligned(scales, 2)))
+    return fail(FATHOM_EINVAL, "k must be 4-byte, codes 16-byte and scales 2-byte aligned");
+  hipError_t e = fathom::launch_pack_nibbles(k, h_kv, n, d, static_cast<uint8_t*>(codes),
+                                             static_cast<uint16_t*>(scales), status, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "pack launch");
+  return ok();
+}
+
+int scan_topk_nibbles(const void* codes, const void* scales, int residency, const float* q, const uint8_t* depth,
+                      const uint8_t* union_depth, int h_q, int h_kv, int64_t n, int d, int k, int32_t* topk_idx,
+                      float* topk_score, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_heads(h_q, h_kv, d);
+  if (st) return st;
+  if (d < 32 || d > 128 || d % 32 != 0) return fail(FATHOM_ESHAPE, "the 4-bit token-major copy needs d in {32, 64, 96, 128} (got %d)", d);
+  st = check_n(n, h_kv, "n");
+  if (st) return st;
+  if (k < 0 || k > n) return fail(FATHOM_ESHAPE, "k=%d outside [0, n=%lld]", k, (long long)n);
+  if (residency != FATHOM_HBM && residency != FATHOM_HOST_DIRECT)
+    return fail(FATHOM_ERESIDENCY, "scan_topk_nibbles reads HBM or pinned host memory in place");
+  if (!q || !depth || !union_depth) return fail(FATHOM_EINVAL, "null q/depth/union_depth");
+  if (!aligned(q, 4)) return fail(FATHOM_EINVAL, "q must be 4-byte aligned");
+  if (k == 0) return ok();
+  if (!topk_idx) return fail(FATHOM_EINVAL, "null topk_idx");
+  if (!codes || !scales) return fail(FATHOM_EINVAL, "null codes or scales");
+  if (!aligned(codes, 16) || !aligned(scales, 2)) return fail(FATHOM_EINVAL, "codes must be 16-byte, scales 2-byte aligned");
+  const size_t need = fathom_workspace_bytes(h_q, h_kv, n, d, k, FATHOM_HBM);
+  if (!workspace || workspace_bytes < need)
+    return fail(FATHOM_EWORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, need);
+  if (!aligned(workspace, 256)) return fail(FATHOM_EINVAL, "workspace must be 256-byte aligned");
+  const uint8_t* cdev = nullptr;
+  const uint8_t* sdev = nullptr;
+  st = resolve_view(codes, residency, "codes", &cdev);
+  if (st) return st;
+  st = resolve_view(scales, residency, "scales", &sdev);
+  if (st) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t ld = score_ld(n);
+  float* scores = static_cast<float*>(workspace);
+  uint8_t* sel_base = static_cast<uint8_t*>(workspace) + al256((size_t)h_q * (size_t)ld * 4);
+  hipError_t e = fathom::launch_nibble_scan(cdev, reinterpret_cast<const uint16_t*>(sdev), q, depth, union_depth, h_kv,
+                                            h_q / h_kv, n, d, scores, ld, s);
+  if (e != hipSuccess) return hip_fail(e, "scan launch");
+  e = fathom::launch_select(scores, ld, h_q, n, k, topk_idx, topk_score, fathom::carve_select(sel_base, h_q, n, k),
+                            false, false, s);
   if (e != hipSuccess) return hip_fail(e, "select launch");
   return ok();
 }

@@ -67,6 +67,8 @@ def load() -> ctypes.CDLL:
         "fathom_attend_workspace_bytes": (S, [I, I, I]),
         "pack_blocks": (I, [P, I, L, L, L, I, P, P, P]),
         "fathom_device_address": (I, [P, I, ctypes.POINTER(ctypes.c_void_p)]),
+        "pack_nibbles": (I, [P, I, L, I, P, P, P, P]),
+        "scan_topk_nibbles": (I, [P, P, I, P, P, P, I, I, L, I, I, P, P, P, S, P]),
         "scan_topk_paged": (I, [P, I, L, L, P, L, P, P, P, I, I, I, I, P, P, P, S, P]),
         "scan_topk_append": (I, [P, I, L, L, P, L, P, P, P, I, I, I, I, P, P, P, S, P]),
         "attend_topk": (I, [P, P, I, P, P, I, I, L, I, I, ctypes.c_float, P, P, P, P, S, P]),
@@ -380,4 +382,48 @@ def scan_topk_paged(table: torch.Tensor | None, page_keys: int, n_sealed: int, t
     _check(load().scan_topk_paged(_ptr(table), residency, page_keys, n_sealed, _ptr(tail_k), n_tail, _ptr(q),
                                   _ptr(depth), _ptr(union_depth), h_q, h_kv, d, k, _ptr(idx), _ptr(scores),
                                   _ptr(workspace), workspace.numel(), _stream(q)))
+    return (idx, scores) if want_scores or scores is not None else idx
+
+
+def pack_nibbles(k: torch.Tensor, status: torch.Tensor | None = None):
+    """pack_nibbles: float32 [h_kv, n, d] -> (codes uint8 [h_kv, n, d/2], scales fp16 [h_kv, nb, d])."""
+    _need(k, "k", torch.float32, 3)
+    h_kv, n, d = k.shape
+    codes = torch.empty((h_kv, n, d // 2), dtype=torch.uint8, device=k.device)
+    scales = torch.empty((h_kv, -(-n // 128), d), dtype=torch.float16, device=k.device)
+    if status is not None:
+        _need(status, "status", torch.int32)
+    _check(load().pack_nibbles(_ptr(k), h_kv, n, d, _ptr(codes), _ptr(scales), _ptr(status), _stream(k)))
+    return codes, scales
+
+
+def scan_topk_nibbles(codes: torch.Tensor, scales: torch.Tensor, q: torch.Tensor, depth: torch.Tensor,
+                      union_depth: torch.Tensor, k: int, residency: int | None = None,
+                      workspace: torch.Tensor | None = None, idx: torch.Tensor | None = None,
+                      scores: torch.Tensor | None = None, want_scores: bool = False):
+    """scan_topk_nibbles: the scan over the token-major 4-bit copy (the free path)."""
+    _need(q, "q", torch.float32, 2)
+    _need(depth, "depth", torch.uint8)
+    _need(union_depth, "union_depth", torch.uint8)
+    _need(codes, "codes", torch.uint8, 3, device=False)
+    if scales.dtype != torch.float16 or not scales.is_contiguous():
+        raise TypeError("scales must be a contiguous float16 tensor")
+    h_q, d = q.shape
+    h_kv, n, _ = codes.shape
+    if residency is None:
+        residency = HBM if codes.is_cuda else HOST_DIRECT
+    if workspace is None:
+        workspace = torch.empty(max(workspace_bytes(h_q, h_kv, n, d, k, HBM), 1), dtype=torch.uint8,
+                                device=q.device)
+    _need(workspace, "workspace", torch.uint8)
+    if idx is None:
+        idx = torch.empty((h_q, k), dtype=torch.int32, device=q.device)
+    _need(idx, "idx", torch.int32)
+    if want_scores and scores is None:
+        scores = torch.empty((h_q, k), dtype=torch.float32, device=q.device)
+    if scores is not None:
+        _need(scores, "scores", torch.float32)
+    _check(load().scan_topk_nibbles(_ptr(codes), _ptr(scales), residency, _ptr(q), _ptr(depth), _ptr(union_depth),
+                                    h_q, h_kv, n, d, k, _ptr(idx), _ptr(scores), _ptr(workspace), workspace.numel(),
+                                    _stream(q)))
     return (idx, scores) if want_scores or scores is not None else idx
