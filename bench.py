@@ -131,11 +131,12 @@ def measure_h2d_peak(torch, dev, mib=512, reps=5) -> float:
     return (mib << 20) / (best * 1e-3) / 1e9
 
 
-def build_records(torch, F, wl, dev, layer=0, caches=False):
+def build_records(torch, F, wl, dev, layer=0, caches=False, nibbles=False):
     """Generate K per KV head (numpy, threaded), pack on the GPU, return records
     resident where the workload puts them, plus q and sigma2 on the device.
     With `caches`, also the bf16 K and V cache rows [h_kv, n, d] (as int16 bit
-    patterns) in the same residency, for the attention over the selection."""
+    patterns) in the same residency, for the attention over the selection; with
+    `nibbles`, also the token-major 4-bit copy (codes, scales) there."""
     from synthetic import kv_head, queries, to_bf16_bits, values
     hk = wl.sessions * wl.h_kv
     r = F.record_bytes(wl.n)
@@ -149,6 +150,11 @@ def build_records(torch, F, wl, dev, layer=0, caches=False):
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     stage = torch.empty((1, wl.d, r), dtype=torch.uint8, device=dev)
     kc = vc = None
+    nib = None
+    if nibbles:
+        nb = -(-wl.n // 128)
+        nib = (torch.empty((hk, wl.n, wl.d // 2), dtype=torch.uint8, pin_memory=host, device=None if host else dev),
+               torch.empty((hk, nb, wl.d), dtype=torch.float16, pin_memory=host, device=None if host else dev))
     if caches:
         kc = torch.empty((hk, wl.n, wl.d), dtype=torch.int16, pin_memory=host, device=None if host else dev)
         vc = torch.empty((hk, wl.n, wl.d), dtype=torch.int16, pin_memory=host, device=None if host else dev)
@@ -174,9 +180,15 @@ def build_records(torch, F, wl, dev, layer=0, caches=False):
             F.pack(kd, records=stage if host else records[v:v + 1], status=status)
             if host:
                 records[v:v + 1].copy_(stage)
+            if nibbles:
+                c4, sc = F.pack_nibbles(kd, status=status)
+                nib[0][v:v + 1].copy_(c4)
+                nib[1][v:v + 1].copy_(sc)
             del kd
     torch.cuda.synchronize(dev)
     assert int(status.item()) == 0, "pack reported non-finite keys or scale overflow"
+    if nibbles:
+        return records, torch.from_numpy(q).to(dev), torch.from_numpy(s2).to(dev), q, s2, kc, vc, nib
     return records, torch.from_numpy(q).to(dev), torch.from_numpy(s2).to(dev), q, s2, kc, vc
 
 
@@ -358,7 +370,10 @@ def main():
     h2d_peak = measure_h2d_peak(torch, dev)
 
     t_setup = time.perf_counter()
-    records, q, s2, q_np, s2_np, kc, vc = build_records(torch, F, wl, dev, caches=not args.no_attend)
+    free_path = not args.no_compare and wl.d % 32 == 0 and wl.d <= 128
+    built = build_records(torch, F, wl, dev, caches=not args.no_attend, nibbles=free_path)
+    records, q, s2, q_np, s2_np, kc, vc = built[:7]
+    nib = built[7] if free_path else None
     setup_s = time.perf_counter() - t_setup
     hk, hq, n, d, k = wl.sessions * wl.h_kv, wl.sessions * wl.h_q, wl.n, wl.d, wl.k
 
@@ -481,6 +496,25 @@ def main():
             for name, sel in picks.items()}
         comparison["recall_sample"] = f"the {hq // hk} query heads of KV head 0, top-{k} of {n} keys"
         comparison["speedup_vs_fixed_136"] = round(comparison["fixed_136"]["ms_per_step"] / step_ms, 3)
+        if nib is not None:
+            # the free path: the same depths over the token-major 4-bit copy,
+            # which every scan reads whole (d/2 + d/64 bytes per key)
+            F.allocate(q, s2, budget, mode=mode, depth=depth, union_depth=uni)
+            for _ in range(2):
+                F.scan_topk_nibbles(nib[0], nib[1], q, depth, uni, k, workspace=ws, idx=idx)
+            torch.cuda.synchronize(dev)
+            f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            f0.record(stream)
+            for _ in range(csteps):
+                F.allocate(q, s2, budget, mode=mode, depth=depth, union_depth=uni)
+                F.scan_topk_nibbles(nib[0], nib[1], q, depth, uni, k, workspace=ws, idx=idx)
+            f1.record(stream)
+            torch.cuda.synchronize(dev)
+            fms = f0.elapsed_time(f1) / csteps
+            comparison[f"free_path_B{budget}"] = {
+                "ms_per_step": round(fms, 4), "bytes_per_key": round(d / 2 + d / 64, 3),
+                "what": "the same depths over the token-major 4-bit copy (scan_topk_nibbles)"}
+            comparison["speedup_vs_free_path"] = round(fms / step_ms, 3)
         b68 = name_of[(68, F.WATERFILL)]
         comparison["bytes_method_B68_vs_fixed_68"] = round(
             comparison[b68]["bytes_per_key"] / comparison["fixed_68"]["bytes_per_key"], 3)

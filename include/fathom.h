@@ -267,8 +267,14 @@ int scan_topk_paged(const void* const* page_table, int residency, int64_t page_k
  * the scan reads every row whole: d/2 + d/64 bytes per key whatever the budget.
  * ------------------------------------------------------------------------- */
 
-/* pack_nibbles -- the token-major 4-bit copy of K (device float32 [h_kv][n][d])
- * into codes and scales (device memory); status as for pack_bitplanes. */
+/* pack_nibbles -- the token-major 4-bit copy of K (device float32 [h_kv][n][d],
+ * 4-byte aligned) into codes (device, 16-byte aligned) and scales (device,
+ * 2-byte aligned), both written whole; the last block of a head may be short.
+ * The codes and scales are the ones pack_bitplanes stores for the same K (the
+ * same threshold search and fp16 block scale).  d outside {32, 64, 96, 128} or
+ * n beyond the record limits: FATHOM_ESHAPE; null or misaligned buffers with
+ * n > 0: FATHOM_EINVAL; n = 0 writes nothing.  status: as for pack_bitplanes
+ * (non-finite keys, scale overflow), OR-ed, may be NULL. */
 int pack_nibbles(const float* k, int h_kv, int64_t n, int d, void* codes, void* scales, uint32_t* status,
                  void* stream);
 
