@@ -175,33 +175,49 @@ size_t fathom_workspace_bytes(int h_q, int h_kv, int64_t n, int d, int k, int re
 
 namespace {
 
+// Launches the scan of the sealed keys described by L (contiguous records at
+// `dev`, or pages through `table`) and prepares the selection on the way: the
+// link-bound host-direct scan builds the first-digit histograms itself after a
+// clearing launch (*hist_done), where the extra work hides behind the link; the
+// arithmetic-bound HBM scan only zeroes them (*cleared).
+hipError_t scan_for_select(const uint8_t* dev, const uint8_t* const* table, int64_t npages, int64_t page_keys,
+                           bool host, const float* q, const uint8_t* depth, const uint8_t* union_depth, int h_q,
+                           int h_kv, const fathom::Layout& L, int d, float* scores, int64_t ld,
+                           const fathom::SelectWorkspace& sel, bool* cleared, bool* hist_done, hipStream_t s) {
+  const int g = h_q / h_kv;
+  hipError_t e;
+  if (host) {
+    e = fathom::launch_select_clear(sel, h_q, s);
+    if (e == hipSuccess)
+      e = fathom::launch_scan_paged(dev, table, npages, page_keys, true, q, depth, union_depth, h_kv, g, L, d, scores,
+                                    ld, nullptr, 0, sel.hist, s);
+    *cleared = *hist_done = e == hipSuccess;
+  } else {
+    e = fathom::launch_scan_paged(dev, table, npages, page_keys, false, q, depth, union_depth, h_kv, g, L, d, scores,
+                                  ld, sel.hist, (int64_t)fathom::select_clear_words(h_q), nullptr, s);
+    *cleared = e == hipSuccess;
+  }
+  return e;
+}
+
 // Scores of every key into `scores` [h_q][ld]; staging comes from the workspace.
-// With a selection to follow (`sel`), the direct scans also prepare it: the
-// HBM scan zeroes its counters on the way (*cleared), and the link-bound
-// host-direct scan, where it fits, also builds its first-digit histograms
-// (*hist_done) after a clearing launch.
+// With a selection to follow (`sel`), the direct scans also prepare it.
 int run_scan(const uint8_t* dev, int residency, const float* q, const uint8_t* depth,
              const uint8_t* union_depth, int h_q, int h_kv, int64_t n, int d, float* scores, int64_t ld,
              uint8_t* staging, const fathom::SelectWorkspace* sel, bool* cleared, bool* hist_done,
              hipStream_t s) {
   const fathom::Layout L = fathom::make_layout(n);
   const int g = h_q / h_kv;
+  const bool host = residency == FATHOM_HOST_DIRECT;
   hipError_t e;
-  *cleared = false;
-  *hist_done = false;
+  *cleared = *hist_done = false;
   if (residency == FATHOM_HOST_STAGED) {
     e = fathom::launch_scan_staged(dev, staging, q, depth, union_depth, h_kv, g, L, d, scores, ld, s);
-  } else if (sel && L.nb > 0 && residency == FATHOM_HOST_DIRECT && fathom::scan_fuses_hist(g)) {
-    e = fathom::launch_select_clear(*sel, h_q, s);
-    if (e == hipSuccess)
-      e = fathom::launch_scan(dev, true, q, depth, union_depth, h_kv, g, L, d, scores, ld, nullptr, 0, sel->hist, s);
-    *cleared = *hist_done = e == hipSuccess;
+  } else if (sel && L.nb > 0) {
+    e = scan_for_select(dev, nullptr, 0, 0, host, q, depth, union_depth, h_q, h_kv, L, d, scores, ld, *sel, cleared,
+                        hist_done, s);
   } else {
-    uint32_t* zero = sel ? sel->hist : nullptr;
-    const int64_t zero_words = sel ? (int64_t)fathom::select_clear_words(h_q) : 0;
-    e = fathom::launch_scan(dev, residency == FATHOM_HOST_DIRECT, q, depth, union_depth, h_kv, g, L, d, scores, ld,
-                            zero, zero_words, nullptr, s);
-    *cleared = zero != nullptr && L.nb > 0;
+    e = fathom::launch_scan(dev, host, q, depth, union_depth, h_kv, g, L, d, scores, ld, nullptr, 0, nullptr, s);
   }
   if (e != hipSuccess) return hip_fail(e, "scan launch");
   return FATHOM_OK;
@@ -374,22 +390,14 @@ int scan_topk_append(const void* records, int residency, int64_t n_cap, int64_t 
   hipError_t e;
   bool cleared = false, hist_done = false;
   if (n_sealed > 0) {
-    // the capacity's geometry, cut to the sealed blocks
+    // the capacity's geometry, cut to the sealed blocks; where the scan builds
+    // the histograms, the tail kernel adds its keys
     fathom::Layout L = fathom::make_layout(n_cap);
     L.n = n_sealed;
     L.nb = (n_sealed + fathom::kBlock - 1) / fathom::kBlock;
-    if (residency == FATHOM_HOST_DIRECT && fathom::scan_fuses_hist(g)) {
-      // the link-bound scan builds the histograms; the tail kernel adds its keys
-      e = fathom::launch_select_clear(sel, h_q, s);
-      if (e == hipSuccess)
-        e = fathom::launch_scan(dev, true, q, depth, union_depth, h_kv, g, L, d, scores, ld, nullptr, 0, sel.hist, s);
-      hist_done = true;
-    } else {
-      e = fathom::launch_scan(dev, residency == FATHOM_HOST_DIRECT, q, depth, union_depth, h_kv, g, L, d, scores,
-                              ld, sel.hist, (int64_t)fathom::select_clear_words(h_q), nullptr, s);
-    }
+    e = scan_for_select(dev, nullptr, 0, 0, residency == FATHOM_HOST_DIRECT, q, depth, union_depth, h_q, h_kv, L, d,
+                        scores, ld, sel, &cleared, &hist_done, s);
     if (e != hipSuccess) return hip_fail(e, "scan launch");
-    cleared = true;
   }
   e = fathom::launch_tail_scores(tail_k, q, h_kv, g, n_tail, d, scores, ld, n_sealed, hist_done ? sel.hist : nullptr,
                                  s);
@@ -451,18 +459,9 @@ int scan_topk_paged(const void* const* page_table, int residency, int64_t page_k
     fathom::Layout L = fathom::make_layout(n_sealed);
     const int64_t npages = (n_sealed + page_keys - 1) / page_keys;
     const auto* table = reinterpret_cast<const uint8_t* const*>(page_table);
-    if (host && fathom::scan_fuses_hist(g)) {
-      e = fathom::launch_select_clear(sel, h_q, s);
-      if (e == hipSuccess)
-        e = fathom::launch_scan_paged(nullptr, table, npages, page_keys, true, q, depth, union_depth, h_kv, g, L, d,
-                                      scores, ld, nullptr, 0, sel.hist, s);
-      hist_done = true;
-    } else {
-      e = fathom::launch_scan_paged(nullptr, table, npages, page_keys, host, q, depth, union_depth, h_kv, g, L, d,
-                                    scores, ld, sel.hist, (int64_t)fathom::select_clear_words(h_q), nullptr, s);
-    }
+    e = scan_for_select(nullptr, table, npages, page_keys, host, q, depth, union_depth, h_q, h_kv, L, d, scores, ld,
+                        sel, &cleared, &hist_done, s);
     if (e != hipSuccess) return hip_fail(e, "scan launch");
-    cleared = true;
   }
   e = fathom::launch_tail_scores(tail_k, q, h_kv, g, n_tail, d, scores, ld, n_sealed, hist_done ? sel.hist : nullptr,
                                  s);

@@ -60,14 +60,13 @@ hipError_t launch_allocate(const float* q, const float* sigma2, int h_kv, int g,
 // Scores of every key from device memory (host = false) or read in place from
 // pinned host memory (host = true, larger tiles for long contiguous runs).
 // The kernel also zeroes `zero_words` words at `zero` (the selection's
-// histograms and state; may be null).  With `hist` (host = true only, and only
-// where scan_fuses_hist(g)), it also adds every score's first selection digit
-// to hist[h][kSelBins], which must be zero beforehand.
+// histograms and state; may be null).  With `hist` (may be null; not together
+// with `zero`) it also adds every score's first selection digit to
+// hist[h][kSelBins], which must be zero beforehand (launch_select_clear).
 hipError_t launch_scan(const uint8_t* rec, bool host, const float* q, const uint8_t* depth,
                        const uint8_t* uni, int h_kv, int g, const Layout& L, int d,
                        float* scores, int64_t ld, uint32_t* zero, int64_t zero_words, uint32_t* hist,
                        hipStream_t s);
-bool scan_fuses_hist(int g);
 // The same over paged records: table[g * npages + p] is the device-visible base
 // of page p of KV head g, [d][R(page_keys)] bytes laid out as whole records of
 // the page's page_keys keys (a multiple of 4096); L describes the keys scanned.
@@ -96,7 +95,9 @@ SelectWorkspace carve_select(void* base, int h_q, int64_t n, int k);
 // Words from ws.hist that must be zero when the selection starts (histograms
 // and state); `cleared` says a previous kernel on the stream zeroed them.
 size_t select_clear_words(int h_q);
-// `hist_done`: the scan already built the histograms (implies cleared).
+// `hist_done`: earlier kernels on the stream built ws.hist (after zeroing it
+// and the per-head state); otherwise the selection builds it first, clearing
+// it unless `cleared`.
 hipError_t launch_select(const float* scores, int64_t ld, int h_q, int64_t n, int k,
                          int32_t* idx, float* val, const SelectWorkspace& ws, bool cleared, bool hist_done,
                          hipStream_t s);

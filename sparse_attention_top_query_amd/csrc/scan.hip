@@ -100,15 +100,18 @@ __device__ __forceinline__ int word_tb(uint64_t w) { return (int)(w & 7); }
 __device__ __forceinline__ int word_th(uint64_t w, int h) { return (int)((w >> (8 + 3 * h)) & 7); }
 __device__ __forceinline__ uint32_t u4(const uint4& v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
 
-// Whether the selection's first-digit histograms of all G heads fit in the
-// tile's staging memory, which is dead once the last group is scored.
+// The fused first-digit histograms live in the tile's staging memory, which is
+// dead once the last group is scored: 16-bit counts, two bins per word (a tile
+// holds at most 4096 keys), for as many heads per round as fit.
+constexpr int kHistWords = kSelBins / 2;
 template <int G, int TB>
-constexpr bool kFusable = sizeof(ScanSmem<G, TB>) >= (size_t)G * kSelBins * 4;
+constexpr int kHistHeads = (int)(sizeof(ScanSmem<G, TB>) / 4 / kHistWords) < G
+                               ? (int)(sizeof(ScanSmem<G, TB>) / 4 / kHistWords) : G;
 
 // Scores of tile `tile` (TB blocks) of KV head g, all its query heads.  With
 // FUSE, the tile's scores are also counted into a.hist by their first
-// selection digit (an LDS histogram in the staging memory, then one global
-// atomic per non-empty bin).
+// selection digit (an LDS histogram per round of heads, then one global atomic
+// per non-empty bin).
 template <int G, int TB, bool FUSE = false>
 __device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t tile, ScanSmem<G, TB>& sm) {
   using C = Cfg<G, TB>;
@@ -356,25 +359,39 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t 
 
   // ---- 5. fused first-digit histogram of the selection ----
   if constexpr (FUSE) {
-    static_assert(kFusable<G, TB>, "histograms must fit in the staging memory");
+    constexpr int HR = kHistHeads<G, TB>;
+    static_assert(HR >= 1 && TB * kBlock < 65536, "16-bit counts of at least one head must fit");
     uint32_t* lh = reinterpret_cast<uint32_t*>(&sm);
-    __syncthreads();   // every wave is past its last read of the staging memory
-    for (int i = tid; i < G * kSelBins; i += NT) lh[i] = 0u;
-    __syncthreads();
-    if (bl < nvalid) {
 #pragma unroll
-      for (int s2 = 0; s2 < kSub; ++s2) {
-        const int64_t j = (blk0 + bl) * kBlock + s2 * 32 + (lane & 31);
-        if (j < a.n) {
+    for (int h0 = 0; h0 < G; h0 += HR) {
+      __syncthreads();   // every wave is past the staging memory (or the previous round's flush)
+      for (int i = tid; i < HR * kHistWords; i += NT) lh[i] = 0u;
+      __syncthreads();
+      if (bl < nvalid) {
 #pragma unroll
-          for (int h = 0; h < G; ++h) atomicAdd(&lh[h * kSelBins + (order_key(acc[s2][h]) >> kSelDigit0)], 1u);
+        for (int s2 = 0; s2 < kSub; ++s2) {
+          const int64_t j = (blk0 + bl) * kBlock + s2 * 32 + (lane & 31);
+          if (j < a.n) {
+#pragma unroll
+            for (int hh = 0; hh < HR; ++hh) {
+              if (h0 + hh < G) {
+                const uint32_t b = order_key(acc[s2][h0 + hh]) >> kSelDigit0;
+                atomicAdd(&lh[hh * kHistWords + (b >> 1)], 1u << (16 * (b & 1u)));
+              }
+            }
+          }
         }
       }
-    }
-    __syncthreads();
-    for (int i = tid; i < G * kSelBins; i += NT) {
-      const uint32_t v = lh[i];
-      if (v) atomicAdd(&a.hist[(g * G + i / kSelBins) * kSelBins + i % kSelBins], v);
+      __syncthreads();
+      for (int i = tid; i < HR * kHistWords; i += NT) {
+        const int hh = h0 + i / kHistWords;
+        const uint32_t v = lh[i];
+        if (hh < G && v) {
+          uint32_t* gh = a.hist + (g * G + hh) * kSelBins + 2 * (i % kHistWords);
+          if (v & 0xffffu) atomicAdd(gh, v & 0xffffu);
+          if (v >> 16) atomicAdd(gh + 1, v >> 16);
+        }
+      }
     }
   }
 }
@@ -505,8 +522,7 @@ template <int G, int TB>
 hipError_t launch_g(const uint8_t* rec, const float* q, const uint8_t* depth, const uint8_t* uni,
                     int h_kv, const Layout& L, int d, float* scores, int64_t ld, uint32_t* zero,
                     int64_t zero_words, uint32_t* hist, const Paging& pg, hipStream_t s) {
-  ScanArgs a{rec, q, depth, uni, L.n, L.nb, L.H, L.P, L.R, d, scores, ld, zero, zero_words, hist,
-             nullptr, 0, 1};
+  ScanArgs a{rec, q, depth, uni, L.n, L.nb, L.H, L.P, L.R, d, scores, ld, zero, zero_words, hist, nullptr, 0, 1};
   if (pg.table) {
     // page records are laid out for page_keys keys; tiles never straddle pages
     const Layout P = make_layout(pg.page_keys);
@@ -521,13 +537,10 @@ hipError_t launch_g(const uint8_t* rec, const float* q, const uint8_t* depth, co
   const int64_t tiles = (L.nb + TB - 1) / TB;
   const int64_t total = tiles * h_kv;
   const int64_t per = (total + kXcds - 1) / kXcds;
-  if constexpr (kFusable<G, TB>) {
-    if (hist) {
-      scan_kernel<G, TB, true><<<(unsigned)(per * kXcds), Cfg<G, TB>::threads, 0, s>>>(a, tiles, total);
-      return hipGetLastError();
-    }
+  if (hist) {
+    scan_kernel<G, TB, true><<<(unsigned)(per * kXcds), Cfg<G, TB>::threads, 0, s>>>(a, tiles, total);
+    return hipGetLastError();
   }
-  if (hist) return hipErrorInvalidValue;
   scan_kernel<G, TB, false><<<(unsigned)(per * kXcds), Cfg<G, TB>::threads, 0, s>>>(a, tiles, total);
   return hipGetLastError();
 }
@@ -566,22 +579,10 @@ hipError_t launch_any(const uint8_t* rec, bool host, const float* q, const uint8
                       uint32_t* zero, int64_t zero_words, uint32_t* hist, const Paging& pg, hipStream_t s) {
   if (host)
     return launch_g<G, HostTile<G>::TB>(rec, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words, hist, pg, s);
-  if (hist) return hipErrorInvalidValue;
-  return launch_g<G, kTileDevice>(rec, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words, nullptr, pg, s);
+  return launch_g<G, kTileDevice>(rec, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words, hist, pg, s);
 }
 
 }  // namespace
-
-bool scan_fuses_hist(int g) {
-  switch (g) {
-    case 1: return kFusable<1, HostTile<1>::TB>;
-    case 2: return kFusable<2, HostTile<2>::TB>;
-    case 4: return kFusable<4, HostTile<4>::TB>;
-    case 8: return kFusable<8, HostTile<8>::TB>;
-    case 16: return kFusable<16, HostTile<16>::TB>;
-    default: return false;
-  }
-}
 
 hipError_t launch_scan(const uint8_t* rec, bool host, const float* q, const uint8_t* depth,
                        const uint8_t* uni, int h_kv, int g, const Layout& L, int d,

@@ -8,13 +8,13 @@
 // The head histograms and the per-head state start at zero: cleared by the
 // scan that writes the scores, or by sel_init.
 //   1. hist     LDS histogram of the top 12 key bits per 4096-key chunk, added
-//               to the head's histogram;
-//   2. find     per head, the bin b holding the k-th largest key and the number
-//               of keys above it;
-//   3. collect  every key in bin b or above is written, as (key, index), to its
-//               4096-key chunk's slot in index order (ballot ranks per
-//               wavefront, no atomics), with the slot's count;
-//   4. resolve  one workgroup per head concatenates the slots in chunk order in
+//               to the head's histogram (or built by the scan itself);
+//   2. collect  every workgroup finds, from its head's histogram, the bin b
+//               holding the k-th largest key; every key of its 4096-key chunk in
+//               bin b or above is written, as (key, index), to the chunk's slot
+//               in index order (ballot ranks per wavefront, no atomics), with the
+//               slot's count;
+//   3. resolve  one workgroup per head concatenates the slots in chunk order in
 //               LDS -- all kept keys, in index order -- radix-selects the exact
 //               k-th key T among them (10 + 10 more bits) and how many keys equal
 //               to T still belong to the top k, and compacts in order: keys above
@@ -96,10 +96,16 @@ __global__ __launch_bounds__(kSelThreads) void sel_hist(const float* __restrict_
   __syncthreads();
   const float* row = scores + (int64_t)h * ld;
   const int64_t j0 = (int64_t)blockIdx.x * kChunk;
-#pragma unroll 4
+  float v[kPerThread];
+#pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
     const int64_t j = j0 + (int64_t)i * kSelThreads + threadIdx.x;
-    if (j < n) atomicAdd(&lh[order_key(row[j]) >> kDigit0], 1u);
+    v[i] = j < n ? row[j] : 0.0f;
+  }
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) {
+    const int64_t j = j0 + (int64_t)i * kSelThreads + threadIdx.x;
+    if (j < n) atomicAdd(&lh[order_key(v[i]) >> kDigit0], 1u);
   }
   __syncthreads();
   for (int b = threadIdx.x; b < kBins; b += kSelThreads) {
@@ -108,56 +114,62 @@ __global__ __launch_bounds__(kSelThreads) void sel_hist(const float* __restrict_
   }
 }
 
-// Bin of the k-th largest key: the bin b with (keys above b) < k <= (keys at or above b).
-// A kernel of its own: the launch boundary orders it after every chunk's
-// histogram atomics (a device-scope fence per chunk instead would write back
-// the XCD's L2 once per workgroup).
-__global__ __launch_bounds__(kSelThreads) void sel_find(const uint32_t* __restrict__ hist,
-                                                        uint32_t* __restrict__ state, int k) {
-  constexpr int kPer = kBins / kSelThreads;   // 16 bins per thread
-  __shared__ uint32_t wsum[kSelThreads / 64];
-  const int h = blockIdx.x;
-  const uint32_t* hh = hist + (int64_t)h * kBins;
-  uint32_t v[kPer];
-  uint32_t mine = 0;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    v[i] = hh[threadIdx.x * kPer + i];
-    mine += v[i];
-  }
-  uint32_t above = block_suffix_inclusive<kSelThreads>(mine, wsum) - mine;   // keys in higher bins
-#pragma unroll
-  for (int i = kPer - 1; i >= 0; --i) {
-    if (above < (uint32_t)k && above + v[i] >= (uint32_t)k) {
-      state[h * 4 + 0] = threadIdx.x * kPer + i;
-      state[h * 4 + 1] = above;
-    }
-    above += v[i];
-  }
-}
-
 // One pass over the scores: the keys of a chunk in bin b or above, in index
 // order, go to the chunk's slot.  Iteration i of wavefront w covers keys
-// j0 + 256 i + 64 w + lane, so (i, w, lane) order is index order.
+// j0 + 256 i + 64 w + lane, so (i, w, lane) order is index order.  Every
+// workgroup finds b itself from the head's histogram (read while its own
+// scores are in flight); the first chunk's records it for the resolve.
 __global__ __launch_bounds__(kSelThreads) void sel_collect(const float* __restrict__ scores, int64_t ld,
-                                                           int64_t n, uint32_t* __restrict__ state,
+                                                           int64_t n, int k, const uint32_t* __restrict__ hist,
+                                                           uint32_t* __restrict__ state,
                                                            uint64_t* __restrict__ kept,
                                                            uint32_t* __restrict__ counts, int64_t nchunks) {
   constexpr int NW = kSelThreads / 64;
+  constexpr int kPer = kBins / kSelThreads;   // 16 bins per thread
   __shared__ uint32_t cnt[kPerThread][NW];
+  __shared__ uint32_t wsum[NW];
+  __shared__ uint32_t sh[2];
   const int h = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-  const uint32_t bin = state[h * 4 + 0];
   const float* row = scores + (int64_t)h * ld;
   const int64_t j0 = (int64_t)blockIdx.x * kChunk;
-  uint32_t key[kPerThread];
-  uint64_t mask[kPerThread];
+  float f[kPerThread];
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
     const int64_t j = j0 + (int64_t)i * kSelThreads + threadIdx.x;
-    key[i] = j < n ? order_key(row[j]) : 0u;
+    f[i] = j < n ? row[j] : 0.0f;
   }
+  // bin b of the k-th largest key
+  {
+    const uint32_t* hh = hist + (int64_t)h * kBins;
+    uint32_t hv[kPer];
+    uint32_t mine = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      hv[i] = hh[threadIdx.x * kPer + i];
+      mine += hv[i];
+    }
+    uint32_t above = block_suffix_inclusive<kSelThreads>(mine, wsum) - mine;
+#pragma unroll
+    for (int i = kPer - 1; i >= 0; --i) {
+      if (above < (uint32_t)k && above + hv[i] >= (uint32_t)k) {
+        sh[0] = threadIdx.x * kPer + i;
+        sh[1] = above;
+      }
+      above += hv[i];
+    }
+    __syncthreads();
+  }
+  const uint32_t bin = sh[0];
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    state[h * 4 + 0] = bin;
+    state[h * 4 + 1] = sh[1];
+  }
+  uint32_t key[kPerThread];
+  uint64_t mask[kPerThread];
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) key[i] = order_key(f[i]);
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
     const int64_t j = j0 + (int64_t)i * kSelThreads + threadIdx.x;
@@ -185,11 +197,12 @@ __global__ __launch_bounds__(kSelThreads) void sel_collect(const float* __restri
   }
 }
 
-// The bin of a kBins histogram holding the need-th largest key: sh[0] = bin,
+// The bin of an NB-bin histogram holding the need-th largest key: sh[0] = bin,
 // sh[1] = keys in higher bins.  Called by every thread; needs 1 <= need <= total.
-template <int NT>
+template <int NT, int NB = kBins>
 __device__ __forceinline__ void find_bin(const uint32_t* lh, uint32_t need, uint32_t* wsum, uint32_t* sh) {
-  constexpr int kPer = kBins / NT;
+  static_assert(NB % NT == 0, "whole bins per thread");
+  constexpr int kPer = NB / NT;
   uint32_t v[kPer];
   uint32_t mine = 0;
 #pragma unroll
@@ -290,15 +303,31 @@ __global__ __launch_bounds__(kResolveThreads) void sel_resolve(const float* __re
     return;
   }
   __syncthreads();
-  // gather the slots in chunk order (binary search of the chunk of item x)
-  for (uint32_t x = threadIdx.x; x < total; x += NT) {
-    int lo = 0, hi = (int)nchunks;            // coff[lo] <= x < coff[hi]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (coff[mid] <= x) lo = mid;
-      else hi = mid;
+  // gather the slots in chunk order: TPC threads per chunk (nchunks <= NT here),
+  // every load issued before the first store
+  {
+    int tpc = 1;
+    while (tpc * 2 * nchunks <= NT) tpc *= 2;
+    const int c = threadIdx.x / tpc;
+    const int r = threadIdx.x % tpc;
+    constexpr int kBatch = 16;
+    if (c < nchunks) {
+      const uint32_t cn = coff[c + 1] - coff[c];
+      const uint64_t* src = kept + ((int64_t)h * nchunks + c) * kSlot;
+      for (uint32_t x0 = r; x0 < cn; x0 += kBatch * tpc) {
+        uint64_t v[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const uint32_t x = x0 + u * tpc;
+          v[u] = x < cn ? src[x] : 0ull;
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const uint32_t x = x0 + u * tpc;
+          if (x < cn) buf[coff[c] + x] = v[u];
+        }
+      }
     }
-    buf[x] = kept[((int64_t)h * nchunks + lo) * kSlot + (x - coff[lo])];
   }
   // the k-th key among the kept ones: keys above bin b are all in; among the keys
   // of bin b find the (k - above)-th largest by the next 11, then 10 bits
@@ -306,14 +335,15 @@ __global__ __launch_bounds__(kResolveThreads) void sel_resolve(const float* __re
   for (int pass = 0; pass < 2; ++pass) {
     const int shift = pass == 0 ? 10 : 0;
     const int hi_shift = pass == 0 ? kDigit0 : 10;
-    for (int b = threadIdx.x; b < kBins; b += NT) lh[b] = 0u;
+    static_assert(NT == 1024, "one of the 1024 bins per thread");
+    lh[threadIdx.x] = 0u;
     __syncthreads();
     for (uint32_t x = threadIdx.x; x < total; x += NT) {
       const uint32_t key = (uint32_t)(buf[x] >> 32);
       if ((key >> hi_shift) == prefix) atomicAdd(&lh[(key >> shift) & 1023u], 1u);
     }
     __syncthreads();
-    find_bin<NT>(lh, need, wsum, sh);
+    find_bin<NT, 1024>(lh, need, wsum, sh);
     prefix = (prefix << 10) | sh[0];
     need -= sh[1];
     __syncthreads();
@@ -329,9 +359,12 @@ __global__ __launch_bounds__(kResolveThreads) void sel_resolve(const float* __re
     gt += x < total && kk[r] > T;
     eq += x < total && kk[r] == T;
   }
-  uint32_t tot_eq = 0, tot_gt = 0;
-  const uint32_t eq_before = block_exclusive<NT>(eq, wsum, &tot_eq);
-  const uint32_t gt_before = block_exclusive<NT>(gt, wsum, &tot_gt);
+  // both counts in one scan, as 16-bit halves (each total is at most kKeep)
+  static_assert(kKeep < 65536, "16-bit halves");
+  uint32_t tot = 0;
+  const uint32_t before = block_exclusive<NT>((gt << 16) | eq, wsum, &tot);
+  const uint32_t eq_before = before & 0xffffu;
+  const uint32_t gt_before = before >> 16;
   uint32_t ties = eq_before;
   uint32_t pos = gt_before + min(eq_before, need);
 #pragma unroll
@@ -366,6 +399,10 @@ size_t select_workspace_bytes(int h_q, int64_t n, int k) {
          al256((size_t)h_q * nc * kSlot * 8);
 }
 
+size_t select_clear_words(int h_q) {
+  return (al256((size_t)h_q * kBins * 4) + al256((size_t)h_q * 4 * 4)) / 4;
+}
+
 SelectWorkspace carve_select(void* base, int h_q, int64_t n, int k) {
   (void)k;
   uint8_t* p = static_cast<uint8_t*>(base);
@@ -381,10 +418,6 @@ SelectWorkspace carve_select(void* base, int h_q, int64_t n, int k) {
   return ws;
 }
 
-size_t select_clear_words(int h_q) {
-  return (al256((size_t)h_q * kBins * 4) + al256((size_t)h_q * 4 * 4)) / 4;
-}
-
 hipError_t launch_select_clear(const SelectWorkspace& ws, int h_q, hipStream_t s) {
   sel_init<<<h_q, kSelThreads, 0, s>>>(ws.hist, ws.state);
   return hipGetLastError();
@@ -393,11 +426,12 @@ hipError_t launch_select_clear(const SelectWorkspace& ws, int h_q, hipStream_t s
 hipError_t launch_select(const float* scores, int64_t ld, int h_q, int64_t n, int k, int32_t* idx,
                          float* val, const SelectWorkspace& ws, bool cleared, bool hist_done, hipStream_t s) {
   if (k == 0 || n == 0 || h_q == 0) return hipSuccess;
-  if (!cleared && !hist_done) sel_init<<<h_q, kSelThreads, 0, s>>>(ws.hist, ws.state);
   dim3 grid((unsigned)ws.nchunks, (unsigned)h_q);
-  if (!hist_done) sel_hist<<<grid, kSelThreads, 0, s>>>(scores, ld, n, ws.hist);
-  sel_find<<<h_q, kSelThreads, 0, s>>>(ws.hist, ws.state, k);
-  sel_collect<<<grid, kSelThreads, 0, s>>>(scores, ld, n, ws.state, ws.kept, ws.counts, ws.nchunks);
+  if (!hist_done) {
+    if (!cleared) sel_init<<<h_q, kSelThreads, 0, s>>>(ws.hist, ws.state);
+    sel_hist<<<grid, kSelThreads, 0, s>>>(scores, ld, n, ws.hist);
+  }
+  sel_collect<<<grid, kSelThreads, 0, s>>>(scores, ld, n, k, ws.hist, ws.state, ws.kept, ws.counts, ws.nchunks);
   sel_resolve<<<h_q, kResolveThreads, 0, s>>>(scores, ld, n, k, ws.state, ws.kept, ws.counts, ws.nchunks, idx,
                                               val);
   return hipGetLastError();
