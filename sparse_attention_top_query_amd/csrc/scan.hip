@@ -269,8 +269,9 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t 
 
   if (n_grp > 0) issue(0);
   for (int gi = 0; gi < n_grp; ++gi) {
-    const int e_lo = sm.grp[gi], e_hi = sm.grp[gi + 1];
-    const int ch_lo = sm.ent_base[e_lo];
+    const int e_lo = __builtin_amdgcn_readfirstlane(sm.grp[gi]);
+    const int e_hi = __builtin_amdgcn_readfirstlane(sm.grp[gi + 1]);
+    const int ch_lo = __builtin_amdgcn_readfirstlane(sm.ent_base[e_lo]);
     commit(gi);
     __syncthreads();
     // coefficients q_h 2^(3-t_h) Delta_b for every entry, block and head of the group
@@ -288,15 +289,16 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t 
     // in it, key l%32 of each of the block's four 32-key words (sub-chunks s).
     if (kWaveBlocks * wv < nvalid) {
       const int pos = lane & 31;
-      uint64_t nword = sm.ent_word[e_lo];
-      int nbase = sm.ent_base[e_lo];
+      // the group's entries (at most 64: each starts in one of its 64 chunk
+      // slots), one per lane; the loop reads them lane by lane into scalars
+      const bool mine = e_lo + lane < e_hi;
+      const uint64_t lword = mine ? sm.ent_word[e_lo + lane] : 0ull;
+      const int lbase = mine ? (int)sm.ent_base[e_lo + lane] - ch_lo : 0;
       for (int e = e_lo; e < e_hi; ++e) {
-        uint64_t word = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)nword);
+        uint64_t word = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)lword, e - e_lo);
         if (8 + 3 * G > 32)
-          word |= (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(nword >> 32)) << 32;
-        const int cb = __builtin_amdgcn_readfirstlane(nbase) - ch_lo;
-        nword = sm.ent_word[e + 1];     // next entry's word, read ahead (array has kMaxD + 1 slots)
-        nbase = sm.ent_base[e + 1];
+          word |= (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(lword >> 32), e - e_lo) << 32;
+        const int cb = __builtin_amdgcn_readlane(lbase, e - e_lo);
         const int tb = word_tb(word);
         const uint4* pp = &sm.planes[cb][bl];
         // plane words of the prefix (only the planes the union depth reads)
