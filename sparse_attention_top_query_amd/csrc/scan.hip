@@ -34,6 +34,7 @@
 #include <hip/hip_fp16.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "fathom_internal.h"
 
@@ -64,7 +65,7 @@ struct ScanSmem {
   uint4 scales[kStageEntries][TB / kUnitBlocks];   // staged fp16 scales per entry of the group
   float coef[kStageEntries][TB][G];                // q_h 2^(3-t_h) Delta_b per entry, block, head
   float ent_q[kMaxD][G];                           // q_h 2^(3-t_h) of each list entry
-  uint64_t ent_word[kMaxD + 1];                    // union depth | used depths | head depths
+  uint64_t ent_word[kMaxD + 1];                    // level masks: bit (t-1) G + h iff head h reads t planes
   uint16_t ent_base[kMaxD + 1];                    // first chunk of entry e (prefix sum)
   uint8_t ent_c[kMaxD];                            // channel of list entry e
   uint16_t grp[kMaxChunks / kGroupChunks + 2];     // first entry of each staging group
@@ -94,10 +95,9 @@ struct ScanArgs {
   int64_t page_tiles;
 };
 
-// Entry word: bits 0-2 union depth, bits 3-6 depths in use (bit 2+t: some head
-// reads exactly t planes), then 3 bits of depth per head from bit 8.
-__device__ __forceinline__ int word_tb(uint64_t w) { return (int)(w & 7); }
-__device__ __forceinline__ int word_th(uint64_t w, int h) { return (int)((w >> (8 + 3 * h)) & 7); }
+// Entry word: one G-bit mask per depth t = 1..4, bit (t - 1) G + h set iff head h
+// reads exactly t planes of the channel (at most 64 bits for G <= 16).  The
+// union depth is the entry's chunk count.
 __device__ __forceinline__ uint32_t u4(const uint4& v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
 
 // The fused first-digit histograms live in the tile's staging memory, which is
@@ -118,7 +118,7 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t 
   constexpr int SLOTS = C::slots;
   constexpr int NT = C::threads;
   constexpr int PPT = C::ppt;
-  static_assert(8 + 3 * G <= 64, "head depths must fit the entry word");
+  static_assert(4 * G <= 64, "the level masks must fit the entry word");
   const uint8_t* __restrict__ rec = a.rec;
   const int64_t nb = a.nb, H = a.H, P = a.P, R = a.R;
   const int d = a.d;
@@ -162,12 +162,11 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t 
     const int e = a_off + a_inc - 1;
     const int base = t_off + t_inc - u;
     if (act) {
-      uint64_t word = (uint64_t)u;
+      uint64_t word = 0;
       for (int h = 0; h < G; ++h) {
         const int64_t row = (g * G + h) * d + c;
         const int th = a.depth[row];
-        if (th > 0) word |= (uint64_t)1 << (2 + th);
-        word |= (uint64_t)th << (8 + 3 * h);
+        if (th > 0) word |= (uint64_t)1 << ((th - 1) * G + h);
         sm.ent_q[e][h] = ldexpf(a.q[row], 3 - th);   // exact power-of-two scaling
       }
       sm.ent_word[e] = word;
@@ -291,15 +290,32 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t 
       const int pos = lane & 31;
       // the group's entries (at most 64: each starts in one of its 64 chunk
       // slots), one per lane; the loop reads them lane by lane into scalars
+      // Per lane: chunk base within the group (< 128) | union depth << 8, and
+      // for G <= 4 the level masks in bits 12 .. 27 of the same word.
+      constexpr int MB = 4 * G;
       const bool mine = e_lo + lane < e_hi;
       const uint64_t lword = mine ? sm.ent_word[e_lo + lane] : 0ull;
-      const int lbase = mine ? (int)sm.ent_base[e_lo + lane] - ch_lo : 0;
+      int linfo = 0;
+      if (mine) {
+        const int b0 = sm.ent_base[e_lo + lane], b1 = sm.ent_base[e_lo + lane + 1];
+        linfo = (b0 - ch_lo) | (b1 - b0) << 8;
+        if (MB <= 16) linfo |= (int)lword << 12;
+      }
+      // a 32-bit word where the masks fit, so a mask test sets the branch condition
+      using Word = std::conditional_t<(MB <= 32), uint32_t, uint64_t>;
       for (int e = e_lo; e < e_hi; ++e) {
-        uint64_t word = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)lword, e - e_lo);
-        if (8 + 3 * G > 32)
-          word |= (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(lword >> 32), e - e_lo) << 32;
-        const int cb = __builtin_amdgcn_readlane(lbase, e - e_lo);
-        const int tb = word_tb(word);
+        const uint32_t info = (uint32_t)__builtin_amdgcn_readlane(linfo, e - e_lo);
+        Word word;
+        if constexpr (MB <= 16) {
+          word = info >> 12;
+        } else if constexpr (MB <= 32) {
+          word = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)lword, e - e_lo);
+        } else {
+          word = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)lword, e - e_lo) |
+                 (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(lword >> 32), e - e_lo) << 32;
+        }
+        const int cb = (int)(info & 0xffu);
+        const int tb = (int)((info >> 8) & 0xfu);
         const uint4* pp = &sm.planes[cb][bl];
         // plane words of the prefix (only the planes the union depth reads)
         uint4 w0 = pp[0], w1, w2, w3;
@@ -317,7 +333,7 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t 
           for (int s2 = 0; s2 < kSub; ++s2) f[s2] = (float)(2 * r[s2] + 1);
 #pragma unroll
           for (int h = 0; h < G; ++h) {
-            if (word_th(word, h) != t) continue;
+            if (!(word & ((Word)1 << ((t - 1) * G + h)))) continue;
 #pragma unroll
             for (int s2 = 0; s2 < kSub; ++s2) acc[s2][h] = fmaf(cf[h], f[s2], acc[s2][h]);
           }
@@ -326,15 +342,16 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t 
         // r_{t+1} = 2 r_t + b_t
 #pragma unroll
         for (int s2 = 0; s2 < kSub; ++s2) r[s2] = __builtin_amdgcn_sbfe((int)u4(w0, s2), pos, 1);
-        if (word & (8u << 0)) level(1);
+        constexpr Word kHeads = (Word)((1ull << G) - 1ull);
+        if (word & kHeads) level(1);
         if (tb > 1) {
 #pragma unroll
           for (int s2 = 0; s2 < kSub; ++s2) r[s2] = 2 * r[s2] + (int)__builtin_amdgcn_ubfe(u4(w1, s2), pos, 1);
-          if (word & (8u << 1)) level(2);
+          if (word & (kHeads << G)) level(2);
           if (tb > 2) {
 #pragma unroll
             for (int s2 = 0; s2 < kSub; ++s2) r[s2] = 2 * r[s2] + (int)__builtin_amdgcn_ubfe(u4(w2, s2), pos, 1);
-            if (word & (8u << 2)) level(3);
+            if (word & (kHeads << (2 * G))) level(3);
             if (tb > 3) {
 #pragma unroll
               for (int s2 = 0; s2 < kSub; ++s2) r[s2] = 2 * r[s2] + (int)__builtin_amdgcn_ubfe(u4(w3, s2), pos, 1);
