@@ -61,7 +61,8 @@ struct Cfg {
 
 template <int G, int TB>
 struct ScanSmem {
-  uint4 planes[kStageChunks][TB];                  // staged plane bits (plane 0 complemented)
+  uint4 planes[kStageChunks + kPlanes - 1][TB];    // staged plane bits (plane 0 complemented); the last
+                                                   // rows pad reads of a prefix's unread planes
   uint4 scales[kStageEntries][TB / kUnitBlocks];   // staged fp16 scales per entry of the group
   float coef[kStageEntries][TB][G];                // q_h 2^(3-t_h) Delta_b per entry, block, head
   float ent_q[kMaxD][G];                           // q_h 2^(3-t_h) of each list entry
@@ -318,10 +319,8 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t 
         const int tb = (int)((info >> 8) & 0xfu);
         const uint4* pp = &sm.planes[cb][bl];
         // plane words of the prefix (only the planes the union depth reads)
-        uint4 w0 = pp[0], w1, w2, w3;
-        if (tb > 1) w1 = pp[TB];
-        if (tb > 2) w2 = pp[2 * TB];
-        if (tb > 3) w3 = pp[3 * TB];
+        // all four rows are read (within the padded array), only tb of them used
+        const uint4 w0 = pp[0], w1 = pp[TB], w2 = pp[2 * TB], w3 = pp[3 * TB];
         float cf[G];
 #pragma unroll
         for (int h = 0; h < G; ++h) cf[h] = sm.coef[e - e_lo][bl][h];
