@@ -291,6 +291,8 @@ __global__ __launch_bounds__(kResolveThreads) void sel_resolve(const float* __re
   const uint32_t above = state[h * 4 + 1];
   bool fallback = state[h * 4 + 2] != 0u || nchunks > NT;
   uint32_t total = 0;
+  static_assert(NT == 1024, "one of the 1024 bins of a 10-bit digit per thread");
+  lh[threadIdx.x] = 0u;   // the first 10-bit digit's histogram, counted during the gather
   if (!fallback) {
     const uint32_t c = threadIdx.x < nchunks ? counts[(int64_t)h * nchunks + threadIdx.x] : 0u;
     const uint32_t off = block_exclusive<NT>(c, wsum, &total);
@@ -304,7 +306,8 @@ __global__ __launch_bounds__(kResolveThreads) void sel_resolve(const float* __re
   }
   __syncthreads();
   // gather the slots in chunk order: TPC threads per chunk (nchunks <= NT here),
-  // every load issued before the first store
+  // every load issued before the first store; keys of bin b are counted by
+  // their next 10 bits on the way
   {
     int tpc = 1;
     while (tpc * 2 * nchunks <= NT) tpc *= 2;
@@ -324,25 +327,29 @@ __global__ __launch_bounds__(kResolveThreads) void sel_resolve(const float* __re
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
           const uint32_t x = x0 + u * tpc;
-          if (x < cn) buf[coff[c] + x] = v[u];
+          if (x < cn) {
+            buf[coff[c] + x] = v[u];
+            const uint32_t key = (uint32_t)(v[u] >> 32);
+            if ((key >> kDigit0) == bin) atomicAdd(&lh[(key >> 10) & 1023u], 1u);
+          }
         }
       }
     }
   }
   // the k-th key among the kept ones: keys above bin b are all in; among the keys
-  // of bin b find the (k - above)-th largest by the next 11, then 10 bits
+  // of bin b find the (k - above)-th largest by the next 10, then the last 10 bits
   uint32_t prefix = bin, need = (uint32_t)k - above;
+  __syncthreads();
   for (int pass = 0; pass < 2; ++pass) {
-    const int shift = pass == 0 ? 10 : 0;
-    const int hi_shift = pass == 0 ? kDigit0 : 10;
-    static_assert(NT == 1024, "one of the 1024 bins per thread");
-    lh[threadIdx.x] = 0u;
-    __syncthreads();
-    for (uint32_t x = threadIdx.x; x < total; x += NT) {
-      const uint32_t key = (uint32_t)(buf[x] >> 32);
-      if ((key >> hi_shift) == prefix) atomicAdd(&lh[(key >> shift) & 1023u], 1u);
+    if (pass == 1) {
+      lh[threadIdx.x] = 0u;
+      __syncthreads();
+      for (uint32_t x = threadIdx.x; x < total; x += NT) {
+        const uint32_t key = (uint32_t)(buf[x] >> 32);
+        if ((key >> 10) == prefix) atomicAdd(&lh[key & 1023u], 1u);
+      }
+      __syncthreads();
     }
-    __syncthreads();
     find_bin<NT, 1024>(lh, need, wsum, sh);
     prefix = (prefix << 10) | sh[0];
     need -= sh[1];
