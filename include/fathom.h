@@ -27,8 +27,9 @@
  *     status nothing was enqueued and no output was written;
  *     fathom_last_error() gives a message (per calling thread).
  *   - Shapes: h_kv KV heads, G = h_q / h_kv query heads per KV head
- *     (G in {1, 2, 4, 8, 16}), d channels (1..256), n keys (0 <= n <= 2^30,
- *     n * h_kv <= 2^33; these keep every launch grid within 2^32 work-items).
+ *     (G in {1, 2, 4, 8, 16}, h_q <= 65535), d channels (1..256), n keys
+ *     (0 <= n <= 2^30, n * h_kv <= 2^33; these keep every launch grid within
+ *     its limits).
  *     Query head h belongs to KV head h / G.  Independent sessions are passed
  *     as extra KV heads (session-major), since sessions never mix.
  */
@@ -162,7 +163,8 @@ size_t fathom_workspace_bytes(int h_q, int h_kv, int64_t n, int d, int k, int re
  * ([Abstract]; [Digest] key modules 4-5 and Output: the scan pulls only the
  * budgeted planes and outputs top-k indices per query).
  *   records      packed records (layout above), device memory (FATHOM_HBM) or
- *                pinned host memory (FATHOM_HOST_DIRECT); read-only.
+ *                pinned host memory (FATHOM_HOST_DIRECT read in place,
+ *                FATHOM_HOST_STAGED copied through the workspace); read-only.
  *   q, depth, union_depth   as for allocate_depths (device).
  *   k            0..n keys to return per query head.
  *   topk_idx     device, int32 [h_q][k]: the k keys of largest score, lowest index

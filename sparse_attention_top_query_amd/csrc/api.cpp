@@ -45,6 +45,7 @@ int check_heads(int h_q, int h_kv, int d) {
   if (h_kv < 1 || h_kv > 65535) return fail(FATHOM_ESHAPE, "h_kv=%d outside [1, 65535]", h_kv);
   if (h_q < h_kv || h_q % h_kv != 0)
     return fail(FATHOM_ESHAPE, "h_q=%d is not a multiple of h_kv=%d", h_q, h_kv);
+  if (h_q > 65535) return fail(FATHOM_ESHAPE, "h_q=%d exceeds 65535 (one grid row per query head)", h_q);
   if (!valid_group(h_q / h_kv))
     return fail(FATHOM_ESHAPE, "query heads per KV head %d not in {1,2,4,8,16}", h_q / h_kv);
   if (d < 1 || d > fathom::kMaxD) return fail(FATHOM_ESHAPE, "d=%d outside [1, %d]", d, fathom::kMaxD);
@@ -297,6 +298,7 @@ int attend_topk(const void* k_cache, const void* v_cache, int residency, const f
   if (h_kv < 1 || h_kv > 65535) return fail(FATHOM_ESHAPE, "h_kv=%d outside [1, 65535]", h_kv);
   if (h_q < h_kv || h_q % h_kv != 0)
     return fail(FATHOM_ESHAPE, "h_q=%d is not a multiple of h_kv=%d", h_q, h_kv);
+  if (h_q > 65535) return fail(FATHOM_ESHAPE, "h_q=%d exceeds 65535 (one grid row per query head)", h_q);
   if (d != 8 && d != 16 && d != 32 && d != 64 && d != 128 && d != 256)
     return fail(FATHOM_ESHAPE, "attend_topk needs d in {8, 16, 32, 64, 128, 256} (got %d)", d);
   if (n < 1 || n > kMaxN) return fail(FATHOM_ESHAPE, "n=%lld outside [1, 2^30]", (long long)n);

@@ -82,6 +82,10 @@ def test_host_validation_errors(lib):
     # scan: shape checks come before any pointer query
     assert lib.scan_topk(fake, 0, fake, fake, fake, 4, 3, 128, 8, 4, fake, None, fake, 1 << 20, None) == -2
     assert lib.scan_topk(fake, 0, fake, fake, fake, 4, 1, -1, 8, 4, fake, None, fake, 1 << 20, None) == -2
+    # at most 65535 query heads (G = 16 over 4096 KV heads is one too many)
+    assert lib.scan_topk(fake, 0, fake, fake, fake, 65536, 4096, 128, 8, 4, fake, None, fake, 1 << 20, None) == -2
+    assert "65535" in _err(lib)
+    assert lib.allocate_depths(fake, fake, 65536, 4096, 8, 0, 6, fake, fake, None, None) == -2
     assert lib.fathom_scan_scores(fake, 0, None, fake, fake, 4, 1, 128, 8, fake, 128, None, 0, None) == -1
 
 
