@@ -101,3 +101,30 @@ def test_all_equal_scores(F, n):
         idx, val = select(F, rec, dq, dep, uni, n, k)
         assert np.array_equal(idx, np.tile(np.arange(k), (4, 1)))
         assert np.all(val == 0)
+
+
+def test_workspace_reuse_across_shapes_and_residencies(F):
+    """One workspace serves calls of different n, k and residency in turn (the
+    HBM scan zeroes the selection counters, the host scan clears and fills
+    them): no state of an earlier call leaks into a later one."""
+    h_kv, g, d = 2, 4, 64
+    kk, q, s2 = small_case(41, h_kv, g, 40000, d, outliers=4)
+    dq = dev(q)
+    dep, uni = F.allocate(dq, dev(s2), 40)
+    recs = {}
+    for n in (40000, 9000, 40000 - 77):
+        rec, st = gpu_pack(np.ascontiguousarray(kk[:, :n]))
+        assert st == 0
+        recs[(n, "hbm")] = rec
+        recs[(n, "host")] = rec.cpu().pin_memory()
+    ws = torch.full((F.workspace_bytes(h_q=h_kv * g, h_kv=h_kv, n=40000, d=d, k=3000, residency=F.HOST_STAGED),),
+                    0x7F, dtype=torch.uint8, device="cuda:0")      # garbage to start from
+    order = [(40000, "hbm", 3000), (9000, "host", 50), (40000 - 77, "hbm", 1), (40000, "host", 2048),
+             (9000, "hbm", 9000), (40000 - 77, "staged", 700), (40000, "hbm", 3000)]
+    for n, res, k in order:
+        rec = recs[(n, "hbm" if res == "hbm" else "host")]
+        residency = {"hbm": F.HBM, "host": F.HOST_DIRECT, "staged": F.HOST_STAGED}[res]
+        sg = F.scan_scores(rec, dq, dep, uni, n, residency=residency).cpu().numpy()
+        idx, val = F.scan_topk(rec, dq, dep, uni, n, k, residency=residency, workspace=ws, want_scores=True)
+        torch.cuda.synchronize()
+        check_exact(idx.cpu().numpy(), val.cpu().numpy(), sg, k, where=f"n={n} {res} k={k}")
