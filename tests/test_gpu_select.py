@@ -128,3 +128,30 @@ def test_workspace_reuse_across_shapes_and_residencies(F):
         idx, val = F.scan_topk(rec, dq, dep, uni, n, k, residency=residency, workspace=ws, want_scores=True)
         torch.cuda.synchronize()
         check_exact(idx.cpu().numpy(), val.cpu().numpy(), sg, k, where=f"n={n} {res} k={k}")
+
+
+@pytest.mark.parametrize("n", [1, 2, 5, 127, 128, 129, 1023, 1025])
+@pytest.mark.parametrize("residency", ["hbm", "host", "staged"])
+def test_tiny_rows(F, n, residency):
+    """Rows shorter than one tile, one block or one 32-key word: scores match the
+    oracle and every k from 1 to n selects exactly."""
+    h_kv, g, d, budget = 2, 4, 32, 20
+    kk, q, s2 = small_case(n, h_kv, g, n, d, outliers=2)
+    rec, st = gpu_pack(kk)
+    assert st == 0
+    if residency != "hbm":
+        rec = rec.cpu().pin_memory()
+    res = {"hbm": F.HBM, "host": F.HOST_DIRECT, "staged": F.HOST_STAGED}[residency]
+    dq = dev(q)
+    dep, uni = F.allocate(dq, dev(s2), budget)
+    sg = F.scan_scores(rec, dq, dep, uni, n, residency=res).cpu().numpy()
+    rd = dep.cpu().numpy()
+    for h in range(h_kv * g):
+        delta = O.block_scales(kk[h // g])
+        kappa = O.quantize_codes(kk[h // g], delta)
+        s, a = O.scores(q[h], kappa, delta, rd[h])
+        assert np.all(np.abs(sg[h].astype(np.float64) - s) <= O.tolerance(a)), f"head {h}"
+    for k in sorted({1, (n + 1) // 2, n}):
+        idx, val = F.scan_topk(rec, dq, dep, uni, n, k, residency=res, want_scores=True)
+        torch.cuda.synchronize()
+        check_exact(idx.cpu().numpy(), val.cpu().numpy(), sg, k, where=f"n={n} {residency} k={k}")
