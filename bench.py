@@ -74,9 +74,11 @@ def algorithmic_bytes(union: np.ndarray, n: int) -> int:
 
 def algorithmic_ops(depth: np.ndarray, union: np.ndarray, n: int) -> int:
     """VALU lane-operations of the reconstruction for all keys: per KV head and
-    union channel with depth u > 0, 2u - 1 integer ops build the signed prefixes,
-    2 ops per distinct depth read by some head form float(2r + 1), and 1 FMA per
-    query head that reads the channel.  Counted per KV-head key."""
+    union channel with depth u > 0, 2u - 1 integer ops build the signed prefixes
+    r, 1 op per distinct depth read by some head converts r to float, and 1 FMA
+    (2c) r per query head that reads the channel; the term c of c (2r + 1) is
+    one add per (query head, channel, 128-key block), i.e. per block, not per
+    key.  Counted per KV-head key."""
     hk, d = union.shape
     g = depth.shape[0] // hk
     dep = depth.reshape(hk, g, d).astype(np.int64)
@@ -84,7 +86,8 @@ def algorithmic_ops(depth: np.ndarray, union: np.ndarray, n: int) -> int:
     chain = np.where(u > 0, 2 * u - 1, 0).sum()
     levels = sum(((dep == t).any(axis=1)).sum() for t in range(1, 5))
     fmas = (dep > 0).sum()
-    return int((chain + 2 * levels + fmas) * n)
+    per_block = fmas                       # one add per (head, channel) per block
+    return int((chain + levels + fmas) * n + per_block * ((n + 127) // 128))
 
 
 def measured_traffic(workload: str, residency: str, kernel: str):

@@ -20,10 +20,11 @@
 // by one word so that lanes reading their own rows hit distinct banks), with
 // the blocks' scales.  Lane l of wavefront w owns keys 128 w + l and 128 w + l
 // + 64 (both in block w).  Channels are visited in order; for a union channel c
-// read to depth t by some head, u = code >> (4 - t) is one bit-field extract
-// and the term is [q 2^(3-t) Delta] (2 (u - 2^(t-1)) + 1), the same fp32
-// operations in the same order as the bit-plane scan, so the scores are
-// bit-identical to it.
+// read to depth t by some head, u = code >> (4 - t) is one bit-field extract,
+// r = u - 2^(t-1), and the term 2c r (2c = 2 [q 2^(3-t) Delta]) joins the
+// score, 2c the head's per-lane sum (half of it is added at the end), the
+// same fp32 operations in the same order as the bit-plane scan, so the scores
+// are bit-identical to it.
 #include <hip/hip_fp16.h>
 
 #include "fathom_internal.h"
@@ -85,7 +86,7 @@ __global__ __launch_bounds__(256) void pack_nibbles_kernel(const float* __restri
 template <int G>
 struct NibSmem {
   uint32_t rows[kNibKeys][kNibMaxD / 8 + 1];   // codes of the tile's keys, 8 channels per word, padded
-  float coef[kNibBlocks][kNibMaxD][G];         // q_h 2^(3-t_h) Delta of each block and channel
+  float coef[kNibBlocks][kNibMaxD][G];         // 2 [q_h 2^(3-t_h) Delta] of each block and channel
   float cq[kNibMaxD][G];                       // q_h 2^(3-t_h) per channel (0 when not read)
   uint64_t cw[kNibMaxD];                       // union depth | depths in use | head depths
   uint32_t wmask[kNibMaxD / 8];                // channels of the union per code word
@@ -156,15 +157,18 @@ __global__ __launch_bounds__(kNibThreads) void nibble_scan_kernel(
     const int64_t b = tile * kNibBlocks + bl;
     const float dl = b < nb ? __half2float(scales[(g * nb + b) * d + c]) : 0.0f;
 #pragma unroll
-    for (int h = 0; h < G; ++h) sm.coef[bl][c][h] = sm.cq[c][h] * dl;
+    for (int h = 0; h < G; ++h) sm.coef[bl][c][h] = 2.0f * (sm.cq[c][h] * dl);   // rounded, then doubled
   }
   __syncthreads();
 
   float acc[2][G];
+  float half_sum[G];
 #pragma unroll
-  for (int s = 0; s < 2; ++s)
+  for (int h = 0; h < G; ++h) {
+    half_sum[h] = 0.0f;
 #pragma unroll
-    for (int h = 0; h < G; ++h) acc[s][h] = 0.0f;
+    for (int s = 0; s < 2; ++s) acc[s][h] = 0.0f;
+  }
   const int r0 = kBlock * wv + lane;          // rows of this lane's two keys
   const int r1 = r0 + 64;
   if (kBlock * wv < nkeys) {
@@ -190,17 +194,23 @@ __global__ __launch_bounds__(kNibThreads) void nibble_scan_kernel(
           // u = code >> (4 - t): the top t bits of the nibble
           const int u0 = (int)__builtin_amdgcn_ubfe(c0, 4 * x + 4 - t, t);
           const int u1 = (int)__builtin_amdgcn_ubfe(c1, 4 * x + 4 - t, t);
-          const float f0 = (float)(2 * (u0 - (1 << (t - 1))) + 1);
-          const float f1 = (float)(2 * (u1 - (1 << (t - 1))) + 1);
+          const float f0 = (float)(u0 - (1 << (t - 1)));
+          const float f1 = (float)(u1 - (1 << (t - 1)));
 #pragma unroll
           for (int h = 0; h < G; ++h) {
             if (nword_th(word, h) != t) continue;
             acc[0][h] = fmaf(cf[h], f0, acc[0][h]);
             acc[1][h] = fmaf(cf[h], f1, acc[1][h]);
+            half_sum[h] += cf[h];
           }
         }
       }
     }
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    acc[0][h] += 0.5f * half_sum[h];
+    acc[1][h] += 0.5f * half_sum[h];
   }
 #pragma unroll
   for (int s = 0; s < 2; ++s) {

@@ -7,10 +7,11 @@
 // is the midpoint of the prefix's cell of the t-bit mid-rise quantizer).
 // Fathom abstract: the prefix of t planes is exactly the channel's t-bit
 // quantizer, so with r_t = (code >> (4-t)) - 2^(t-1), a signed t-bit integer,
-//   q * k_hat_t = q Delta 2^(4-t) (r_t + 1/2) = [q 2^(3-t) Delta] * (2 r_t + 1).
-// The bracket is one fp32 rounding, the odd integer 2 r_t + 1 is exact, so every
-// term is the centered product q k_hat up to one rounding and the fp32 sum stays
-// within about (m + 1) 2^-24 sum_c |q_c k_hat_c| for m channels.
+//   q * k_hat_t = q Delta 2^(4-t) (r_t + 1/2) = c (2 r_t + 1),  c = [q 2^(3-t) Delta],
+// and the scan accumulates it as (2c) r_t per key plus, once per block, c: with
+// c one fp32 rounding (2c exact), every term is bounded by |2 c r_t| <= 2 |q k_hat|
+// and |c| <= |q k_hat| (|2 r_t + 1| >= 1), so the fp32 sum over m channels stays
+// within about 3 (m + 2) 2^-24 sum_c |q_c k_hat_c|.
 //
 // Work decomposition: one workgroup scores a tile of TB 128-key blocks of one KV
 // head for all of its G query heads; each wavefront owns 2 blocks (256 keys):
@@ -26,11 +27,13 @@
 //     significant plane complemented.  The same code reads HBM, an HBM staging
 //     mirror, or pinned host memory over the host link; the tile size sets the
 //     contiguous run per channel-plane (16 B per block).
-//  3. Per (channel, block) the coefficients q_h 2^(3-t_h) Delta are formed once in
-//     LDS.  Per key, each lane reads its own plane words and builds the signed
-//     prefix MSB first: r_1 = -(complemented bit) = b_0 - 1, then
-//     r_{t+1} = 2 r_t + b_t, which yields every shorter prefix on the way for
-//     heads that read fewer planes; per head one fma with float(2 r_t + 1).
+//  3. Per (channel, block) the doubled coefficients 2 c = 2 [q_h 2^(3-t_h) Delta]
+//     are formed once in LDS.  Per key, each lane reads its own plane words and
+//     builds the signed prefix MSB first: r_1 = -(complemented bit) = b_0 - 1,
+//     then r_{t+1} = 2 r_t + b_t, which yields every shorter prefix on the way
+//     for heads that read fewer planes; float(r_t) once per depth in use, and
+//     per head one fma with 2c and one add of 2c to the lane's per-head sum,
+//     half of which joins every score at the end.
 #include <hip/hip_fp16.h>
 
 #include <algorithm>
@@ -64,7 +67,7 @@ struct ScanSmem {
   uint4 planes[kStageChunks + kPlanes - 1][TB];    // staged plane bits (plane 0 complemented); the last
                                                    // rows pad reads of a prefix's unread planes
   uint4 scales[kStageEntries][TB / kUnitBlocks];   // staged fp16 scales per entry of the group
-  float coef[kStageEntries][TB][G];                // q_h 2^(3-t_h) Delta_b per entry, block, head
+  float coef[kStageEntries][TB][G];                // 2 [q_h 2^(3-t_h) Delta_b] per entry, block, head
   float ent_q[kMaxD][G];                           // q_h 2^(3-t_h) of each list entry
   uint64_t ent_word[kMaxD + 1];                    // level masks: bit (t-1) G + h iff head h reads t planes
   uint16_t ent_base[kMaxD + 1];                    // first chunk of entry e (prefix sum)
@@ -195,10 +198,13 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t 
   }
 
   float acc[kSub][G];
+  float half_sum[G];   // per head: the sum of its coefficients 2 c over the channels it reads
 #pragma unroll
-  for (int s = 0; s < kSub; ++s)
+  for (int h = 0; h < G; ++h) {
+    half_sum[h] = 0.0f;
 #pragma unroll
-    for (int h = 0; h < G; ++h) acc[s][h] = 0.0f;
+    for (int s = 0; s < kSub; ++s) acc[s][h] = 0.0f;
+  }
 
   // the tile's records: the KV head's own, or its page (addressed page-locally)
   const uint8_t* recg;
@@ -280,7 +286,7 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t 
       const int b = (i / G) % TB;
       const int h = i % G;
       const __half dl = reinterpret_cast<const __half*>(&sm.scales[el][0])[b];
-      sm.coef[el][b][h] = sm.ent_q[e_lo + el][h] * __half2float(dl);
+      sm.coef[el][b][h] = 2.0f * (sm.ent_q[e_lo + el][h] * __half2float(dl));   // rounded, then doubled
     }
     __syncthreads();
     if (gi + 1 < n_grp) issue(gi + 1);
@@ -325,16 +331,18 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t 
 #pragma unroll
         for (int h = 0; h < G; ++h) cf[h] = sm.coef[e - e_lo][bl][h];
         int r[kSub];
-        // one depth t: float(2 r_t + 1) once, then every head that reads exactly t planes
+        // one depth t: float(r_t) once, then every head that reads exactly t planes
+        // adds (2c) r_t per key and 2c to its per-lane sum (c (2 r_t + 1) in total)
         auto level = [&](int t) {
           float f[kSub];
 #pragma unroll
-          for (int s2 = 0; s2 < kSub; ++s2) f[s2] = (float)(2 * r[s2] + 1);
+          for (int s2 = 0; s2 < kSub; ++s2) f[s2] = (float)r[s2];
 #pragma unroll
           for (int h = 0; h < G; ++h) {
             if (!(word & ((Word)1 << ((t - 1) * G + h)))) continue;
 #pragma unroll
             for (int s2 = 0; s2 < kSub; ++s2) acc[s2][h] = fmaf(cf[h], f[s2], acc[s2][h]);
+            half_sum[h] += cf[h];
           }
         };
         // signed prefixes MSB first (plane 0 is stored complemented): r_1 = b_0 - 1,
@@ -363,7 +371,12 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t 
     __syncthreads();
   }
 
-  // ---- 4. scores ----
+  // ---- 4. scores: sum_c (2c) r + (1/2) sum_c 2c = sum_c c (2 r + 1) ----
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+#pragma unroll
+    for (int s = 0; s < kSub; ++s) acc[s][h] += 0.5f * half_sum[h];
+  }
   if (bl < nvalid) {
 #pragma unroll
     for (int s2 = 0; s2 < kSub; ++s2) {
