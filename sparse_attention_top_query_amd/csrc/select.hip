@@ -19,9 +19,12 @@
 //               k-th key T among them (10 + 10 more bits) and how many keys equal
 //               to T still belong to the top k, and compacts in order: keys above
 //               T and the lowest-index keys equal to T.  No sorting is needed.
-// A head whose kept keys overflow a chunk slot or the LDS buffer takes an exact
-// in-order fallback in the resolve kernel: three radix passes over its whole row
-// find T, then one ordered pass writes the selection.
+// A chunk whose kept keys overflow its slot writes them, still in index order,
+// to a segment of its head's spill area (claimed with one atomic), so kept keys
+// concentrated in a few chunks stay on the fast path.  Only a head whose kept
+// keys exceed the resolve's LDS buffer (16384) takes an exact in-order fallback
+// in the resolve kernel: three radix passes over its whole row find T, then one
+// ordered pass writes the selection.
 #include <algorithm>
 
 #include "fathom_internal.h"
@@ -123,10 +126,14 @@ __global__ __launch_bounds__(kSelThreads) void sel_collect(const float* __restri
                                                            int64_t n, int k, const uint32_t* __restrict__ hist,
                                                            uint32_t* __restrict__ state,
                                                            uint64_t* __restrict__ kept,
-                                                           uint32_t* __restrict__ counts, int64_t nchunks) {
+                                                           uint32_t* __restrict__ counts,
+                                                           uint32_t* __restrict__ soff,
+                                                           uint64_t* __restrict__ spill, int64_t nchunks) {
   constexpr int NW = kSelThreads / 64;
   constexpr int kPer = kBins / kSelThreads;   // 16 bins per thread
   __shared__ uint32_t cnt[kPerThread][NW];
+  __shared__ uint64_t* dst_sh;
+  __shared__ uint32_t cap_sh;
   __shared__ uint32_t wsum[NW];
   __shared__ uint32_t sh[2];
   const int h = blockIdx.y;
@@ -177,8 +184,36 @@ __global__ __launch_bounds__(kSelThreads) void sel_collect(const float* __restri
     if (lane == 0) cnt[i][w] = (uint32_t)__popcll(mask[i]);
   }
   __syncthreads();
-  // slot offset of (i, w): keys kept by the (i', w') pairs before it
-  uint64_t* slot = kept + ((int64_t)h * nchunks + blockIdx.x) * kSlot;
+  // where the chunk's keys go: its slot, or, if they do not fit there, a segment
+  // of the head's spill area claimed with one atomic (all of the head's kept keys
+  // must fit the resolve's on-chip buffer, so the area has that size; beyond it
+  // the head takes the resolve's full-row path)
+  if (threadIdx.x == 0) {
+    uint32_t tot = 0;
+    for (int i = 0; i < kPerThread; ++i)
+      for (int x = 0; x < NW; ++x) tot += cnt[i][x];
+    const int64_t c = (int64_t)h * nchunks + blockIdx.x;
+    uint64_t* dst = kept + c * kSlot;
+    uint32_t cap = (uint32_t)kSlot;
+    if (tot > (uint32_t)kSlot) {
+      const uint32_t base = atomicAdd(&state[h * 4 + 3], tot);
+      if (base + tot <= (uint32_t)kKeep) {
+        dst = spill + (int64_t)h * kKeep + base;
+        cap = tot;
+        soff[c] = base;
+      } else {
+        state[h * 4 + 2] = 1u;
+        cap = 0;
+      }
+    }
+    counts[c] = tot;
+    dst_sh = dst;
+    cap_sh = cap;
+  }
+  __syncthreads();
+  // offset of (i, w): keys kept by the (i', w') pairs before it
+  uint64_t* dst = dst_sh;
+  const uint32_t cap = cap_sh;
   uint32_t run = 0;
   for (int i = 0; i < kPerThread; ++i) {
     uint32_t off = run;
@@ -187,13 +222,9 @@ __global__ __launch_bounds__(kSelThreads) void sel_collect(const float* __restri
     if ((m >> lane) & 1ull) {
       const uint32_t pos = off + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
       const int64_t j = j0 + (int64_t)i * kSelThreads + threadIdx.x;
-      if (pos < (uint32_t)kSlot) slot[pos] = ((uint64_t)key[i] << 32) | (uint32_t)j;
+      if (pos < cap) dst[pos] = ((uint64_t)key[i] << 32) | (uint32_t)j;
     }
     for (int x = 0; x < NW; ++x) run += cnt[i][x];
-  }
-  if (threadIdx.x == 0) {
-    counts[(int64_t)h * nchunks + blockIdx.x] = run;
-    if (run > (uint32_t)kSlot) state[h * 4 + 2] = 1u;   // overflow: resolve from the row
   }
 }
 
@@ -222,46 +253,42 @@ __device__ __forceinline__ void find_bin(const uint32_t* lh, uint32_t need, uint
   __syncthreads();
 }
 
-// Exact in-order selection over the whole row by one workgroup (fallback).
-__device__ void resolve_row(const float* __restrict__ row, int64_t n, int k, int32_t* __restrict__ out,
-                            float* __restrict__ outv, uint32_t* lh, uint32_t* wsum, uint32_t* sh) {
-  constexpr int NT = kResolveThreads;
-  uint32_t prefix = 0, need = (uint32_t)k;
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? kDigit0 : (pass == 1 ? 10 : 0);
-    const int bits = pass == 0 ? 32 - kDigit0 : 10;
-    const int hi_shift = pass == 0 ? 32 : (pass == 1 ? kDigit0 : 10);
-    const uint32_t mask = (1u << bits) - 1u;
-    for (int b = threadIdx.x; b < kBins; b += NT) lh[b] = 0u;
-    __syncthreads();
-    for (int64_t j = threadIdx.x; j < n; j += NT) {
-      const uint32_t key = order_key(row[j]);
-      if (hi_shift == 32 || (key >> hi_shift) == prefix) atomicAdd(&lh[(key >> shift) & mask], 1u);
+// Streams wavefront w's contiguous part of a row -- the w-th of NW parts, each a
+// multiple of 256 keys -- in sweeps of 256 keys, lane l taking keys 4l .. 4l+3 of
+// each (so lane-major order within a sweep is index order), U sweeps of loads in
+// flight.  f(j, v, valid) gets a lane's first key index, its 4 scores and how
+// many of them lie in the row.
+template <int NW, class Fn>
+__device__ __forceinline__ void stream_part(const float* __restrict__ row, int64_t n, Fn&& f) {
+  constexpr int U = 8;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int64_t seg = ((n + NW - 1) / NW + 255) / 256 * 256;
+  const int64_t j_lo = (int64_t)w * seg;
+  const int64_t j_hi = min(n, j_lo + seg);
+  const bool vec = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
+  for (int64_t s0 = j_lo; s0 < j_hi; s0 += 256 * U) {
+    float v[U][4];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t j = s0 + 256 * u + 4 * lane;
+      if (vec && j + 3 < j_hi) {
+        const float4 x = *reinterpret_cast<const float4*>(row + j);
+        v[u][0] = x.x;
+        v[u][1] = x.y;
+        v[u][2] = x.z;
+        v[u][3] = x.w;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[u][i] = j + i < j_hi ? row[j + i] : 0.0f;
+      }
     }
-    __syncthreads();
-    find_bin<NT>(lh, need, wsum, sh);
-    prefix = (prefix << bits) | sh[0];
-    need -= sh[1];
-    __syncthreads();
-  }
-  const uint32_t T = prefix;
-  // ordered pass: keys above T, then the first `need` keys equal to T
-  uint32_t written = 0, ties = 0;
-  for (int64_t j0 = 0; j0 < n; j0 += NT) {
-    const int64_t j = j0 + threadIdx.x;
-    const uint32_t key = j < n ? order_key(row[j]) : 0u;
-    const uint32_t gt = (j < n && key > T) ? 1u : 0u;
-    const uint32_t eq = (j < n && key == T) ? 1u : 0u;
-    uint32_t tot_eq = 0, tot_sel = 0;
-    const uint32_t eq_before = block_exclusive<NT>(eq, wsum, &tot_eq);
-    const uint32_t sel = (gt || (eq && ties + eq_before < need)) ? 1u : 0u;
-    const uint32_t pos = block_exclusive<NT>(sel, wsum, &tot_sel);
-    if (sel) {
-      out[written + pos] = (int32_t)j;
-      if (outv) outv[written + pos] = row[j];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t j = s0 + 256 * u + 4 * lane;
+      const int valid = (int)max<int64_t>(0, min<int64_t>(4, j_hi - j));
+      f(j, v[u], valid);
     }
-    written += tot_sel;
-    ties += tot_eq;
   }
 }
 
@@ -270,11 +297,130 @@ __device__ __forceinline__ float key_to_float(uint32_t key) {
   return __uint_as_float(b);
 }
 
+// Exact in-order selection of one head from its whole row by one workgroup:
+// the path for heads whose kept keys do not fit the on-chip buffer (keys
+// concentrated in one chunk beyond the spill area, or a first-digit bin that
+// holds too many of them, e.g. massive ties or scores far from zero).  The
+// threshold bin b and the keys above it come from the head's histogram; two
+// passes over the row count the keys of bin b by their next 10, then last 10
+// bits and give the exact k-th key T; then each wavefront counts, over its own
+// part of the row, the keys above T and equal to T, and a second pass writes the
+// keys above T and the first `need` keys equal to T in index order.  Barriers:
+// a handful in all, none per sweep.
+__device__ void resolve_row(const float* __restrict__ row, int64_t n, int k, uint32_t bin, uint32_t above,
+                            int32_t* __restrict__ out, float* __restrict__ outv, uint32_t* lh, uint32_t* wsum,
+                            uint32_t* sh) {
+  constexpr int NT = kResolveThreads;
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const uint64_t lt = (1ull << lane) - 1ull;
+  uint32_t prefix = bin, need = (uint32_t)k - above;
+  for (int pass = 0; pass < 2; ++pass) {
+    const int shift = pass == 0 ? 10 : 0;
+    const int hi_shift = pass == 0 ? kDigit0 : 10;
+    lh[threadIdx.x] = 0u;
+    __syncthreads();
+    stream_part<NW>(row, n, [&](int64_t, const float (&v)[4], int valid) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t key = order_key(v[i]);
+        const bool act = i < valid && (key >> hi_shift) == prefix;
+        const uint32_t b = (key >> shift) & 1023u;
+        // one atomic for the wavefront when all its keys share a bin (ties)
+        const uint64_t m = __ballot(act);
+        if (m == 0ull) continue;
+        const int leader = __builtin_ctzll(m);
+        const uint32_t lb = (uint32_t)__shfl((int)b, leader, 64);
+        if (__ballot(act && b == lb) == m) {
+          if (lane == leader) atomicAdd(&lh[lb], (uint32_t)__popcll(m));
+        } else if (act) {
+          atomicAdd(&lh[b], 1u);
+        }
+      }
+    });
+    __syncthreads();
+    find_bin<NT, 1024>(lh, need, wsum, sh);
+    prefix = (prefix << 10) | sh[0];
+    need -= sh[1];
+    __syncthreads();
+  }
+  const uint32_t T = prefix;
+  // per wavefront: keys above T and equal to T in its part
+  uint32_t gt = 0, eq = 0;
+  stream_part<NW>(row, n, [&](int64_t, const float (&v)[4], int valid) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t key = order_key(v[i]);
+      gt += (uint32_t)__popcll(__ballot(i < valid && key > T));
+      eq += (uint32_t)__popcll(__ballot(i < valid && key == T));
+    }
+  });
+  uint32_t* wgt = lh;          // the histogram is no longer needed
+  uint32_t* weq = lh + NW;
+  if (lane == 0) {
+    wgt[w] = gt;
+    weq[w] = eq;
+  }
+  __syncthreads();
+  uint32_t pos = 0, ties = 0;
+  for (int x = 0; x < w; ++x) {
+    pos += wgt[x];
+    ties += weq[x];
+  }
+  pos += min(ties, need);
+  // ordered writes: ranks from ballots, lane-major within a sweep
+  stream_part<NW>(row, n, [&](int64_t j, const float (&v)[4], int valid) {
+    uint32_t key[4];
+    uint64_t mg[4], me[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      key[i] = order_key(v[i]);
+      mg[i] = __ballot(i < valid && key[i] > T);
+      me[i] = __ballot(i < valid && key[i] == T);
+    }
+    if (((mg[0] | mg[1] | mg[2] | mg[3]) | (me[0] | me[1] | me[2] | me[3])) == 0ull) return;
+    uint32_t rank = ties;   // equal keys before this lane's first key
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rank += (uint32_t)__popcll(me[i] & lt);
+    bool take[4];
+    uint64_t mt[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool e = (me[i] >> lane) & 1ull;
+      take[i] = ((mg[i] >> lane) & 1ull) || (e && rank < need);
+      if (e) ++rank;
+      mt[i] = __ballot(take[i]);
+    }
+    uint32_t p = pos;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p += (uint32_t)__popcll(mt[i] & lt);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (take[i]) {
+        if (p < (uint32_t)k) {
+          out[p] = (int32_t)(j + i);
+          if (outv) outv[p] = v[i];
+        }
+        ++p;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pos += (uint32_t)__popcll(mt[i]);
+      ties += (uint32_t)__popcll(me[i]);
+    }
+  });
+}
+
+
 __global__ __launch_bounds__(kResolveThreads) void sel_resolve(const float* __restrict__ scores, int64_t ld,
                                                                int64_t n, int k,
                                                                const uint32_t* __restrict__ state,
                                                                const uint64_t* __restrict__ kept,
                                                                const uint32_t* __restrict__ counts,
+                                                               const uint32_t* __restrict__ soff,
+                                                               const uint64_t* __restrict__ spill,
                                                                int64_t nchunks, int32_t* __restrict__ idx,
                                                                float* __restrict__ val) {
   constexpr int NT = kResolveThreads;
@@ -289,34 +435,72 @@ __global__ __launch_bounds__(kResolveThreads) void sel_resolve(const float* __re
   float* outv = val ? val + (int64_t)h * k : nullptr;
   const uint32_t bin = state[h * 4 + 0];
   const uint32_t above = state[h * 4 + 1];
-  bool fallback = state[h * 4 + 2] != 0u || nchunks > NT;
+  bool fallback = state[h * 4 + 2] != 0u;
   uint32_t total = 0;
   static_assert(NT == 1024, "one of the 1024 bins of a 10-bit digit per thread");
   lh[threadIdx.x] = 0u;   // the first 10-bit digit's histogram, counted during the gather
+  // Chunk offsets in the concatenation: up to NT chunks one per thread (kept in
+  // LDS for the parallel gather), beyond that a consecutive range per thread,
+  // which gathers its own chunks.
+  const uint32_t* cnt_h = counts + (int64_t)h * nchunks;
+  const bool wide = nchunks > NT;
+  const int64_t per = wide ? (nchunks + NT - 1) / NT : 1;
+  const int64_t c0 = min<int64_t>((int64_t)threadIdx.x * per, nchunks);
+  const int64_t c1 = min<int64_t>(c0 + per, nchunks);
+  uint32_t off = 0;
   if (!fallback) {
-    const uint32_t c = threadIdx.x < nchunks ? counts[(int64_t)h * nchunks + threadIdx.x] : 0u;
-    const uint32_t off = block_exclusive<NT>(c, wsum, &total);
-    coff[threadIdx.x] = off;
-    if (threadIdx.x == 0) coff[nchunks] = total;
+    uint32_t mine = 0;
+    for (int64_t c = c0; c < c1; ++c) mine += cnt_h[c];
+    off = block_exclusive<NT>(mine, wsum, &total);
+    if (!wide) {
+      coff[threadIdx.x] = off;
+      if (threadIdx.x == 0) coff[nchunks] = total;
+    }
     fallback = total > (uint32_t)kKeep;
   }
   if (fallback) {
-    resolve_row(row, n, k, out, outv, lh, wsum, sh);
+    resolve_row(row, n, k, bin, above, out, outv, lh, wsum, sh);
     return;
   }
   __syncthreads();
-  // gather the slots in chunk order: TPC threads per chunk (nchunks <= NT here),
-  // every load issued before the first store; keys of bin b are counted by
-  // their next 10 bits on the way
-  {
+  // a chunk's kept keys: its slot, or its spill segment when they overflowed it
+  auto src_of = [&](int64_t c, uint32_t cn) -> const uint64_t* {
+    return cn <= (uint32_t)kSlot ? kept + ((int64_t)h * nchunks + c) * kSlot
+                                 : spill + (int64_t)h * kKeep + soff[(int64_t)h * nchunks + c];
+  };
+  // gather in chunk order, every load of a batch issued before its stores; keys
+  // of bin b are counted by their next 10 bits on the way
+  constexpr int kBatch = 16;
+  auto put = [&](uint32_t at, uint64_t v) {
+    buf[at] = v;
+    const uint32_t key = (uint32_t)(v >> 32);
+    if ((key >> kDigit0) == bin) atomicAdd(&lh[(key >> 10) & 1023u], 1u);
+  };
+  if (wide) {
+    uint32_t at = off;
+    for (int64_t c = c0; c < c1; ++c) {
+      const uint32_t cn = cnt_h[c];
+      if (cn == 0) continue;
+      const uint64_t* src = src_of(c, cn);
+      for (uint32_t x0 = 0; x0 < cn; x0 += kBatch) {
+        uint64_t v[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) v[u] = x0 + u < cn ? src[x0 + u] : 0ull;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+          if (x0 + u < cn) put(at + x0 + u, v[u]);
+      }
+      at += cn;
+    }
+  } else {
+    // TPC threads per chunk
     int tpc = 1;
     while (tpc * 2 * nchunks <= NT) tpc *= 2;
     const int c = threadIdx.x / tpc;
     const int r = threadIdx.x % tpc;
-    constexpr int kBatch = 16;
     if (c < nchunks) {
       const uint32_t cn = coff[c + 1] - coff[c];
-      const uint64_t* src = kept + ((int64_t)h * nchunks + c) * kSlot;
+      const uint64_t* src = src_of(c, cn);
       for (uint32_t x0 = r; x0 < cn; x0 += kBatch * tpc) {
         uint64_t v[kBatch];
 #pragma unroll
@@ -327,11 +511,7 @@ __global__ __launch_bounds__(kResolveThreads) void sel_resolve(const float* __re
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
           const uint32_t x = x0 + u * tpc;
-          if (x < cn) {
-            buf[coff[c] + x] = v[u];
-            const uint32_t key = (uint32_t)(v[u] >> 32);
-            if ((key >> kDigit0) == bin) atomicAdd(&lh[(key >> 10) & 1023u], 1u);
-          }
+          if (x < cn) put(coff[c] + x, v[u]);
         }
       }
     }
@@ -402,8 +582,8 @@ int64_t select_chunks(int64_t n) { return (n + kChunk - 1) / kChunk; }
 size_t select_workspace_bytes(int h_q, int64_t n, int k) {
   (void)k;
   const size_t nc = (size_t)select_chunks(n);
-  return al256((size_t)h_q * kBins * 4) + al256((size_t)h_q * 4 * 4) + al256((size_t)h_q * nc * 4) +
-         al256((size_t)h_q * nc * kSlot * 8);
+  return al256((size_t)h_q * kBins * 4) + al256((size_t)h_q * 4 * 4) + 2 * al256((size_t)h_q * nc * 4) +
+         al256((size_t)h_q * nc * kSlot * 8) + al256((size_t)h_q * kKeep * 8);
 }
 
 size_t select_clear_words(int h_q) {
@@ -421,7 +601,11 @@ SelectWorkspace carve_select(void* base, int h_q, int64_t n, int k) {
   p += al256((size_t)h_q * 4 * 4);
   ws.counts = reinterpret_cast<uint32_t*>(p);
   p += al256((size_t)h_q * (size_t)ws.nchunks * 4);
+  ws.soff = reinterpret_cast<uint32_t*>(p);
+  p += al256((size_t)h_q * (size_t)ws.nchunks * 4);
   ws.kept = reinterpret_cast<uint64_t*>(p);
+  p += al256((size_t)h_q * (size_t)ws.nchunks * kSlot * 8);
+  ws.spill = reinterpret_cast<uint64_t*>(p);
   return ws;
 }
 
@@ -438,9 +622,10 @@ hipError_t launch_select(const float* scores, int64_t ld, int h_q, int64_t n, in
     if (!cleared) sel_init<<<h_q, kSelThreads, 0, s>>>(ws.hist, ws.state);
     sel_hist<<<grid, kSelThreads, 0, s>>>(scores, ld, n, ws.hist);
   }
-  sel_collect<<<grid, kSelThreads, 0, s>>>(scores, ld, n, k, ws.hist, ws.state, ws.kept, ws.counts, ws.nchunks);
-  sel_resolve<<<h_q, kResolveThreads, 0, s>>>(scores, ld, n, k, ws.state, ws.kept, ws.counts, ws.nchunks, idx,
-                                              val);
+  sel_collect<<<grid, kSelThreads, 0, s>>>(scores, ld, n, k, ws.hist, ws.state, ws.kept, ws.counts, ws.soff,
+                                           ws.spill, ws.nchunks);
+  sel_resolve<<<h_q, kResolveThreads, 0, s>>>(scores, ld, n, k, ws.state, ws.kept, ws.counts, ws.soff, ws.spill,
+                                              ws.nchunks, idx, val);
   return hipGetLastError();
 }
 

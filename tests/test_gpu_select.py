@@ -155,3 +155,23 @@ def test_tiny_rows(F, n, residency):
         idx, val = F.scan_topk(rec, dq, dep, uni, n, k, residency=res, want_scores=True)
         torch.cuda.synchronize()
         check_exact(idx.cpu().numpy(), val.cpu().numpy(), sg, k, where=f"n={n} {residency} k={k}")
+
+
+@pytest.mark.parametrize("rising", [False, True])
+def test_rows_of_more_than_1024_chunks(F, rising):
+    """Rows of more than 1024 select chunks (over 4M keys): the resolve gathers
+    chunk ranges per thread; with rising scores the kept keys also sit in spill
+    segments of the last chunks."""
+    n, d = 4_300_000, 16
+    if rising:
+        kk, q, s2 = rising_case(n, d=d, seed=8)
+    else:
+        kk, q, s2 = small_case(13, 1, 2, n, d, outliers=2)
+    rec, st = gpu_pack(kk)
+    assert st == 0
+    dq = dev(q)
+    dep, uni = F.allocate(dq, dev(s2), 4 * d if rising else 24)
+    sg = F.scan_scores(rec, dq, dep, uni, n).cpu().numpy()
+    for k in (1, 2048, 5000):
+        idx, val = select(F, rec, dq, dep, uni, n, k)
+        check_exact(idx, val, sg, k, where=f"n={n} rising={rising} k={k}")
