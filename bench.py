@@ -49,6 +49,8 @@ def parse():
                     help="skip the attention over the selected keys (bf16 K/V caches are not built)")
     ap.add_argument("--no-append", action="store_true",
                     help="skip the growing-cache measurement (open tail block, sealing one block)")
+    ap.add_argument("--no-paged", action="store_true",
+                    help="skip the paged-records measurement (the same step over pages of 65536 keys)")
     ap.add_argument("--no-compare", action="store_true",
                     help="skip the fixed-depth (136-bit, 68-bit) comparison scans")
     ap.add_argument("--kernel-reps", type=int, default=20)
@@ -604,6 +606,56 @@ def main():
                   "step_with_open_tail_ms": round(b0.elapsed_time(b1) / tsteps, 4),
                   "seal_one_block_all_kv_heads_us": round(c0.elapsed_time(c1) / 20 * 1e3, 2)}
         del seal_rec, blk, tail, aws2
+    # Paged records: the same step over pages of 65536 keys, each page its own
+    # allocation in the workload's residency, placed in shuffled order and
+    # reached through a device page table.
+    paged = None
+    page_keys = 65536
+    if not args.no_paged and n % page_keys == 0:
+        from synthetic import kv_head
+        npages = n // page_keys
+        pr = F.record_bytes(page_keys)
+        slots = np.random.default_rng(7).permutation(hk * npages)
+        pool = [torch.empty((d, pr), dtype=torch.uint8, pin_memory=True) if host else
+                torch.empty((d, pr), dtype=torch.uint8, device=dev) for _ in range(hk * npages)]
+        stage = torch.empty((1, d, pr), dtype=torch.uint8, device=dev)
+        pages = [[None] * npages for _ in range(hk)]
+        with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+            for v, kv in enumerate(ex.map(lambda v: kv_head(wl.key, 0, v // wl.h_kv, v % wl.h_kv, n, d,
+                                                            wl.outliers)[0], range(hk))):
+                kd = torch.from_numpy(kv).to(dev)[None]
+                for p in range(npages):
+                    view = pool[int(slots[v * npages + p])]
+                    F.pack_blocks(kd[:, p * page_keys:(p + 1) * page_keys], stage if host else view[None],
+                                  page_keys, 0)
+                    if host:
+                        view.copy_(stage[0])
+                    pages[v][p] = view
+                del kd
+        table = F.page_table(pages, residency=F.HOST_DIRECT if host else F.HBM)
+        pres = F.HOST_DIRECT if host else F.HBM
+        pidx = torch.empty((hq, k), dtype=torch.int32, device=dev)
+
+        def step_paged():
+            F.allocate(q, s2, budget, mode=mode, depth=depth, union_depth=uni)
+            F.scan_topk_paged(table, page_keys, n, None, q, depth, uni, k, residency=pres, workspace=ws, idx=pidx)
+        for _ in range(2):
+            step_paged()
+        torch.cuda.synchronize(dev)
+        p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        psteps = max(3, min(args.steps, 20))
+        p0.record(stream)
+        for _ in range(psteps):
+            step_paged()
+        p1.record(stream)
+        torch.cuda.synchronize(dev)
+        step()
+        torch.cuda.synchronize(dev)
+        paged = {"page_keys": page_keys, "pages_per_kv_head": npages,
+                 "step_ms": round(p0.elapsed_time(p1) / psteps, 4),
+                 "contiguous_step_ms": round(step_ms, 4),
+                 "same_selection_as_contiguous": bool(torch.equal(pidx, idx))}
+        del pool, pages, table, stage
     out = {
         "metric": "keys scanned/s per top-k step at 1M tokens (host-resident), % of link/HBM BW",
         "value": round(keys_per_s, 1),
@@ -625,6 +677,7 @@ def main():
         "comparison": comparison,
         "attention": attention,
         "append": append,
+        "paged": paged,
         "bytes_per_key": round(alg_bytes / (hk * n), 3),
         "link_frac_of_measured_h2d_per_step": round(alg_bytes / (step_ms * 1e-3) / 1e9 / h2d_peak, 4)
         if host else None,
