@@ -516,8 +516,13 @@ def main():
             f1.record(stream)
             torch.cuda.synchronize(dev)
             fms = f0.elapsed_time(f1) / csteps
+            fbytes = hk * (n * (d // 2) + -(-n // 128) * d * 2)   # codes, then one fp16 scale per block and channel
+            fgbps = fbytes / (fms * 1e-3) / 1e9
             comparison[f"free_path_B{budget}"] = {
                 "ms_per_step": round(fms, 4), "bytes_per_key": round(d / 2 + d / 64, 3),
+                "bytes_per_step": fbytes, "gbps_over_the_step": round(fgbps, 2),
+                "frac_of_measured_h2d" if host else "frac_of_hbm_peak":
+                    round(fgbps / (h2d_peak if host else HBM_PEAK_GBPS), 4),
                 "what": "the same depths over the token-major 4-bit copy (scan_topk_nibbles)"}
             comparison["speedup_vs_free_path"] = round(fms / step_ms, 3)
         b68 = name_of[(68, F.WATERFILL)]
