@@ -20,8 +20,9 @@
 //               to T still belong to the top k, and compacts in order: keys above
 //               T and the lowest-index keys equal to T.  No sorting is needed.
 // A chunk whose kept keys overflow its slot writes them, still in index order,
-// to a segment of its head's spill area (claimed with one atomic), so kept keys
-// concentrated in a few chunks stay on the fast path.  Only a head whose kept
+// to a segment of its head's spill area (claimed with one atomic; rows of more
+// than 65536 keys), so kept keys concentrated in a few chunks stay on the fast
+// path.  Only a head whose kept
 // keys exceed the resolve's LDS buffer (16384) takes an exact in-order fallback
 // in the resolve kernel: three radix passes over its whole row find T, then one
 // ordered pass writes the selection.
@@ -128,7 +129,8 @@ __global__ __launch_bounds__(kSelThreads) void sel_collect(const float* __restri
                                                            uint64_t* __restrict__ kept,
                                                            uint32_t* __restrict__ counts,
                                                            uint32_t* __restrict__ soff,
-                                                           uint64_t* __restrict__ spill, int64_t nchunks) {
+                                                           uint64_t* __restrict__ spill, int64_t spill_cap,
+                                                           int64_t nchunks) {
   constexpr int NW = kSelThreads / 64;
   constexpr int kPer = kBins / kSelThreads;   // 16 bins per thread
   __shared__ uint32_t cnt[kPerThread][NW];
@@ -197,8 +199,8 @@ __global__ __launch_bounds__(kSelThreads) void sel_collect(const float* __restri
     uint32_t cap = (uint32_t)kSlot;
     if (tot > (uint32_t)kSlot) {
       const uint32_t base = atomicAdd(&state[h * 4 + 3], tot);
-      if (base + tot <= (uint32_t)kKeep) {
-        dst = spill + (int64_t)h * kKeep + base;
+      if ((int64_t)base + tot <= spill_cap) {
+        dst = spill + (int64_t)h * spill_cap + base;
         cap = tot;
         soff[c] = base;
       } else {
@@ -420,7 +422,7 @@ __global__ __launch_bounds__(kResolveThreads) void sel_resolve(const float* __re
                                                                const uint64_t* __restrict__ kept,
                                                                const uint32_t* __restrict__ counts,
                                                                const uint32_t* __restrict__ soff,
-                                                               const uint64_t* __restrict__ spill,
+                                                               const uint64_t* __restrict__ spill, int64_t spill_cap,
                                                                int64_t nchunks, int32_t* __restrict__ idx,
                                                                float* __restrict__ val) {
   constexpr int NT = kResolveThreads;
@@ -466,7 +468,7 @@ __global__ __launch_bounds__(kResolveThreads) void sel_resolve(const float* __re
   // a chunk's kept keys: its slot, or its spill segment when they overflowed it
   auto src_of = [&](int64_t c, uint32_t cn) -> const uint64_t* {
     return cn <= (uint32_t)kSlot ? kept + ((int64_t)h * nchunks + c) * kSlot
-                                 : spill + (int64_t)h * kKeep + soff[(int64_t)h * nchunks + c];
+                                 : spill + (int64_t)h * spill_cap + soff[(int64_t)h * nchunks + c];
   };
   // gather in chunk order, every load of a batch issued before its stores; keys
   // of bin b are counted by their next 10 bits on the way
@@ -579,11 +581,17 @@ size_t al256(size_t x) { return (x + 255) / 256 * 256; }
 
 int64_t select_chunks(int64_t n) { return (n + kChunk - 1) / kChunk; }
 
+// Spill entries per head (the resolve holds at most kKeep kept keys).  Rows of
+// at most 65536 keys get none: a head of theirs whose chunk overflows takes the
+// row path, four passes over at most 256 KB; a spill area would cost twice the
+// memory of their scores.
+int64_t spill_entries(int64_t n) { return n > 65536 ? kKeep : 0; }
+
 size_t select_workspace_bytes(int h_q, int64_t n, int k) {
   (void)k;
   const size_t nc = (size_t)select_chunks(n);
   return al256((size_t)h_q * kBins * 4) + al256((size_t)h_q * 4 * 4) + 2 * al256((size_t)h_q * nc * 4) +
-         al256((size_t)h_q * nc * kSlot * 8) + al256((size_t)h_q * kKeep * 8);
+         al256((size_t)h_q * nc * kSlot * 8) + al256((size_t)h_q * (size_t)spill_entries(n) * 8);
 }
 
 size_t select_clear_words(int h_q) {
@@ -606,6 +614,7 @@ SelectWorkspace carve_select(void* base, int h_q, int64_t n, int k) {
   ws.kept = reinterpret_cast<uint64_t*>(p);
   p += al256((size_t)h_q * (size_t)ws.nchunks * kSlot * 8);
   ws.spill = reinterpret_cast<uint64_t*>(p);
+  ws.spill_cap = spill_entries(n);
   return ws;
 }
 
@@ -623,9 +632,9 @@ hipError_t launch_select(const float* scores, int64_t ld, int h_q, int64_t n, in
     sel_hist<<<grid, kSelThreads, 0, s>>>(scores, ld, n, ws.hist);
   }
   sel_collect<<<grid, kSelThreads, 0, s>>>(scores, ld, n, k, ws.hist, ws.state, ws.kept, ws.counts, ws.soff,
-                                           ws.spill, ws.nchunks);
+                                           ws.spill, ws.spill_cap, ws.nchunks);
   sel_resolve<<<h_q, kResolveThreads, 0, s>>>(scores, ld, n, k, ws.state, ws.kept, ws.counts, ws.soff, ws.spill,
-                                              ws.nchunks, idx, val);
+                                              ws.spill_cap, ws.nchunks, idx, val);
   return hipGetLastError();
 }
 
