@@ -51,6 +51,25 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+// Loads and stores through the global address space, for pointers whose origin
+// the compiler cannot see (chosen at run time, passed through LDS).  A generic
+// (flat) access also counts against the LDS wait counter, so any later LDS wait
+// would stall until it completed.
+template <typename T>
+__device__ __forceinline__ T load_global(const T* p) {
+  return *(const __attribute__((address_space(1))) T*)p;
+}
+template <typename T>
+__device__ __forceinline__ void store_global(T* p, T v) {
+  *(__attribute__((address_space(1))) T*)p = v;
+}
+// (uint4's copy constructor takes a generic reference: load it as a vector)
+__device__ __forceinline__ uint4 load_global(const uint4* p) {
+  typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+  const v4u x = *(const __attribute__((address_space(1))) v4u*)p;
+  return make_uint4(x.x, x.y, x.z, x.w);
+}
+
 // ---- launchers (each returns hipSuccess or the launch error) ----
 hipError_t launch_pack(const float* k, int h_kv, const Layout& L, int d, uint8_t* rec,
                        uint32_t* status, hipStream_t s);

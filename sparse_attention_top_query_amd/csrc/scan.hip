@@ -71,10 +71,8 @@ struct ScanSmem {
   float ent_q[kMaxD][G];                           // q_h 2^(3-t_h) of each list entry
   uint64_t ent_word[kMaxD + 1];                    // level masks: bit (t-1) G + h iff head h reads t planes
   uint16_t ent_base[kMaxD + 1];                    // first chunk of entry e (prefix sum)
-  uint8_t ent_c[kMaxD];                            // channel of list entry e
   uint16_t grp[kMaxChunks / kGroupChunks + 2];     // first entry of each staging group
-  uint8_t chunk_e[kMaxChunks];
-  uint8_t chunk_p[kMaxChunks];
+  uint32_t chunk_meta[kMaxChunks];                 // entry | channel << 8 | plane << 16 of each chunk
   int wsum[2][16];
   int n_grp;
 };
@@ -103,6 +101,7 @@ struct ScanArgs {
 // reads exactly t planes of the channel (at most 64 bits for G <= 16).  The
 // union depth is the entry's chunk count.
 __device__ __forceinline__ uint32_t u4(const uint4& v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
+
 
 // The fused first-digit histograms live in the tile's staging memory, which is
 // dead once the last group is scored: 16-bit counts, two bins per word (a tile
@@ -174,7 +173,6 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t 
         sm.ent_q[e][h] = ldexpf(a.q[row], 3 - th);   // exact power-of-two scaling
       }
       sm.ent_word[e] = word;
-      sm.ent_c[e] = (uint8_t)c;
       sm.ent_base[e] = (uint16_t)base;
       if (e == n_ent - 1) {
         sm.ent_base[n_ent] = (uint16_t)(base + u);
@@ -183,10 +181,7 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t 
         sm.n_grp = base / kGroupChunks + 1;
         sm.grp[base / kGroupChunks + 1] = (uint16_t)n_ent;
       }
-      for (int p = 0; p < u; ++p) {
-        sm.chunk_e[base + p] = (uint8_t)e;
-        sm.chunk_p[base + p] = (uint8_t)p;
-      }
+      for (int p = 0; p < u; ++p) sm.chunk_meta[base + p] = (uint32_t)e | (uint32_t)c << 8 | (uint32_t)p << 16;
     }
     if (tid == 0 && n_ent == 0) sm.n_grp = 0;
     __syncthreads();
@@ -220,31 +215,37 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t 
   const int n_grp = sm.n_grp;
 
   // ---- 2. staging.  Piece i of a group is slot i % SLOTS of chunk i / SLOTS.  A
-  // plane-0 chunk walks the tile's head slice in memory order (per unit: 1 scale
-  // piece, then 8 plane-0 pieces); a chunk of plane p >= 1 uses its first TB slots.
+  // record-head chunk walks the tile's head slice in memory order (per unit: 1
+  // scale piece, then 8 plane-0 pieces); a chunk of plane p >= 1 uses its first
+  // TB slots.  A thread's pieces sit at the same (chunk, slot) of every group, so
+  // their slot offsets are fixed; issue keeps each piece's chunk meta for commit.
   uint4 v[PPT];
+  uint32_t meta[PPT];
+  const uint32_t R32 = (uint32_t)R, H32 = (uint32_t)H, P32 = (uint32_t)P;
   auto issue = [&](int gi) {
     const int ch_lo = sm.ent_base[sm.grp[gi]];
     const int n_pieces = (sm.ent_base[sm.grp[gi + 1]] - ch_lo) * SLOTS;
 #pragma unroll
     for (int r = 0; r < PPT; ++r) {
       const int i = tid + r * NT;
+      const int k = i % SLOTS;
+      const int un = k / (kUnitBlocks + 1);
+      const int w = k % (kUnitBlocks + 1);
       const uint4* src = nullptr;
+      meta[r] = 0u;
       if (i < n_pieces) {
-        const int ch = ch_lo + i / SLOTS;
-        const int k = i % SLOTS;
-        const int p = sm.chunk_p[ch];
-        const uint8_t* base = recg + (int64_t)sm.ent_c[sm.chunk_e[ch]] * R;
-        if (p == 0) {
-          const int un = k / (kUnitBlocks + 1);
-          const int w = k % (kUnitBlocks + 1);
-          if (un * kUnitBlocks + (w == 0 ? 0 : w - 1) < nvalid)
-            src = reinterpret_cast<const uint4*>(base + kUnitHead * (unit0 + un) + 16 * w);
-        } else if (k < nvalid) {   // also skips the unused slots k >= TB
-          src = reinterpret_cast<const uint4*>(base + H + (p - 1) * P + (ablk0 + k) * 16);
-        }
+        const uint32_t m = sm.chunk_meta[i / SLOTS + ch_lo];
+        const uint32_t p = m >> 16;
+        meta[r] = m;
+        // byte offset within the channel's record (records hold at most 2^30 keys,
+        // so R < 2^32): the unit's head slice, or the blocks' slice of plane p
+        // (the second test also skips the unused slots k >= TB)
+        const bool ok = p == 0u ? un * kUnitBlocks + (w == 0 ? 0 : w - 1) < nvalid : k < nvalid;
+        const uint32_t at = p == 0u ? kUnitHead * (uint32_t)(unit0 + un) + 16u * w
+                                    : H32 + (p - 1u) * P32 + 16u * (uint32_t)(ablk0 + k);
+        if (ok) src = reinterpret_cast<const uint4*>(recg + (uint64_t)((m >> 8) & 0xffu) * R32 + at);
       }
-      v[r] = src ? *src : make_uint4(0u, 0u, 0u, 0u);
+      v[r] = src ? load_global(src) : make_uint4(0u, 0u, 0u, 0u);   // not flat: the loop's LDS waits stay short
     }
   };
   auto commit = [&](int gi) {
@@ -257,11 +258,11 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t 
       if (i < n_pieces) {
         const int chl = i / SLOTS;
         const int k = i % SLOTS;
-        if (sm.chunk_p[ch_lo + chl] == 0) {
+        if ((meta[r] >> 16) == 0u) {
           const int un = k / (kUnitBlocks + 1);
           const int w = k % (kUnitBlocks + 1);
           if (w == 0) {
-            sm.scales[sm.chunk_e[ch_lo + chl] - e_lo][un] = v[r];
+            sm.scales[(int)(meta[r] & 0xffu) - e_lo][un] = v[r];
           } else {
             const uint4 x = v[r];
             sm.planes[chl][un * kUnitBlocks + w - 1] = make_uint4(~x.x, ~x.y, ~x.z, ~x.w);
@@ -281,12 +282,15 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t 
     commit(gi);
     __syncthreads();
     // coefficients q_h 2^(3-t_h) Delta_b for every entry, block and head of the group
-    for (int i = tid; i < (e_hi - e_lo) * TB * G; i += NT) {
-      const int el = i / (TB * G);
-      const int b = (i / G) % TB;
-      const int h = i % G;
-      const __half dl = reinterpret_cast<const __half*>(&sm.scales[el][0])[b];
-      sm.coef[el][b][h] = 2.0f * (sm.ent_q[e_lo + el][h] * __half2float(dl));   // rounded, then doubled
+    for (int i = tid; i < (e_hi - e_lo) * TB; i += NT) {   // one (entry, block) per thread, all heads
+      const int el = i / TB;
+      const int b = i % TB;
+      const float dl = __half2float(reinterpret_cast<const __half*>(&sm.scales[el][0])[b]);
+      float qh[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) qh[h] = sm.ent_q[e_lo + el][h];
+#pragma unroll
+      for (int h = 0; h < G; ++h) sm.coef[el][b][h] = 2.0f * (qh[h] * dl);   // rounded, then doubled
     }
     __syncthreads();
     if (gi + 1 < n_grp) issue(gi + 1);

@@ -224,7 +224,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_collect(const float* __restri
     if ((m >> lane) & 1ull) {
       const uint32_t pos = off + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
       const int64_t j = j0 + (int64_t)i * kSelThreads + threadIdx.x;
-      if (pos < cap) dst[pos] = ((uint64_t)key[i] << 32) | (uint32_t)j;
+      if (pos < cap) store_global(dst + pos, ((uint64_t)key[i] << 32) | (uint32_t)j);
     }
     for (int x = 0; x < NW; ++x) run += cnt[i][x];
   }
