@@ -67,7 +67,9 @@ struct ScanSmem {
   uint4 planes[kStageChunks + kPlanes - 1][TB];    // staged plane bits (plane 0 complemented); the last
                                                    // rows pad reads of a prefix's unread planes
   uint4 scales[kStageEntries][TB / kUnitBlocks];   // staged fp16 scales per entry of the group
-  float coef[kStageEntries][TB][G];                // 2 [q_h 2^(3-t_h) Delta_b] per entry, block, head
+  float coef[kStageChunks][TB][G];                 // 2 [q_h 2^(3-t_h) Delta_b] per block and head, in the
+                                                   // row of the entry's first chunk (for G = 4 a row has the
+                                                   // planes' stride: one address serves both)
   float ent_q[kMaxD][G];                           // q_h 2^(3-t_h) of each list entry
   uint64_t ent_word[kMaxD + 1];                    // level masks: bit (t-1) G + h iff head h reads t planes
   uint16_t ent_base[kMaxD + 1];                    // first chunk of entry e (prefix sum)
@@ -136,7 +138,19 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t 
   // ---- 1. list of union channels, in channel order, and staging groups ----
   {
     const int c = tid;
-    const int u = (c < d) ? (int)a.uni[g * d + c] : 0;
+    // every input of the list in one round trip, without branches: threads past
+    // the last channel read channel d-1 and drop it
+    const int cs = c < d ? c : d - 1;
+    const int u0 = (int)a.uni[g * d + cs];
+    int th[G];
+    float qc[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const int64_t row = (g * G + h) * d + cs;
+      th[h] = (int)a.depth[row];
+      qc[h] = a.q[row];
+    }
+    const int u = c < d ? u0 : 0;
     const int act = u > 0;
     int a_inc = act, t_inc = u;
 #pragma unroll
@@ -166,11 +180,10 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t 
     const int base = t_off + t_inc - u;
     if (act) {
       uint64_t word = 0;
+#pragma unroll
       for (int h = 0; h < G; ++h) {
-        const int64_t row = (g * G + h) * d + c;
-        const int th = a.depth[row];
-        if (th > 0) word |= (uint64_t)1 << ((th - 1) * G + h);
-        sm.ent_q[e][h] = ldexpf(a.q[row], 3 - th);   // exact power-of-two scaling
+        if (th[h] > 0) word |= (uint64_t)1 << ((th[h] - 1) * G + h);
+        sm.ent_q[e][h] = ldexpf(qc[h], 3 - th[h]);   // exact power-of-two scaling
       }
       sm.ent_word[e] = word;
       sm.ent_base[e] = (uint16_t)base;
@@ -181,7 +194,9 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t 
         sm.n_grp = base / kGroupChunks + 1;
         sm.grp[base / kGroupChunks + 1] = (uint16_t)n_ent;
       }
-      for (int p = 0; p < u; ++p) sm.chunk_meta[base + p] = (uint32_t)e | (uint32_t)c << 8 | (uint32_t)p << 16;
+#pragma unroll
+      for (int p = 0; p < kPlanes; ++p)
+        if (p < u) sm.chunk_meta[base + p] = (uint32_t)e | (uint32_t)c << 8 | (uint32_t)p << 16;
     }
     if (tid == 0 && n_ent == 0) sm.n_grp = 0;
     __syncthreads();
@@ -286,11 +301,12 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t 
       const int el = i / TB;
       const int b = i % TB;
       const float dl = __half2float(reinterpret_cast<const __half*>(&sm.scales[el][0])[b]);
+      const int row = sm.ent_base[e_lo + el] - ch_lo;
       float qh[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) qh[h] = sm.ent_q[e_lo + el][h];
 #pragma unroll
-      for (int h = 0; h < G; ++h) sm.coef[el][b][h] = 2.0f * (qh[h] * dl);   // rounded, then doubled
+      for (int h = 0; h < G; ++h) sm.coef[row][b][h] = 2.0f * (qh[h] * dl);   // rounded, then doubled
     }
     __syncthreads();
     if (gi + 1 < n_grp) issue(gi + 1);
@@ -333,7 +349,7 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t 
         const uint4 w0 = pp[0], w1 = pp[TB], w2 = pp[2 * TB], w3 = pp[3 * TB];
         float cf[G];
 #pragma unroll
-        for (int h = 0; h < G; ++h) cf[h] = sm.coef[e - e_lo][bl][h];
+        for (int h = 0; h < G; ++h) cf[h] = sm.coef[cb][bl][h];
         int r[kSub];
         // one depth t: float(r_t) once, then every head that reads exactly t planes
         // adds (2c) r_t per key and 2c to its per-lane sum (c (2 r_t + 1) in total)
@@ -441,24 +457,28 @@ struct HostTile {
 };
 
 // Workgroup ids are dealt round-robin to the 8 XCDs, each with its own L2.  The
-// kernel maps id w to logical tile (w % 8) * per + w / 8 so that every XCD scans
-// one contiguous range of (KV head, tile) pairs: neighbouring tiles, whose head
-// runs can share a cache line at their boundary, then meet in the same L2.
+// kernel gives XCD x = w % 8 the x-th eighth of every KV head's tiles (t8 =
+// ceil(tiles / 8) of them), head after head: neighbouring tiles, whose head runs
+// can share a cache line at their boundary, mostly meet in the same L2, and
+// every XCD gets the same mix of heads (whose union depths, and so work, differ).
 constexpr int kXcds = 8;
 
 template <int G, int TB, bool FUSE>
 __global__ __launch_bounds__((Cfg<G, TB>::threads)) void scan_kernel(ScanArgs a, int64_t tiles, int64_t total) {
   __shared__ ScanSmem<G, TB> sm;
   const int64_t w = blockIdx.x;
-  const int64_t per = (total + kXcds - 1) / kXcds;
-  const int64_t L = (w % kXcds) * per + w / kXcds;
-  if (L >= total) return;
+  const int64_t t8 = (tiles + kXcds - 1) / kXcds;
+  const int64_t j = w / kXcds;
+  const int64_t g = j / t8;
+  const int64_t tile = (w % kXcds) * t8 + j % t8;
+  if (tile >= tiles) return;
+  const int64_t L = g * tiles + tile;   // distinct in [0, total)
   if (a.zero) {   // the selection's counters: one slice per workgroup
     const int64_t slice = (a.zero_words + total - 1) / total;
     const int64_t z1 = min((L + 1) * slice, a.zero_words);
     for (int64_t i = L * slice + threadIdx.x; i < z1; i += Cfg<G, TB>::threads) a.zero[i] = 0u;
   }
-  scan_tile<G, TB, FUSE>(a, L / tiles, L % tiles, sm);
+  scan_tile<G, TB, FUSE>(a, g, tile, sm);
 }
 
 // ---------------------------------------------------------------------------
@@ -571,12 +591,12 @@ hipError_t launch_g(const uint8_t* rec, const float* q, const uint8_t* depth, co
   }
   const int64_t tiles = (L.nb + TB - 1) / TB;
   const int64_t total = tiles * h_kv;
-  const int64_t per = (total + kXcds - 1) / kXcds;
+  const int64_t grid = kXcds * h_kv * ((tiles + kXcds - 1) / kXcds);
   if (hist) {
-    scan_kernel<G, TB, true><<<(unsigned)(per * kXcds), Cfg<G, TB>::threads, 0, s>>>(a, tiles, total);
+    scan_kernel<G, TB, true><<<(unsigned)grid, Cfg<G, TB>::threads, 0, s>>>(a, tiles, total);
     return hipGetLastError();
   }
-  scan_kernel<G, TB, false><<<(unsigned)(per * kXcds), Cfg<G, TB>::threads, 0, s>>>(a, tiles, total);
+  scan_kernel<G, TB, false><<<(unsigned)grid, Cfg<G, TB>::threads, 0, s>>>(a, tiles, total);
   return hipGetLastError();
 }
 
