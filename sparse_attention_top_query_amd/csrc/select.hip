@@ -98,18 +98,23 @@ __global__ __launch_bounds__(kSelThreads) void sel_hist(const float* __restrict_
   const int h = blockIdx.y;
   for (int b = threadIdx.x; b < kBins; b += kSelThreads) lh[b] = 0u;
   __syncthreads();
-  const float* row = scores + (int64_t)h * ld;
+  const float* row = scores + (int64_t)h * ld;   // rows are 256-byte aligned, padded to 64 keys
   const int64_t j0 = (int64_t)blockIdx.x * kChunk;
-  float v[kPerThread];
+  // 16-byte loads: thread t counts keys j0 + 4 (t + 256 i) + e (the order does not matter here)
+  constexpr int kQuads = kPerThread / 4;
+  float4 v[kQuads];
 #pragma unroll
-  for (int i = 0; i < kPerThread; ++i) {
-    const int64_t j = j0 + (int64_t)i * kSelThreads + threadIdx.x;
-    v[i] = j < n ? row[j] : 0.0f;
+  for (int i = 0; i < kQuads; ++i) {
+    const int64_t j = j0 + 4 * ((int64_t)i * kSelThreads + threadIdx.x);
+    v[i] = j < n ? *reinterpret_cast<const float4*>(row + j) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
 #pragma unroll
-  for (int i = 0; i < kPerThread; ++i) {
-    const int64_t j = j0 + (int64_t)i * kSelThreads + threadIdx.x;
-    if (j < n) atomicAdd(&lh[order_key(v[i]) >> kDigit0], 1u);
+  for (int i = 0; i < kQuads; ++i) {
+    const int64_t j = j0 + 4 * ((int64_t)i * kSelThreads + threadIdx.x);
+    const float e4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (j + e < n) atomicAdd(&lh[order_key(e4[e]) >> kDigit0], 1u);
   }
   __syncthreads();
   for (int b = threadIdx.x; b < kBins; b += kSelThreads) {
@@ -119,8 +124,9 @@ __global__ __launch_bounds__(kSelThreads) void sel_hist(const float* __restrict_
 }
 
 // One pass over the scores: the keys of a chunk in bin b or above, in index
-// order, go to the chunk's slot.  Iteration i of wavefront w covers keys
-// j0 + 256 i + 64 w + lane, so (i, w, lane) order is index order.  Every
+// order, go to the chunk's slot.  Quad i of wavefront w holds keys
+// j0 + 4 (256 i + 64 w + lane) + e, e < 4, so (i, w, lane, e) order is index
+// order.  Every
 // workgroup finds b itself from the head's histogram (read while its own
 // scores are in flight); the first chunk's records it for the resolve.
 __global__ __launch_bounds__(kSelThreads) void sel_collect(const float* __restrict__ scores, int64_t ld,
@@ -133,7 +139,8 @@ __global__ __launch_bounds__(kSelThreads) void sel_collect(const float* __restri
                                                            int64_t nchunks) {
   constexpr int NW = kSelThreads / 64;
   constexpr int kPer = kBins / kSelThreads;   // 16 bins per thread
-  __shared__ uint32_t cnt[kPerThread][NW];
+  constexpr int kQuads = kPerThread / 4;
+  __shared__ uint32_t cnt[kQuads][NW];
   __shared__ uint64_t* dst_sh;
   __shared__ uint32_t cap_sh;
   __shared__ uint32_t wsum[NW];
@@ -141,13 +148,13 @@ __global__ __launch_bounds__(kSelThreads) void sel_collect(const float* __restri
   const int h = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-  const float* row = scores + (int64_t)h * ld;
+  const float* row = scores + (int64_t)h * ld;   // rows are 256-byte aligned, padded to 64 keys
   const int64_t j0 = (int64_t)blockIdx.x * kChunk;
-  float f[kPerThread];
+  float4 f[kQuads];
 #pragma unroll
-  for (int i = 0; i < kPerThread; ++i) {
-    const int64_t j = j0 + (int64_t)i * kSelThreads + threadIdx.x;
-    f[i] = j < n ? row[j] : 0.0f;
+  for (int i = 0; i < kQuads; ++i) {
+    const int64_t j = j0 + 4 * ((int64_t)i * kSelThreads + threadIdx.x);
+    f[i] = j < n ? *reinterpret_cast<const float4*>(row + j) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   // bin b of the k-th largest key
   {
@@ -175,15 +182,20 @@ __global__ __launch_bounds__(kSelThreads) void sel_collect(const float* __restri
     state[h * 4 + 0] = bin;
     state[h * 4 + 1] = sh[1];
   }
-  uint32_t key[kPerThread];
-  uint64_t mask[kPerThread];
+  uint32_t key[kQuads][4];
+  uint64_t mask[kQuads][4];
 #pragma unroll
-  for (int i = 0; i < kPerThread; ++i) key[i] = order_key(f[i]);
+  for (int i = 0; i < kQuads; ++i) {
+    const int64_t j = j0 + 4 * ((int64_t)i * kSelThreads + threadIdx.x);
+    const float e4[4] = {f[i].x, f[i].y, f[i].z, f[i].w};
+    uint32_t c = 0;
 #pragma unroll
-  for (int i = 0; i < kPerThread; ++i) {
-    const int64_t j = j0 + (int64_t)i * kSelThreads + threadIdx.x;
-    mask[i] = __ballot(j < n && (key[i] >> kDigit0) >= bin);
-    if (lane == 0) cnt[i][w] = (uint32_t)__popcll(mask[i]);
+    for (int e = 0; e < 4; ++e) {
+      key[i][e] = order_key(e4[e]);
+      mask[i][e] = __ballot(j + e < n && (key[i][e] >> kDigit0) >= bin);
+      c += (uint32_t)__popcll(mask[i][e]);
+    }
+    if (lane == 0) cnt[i][w] = c;
   }
   __syncthreads();
   // where the chunk's keys go: its slot, or, if they do not fit there, a segment
@@ -192,7 +204,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_collect(const float* __restri
   // the head takes the resolve's full-row path)
   if (threadIdx.x == 0) {
     uint32_t tot = 0;
-    for (int i = 0; i < kPerThread; ++i)
+    for (int i = 0; i < kQuads; ++i)
       for (int x = 0; x < NW; ++x) tot += cnt[i][x];
     const int64_t c = (int64_t)h * nchunks + blockIdx.x;
     uint64_t* dst = kept + c * kSlot;
@@ -216,15 +228,21 @@ __global__ __launch_bounds__(kSelThreads) void sel_collect(const float* __restri
   // offset of (i, w): keys kept by the (i', w') pairs before it
   uint64_t* dst = dst_sh;
   const uint32_t cap = cap_sh;
+  const uint64_t lt = (1ull << lane) - 1ull;
   uint32_t run = 0;
-  for (int i = 0; i < kPerThread; ++i) {
-    uint32_t off = run;
+#pragma unroll
+  for (int i = 0; i < kQuads; ++i) {
+    uint32_t off = run;   // kept keys of the quads before (i, w, lane)
     for (int x = 0; x < w; ++x) off += cnt[i][x];
-    const uint64_t m = mask[i];
-    if ((m >> lane) & 1ull) {
-      const uint32_t pos = off + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
-      const int64_t j = j0 + (int64_t)i * kSelThreads + threadIdx.x;
-      if (pos < cap) store_global(dst + pos, ((uint64_t)key[i] << 32) | (uint32_t)j);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) off += (uint32_t)__popcll(mask[i][e] & lt);
+    const int64_t j = j0 + 4 * ((int64_t)i * kSelThreads + threadIdx.x);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if ((mask[i][e] >> lane) & 1ull) {
+        if (off < cap) store_global(dst + off, ((uint64_t)key[i][e] << 32) | (uint32_t)(j + e));
+        ++off;
+      }
     }
     for (int x = 0; x < NW; ++x) run += cnt[i][x];
   }
@@ -450,9 +468,9 @@ __global__ __launch_bounds__(kResolveThreads) void sel_resolve(const float* __re
   const int64_t c0 = min<int64_t>((int64_t)threadIdx.x * per, nchunks);
   const int64_t c1 = min<int64_t>(c0 + per, nchunks);
   uint32_t off = 0;
+  uint32_t mine = 0;   // read beside the state, not after it (the counts are always written)
+  for (int64_t c = c0; c < c1; ++c) mine += cnt_h[c];
   if (!fallback) {
-    uint32_t mine = 0;
-    for (int64_t c = c0; c < c1; ++c) mine += cnt_h[c];
     off = block_exclusive<NT>(mine, wsum, &total);
     if (!wide) {
       coff[threadIdx.x] = off;
