@@ -92,29 +92,34 @@ __device__ __forceinline__ uint32_t block_exclusive(uint32_t v, uint32_t* wsum, 
   return base + inc - v;
 }
 
+// First-digit histogram of `per` consecutive chunks per workgroup (long rows
+// take several, so that fewer workgroups flush their bins to the global one).
 __global__ __launch_bounds__(kSelThreads) void sel_hist(const float* __restrict__ scores, int64_t ld,
-                                                        int64_t n, uint32_t* __restrict__ hist) {
+                                                        int64_t n, uint32_t* __restrict__ hist, int per) {
   __shared__ uint32_t lh[kBins];
   const int h = blockIdx.y;
   for (int b = threadIdx.x; b < kBins; b += kSelThreads) lh[b] = 0u;
   __syncthreads();
   const float* row = scores + (int64_t)h * ld;   // rows are 256-byte aligned, padded to 64 keys
-  const int64_t j0 = (int64_t)blockIdx.x * kChunk;
-  // 16-byte loads: thread t counts keys j0 + 4 (t + 256 i) + e (the order does not matter here)
-  constexpr int kQuads = kPerThread / 4;
-  float4 v[kQuads];
+  for (int sc = 0; sc < per; ++sc) {
+    const int64_t j0 = ((int64_t)blockIdx.x * per + sc) * kChunk;
+    if (j0 >= n) break;
+    // 16-byte loads: thread t counts keys j0 + 4 (t + 256 i) + e (the order does not matter here)
+    constexpr int kQuads = kPerThread / 4;
+    float4 v[kQuads];
 #pragma unroll
-  for (int i = 0; i < kQuads; ++i) {
-    const int64_t j = j0 + 4 * ((int64_t)i * kSelThreads + threadIdx.x);
-    v[i] = j < n ? *reinterpret_cast<const float4*>(row + j) : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
+    for (int i = 0; i < kQuads; ++i) {
+      const int64_t j = j0 + 4 * ((int64_t)i * kSelThreads + threadIdx.x);
+      v[i] = j < n ? *reinterpret_cast<const float4*>(row + j) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
 #pragma unroll
-  for (int i = 0; i < kQuads; ++i) {
-    const int64_t j = j0 + 4 * ((int64_t)i * kSelThreads + threadIdx.x);
-    const float e4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+    for (int i = 0; i < kQuads; ++i) {
+      const int64_t j = j0 + 4 * ((int64_t)i * kSelThreads + threadIdx.x);
+      const float e4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (j + e < n) atomicAdd(&lh[order_key(e4[e]) >> kDigit0], 1u);
+      for (int e = 0; e < 4; ++e)
+        if (j + e < n) atomicAdd(&lh[order_key(e4[e]) >> kDigit0], 1u);
+    }
   }
   __syncthreads();
   for (int b = threadIdx.x; b < kBins; b += kSelThreads) {
@@ -647,7 +652,11 @@ hipError_t launch_select(const float* scores, int64_t ld, int h_q, int64_t n, in
   dim3 grid((unsigned)ws.nchunks, (unsigned)h_q);
   if (!hist_done) {
     if (!cleared) sel_init<<<h_q, kSelThreads, 0, s>>>(ws.hist, ws.state);
-    sel_hist<<<grid, kSelThreads, 0, s>>>(scores, ld, n, ws.hist);
+    // chunks per histogram workgroup: 1, or more while the grid keeps >= 4096 workgroups
+    int per = 1;
+    while (per < 8 && (ws.nchunks + 2 * per - 1) / (2 * per) * h_q >= 4096) per *= 2;
+    const dim3 hgrid((unsigned)((ws.nchunks + per - 1) / per), (unsigned)h_q);
+    sel_hist<<<hgrid, kSelThreads, 0, s>>>(scores, ld, n, ws.hist, per);
   }
   sel_collect<<<grid, kSelThreads, 0, s>>>(scores, ld, n, k, ws.hist, ws.state, ws.kept, ws.counts, ws.soff,
                                            ws.spill, ws.spill_cap, ws.nchunks);
