@@ -70,6 +70,20 @@ __device__ __forceinline__ uint4 load_global(const uint4* p) {
   return make_uint4(x.x, x.y, x.z, x.w);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wavefront, in lane order, with DPP
+// moves (no LDS round trips): shifts by 1, 2, 4, 8 within each row of 16 lanes
+// (zero fill), then lane 15 of rows 0 and 2 is added to rows 1 and 3, and lane
+// 31 to rows 2 and 3.  Every lane must be active.
+__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true);   // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true);   // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true);   // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, true);   // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return v;
+}
+
 // ---- launchers (each returns hipSuccess or the launch error) ----
 hipError_t launch_pack(const float* k, int h_kv, const Layout& L, int d, uint8_t* rec,
                        uint32_t* status, hipStream_t s);

@@ -152,16 +152,9 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t 
     }
     const int u = c < d ? u0 : 0;
     const int act = u > 0;
-    int a_inc = act, t_inc = u;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int xa = __shfl_up(a_inc, off, 64);
-      const int xt = __shfl_up(t_inc, off, 64);
-      if (lane >= off) {
-        a_inc += xa;
-        t_inc += xt;
-      }
-    }
+    // entry and chunk counts in one scan (16-bit halves: at most 64 and 256 per wave)
+    const uint32_t both = wave_inclusive_sum((uint32_t)act | (uint32_t)u << 16);
+    const int a_inc = (int)(both & 0xffffu), t_inc = (int)(both >> 16);
     if (lane == 63) {
       sm.wsum[0][wv] = a_inc;
       sm.wsum[1][wv] = t_inc;
@@ -512,12 +505,7 @@ __device__ __forceinline__ void copy_piece(const uint8_t* __restrict__ src, uint
   const int t = c < d ? (int)uni[g * d + c] : 0;
   const int64_t bytes = t > 0 ? H + (int64_t)(t - 1) * P : 0;
   const int np = (int)((bytes + kCopyPiece - 1) / kCopyPiece);
-  int inc = np;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int x = __shfl_up(inc, off, 64);
-    if (lane >= off) inc += x;
-  }
+  const int inc = (int)wave_inclusive_sum((uint32_t)np);
   if (lane == 63) sm.wsum[0][wv] = inc;
   if (tid == 0) sm.n_grp = -1;
   __syncthreads();

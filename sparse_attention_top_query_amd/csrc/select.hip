@@ -55,12 +55,8 @@ template <int NT>
 __device__ __forceinline__ uint32_t block_suffix_inclusive(uint32_t v, uint32_t* wsum) {
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-  uint32_t s = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t x = __shfl_down(s, off, 64);
-    if (lane + off < 64) s += x;
-  }
+  const uint32_t inc = wave_inclusive_sum(v);
+  const uint32_t s = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63) - inc + v;   // lanes >= this one
   __syncthreads();
   if (lane == 0) wsum[w] = s;
   __syncthreads();
@@ -74,12 +70,7 @@ template <int NT>
 __device__ __forceinline__ uint32_t block_exclusive(uint32_t v, uint32_t* wsum, uint32_t* total) {
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-  uint32_t inc = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t x = __shfl_up(inc, off, 64);
-    if (lane >= off) inc += x;
-  }
+  const uint32_t inc = wave_inclusive_sum(v);
   __syncthreads();
   if (lane == 63) wsum[w] = inc;
   __syncthreads();
@@ -561,15 +552,20 @@ __global__ __launch_bounds__(kResolveThreads) void sel_resolve(const float* __re
     __syncthreads();
   }
   const uint32_t T = prefix;
-  // ordered compaction: thread t owns kept items [kKeepPer t, kKeepPer (t+1))
+  // ordered compaction: thread t owns kept items [span t, span (t+1)), span as small
+  // as the kept count allows (short strides keep the LDS reads conflict-light)
+  const uint32_t span = (total + NT - 1) / NT;   // <= kKeepPer
+  const uint32_t x0 = threadIdx.x * span;
   uint32_t gt = 0, eq = 0;
-  uint32_t kk[kKeepPer];
+  uint64_t kv[kKeepPer];
 #pragma unroll
   for (int r = 0; r < kKeepPer; ++r) {
-    const uint32_t x = threadIdx.x * kKeepPer + r;
-    kk[r] = x < total ? (uint32_t)(buf[x] >> 32) : 0u;
-    gt += x < total && kk[r] > T;
-    eq += x < total && kk[r] == T;
+    const uint32_t x = x0 + r;
+    const bool in = (uint32_t)r < span && x < total;
+    kv[r] = in ? buf[x] : 0ull;
+    const uint32_t key = (uint32_t)(kv[r] >> 32);
+    gt += in && key > T;
+    eq += in && key == T;
   }
   // both counts in one scan, as 16-bit halves (each total is at most kKeep)
   static_assert(kKeep < 65536, "16-bit halves");
@@ -581,17 +577,17 @@ __global__ __launch_bounds__(kResolveThreads) void sel_resolve(const float* __re
   uint32_t pos = gt_before + min(eq_before, need);
 #pragma unroll
   for (int r = 0; r < kKeepPer; ++r) {
-    const uint32_t x = threadIdx.x * kKeepPer + r;
-    if (x >= total) break;
-    bool take = kk[r] > T;
-    if (kk[r] == T) {
+    if ((uint32_t)r >= span || x0 + r >= total) break;
+    const uint32_t key = (uint32_t)(kv[r] >> 32);
+    bool take = key > T;
+    if (key == T) {
       take = ties < need;
       ++ties;
     }
     if (take) {
       if (pos < (uint32_t)k) {
-        out[pos] = (int32_t)(buf[x] & 0xffffffffu);
-        if (outv) outv[pos] = key_to_float(kk[r]);
+        out[pos] = (int32_t)(kv[r] & 0xffffffffu);
+        if (outv) outv[pos] = key_to_float(key);
       }
       ++pos;
     }
