@@ -122,7 +122,7 @@ struct SelectWorkspace {
   uint32_t* soff;     // [h_q][nchunks] spill offset of a chunk whose kept keys overflow its slot
   uint64_t* kept;     // [h_q][nchunks][512] (key, index) at or above the threshold bin
   uint64_t* spill;    // [h_q][spill_cap] kept keys of overflowing chunks, one segment per chunk
-  int64_t spill_cap;  // 16384 for rows of more than 65536 keys, else 0 (no spill)
+  int64_t spill_cap;  // spill entries per head: min(16384, n)
   int64_t nchunks;
 };
 int64_t select_chunks(int64_t n);

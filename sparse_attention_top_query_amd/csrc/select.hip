@@ -20,9 +20,8 @@
 //               to T still belong to the top k, and compacts in order: keys above
 //               T and the lowest-index keys equal to T.  No sorting is needed.
 // A chunk whose kept keys overflow its slot writes them, still in index order,
-// to a segment of its head's spill area (claimed with one atomic; rows of more
-// than 65536 keys), so kept keys concentrated in a few chunks stay on the fast
-// path.  Only a head whose kept
+// to a segment of its head's spill area (claimed with one atomic), so kept keys
+// concentrated in a few chunks stay on the fast path.  Only a head whose kept
 // keys exceed the resolve's LDS buffer (16384) takes an exact in-order fallback
 // in the resolve kernel: three radix passes over its whole row find T, then one
 // ordered pass writes the selection.
@@ -600,11 +599,10 @@ size_t al256(size_t x) { return (x + 255) / 256 * 256; }
 
 int64_t select_chunks(int64_t n) { return (n + kChunk - 1) / kChunk; }
 
-// Spill entries per head (the resolve holds at most kKeep kept keys).  Rows of
-// at most 65536 keys get none: a head of theirs whose chunk overflows takes the
-// row path, four passes over at most 256 KB; a spill area would cost twice the
-// memory of their scores.
-int64_t spill_entries(int64_t n) { return n > 65536 ? kKeep : 0; }
+// Spill entries per head: the resolve holds at most kKeep kept keys, and a head
+// keeps at most its n keys.  Short rows need it most: with k = 2048 every chunk
+// of a row under 16384 keys keeps more than its slot holds.
+int64_t spill_entries(int64_t n) { return n < kKeep ? (n > 0 ? n : 1) : kKeep; }
 
 size_t select_workspace_bytes(int h_q, int64_t n, int k) {
   (void)k;
