@@ -175,3 +175,25 @@ def test_rows_of_more_than_1024_chunks(F, rising):
     for k in (1, 2048, 5000):
         idx, val = select(F, rec, dq, dep, uni, n, k)
         check_exact(idx, val, sg, k, where=f"n={n} rising={rising} k={k}")
+
+
+@pytest.mark.parametrize("n,k", [(50000, 2048), (50000, 20000), (300000, 2048)])
+def test_scores_in_a_narrow_band(F, n, k):
+    """One dominant channel puts every score within a few percent of the same
+    value (one or two first-digit bins of 1/8 octave, so more candidates than
+    the resolve holds on chip), while 15 small channels keep them apart: the
+    resolve refines the threshold over the whole row and still selects
+    exactly."""
+    rng = np.random.default_rng(n + k)
+    d = 16
+    kk = rng.standard_normal((1, n, d)).astype(np.float32)
+    kk[0, :, 0] = 1.0
+    q = np.concatenate([[1.0], 0.001 * rng.standard_normal(d - 1)]).astype(np.float32)[None]
+    s2 = np.ones((1, d), np.float32)
+    rec, _ = gpu_pack(kk)
+    dq = dev(q)
+    dep, uni = F.allocate(dq, dev(s2), 4 * d)
+    sg = F.scan_scores(rec, dq, dep, uni, n).cpu().numpy()
+    assert np.ptp(sg[0]) < 0.1 * abs(float(np.median(sg[0])))   # one narrow band
+    idx, val = select(F, rec, dq, dep, uni, n, k)
+    check_exact(idx, val, sg, k, where=f"narrow band n={n} k={k}")
