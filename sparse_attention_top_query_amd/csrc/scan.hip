@@ -15,8 +15,9 @@
 //
 // Work decomposition: one workgroup scores a tile of TB 128-key blocks of one KV
 // head for all of its G query heads; each wavefront owns 2 blocks (256 keys):
-// lanes 0-31 one block, lanes 32-63 the other, and lane l scores key l%32 of
-// each of its block's four 32-key words.
+// lanes 0-31 one block, lanes 32-63 the other, and lane l scores the 4
+// consecutive keys 4 (l%32) .. 4 (l%32) + 3 of its block, which one 32-bit
+// word of each plane row holds.
 //  1. The union depths of the KV head list the channels to read; every query
 //     head of the group is scored from the one read of the longest prefix.
 //  2. Staging, channel group by channel group (about 64 channel-planes): the
@@ -102,7 +103,6 @@ struct ScanArgs {
 // Entry word: one G-bit mask per depth t = 1..4, bit (t - 1) G + h set iff head h
 // reads exactly t planes of the channel (at most 64 bits for G <= 16).  The
 // union depth is the entry's chunk count.
-__device__ __forceinline__ uint32_t u4(const uint4& v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
 
 
 // The fused first-digit histograms live in the tile's staging memory, which is
@@ -305,9 +305,11 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t 
     if (gi + 1 < n_grp) issue(gi + 1);
 
     // ---- 3. reconstruct and accumulate.  Lane l owns block bl = 2wv + l/32 and,
-    // in it, key l%32 of each of the block's four 32-key words (sub-chunks s).
+    // in it, keys 4 (l%32) .. 4 (l%32) + 3, bits 4 (l%8) .. of the block's word
+    // (l%32)/8: a lane reads one 32-bit word per plane row (a quarter of the
+    // row), which keeps the loop's LDS reads to what it uses.
     if (kWaveBlocks * wv < nvalid) {
-      const int pos = lane & 31;
+      const int bit0 = 4 * (lane & 7);
       // the group's entries (at most 64: each starts in one of its 64 chunk
       // slots), one per lane; the loop reads them lane by lane into scalars
       // Per lane: chunk base within the group (< 128) | union depth << 8, and
@@ -336,10 +338,10 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t 
         }
         const int cb = (int)(info & 0xffu);
         const int tb = (int)((info >> 8) & 0xfu);
-        const uint4* pp = &sm.planes[cb][bl];
-        // plane words of the prefix (only the planes the union depth reads)
-        // all four rows are read (within the padded array), only tb of them used
-        const uint4 w0 = pp[0], w1 = pp[TB], w2 = pp[2 * TB], w3 = pp[3 * TB];
+        const uint32_t* pp = reinterpret_cast<const uint32_t*>(&sm.planes[cb][bl]) + ((lane & 31) >> 3);
+        // the lane's word of each plane row: all four rows are read (within the
+        // padded array), only tb of them used
+        const uint32_t w0 = pp[0], w1 = pp[4 * TB], w2 = pp[8 * TB], w3 = pp[12 * TB];
         float cf[G];
 #pragma unroll
         for (int h = 0; h < G; ++h) cf[h] = sm.coef[cb][bl][h];
@@ -361,20 +363,20 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t 
         // signed prefixes MSB first (plane 0 is stored complemented): r_1 = b_0 - 1,
         // r_{t+1} = 2 r_t + b_t
 #pragma unroll
-        for (int s2 = 0; s2 < kSub; ++s2) r[s2] = __builtin_amdgcn_sbfe((int)u4(w0, s2), pos, 1);
+        for (int s2 = 0; s2 < kSub; ++s2) r[s2] = __builtin_amdgcn_sbfe((int)w0, bit0 + s2, 1);
         constexpr Word kHeads = (Word)((1ull << G) - 1ull);
         if (word & kHeads) level(1);
         if (tb > 1) {
 #pragma unroll
-          for (int s2 = 0; s2 < kSub; ++s2) r[s2] = 2 * r[s2] + (int)__builtin_amdgcn_ubfe(u4(w1, s2), pos, 1);
+          for (int s2 = 0; s2 < kSub; ++s2) r[s2] = 2 * r[s2] + (int)__builtin_amdgcn_ubfe(w1, bit0 + s2, 1);
           if (word & (kHeads << G)) level(2);
           if (tb > 2) {
 #pragma unroll
-            for (int s2 = 0; s2 < kSub; ++s2) r[s2] = 2 * r[s2] + (int)__builtin_amdgcn_ubfe(u4(w2, s2), pos, 1);
+            for (int s2 = 0; s2 < kSub; ++s2) r[s2] = 2 * r[s2] + (int)__builtin_amdgcn_ubfe(w2, bit0 + s2, 1);
             if (word & (kHeads << (2 * G))) level(3);
             if (tb > 3) {
 #pragma unroll
-              for (int s2 = 0; s2 < kSub; ++s2) r[s2] = 2 * r[s2] + (int)__builtin_amdgcn_ubfe(u4(w3, s2), pos, 1);
+              for (int s2 = 0; s2 < kSub; ++s2) r[s2] = 2 * r[s2] + (int)__builtin_amdgcn_ubfe(w3, bit0 + s2, 1);
               level(4);
             }
           }
@@ -393,7 +395,7 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t 
   if (bl < nvalid) {
 #pragma unroll
     for (int s2 = 0; s2 < kSub; ++s2) {
-      const int64_t j = (blk0 + bl) * kBlock + s2 * 32 + (lane & 31);
+      const int64_t j = (blk0 + bl) * kBlock + 4 * (lane & 31) + s2;
       if (j < a.n) {
 #pragma unroll
         for (int h = 0; h < G; ++h) a.scores[(g * G + h) * a.ld + j] = acc[s2][h];
@@ -414,7 +416,7 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t 
       if (bl < nvalid) {
 #pragma unroll
         for (int s2 = 0; s2 < kSub; ++s2) {
-          const int64_t j = (blk0 + bl) * kBlock + s2 * 32 + (lane & 31);
+          const int64_t j = (blk0 + bl) * kBlock + 4 * (lane & 31) + s2;
           if (j < a.n) {
 #pragma unroll
             for (int hh = 0; hh < HR; ++hh) {
