@@ -63,11 +63,20 @@ template <typename T>
 __device__ __forceinline__ void store_global(T* p, T v) {
   *(__attribute__((address_space(1))) T*)p = v;
 }
-// (uint4's copy constructor takes a generic reference: load it as a vector)
+// (the HIP vector types' copies take generic references: move them as vectors)
 __device__ __forceinline__ uint4 load_global(const uint4* p) {
   typedef unsigned int v4u __attribute__((ext_vector_type(4)));
   const v4u x = *(const __attribute__((address_space(1))) v4u*)p;
   return make_uint4(x.x, x.y, x.z, x.w);
+}
+__device__ __forceinline__ void store_global(float4* p, float4 v) {
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  v4f x;
+  x.x = v.x;
+  x.y = v.y;
+  x.z = v.z;
+  x.w = v.w;
+  *(__attribute__((address_space(1))) v4f*)p = x;
 }
 
 // Inclusive prefix sum over the 64 lanes of a wavefront, in lane order, with DPP

@@ -393,12 +393,22 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t 
     for (int s = 0; s < kSub; ++s) acc[s][h] += 0.5f * half_sum[h];
   }
   if (bl < nvalid) {
+    // a lane's 4 keys are consecutive: one 16-byte store per head where the rows
+    // allow it (so a wavefront writes 1 KB runs), else one store per key
+    const int64_t j0 = (blk0 + bl) * kBlock + 4 * (lane & 31);
+    const bool vec = (a.ld & 3) == 0 && (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0;
+    if (vec && j0 + 3 < a.n) {
 #pragma unroll
-    for (int s2 = 0; s2 < kSub; ++s2) {
-      const int64_t j = (blk0 + bl) * kBlock + 4 * (lane & 31) + s2;
-      if (j < a.n) {
+      for (int h = 0; h < G; ++h)
+        store_global(reinterpret_cast<float4*>(a.scores + (g * G + h) * a.ld + j0),
+                     make_float4(acc[0][h], acc[1][h], acc[2][h], acc[3][h]));
+    } else {
 #pragma unroll
-        for (int h = 0; h < G; ++h) a.scores[(g * G + h) * a.ld + j] = acc[s2][h];
+      for (int s2 = 0; s2 < kSub; ++s2) {
+        if (j0 + s2 < a.n) {
+#pragma unroll
+          for (int h = 0; h < G; ++h) a.scores[(g * G + h) * a.ld + j0 + s2] = acc[s2][h];
+        }
       }
     }
   }
