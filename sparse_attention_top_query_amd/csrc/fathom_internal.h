@@ -126,12 +126,14 @@ hipError_t launch_scan_staged(const uint8_t* host, uint8_t* staging, const float
 // Top-k selection over scores [h_q][ld], first n entries per row.
 struct SelectWorkspace {
   uint32_t* hist;     // [h_q][4096] histogram of the top 12 key bits
-  uint32_t* state;    // [h_q][4]: threshold bin, keys above it, overflow flag, spill fill
+  uint32_t* state;    // [h_q][8]: threshold bin, keys above it, overflow flag, spill fill, and the same
+                      // four for the refinement stage's second digit
   uint32_t* counts;   // [h_q][nchunks] kept keys per 4096-key chunk
   uint32_t* soff;     // [h_q][nchunks] spill offset of a chunk whose kept keys overflow its slot
   uint64_t* kept;     // [h_q][nchunks][512] (key, index) at or above the threshold bin
   uint64_t* spill;    // [h_q][spill_cap] kept keys of overflowing chunks, one segment per chunk
   int64_t spill_cap;  // spill entries per head: min(16384, n)
+  uint32_t* hist2;    // [h_q][1024] second-digit histogram of the refinement stage (long rows), or null
   int64_t nchunks;
 };
 int64_t select_chunks(int64_t n);

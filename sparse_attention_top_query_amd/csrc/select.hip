@@ -41,12 +41,19 @@ constexpr int kResolveThreads = 1024;
 constexpr int kSlot = 512;                         // kept keys per 4096-key chunk
 constexpr int kKeep = 16384;                       // kept keys per head resolved in LDS (128 KB)
 constexpr int kKeepPer = kKeep / kResolveThreads;
+constexpr int k2ndBins = 1024;                     // second digit: the next 10 key bits
+constexpr int64_t kRefineMin = 262144;             // rows at least this long get the refinement stage
+// State per head: [0] first-digit bin b of the k-th key, [1] keys above bin b,
+// [2] spill overflow of the collect, [3] its spill counter, [4] the refined
+// second digit b2 | kRefined, [5] keys of bin b above b2, [6] spill overflow
+// of the recollect, [7] its spill counter.
+constexpr int kStateWords = 8;
+constexpr uint32_t kRefined = 0x80000000u;
 
-// state per head: [0] bin b, [1] keys above bin b, [2] overflow flag, [3] unused
 __global__ __launch_bounds__(kSelThreads) void sel_init(uint32_t* hist, uint32_t* state) {
   const int h = blockIdx.x;
   for (int b = threadIdx.x; b < kBins; b += kSelThreads) hist[(int64_t)h * kBins + b] = 0u;
-  if (threadIdx.x < 4) state[h * 4 + threadIdx.x] = 0u;
+  if (threadIdx.x < kStateWords) state[h * kStateWords + threadIdx.x] = 0u;
 }
 
 // inclusive suffix sum over the workgroup's threads (thread t gets sum over t' >= t)
@@ -118,12 +125,100 @@ __global__ __launch_bounds__(kSelThreads) void sel_hist(const float* __restrict_
   }
 }
 
-// One pass over the scores: the keys of a chunk in bin b or above, in index
-// order, go to the chunk's slot.  Quad i of wavefront w holds keys
+// Compacts the keys of chunk c of a head (its scores f, first key j0) whose
+// key >> shift is at least thr, in index order, into the chunk's slot or, if
+// they do not fit there, a segment of the head's spill area claimed with one
+// atomic on *ctr (all of the head's kept keys must fit the resolve's on-chip
+// buffer, so the area has that size; beyond it *overflow is set and the head
+// takes the resolve's full-row path).  Quad i of wavefront w holds keys
 // j0 + 4 (256 i + 64 w + lane) + e, e < 4, so (i, w, lane, e) order is index
-// order.  Every
-// workgroup finds b itself from the head's histogram (read while its own
-// scores are in flight); the first chunk's records it for the resolve.
+// order.  Called by every thread of the workgroup.
+template <int NW, int NQ>
+__device__ __forceinline__ void compact_chunk(const float4 (&f)[NQ], int64_t n, int64_t j0, int shift, uint32_t thr,
+                                              uint32_t* ctr, uint32_t* overflow, int64_t c, uint64_t* kept,
+                                              uint32_t* counts, uint32_t* soff, uint64_t* spill_h,
+                                              int64_t spill_cap, uint32_t (*cnt)[NW], uint64_t** dst_sh,
+                                              uint32_t* cap_sh) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  uint32_t key[NQ][4];
+  uint64_t mask[NQ][4];
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    const int64_t j = j0 + 4 * ((int64_t)i * kSelThreads + threadIdx.x);
+    const float e4[4] = {f[i].x, f[i].y, f[i].z, f[i].w};
+    uint32_t cc = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      key[i][e] = order_key(e4[e]);
+      mask[i][e] = __ballot(j + e < n && (key[i][e] >> shift) >= thr);
+      cc += (uint32_t)__popcll(mask[i][e]);
+    }
+    if (lane == 0) cnt[i][w] = cc;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t tot = 0;
+    for (int i = 0; i < NQ; ++i)
+      for (int x = 0; x < NW; ++x) tot += cnt[i][x];
+    uint64_t* dst = kept + c * kSlot;
+    uint32_t cap = (uint32_t)kSlot;
+    if (tot > (uint32_t)kSlot) {
+      const uint32_t base = atomicAdd(ctr, tot);
+      if ((int64_t)base + tot <= spill_cap) {
+        dst = spill_h + base;
+        cap = tot;
+        soff[c] = base;
+      } else {
+        *overflow = 1u;
+        cap = 0;
+      }
+    }
+    counts[c] = tot;
+    *dst_sh = dst;
+    *cap_sh = cap;
+  }
+  __syncthreads();
+  // offset of (i, w): keys kept by the (i', w') pairs before it
+  uint64_t* dst = *dst_sh;
+  const uint32_t cap = *cap_sh;
+  const uint64_t lt = (1ull << lane) - 1ull;
+  uint32_t run = 0;
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    uint32_t off = run;   // kept keys of the quads before (i, w, lane)
+    for (int x = 0; x < w; ++x) off += cnt[i][x];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) off += (uint32_t)__popcll(mask[i][e] & lt);
+    const int64_t j = j0 + 4 * ((int64_t)i * kSelThreads + threadIdx.x);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if ((mask[i][e] >> lane) & 1ull) {
+        if (off < cap) store_global(dst + off, ((uint64_t)key[i][e] << 32) | (uint32_t)(j + e));
+        ++off;
+      }
+    }
+    for (int x = 0; x < NW; ++x) run += cnt[i][x];
+  }
+}
+
+// The 16-byte loads of chunk c of a row (rows are 256-byte aligned and padded
+// to 64 keys, so a quad that starts inside the row is readable whole).
+template <int NQ>
+__device__ __forceinline__ void load_chunk(const float* __restrict__ row, int64_t n, int64_t c, float4 (&f)[NQ]) {
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    const int64_t j = c * kChunk + 4 * ((int64_t)i * kSelThreads + threadIdx.x);
+    f[i] = j < n ? *reinterpret_cast<const float4*>(row + j) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+}
+
+// One pass over the scores: the keys of a chunk in bin b or above go to the
+// chunk's slot (compact_chunk).  Every workgroup finds b itself from the head's
+// histogram (read while its own scores are in flight); the first chunk's
+// records it for the resolve.  With hist2 (rows long enough for the refinement
+// stage), each workgroup also clears its slice of the head's second-digit
+// histogram.
 __global__ __launch_bounds__(kSelThreads) void sel_collect(const float* __restrict__ scores, int64_t ld,
                                                            int64_t n, int k, const uint32_t* __restrict__ hist,
                                                            uint32_t* __restrict__ state,
@@ -131,7 +226,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_collect(const float* __restri
                                                            uint32_t* __restrict__ counts,
                                                            uint32_t* __restrict__ soff,
                                                            uint64_t* __restrict__ spill, int64_t spill_cap,
-                                                           int64_t nchunks) {
+                                                           int64_t nchunks, uint32_t* __restrict__ hist2) {
   constexpr int NW = kSelThreads / 64;
   constexpr int kPer = kBins / kSelThreads;   // 16 bins per thread
   constexpr int kQuads = kPerThread / 4;
@@ -141,15 +236,13 @@ __global__ __launch_bounds__(kSelThreads) void sel_collect(const float* __restri
   __shared__ uint32_t wsum[NW];
   __shared__ uint32_t sh[2];
   const int h = blockIdx.y;
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const float* row = scores + (int64_t)h * ld;   // rows are 256-byte aligned, padded to 64 keys
-  const int64_t j0 = (int64_t)blockIdx.x * kChunk;
+  const float* row = scores + (int64_t)h * ld;
   float4 f[kQuads];
-#pragma unroll
-  for (int i = 0; i < kQuads; ++i) {
-    const int64_t j = j0 + 4 * ((int64_t)i * kSelThreads + threadIdx.x);
-    f[i] = j < n ? *reinterpret_cast<const float4*>(row + j) : make_float4(0.f, 0.f, 0.f, 0.f);
+  load_chunk(row, n, blockIdx.x, f);
+  if (hist2) {
+    const int slice = (k2ndBins + (int)gridDim.x - 1) / (int)gridDim.x;
+    const int b1 = min(k2ndBins, ((int)blockIdx.x + 1) * slice);
+    for (int b = (int)blockIdx.x * slice + threadIdx.x; b < b1; b += kSelThreads) hist2[h * k2ndBins + b] = 0u;
   }
   // bin b of the k-th largest key
   {
@@ -173,73 +266,126 @@ __global__ __launch_bounds__(kSelThreads) void sel_collect(const float* __restri
     __syncthreads();
   }
   const uint32_t bin = sh[0];
+  uint32_t* st = state + h * kStateWords;
   if (blockIdx.x == 0 && threadIdx.x == 0) {
-    state[h * 4 + 0] = bin;
-    state[h * 4 + 1] = sh[1];
+    st[0] = bin;
+    st[1] = sh[1];
   }
-  uint32_t key[kQuads][4];
-  uint64_t mask[kQuads][4];
-#pragma unroll
-  for (int i = 0; i < kQuads; ++i) {
-    const int64_t j = j0 + 4 * ((int64_t)i * kSelThreads + threadIdx.x);
-    const float e4[4] = {f[i].x, f[i].y, f[i].z, f[i].w};
-    uint32_t c = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      key[i][e] = order_key(e4[e]);
-      mask[i][e] = __ballot(j + e < n && (key[i][e] >> kDigit0) >= bin);
-      c += (uint32_t)__popcll(mask[i][e]);
-    }
-    if (lane == 0) cnt[i][w] = c;
+  if (sh[1] + hist[(int64_t)h * kBins + bin] > (uint32_t)kKeep) {
+    // more candidates than the resolve holds: nothing to compact (the refinement
+    // stage or the resolve's full-row path takes the head)
+    if (blockIdx.x == 0 && threadIdx.x == 0) st[2] = 1u;
+    return;
   }
+  compact_chunk<NW>(f, n, (int64_t)blockIdx.x * kChunk, kDigit0, bin, &st[3], &st[2],
+                    (int64_t)h * nchunks + blockIdx.x, kept, counts, soff, spill + (int64_t)h * spill_cap, spill_cap,
+                    cnt, &dst_sh, &cap_sh);
+}
+
+// Refinement stage, for long rows whose first-digit bin b holds more candidates
+// than the resolve keeps on chip (scores in a narrow band: one or two bins of
+// 1/8 octave): every workgroup of such a head counts its chunk's keys of bin b
+// by their next 10 bits into the head's second-digit histogram.  Heads without
+// that need return at once.
+__global__ __launch_bounds__(kSelThreads) void sel_refine_hist(const float* __restrict__ scores, int64_t ld,
+                                                               int64_t n, const uint32_t* __restrict__ hist,
+                                                               const uint32_t* __restrict__ state,
+                                                               uint32_t* __restrict__ hist2, int64_t nchunks,
+                                                               int per) {
+  constexpr int kQuads = kPerThread / 4;
+  __shared__ uint32_t lh[k2ndBins];
+  const int h = blockIdx.y;
+  const uint32_t* st = state + h * kStateWords;
+  const uint32_t bin = st[0];
+  if (st[1] + hist[(int64_t)h * kBins + bin] <= (uint32_t)kKeep) return;
+  for (int b = threadIdx.x; b < k2ndBins; b += kSelThreads) lh[b] = 0u;
   __syncthreads();
-  // where the chunk's keys go: its slot, or, if they do not fit there, a segment
-  // of the head's spill area claimed with one atomic (all of the head's kept keys
-  // must fit the resolve's on-chip buffer, so the area has that size; beyond it
-  // the head takes the resolve's full-row path)
-  if (threadIdx.x == 0) {
-    uint32_t tot = 0;
-    for (int i = 0; i < kQuads; ++i)
-      for (int x = 0; x < NW; ++x) tot += cnt[i][x];
-    const int64_t c = (int64_t)h * nchunks + blockIdx.x;
-    uint64_t* dst = kept + c * kSlot;
-    uint32_t cap = (uint32_t)kSlot;
-    if (tot > (uint32_t)kSlot) {
-      const uint32_t base = atomicAdd(&state[h * 4 + 3], tot);
-      if ((int64_t)base + tot <= spill_cap) {
-        dst = spill + (int64_t)h * spill_cap + base;
-        cap = tot;
-        soff[c] = base;
-      } else {
-        state[h * 4 + 2] = 1u;
-        cap = 0;
+  const int64_t c1 = min<int64_t>(((int64_t)blockIdx.x + 1) * per, nchunks);
+  for (int64_t c = (int64_t)blockIdx.x * per; c < c1; ++c) {
+    float4 f[kQuads];
+    load_chunk(scores + (int64_t)h * ld, n, c, f);
+#pragma unroll
+    for (int i = 0; i < kQuads; ++i) {
+      const int64_t j = c * kChunk + 4 * ((int64_t)i * kSelThreads + threadIdx.x);
+      const float e4[4] = {f[i].x, f[i].y, f[i].z, f[i].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t key = order_key(e4[e]);
+        if (j + e < n && (key >> kDigit0) == bin) atomicAdd(&lh[(key >> 10) & (k2ndBins - 1)], 1u);
       }
     }
-    counts[c] = tot;
-    dst_sh = dst;
-    cap_sh = cap;
   }
   __syncthreads();
-  // offset of (i, w): keys kept by the (i', w') pairs before it
-  uint64_t* dst = dst_sh;
-  const uint32_t cap = cap_sh;
-  const uint64_t lt = (1ull << lane) - 1ull;
-  uint32_t run = 0;
+  for (int b = threadIdx.x; b < k2ndBins; b += kSelThreads) {
+    const uint32_t v = lh[b];
+    if (v) atomicAdd(&hist2[h * k2ndBins + b], v);
+  }
+}
+
+// Refinement stage, second pass: for the same heads, the second digit b2 of the
+// k-th key from the second-digit histogram, then every chunk's keys whose top
+// 22 bits are at least (b, b2) replace the collect's (compact_chunk, with the
+// state's second spill counter and flag).  The first chunk's workgroup records
+// b2 (marked refined) and the keys of bin b above it for the resolve.
+__global__ __launch_bounds__(kSelThreads) void sel_recollect(const float* __restrict__ scores, int64_t ld,
+                                                             int64_t n, int k, const uint32_t* __restrict__ hist,
+                                                             uint32_t* __restrict__ state,
+                                                             const uint32_t* __restrict__ hist2,
+                                                             uint64_t* __restrict__ kept,
+                                                             uint32_t* __restrict__ counts,
+                                                             uint32_t* __restrict__ soff,
+                                                             uint64_t* __restrict__ spill, int64_t spill_cap,
+                                                             int64_t nchunks, int per) {
+  constexpr int NW = kSelThreads / 64;
+  constexpr int kPer = k2ndBins / kSelThreads;   // 4 bins per thread
+  constexpr int kQuads = kPerThread / 4;
+  __shared__ uint32_t cnt[kQuads][NW];
+  __shared__ uint64_t* dst_sh;
+  __shared__ uint32_t cap_sh;
+  __shared__ uint32_t wsum[NW];
+  __shared__ uint32_t sh[2];
+  const int h = blockIdx.y;
+  uint32_t* st = state + h * kStateWords;
+  const uint32_t bin = st[0];
+  const uint32_t above = st[1];
+  if (above + hist[(int64_t)h * kBins + bin] <= (uint32_t)kKeep) return;
+  const float* row = scores + (int64_t)h * ld;
+  const int64_t c0 = (int64_t)blockIdx.x * per;
+  const int64_t c1 = min<int64_t>(c0 + per, nchunks);
+  float4 f[kQuads];
+  load_chunk(row, n, c0, f);
+  {
+    const uint32_t need = (uint32_t)k - above;
+    uint32_t hv[kPer];
+    uint32_t mine = 0;
 #pragma unroll
-  for (int i = 0; i < kQuads; ++i) {
-    uint32_t off = run;   // kept keys of the quads before (i, w, lane)
-    for (int x = 0; x < w; ++x) off += cnt[i][x];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) off += (uint32_t)__popcll(mask[i][e] & lt);
-    const int64_t j = j0 + 4 * ((int64_t)i * kSelThreads + threadIdx.x);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if ((mask[i][e] >> lane) & 1ull) {
-        if (off < cap) store_global(dst + off, ((uint64_t)key[i][e] << 32) | (uint32_t)(j + e));
-        ++off;
-      }
+    for (int i = 0; i < kPer; ++i) {
+      hv[i] = hist2[h * k2ndBins + threadIdx.x * kPer + i];
+      mine += hv[i];
     }
-    for (int x = 0; x < NW; ++x) run += cnt[i][x];
+    uint32_t ab = block_suffix_inclusive<kSelThreads>(mine, wsum) - mine;
+#pragma unroll
+    for (int i = kPer - 1; i >= 0; --i) {
+      if (ab < need && ab + hv[i] >= need) {
+        sh[0] = threadIdx.x * kPer + i;
+        sh[1] = ab;
+      }
+      ab += hv[i];
+    }
+    __syncthreads();
+  }
+  const uint32_t b2 = sh[0];
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    st[4] = b2 | kRefined;
+    st[5] = sh[1];
+  }
+  for (int64_t c = c0; c < c1; ++c) {
+    if (c > c0) {
+      __syncthreads();   // the previous chunk's counts and destination are read
+      load_chunk(row, n, c, f);
+    }
+    compact_chunk<NW>(f, n, c * kChunk, 10, (bin << 10) | b2, &st[7], &st[6], (int64_t)h * nchunks + c, kept, counts,
+                      soff, spill + (int64_t)h * spill_cap, spill_cap, cnt, &dst_sh, &cap_sh);
   }
 }
 
@@ -448,9 +594,12 @@ __global__ __launch_bounds__(kResolveThreads) void sel_resolve(const float* __re
   const float* row = scores + (int64_t)h * ld;
   int32_t* out = idx + (int64_t)h * k;
   float* outv = val ? val + (int64_t)h * k : nullptr;
-  const uint32_t bin = state[h * 4 + 0];
-  const uint32_t above = state[h * 4 + 1];
-  bool fallback = state[h * 4 + 2] != 0u;
+  const uint32_t* st = state + h * kStateWords;
+  const uint32_t bin = st[0];
+  const uint32_t above = st[1];
+  const uint32_t r2 = st[4];
+  const bool refined = (r2 & kRefined) != 0u;   // the recollect's kept keys replaced the collect's
+  bool fallback = st[refined ? 6 : 2] != 0u;
   uint32_t total = 0;
   static_assert(NT == 1024, "one of the 1024 bins of a 10-bit digit per thread");
   lh[threadIdx.x] = 0u;   // the first 10-bit digit's histogram, counted during the gather
@@ -533,9 +682,16 @@ __global__ __launch_bounds__(kResolveThreads) void sel_resolve(const float* __re
   }
   // the k-th key among the kept ones: keys above bin b are all in; among the keys
   // of bin b find the (k - above)-th largest by the next 10, then the last 10 bits
+  // (refined: the next 10 bits are b2 already, and keys of bin b above b2 are in)
   uint32_t prefix = bin, need = (uint32_t)k - above;
+  int pass0 = 0;
+  if (refined) {
+    prefix = (bin << 10) | (r2 & (uint32_t)(k2ndBins - 1));
+    need -= st[5];
+    pass0 = 1;
+  }
   __syncthreads();
-  for (int pass = 0; pass < 2; ++pass) {
+  for (int pass = pass0; pass < 2; ++pass) {
     if (pass == 1) {
       lh[threadIdx.x] = 0u;
       __syncthreads();
@@ -607,12 +763,13 @@ int64_t spill_entries(int64_t n) { return n < kKeep ? (n > 0 ? n : 1) : kKeep; }
 size_t select_workspace_bytes(int h_q, int64_t n, int k) {
   (void)k;
   const size_t nc = (size_t)select_chunks(n);
-  return al256((size_t)h_q * kBins * 4) + al256((size_t)h_q * 4 * 4) + 2 * al256((size_t)h_q * nc * 4) +
-         al256((size_t)h_q * nc * kSlot * 8) + al256((size_t)h_q * (size_t)spill_entries(n) * 8);
+  return al256((size_t)h_q * kBins * 4) + al256((size_t)h_q * kStateWords * 4) + 2 * al256((size_t)h_q * nc * 4) +
+         al256((size_t)h_q * nc * kSlot * 8) + al256((size_t)h_q * (size_t)spill_entries(n) * 8) +
+         (n >= kRefineMin ? al256((size_t)h_q * k2ndBins * 4) : 0);
 }
 
 size_t select_clear_words(int h_q) {
-  return (al256((size_t)h_q * kBins * 4) + al256((size_t)h_q * 4 * 4)) / 4;
+  return (al256((size_t)h_q * kBins * 4) + al256((size_t)h_q * kStateWords * 4)) / 4;
 }
 
 SelectWorkspace carve_select(void* base, int h_q, int64_t n, int k) {
@@ -623,7 +780,7 @@ SelectWorkspace carve_select(void* base, int h_q, int64_t n, int k) {
   ws.hist = reinterpret_cast<uint32_t*>(p);
   p += al256((size_t)h_q * kBins * 4);
   ws.state = reinterpret_cast<uint32_t*>(p);
-  p += al256((size_t)h_q * 4 * 4);
+  p += al256((size_t)h_q * kStateWords * 4);
   ws.counts = reinterpret_cast<uint32_t*>(p);
   p += al256((size_t)h_q * (size_t)ws.nchunks * 4);
   ws.soff = reinterpret_cast<uint32_t*>(p);
@@ -632,6 +789,8 @@ SelectWorkspace carve_select(void* base, int h_q, int64_t n, int k) {
   p += al256((size_t)h_q * (size_t)ws.nchunks * kSlot * 8);
   ws.spill = reinterpret_cast<uint64_t*>(p);
   ws.spill_cap = spill_entries(n);
+  p += al256((size_t)h_q * (size_t)ws.spill_cap * 8);
+  ws.hist2 = n >= kRefineMin ? reinterpret_cast<uint32_t*>(p) : nullptr;
   return ws;
 }
 
@@ -652,8 +811,17 @@ hipError_t launch_select(const float* scores, int64_t ld, int h_q, int64_t n, in
     const dim3 hgrid((unsigned)((ws.nchunks + per - 1) / per), (unsigned)h_q);
     sel_hist<<<hgrid, kSelThreads, 0, s>>>(scores, ld, n, ws.hist, per);
   }
+  const bool refine = n >= kRefineMin;
   sel_collect<<<grid, kSelThreads, 0, s>>>(scores, ld, n, k, ws.hist, ws.state, ws.kept, ws.counts, ws.soff,
-                                           ws.spill, ws.spill_cap, ws.nchunks);
+                                           ws.spill, ws.spill_cap, ws.nchunks, refine ? ws.hist2 : nullptr);
+  if (refine) {   // both return at once for heads whose candidates fit on chip
+    int rper = 1;   // chunks per workgroup: up to 8 while the grid keeps >= 1024 workgroups
+    while (rper < 8 && (ws.nchunks + 2 * rper - 1) / (2 * rper) * h_q >= 1024) rper *= 2;
+    const dim3 rgrid((unsigned)((ws.nchunks + rper - 1) / rper), (unsigned)h_q);
+    sel_refine_hist<<<rgrid, kSelThreads, 0, s>>>(scores, ld, n, ws.hist, ws.state, ws.hist2, ws.nchunks, rper);
+    sel_recollect<<<rgrid, kSelThreads, 0, s>>>(scores, ld, n, k, ws.hist, ws.state, ws.hist2, ws.kept, ws.counts,
+                                                ws.soff, ws.spill, ws.spill_cap, ws.nchunks, rper);
+  }
   sel_resolve<<<h_q, kResolveThreads, 0, s>>>(scores, ld, n, k, ws.state, ws.kept, ws.counts, ws.soff, ws.spill,
                                               ws.spill_cap, ws.nchunks, idx, val);
   return hipGetLastError();

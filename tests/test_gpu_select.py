@@ -177,12 +177,14 @@ def test_rows_of_more_than_1024_chunks(F, rising):
         check_exact(idx, val, sg, k, where=f"n={n} rising={rising} k={k}")
 
 
-@pytest.mark.parametrize("n,k", [(50000, 2048), (50000, 20000), (300000, 2048)])
+@pytest.mark.parametrize("n,k", [(50000, 2048), (50000, 20000), (300000, 2048), (300000, 30000), (1 << 20, 2048)])
 def test_scores_in_a_narrow_band(F, n, k):
     """One dominant channel puts every score within a few percent of the same
     value (one or two first-digit bins of 1/8 octave, so more candidates than
-    the resolve holds on chip), while 15 small channels keep them apart: the
-    resolve refines the threshold over the whole row and still selects
+    the resolve holds on chip), while 15 small channels keep them apart.  Short
+    rows resolve over the whole row; rows of 262144 keys or more take the
+    refinement stage (a second-digit histogram and a second collect), and k =
+    30000 keeps more than the resolve holds even then.  Every case selects
     exactly."""
     rng = np.random.default_rng(n + k)
     d = 16
@@ -197,3 +199,18 @@ def test_scores_in_a_narrow_band(F, n, k):
     assert np.ptp(sg[0]) < 0.1 * abs(float(np.median(sg[0])))   # one narrow band
     idx, val = select(F, rec, dq, dep, uni, n, k)
     check_exact(idx, val, sg, k, where=f"narrow band n={n} k={k}")
+
+
+def test_all_equal_scores_long_row(F):
+    """Budget 0 on a row long enough for the refinement stage: every key ties,
+    the refined candidates still overflow, and the full-row path takes the
+    lowest indices."""
+    n = 300000
+    kk, q, s2 = small_case(4, 1, 2, n, 16)
+    rec, _ = gpu_pack(kk)
+    dq = dev(q)
+    dep, uni = F.allocate(dq, dev(s2), 0)
+    for k in (1, 2048, 20000):
+        idx, val = select(F, rec, dq, dep, uni, n, k)
+        assert np.array_equal(idx, np.tile(np.arange(k), (2, 1)))
+        assert np.all(val == 0)
