@@ -195,7 +195,7 @@ hipError_t scan_for_select(const uint8_t* dev, const uint8_t* const* table, int6
     *cleared = *hist_done = e == hipSuccess;
   } else {
     e = fathom::launch_scan_paged(dev, table, npages, page_keys, false, q, depth, union_depth, h_kv, g, L, d, scores,
-                                  ld, sel.hist, (int64_t)fathom::select_clear_words(h_q), nullptr, s);
+                                  ld, sel.hist, (int64_t)fathom::select_clear_words(sel, h_q), nullptr, s);
     *cleared = e == hipSuccess;
   }
   return e;

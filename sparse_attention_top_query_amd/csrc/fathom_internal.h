@@ -139,9 +139,10 @@ struct SelectWorkspace {
 int64_t select_chunks(int64_t n);
 size_t select_workspace_bytes(int h_q, int64_t n, int k);
 SelectWorkspace carve_select(void* base, int h_q, int64_t n, int k);
-// Words from ws.hist that must be zero when the selection starts (histograms
-// and state); `cleared` says a previous kernel on the stream zeroed them.
-size_t select_clear_words(int h_q);
+// Words from ws.hist that must be zero when the selection starts (histograms,
+// state, and for rows long enough for the refinement stage its second-digit
+// histograms); `cleared` says a previous kernel on the stream zeroed them.
+size_t select_clear_words(const SelectWorkspace& ws, int h_q);
 // `hist_done`: earlier kernels on the stream built ws.hist (after zeroing it
 // and the per-head state); otherwise the selection builds it first, clearing
 // it unless `cleared`.

@@ -50,10 +50,12 @@ constexpr int64_t kRefineMin = 262144;             // rows at least this long ge
 constexpr int kStateWords = 8;
 constexpr uint32_t kRefined = 0x80000000u;
 
-__global__ __launch_bounds__(kSelThreads) void sel_init(uint32_t* hist, uint32_t* state) {
+__global__ __launch_bounds__(kSelThreads) void sel_init(uint32_t* hist, uint32_t* state, uint32_t* hist2) {
   const int h = blockIdx.x;
   for (int b = threadIdx.x; b < kBins; b += kSelThreads) hist[(int64_t)h * kBins + b] = 0u;
   if (threadIdx.x < kStateWords) state[h * kStateWords + threadIdx.x] = 0u;
+  if (hist2)
+    for (int b = threadIdx.x; b < k2ndBins; b += kSelThreads) hist2[(int64_t)h * k2ndBins + b] = 0u;
 }
 
 // inclusive suffix sum over the workgroup's threads (thread t gets sum over t' >= t)
@@ -235,15 +237,11 @@ __global__ __launch_bounds__(kSelThreads) void sel_collect(const float* __restri
   __shared__ uint32_t cap_sh;
   __shared__ uint32_t wsum[NW];
   __shared__ uint32_t sh[2];
+  __shared__ uint32_t lh2[k2ndBins];
   const int h = blockIdx.y;
   const float* row = scores + (int64_t)h * ld;
   float4 f[kQuads];
   load_chunk(row, n, blockIdx.x, f);
-  if (hist2) {
-    const int slice = (k2ndBins + (int)gridDim.x - 1) / (int)gridDim.x;
-    const int b1 = min(k2ndBins, ((int)blockIdx.x + 1) * slice);
-    for (int b = (int)blockIdx.x * slice + threadIdx.x; b < b1; b += kSelThreads) hist2[h * k2ndBins + b] = 0u;
-  }
   // bin b of the k-th largest key
   {
     const uint32_t* hh = hist + (int64_t)h * kBins;
@@ -272,9 +270,31 @@ __global__ __launch_bounds__(kSelThreads) void sel_collect(const float* __restri
     st[1] = sh[1];
   }
   if (sh[1] + hist[(int64_t)h * kBins + bin] > (uint32_t)kKeep) {
-    // more candidates than the resolve holds: nothing to compact (the refinement
-    // stage or the resolve's full-row path takes the head)
+    // more candidates than the resolve holds: nothing to compact.  Rows long
+    // enough for the refinement stage count the chunk's keys of bin b by their
+    // next 10 bits instead (the recollect's histogram); shorter rows take the
+    // resolve's full-row path.
     if (blockIdx.x == 0 && threadIdx.x == 0) st[2] = 1u;
+    if (hist2) {
+      uint32_t* lh = reinterpret_cast<uint32_t*>(lh2);
+      for (int b = threadIdx.x; b < k2ndBins; b += kSelThreads) lh[b] = 0u;
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < kQuads; ++i) {
+        const int64_t j = (int64_t)blockIdx.x * kChunk + 4 * ((int64_t)i * kSelThreads + threadIdx.x);
+        const float e4[4] = {f[i].x, f[i].y, f[i].z, f[i].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t key = order_key(e4[e]);
+          if (j + e < n && (key >> kDigit0) == bin) atomicAdd(&lh[(key >> 10) & (k2ndBins - 1)], 1u);
+        }
+      }
+      __syncthreads();
+      for (int b = threadIdx.x; b < k2ndBins; b += kSelThreads) {
+        const uint32_t v = lh[b];
+        if (v) atomicAdd(&hist2[h * k2ndBins + b], v);
+      }
+    }
     return;
   }
   compact_chunk<NW>(f, n, (int64_t)blockIdx.x * kChunk, kDigit0, bin, &st[3], &st[2],
@@ -284,49 +304,12 @@ __global__ __launch_bounds__(kSelThreads) void sel_collect(const float* __restri
 
 // Refinement stage, for long rows whose first-digit bin b holds more candidates
 // than the resolve keeps on chip (scores in a narrow band: one or two bins of
-// 1/8 octave): every workgroup of such a head counts its chunk's keys of bin b
-// by their next 10 bits into the head's second-digit histogram.  Heads without
-// that need return at once.
-__global__ __launch_bounds__(kSelThreads) void sel_refine_hist(const float* __restrict__ scores, int64_t ld,
-                                                               int64_t n, const uint32_t* __restrict__ hist,
-                                                               const uint32_t* __restrict__ state,
-                                                               uint32_t* __restrict__ hist2, int64_t nchunks,
-                                                               int per) {
-  constexpr int kQuads = kPerThread / 4;
-  __shared__ uint32_t lh[k2ndBins];
-  const int h = blockIdx.y;
-  const uint32_t* st = state + h * kStateWords;
-  const uint32_t bin = st[0];
-  if (st[1] + hist[(int64_t)h * kBins + bin] <= (uint32_t)kKeep) return;
-  for (int b = threadIdx.x; b < k2ndBins; b += kSelThreads) lh[b] = 0u;
-  __syncthreads();
-  const int64_t c1 = min<int64_t>(((int64_t)blockIdx.x + 1) * per, nchunks);
-  for (int64_t c = (int64_t)blockIdx.x * per; c < c1; ++c) {
-    float4 f[kQuads];
-    load_chunk(scores + (int64_t)h * ld, n, c, f);
-#pragma unroll
-    for (int i = 0; i < kQuads; ++i) {
-      const int64_t j = c * kChunk + 4 * ((int64_t)i * kSelThreads + threadIdx.x);
-      const float e4[4] = {f[i].x, f[i].y, f[i].z, f[i].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t key = order_key(e4[e]);
-        if (j + e < n && (key >> kDigit0) == bin) atomicAdd(&lh[(key >> 10) & (k2ndBins - 1)], 1u);
-      }
-    }
-  }
-  __syncthreads();
-  for (int b = threadIdx.x; b < k2ndBins; b += kSelThreads) {
-    const uint32_t v = lh[b];
-    if (v) atomicAdd(&hist2[h * k2ndBins + b], v);
-  }
-}
-
-// Refinement stage, second pass: for the same heads, the second digit b2 of the
-// k-th key from the second-digit histogram, then every chunk's keys whose top
-// 22 bits are at least (b, b2) replace the collect's (compact_chunk, with the
-// state's second spill counter and flag).  The first chunk's workgroup records
-// b2 (marked refined) and the keys of bin b above it for the resolve.
+// 1/8 octave): the collect has counted the keys of bin b by their next 10 bits;
+// here the second digit b2 of the k-th key comes from that histogram, then
+// every chunk's keys whose top 22 bits are at least (b, b2) are compacted
+// (compact_chunk, with the state's second spill counter and flag).  The first
+// chunk's workgroup records b2 (marked refined) and the keys of bin b above it
+// for the resolve.  Heads without that need return at once.
 __global__ __launch_bounds__(kSelThreads) void sel_recollect(const float* __restrict__ scores, int64_t ld,
                                                              int64_t n, int k, const uint32_t* __restrict__ hist,
                                                              uint32_t* __restrict__ state,
@@ -760,16 +743,21 @@ int64_t select_chunks(int64_t n) { return (n + kChunk - 1) / kChunk; }
 // of a row under 16384 keys keeps more than its slot holds.
 int64_t spill_entries(int64_t n) { return n < kKeep ? (n > 0 ? n : 1) : kKeep; }
 
+// The words that must be zero when the selection starts lead the workspace:
+// histograms, state, and for long rows the second-digit histograms.
+static size_t hist2_bytes(int h_q, int64_t n) { return n >= kRefineMin ? al256((size_t)h_q * k2ndBins * 4) : 0; }
+
 size_t select_workspace_bytes(int h_q, int64_t n, int k) {
   (void)k;
   const size_t nc = (size_t)select_chunks(n);
-  return al256((size_t)h_q * kBins * 4) + al256((size_t)h_q * kStateWords * 4) + 2 * al256((size_t)h_q * nc * 4) +
-         al256((size_t)h_q * nc * kSlot * 8) + al256((size_t)h_q * (size_t)spill_entries(n) * 8) +
-         (n >= kRefineMin ? al256((size_t)h_q * k2ndBins * 4) : 0);
+  return al256((size_t)h_q * kBins * 4) + al256((size_t)h_q * kStateWords * 4) + hist2_bytes(h_q, n) +
+         2 * al256((size_t)h_q * nc * 4) + al256((size_t)h_q * nc * kSlot * 8) +
+         al256((size_t)h_q * (size_t)spill_entries(n) * 8);
 }
 
-size_t select_clear_words(int h_q) {
-  return (al256((size_t)h_q * kBins * 4) + al256((size_t)h_q * kStateWords * 4)) / 4;
+size_t select_clear_words(const SelectWorkspace& ws, int h_q) {
+  return (al256((size_t)h_q * kBins * 4) + al256((size_t)h_q * kStateWords * 4) +
+          (ws.hist2 ? al256((size_t)h_q * k2ndBins * 4) : 0)) / 4;
 }
 
 SelectWorkspace carve_select(void* base, int h_q, int64_t n, int k) {
@@ -781,6 +769,8 @@ SelectWorkspace carve_select(void* base, int h_q, int64_t n, int k) {
   p += al256((size_t)h_q * kBins * 4);
   ws.state = reinterpret_cast<uint32_t*>(p);
   p += al256((size_t)h_q * kStateWords * 4);
+  ws.hist2 = n >= kRefineMin ? reinterpret_cast<uint32_t*>(p) : nullptr;
+  p += hist2_bytes(h_q, n);
   ws.counts = reinterpret_cast<uint32_t*>(p);
   p += al256((size_t)h_q * (size_t)ws.nchunks * 4);
   ws.soff = reinterpret_cast<uint32_t*>(p);
@@ -789,13 +779,11 @@ SelectWorkspace carve_select(void* base, int h_q, int64_t n, int k) {
   p += al256((size_t)h_q * (size_t)ws.nchunks * kSlot * 8);
   ws.spill = reinterpret_cast<uint64_t*>(p);
   ws.spill_cap = spill_entries(n);
-  p += al256((size_t)h_q * (size_t)ws.spill_cap * 8);
-  ws.hist2 = n >= kRefineMin ? reinterpret_cast<uint32_t*>(p) : nullptr;
   return ws;
 }
 
 hipError_t launch_select_clear(const SelectWorkspace& ws, int h_q, hipStream_t s) {
-  sel_init<<<h_q, kSelThreads, 0, s>>>(ws.hist, ws.state);
+  sel_init<<<h_q, kSelThreads, 0, s>>>(ws.hist, ws.state, ws.hist2);
   return hipGetLastError();
 }
 
@@ -804,7 +792,7 @@ hipError_t launch_select(const float* scores, int64_t ld, int h_q, int64_t n, in
   if (k == 0 || n == 0 || h_q == 0) return hipSuccess;
   dim3 grid((unsigned)ws.nchunks, (unsigned)h_q);
   if (!hist_done) {
-    if (!cleared) sel_init<<<h_q, kSelThreads, 0, s>>>(ws.hist, ws.state);
+    if (!cleared) sel_init<<<h_q, kSelThreads, 0, s>>>(ws.hist, ws.state, ws.hist2);
     // chunks per histogram workgroup: 1, or more while the grid keeps >= 4096 workgroups
     int per = 1;
     while (per < 8 && (ws.nchunks + 2 * per - 1) / (2 * per) * h_q >= 4096) per *= 2;
@@ -814,11 +802,10 @@ hipError_t launch_select(const float* scores, int64_t ld, int h_q, int64_t n, in
   const bool refine = n >= kRefineMin;
   sel_collect<<<grid, kSelThreads, 0, s>>>(scores, ld, n, k, ws.hist, ws.state, ws.kept, ws.counts, ws.soff,
                                            ws.spill, ws.spill_cap, ws.nchunks, refine ? ws.hist2 : nullptr);
-  if (refine) {   // both return at once for heads whose candidates fit on chip
+  if (refine) {   // returns at once for heads whose candidates fit on chip
     int rper = 1;   // chunks per workgroup: up to 8 while the grid keeps >= 1024 workgroups
     while (rper < 8 && (ws.nchunks + 2 * rper - 1) / (2 * rper) * h_q >= 1024) rper *= 2;
     const dim3 rgrid((unsigned)((ws.nchunks + rper - 1) / rper), (unsigned)h_q);
-    sel_refine_hist<<<rgrid, kSelThreads, 0, s>>>(scores, ld, n, ws.hist, ws.state, ws.hist2, ws.nchunks, rper);
     sel_recollect<<<rgrid, kSelThreads, 0, s>>>(scores, ld, n, k, ws.hist, ws.state, ws.hist2, ws.kept, ws.counts,
                                                 ws.soff, ws.spill, ws.spill_cap, ws.nchunks, rper);
   }
