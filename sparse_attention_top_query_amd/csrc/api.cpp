@@ -187,6 +187,11 @@ hipError_t scan_for_select(const uint8_t* dev, const uint8_t* const* table, int6
                            const fathom::SelectWorkspace& sel, bool* cleared, bool* hist_done, hipStream_t s) {
   const int g = h_q / h_kv;
   hipError_t e;
+  if (sel.small) {   // the selection builds no histogram and needs no clearing
+    *cleared = *hist_done = false;
+    return fathom::launch_scan_paged(dev, table, npages, page_keys, host, q, depth, union_depth, h_kv, g, L, d, scores,
+                                     ld, nullptr, 0, nullptr, s);
+  }
   if (host) {
     e = fathom::launch_select_clear(sel, h_q, s);
     if (e == hipSuccess)

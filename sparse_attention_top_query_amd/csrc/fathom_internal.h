@@ -135,6 +135,7 @@ struct SelectWorkspace {
   int64_t spill_cap;  // spill entries per head: min(16384, n)
   uint32_t* hist2;    // [h_q][1024] second-digit histogram of the refinement stage (long rows), or null
   int64_t nchunks;
+  bool small;         // rows of at most 16384 keys: one launch, selecting in LDS, needs none of the above
 };
 int64_t select_chunks(int64_t n);
 size_t select_workspace_bytes(int h_q, int64_t n, int k);

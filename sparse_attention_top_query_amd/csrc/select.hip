@@ -48,6 +48,7 @@ constexpr int64_t kRefineMin = 262144;             // rows at least this long ge
 // second digit b2 | kRefined, [5] keys of bin b above b2, [6] spill overflow
 // of the recollect, [7] its spill counter.
 constexpr int kStateWords = 8;
+constexpr int kSmallRow = 16384;                   // rows up to this long are selected by sel_small
 constexpr uint32_t kRefined = 0x80000000u;
 
 __global__ __launch_bounds__(kSelThreads) void sel_init(uint32_t* hist, uint32_t* state, uint32_t* hist2) {
@@ -732,6 +733,89 @@ __global__ __launch_bounds__(kResolveThreads) void sel_resolve(const float* __re
   }
 }
 
+// Rows of at most kSmallRow keys: one workgroup per head holds the row's keys
+// in LDS and runs the whole radix select there (first 12-bit digit, then two
+// 10-bit digits, each counted over LDS), then the ordered compaction: one
+// launch instead of histogram, collect and resolve.
+__global__ __launch_bounds__(kResolveThreads) void sel_small(const float* __restrict__ scores, int64_t ld,
+                                                             int n, int k, int32_t* __restrict__ idx,
+                                                             float* __restrict__ val) {
+  constexpr int NT = kResolveThreads;
+  constexpr int kSpan = kSmallRow / NT;
+  __shared__ uint32_t keys[kSmallRow];
+  __shared__ uint32_t lh[kBins];
+  __shared__ uint32_t wsum[NT / 64];
+  __shared__ uint32_t sh[2];
+  const int h = blockIdx.x;
+  const float* row = scores + (int64_t)h * ld;   // 256-byte aligned rows padded to 64 keys
+  int32_t* out = idx + (int64_t)h * k;
+  float* outv = val ? val + (int64_t)h * k : nullptr;
+  for (int q = threadIdx.x; 4 * q < n; q += NT) {
+    const float4 v = *reinterpret_cast<const float4*>(row + 4 * q);
+    const float e4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (4 * q + e < n) keys[4 * q + e] = order_key(e4[e]);
+  }
+  for (int b = threadIdx.x; b < kBins; b += NT) lh[b] = 0u;
+  __syncthreads();
+  for (int x = threadIdx.x; x < n; x += NT) atomicAdd(&lh[keys[x] >> kDigit0], 1u);
+  __syncthreads();
+  find_bin<NT, kBins>(lh, (uint32_t)k, wsum, sh);
+  uint32_t prefix = sh[0], need = (uint32_t)k - sh[1];
+  __syncthreads();
+  // two 10-bit digits among the keys that share the prefix found so far
+  for (int shift = 10; shift >= 0; shift -= 10) {
+    lh[threadIdx.x] = 0u;
+    __syncthreads();
+    for (int x = threadIdx.x; x < n; x += NT) {
+      const uint32_t key = keys[x];
+      if ((key >> (shift + 10)) == prefix) atomicAdd(&lh[(key >> shift) & 1023u], 1u);
+    }
+    __syncthreads();
+    find_bin<NT, 1024>(lh, need, wsum, sh);
+    prefix = (prefix << 10) | sh[0];
+    need -= sh[1];
+    __syncthreads();
+  }
+  const uint32_t T = prefix;
+  // ordered compaction: thread t owns keys [span t, span (t+1))
+  const int span = (n + NT - 1) / NT;   // <= kSpan
+  const int x0 = threadIdx.x * span;
+  uint32_t gt = 0, eq = 0;
+#pragma unroll
+  for (int r = 0; r < kSpan; ++r) {
+    const int x = x0 + r;
+    if (r < span && x < n) {
+      gt += keys[x] > T;
+      eq += keys[x] == T;
+    }
+  }
+  uint32_t tot = 0;
+  const uint32_t before = block_exclusive<NT>((gt << 16) | eq, wsum, &tot);
+  const uint32_t eq_before = before & 0xffffu;
+  uint32_t ties = eq_before;
+  uint32_t pos = (before >> 16) + min(eq_before, need);
+#pragma unroll
+  for (int r = 0; r < kSpan; ++r) {
+    const int x = x0 + r;
+    if (r >= span || x >= n) break;
+    const uint32_t key = keys[x];
+    bool take = key > T;
+    if (key == T) {
+      take = ties < need;
+      ++ties;
+    }
+    if (take) {
+      if (pos < (uint32_t)k) {
+        out[pos] = x;
+        if (outv) outv[pos] = key_to_float(key);
+      }
+      ++pos;
+    }
+  }
+}
+
 size_t al256(size_t x) { return (x + 255) / 256 * 256; }
 
 }  // namespace
@@ -779,6 +863,7 @@ SelectWorkspace carve_select(void* base, int h_q, int64_t n, int k) {
   p += al256((size_t)h_q * (size_t)ws.nchunks * kSlot * 8);
   ws.spill = reinterpret_cast<uint64_t*>(p);
   ws.spill_cap = spill_entries(n);
+  ws.small = n <= kSmallRow;
   return ws;
 }
 
@@ -790,6 +875,10 @@ hipError_t launch_select_clear(const SelectWorkspace& ws, int h_q, hipStream_t s
 hipError_t launch_select(const float* scores, int64_t ld, int h_q, int64_t n, int k, int32_t* idx,
                          float* val, const SelectWorkspace& ws, bool cleared, bool hist_done, hipStream_t s) {
   if (k == 0 || n == 0 || h_q == 0) return hipSuccess;
+  if (n <= kSmallRow) {
+    sel_small<<<h_q, kResolveThreads, 0, s>>>(scores, ld, (int)n, k, idx, val);
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)ws.nchunks, (unsigned)h_q);
   if (!hist_done) {
     if (!cleared) sel_init<<<h_q, kSelThreads, 0, s>>>(ws.hist, ws.state, ws.hist2);
