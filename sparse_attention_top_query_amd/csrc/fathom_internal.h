@@ -132,7 +132,7 @@ struct SelectWorkspace {
   uint32_t* soff;     // [h_q][nchunks] spill offset of a chunk whose kept keys overflow its slot
   uint64_t* kept;     // [h_q][nchunks][512] (key, index) at or above the threshold bin
   uint64_t* spill;    // [h_q][spill_cap] kept keys of overflowing chunks, one segment per chunk
-  int64_t spill_cap;  // spill entries per head: min(16384, n)
+  int64_t spill_cap;  // spill entries per head: 16384 (0 for rows of at most 16384 keys)
   uint32_t* hist2;    // [h_q][1024] second-digit histogram of the refinement stage (long rows), or null
   int64_t nchunks;
   bool small;         // rows of at most 16384 keys: one launch, selecting in LDS, needs none of the above

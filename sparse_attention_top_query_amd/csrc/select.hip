@@ -822,10 +822,9 @@ size_t al256(size_t x) { return (x + 255) / 256 * 256; }
 
 int64_t select_chunks(int64_t n) { return (n + kChunk - 1) / kChunk; }
 
-// Spill entries per head: the resolve holds at most kKeep kept keys, and a head
-// keeps at most its n keys.  Short rows need it most: with k = 2048 every chunk
-// of a row under 16384 keys keeps more than its slot holds.
-int64_t spill_entries(int64_t n) { return n < kKeep ? (n > 0 ? n : 1) : kKeep; }
+// Spill entries per head: the resolve holds at most kKeep kept keys (rows of at
+// most kSmallRow keys are selected by sel_small and need none).
+int64_t spill_entries(int64_t n) { return n <= kSmallRow ? 0 : kKeep; }
 
 // The words that must be zero when the selection starts lead the workspace:
 // histograms, state, and for long rows the second-digit histograms.
