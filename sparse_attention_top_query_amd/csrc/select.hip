@@ -21,10 +21,14 @@
 //               T and the lowest-index keys equal to T.  No sorting is needed.
 // A chunk whose kept keys overflow its slot writes them, still in index order,
 // to a segment of its head's spill area (claimed with one atomic), so kept keys
-// concentrated in a few chunks stay on the fast path.  Only a head whose kept
-// keys exceed the resolve's LDS buffer (16384) takes an exact in-order fallback
-// in the resolve kernel: three radix passes over its whole row find T, then one
-// ordered pass writes the selection.
+// concentrated in a few chunks stay on the fast path.  A head whose candidates
+// (the keys in bin b or above) exceed the resolve's LDS buffer (16384) is known
+// from the histogram: in rows of 262144 keys or more the collect counts its bin
+// b keys by their next 10 bits and a recollect keeps the keys whose top 22 bits
+// reach the refined threshold; otherwise, or if those still overflow, the
+// resolve takes an exact in-order fallback: radix passes over the whole row
+// find T, then one ordered pass writes the selection.  Rows of at most 16384
+// keys skip all of this: sel_small selects each in LDS in one launch.
 #include <algorithm>
 
 #include "fathom_internal.h"
