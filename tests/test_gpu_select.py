@@ -177,7 +177,8 @@ def test_rows_of_more_than_1024_chunks(F, rising):
         check_exact(idx, val, sg, k, where=f"n={n} rising={rising} k={k}")
 
 
-@pytest.mark.parametrize("n,k", [(50000, 2048), (50000, 20000), (300000, 2048), (300000, 30000), (1 << 20, 2048)])
+@pytest.mark.parametrize("n,k", [(50000, 2048), (50000, 20000), (262143, 2048), (262144, 2048), (300000, 2048),
+                                 (300000, 30000), (1 << 20, 2048)])
 def test_scores_in_a_narrow_band(F, n, k):
     """One dominant channel puts every score within a few percent of the same
     value (one or two first-digit bins of 1/8 octave, so more candidates than
@@ -214,3 +215,25 @@ def test_all_equal_scores_long_row(F):
         idx, val = select(F, rec, dq, dep, uni, n, k)
         assert np.array_equal(idx, np.tile(np.arange(k), (2, 1)))
         assert np.all(val == 0)
+
+
+@pytest.mark.parametrize("n", [16384, 16385])
+@pytest.mark.parametrize("residency", ["hbm", "host"])
+def test_rows_at_the_one_launch_limit(F, n, residency):
+    """Rows of 16384 keys are selected in one launch per head with the row in
+    LDS, rows of 16385 by the chunked kernels: both select exactly, k from 1 to
+    n."""
+    h_kv, g, d, budget = 2, 4, 64, 40
+    kk, q, s2 = small_case(n + 3, h_kv, g, n, d, outliers=2)
+    rec, st = gpu_pack(kk)
+    assert st == 0
+    if residency == "host":
+        rec = rec.cpu().pin_memory()
+    res = F.HBM if residency == "hbm" else F.HOST_DIRECT
+    dq = dev(q)
+    dep, uni = F.allocate(dq, dev(s2), budget)
+    sg = F.scan_scores(rec, dq, dep, uni, n, residency=res).cpu().numpy()
+    for k in (1, 2048, 5000, n):
+        idx, val = F.scan_topk(rec, dq, dep, uni, n, k, residency=res, want_scores=True)
+        torch.cuda.synchronize()
+        check_exact(idx.cpu().numpy(), val.cpu().numpy(), sg, k, where=f"n={n} {residency} k={k}")
