@@ -36,6 +36,25 @@ Parity status (what pins it, in tests/test_oracle_attention.py):
                         not overflow; skipped indices equal the valid subset.
   attention_tolerance   derived from the fp32 arithmetic of the GPU kernel
                         (see its docstring); not a pin.
+  topk_recall           pinned: identical, disjoint and half-overlapping sets
+                        (exact fractions), order independence.
+  attention_error       pinned: 0 for the full index set and for constant
+                        value rows; the two-key closed form (one key kept:
+                        error = p_1 |V_1 - V_0| / |o|, p from scipy's
+                        softmax); value rows e_0 on the kept keys and e_1 on
+                        the others at q = 0, where the error is
+                        sqrt(2) (1 - m) / sqrt(m^2 + (1 - m)^2) for the kept
+                        share m = |S| / n.
+
+Fidelity metrics.  The pages report "attention error" against full attention
+and the recovery of the exact top-k (every per-token scan matching exact top-k
+decoding on RULER-style tasks), measured on a real model ([Abstract];
+[Digest] Experiments: design and key findings), without formulas.  Readings taken, for seeded synthetic
+caches: attention error is the relative L2 distance of the query's attention
+over the selected keys from its attention over all n keys, both with the same
+bf16 K/V rows; recall is the fraction of the exact top-k (largest q . K_j with
+K the unquantised fp32 keys, lowest index first on ties) that the selection
+contains.
 """
 
 from __future__ import annotations
@@ -103,3 +122,24 @@ def attention_tolerance(q, k_rows, v_rows, idx, scale, chain: int = 128):
     tau_o = 4 * (2 * eta + 2 * chain * u) * pv
     tau_lse = 4 * (e_s + eta + chain * u + 2 * u * abs(lse))
     return tau_o, tau_lse
+
+
+def topk_recall(idx: np.ndarray, exact_idx: np.ndarray) -> float:
+    """|S & S*| / |S*|: the share of the exact top-k index set S* that the
+    selection S contains (both index sets, duplicates not allowed)."""
+    exact = np.asarray(exact_idx, dtype=np.int64)
+    if exact.size == 0:
+        return 1.0
+    hit = np.intersect1d(np.asarray(idx, dtype=np.int64), exact, assume_unique=True)
+    return hit.size / exact.size
+
+
+def attention_error(q: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray, idx: np.ndarray,
+                    scale: float, full=None) -> float:
+    """|o_S - o_all| / |o_all| (Euclidean norms over the d channels): o_S is the
+    attention of q over the keys idx, o_all over all n keys of the same rows.
+    ``full`` may pass a precomputed o_all."""
+    n = k_rows.shape[0]
+    o_all = sparse_attention(q, k_rows, v_rows, np.arange(n), scale)[0] if full is None else full
+    o_s = sparse_attention(q, k_rows, v_rows, idx, scale)[0]
+    return float(np.linalg.norm(o_s - o_all) / np.linalg.norm(o_all))

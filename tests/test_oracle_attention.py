@@ -147,3 +147,55 @@ def test_tolerance_is_positive_and_scales_with_the_values():
     assert np.all(t1 > 0) and l1 > 0
     np.testing.assert_allclose(t2, 4 * t1, rtol=1e-12)
     assert np.all(t1 < 1e-3)
+
+
+# ---- fidelity metrics --------------------------------------------------------
+
+def test_recall_exact_fractions():
+    exact = np.array([3, 10, 11, 40])
+    assert A.topk_recall(exact, exact) == 1.0
+    assert A.topk_recall(np.array([0, 1, 2, 5]), exact) == 0.0
+    assert A.topk_recall(np.array([40, 0, 3, 7]), exact) == 0.5
+    assert A.topk_recall(np.array([7, 3, 0, 40]), exact) == 0.5          # order does not matter
+    assert A.topk_recall(np.array([11]), exact) == 0.25
+    assert A.topk_recall(np.array([], dtype=np.int64), np.array([], dtype=np.int64)) == 1.0
+
+
+def test_attention_error_is_zero_for_the_full_set_and_for_constant_values():
+    rng = np.random.default_rng(8)
+    n, d = 257, 32
+    kr, vr = rows(rng, n, d), rows(rng, n, d)
+    q = rng.standard_normal(d).astype(np.float32)
+    assert A.attention_error(q, kr, vr, np.arange(n), 0.3) == 0.0
+    const = np.tile(to_bf16_bits(rng.standard_normal(d).astype(np.float32)), (n, 1))
+    for idx in (np.array([0]), np.arange(0, n, 7), np.array([n - 1, 5])):
+        assert A.attention_error(q, kr, const, idx, 0.3) < 1e-15
+
+
+def test_attention_error_two_keys_closed_form():
+    rng = np.random.default_rng(9)
+    d = 16
+    kr, vr = rows(rng, 2, d), rows(rng, 2, d)
+    q = rng.standard_normal(d).astype(np.float32)
+    scale = 0.25
+    kk, vv = A.bf16_to_f64(kr), A.bf16_to_f64(vr)
+    p = scipy.special.softmax(scale * (kk @ q.astype(np.float64)))
+    o = p[0] * vv[0] + p[1] * vv[1]
+    want = p[1] * np.linalg.norm(vv[1] - vv[0]) / np.linalg.norm(o)
+    got = A.attention_error(q, kr, vr, np.array([0]), scale)
+    assert got == pytest.approx(want, rel=1e-12)
+
+
+def test_attention_error_one_hot_values_at_zero_query():
+    n, d = 96, 4
+    kr = rows(np.random.default_rng(10), n, d)
+    q = np.zeros(d, np.float32)                       # uniform weights 1/n
+    for kept in ([0], [5, 17, 80], list(range(0, 96, 2)), list(range(95))):
+        e0 = np.array([1, 0, 0, 0], np.float32)
+        e1 = np.array([0, 1, 0, 0], np.float32)
+        v = np.tile(e1, (n, 1))
+        v[kept] = e0
+        m = Fraction(len(kept), n)
+        want = np.sqrt(2.0) * float(1 - m) / np.sqrt(float(m * m + (1 - m) * (1 - m)))
+        got = A.attention_error(q, kr, to_bf16_bits(v), np.array(kept), 1.0)
+        assert got == pytest.approx(want, rel=1e-13)
