@@ -885,9 +885,10 @@ hipError_t launch_select(const float* scores, int64_t ld, int h_q, int64_t n, in
   dim3 grid((unsigned)ws.nchunks, (unsigned)h_q);
   if (!hist_done) {
     if (!cleared) sel_init<<<h_q, kSelThreads, 0, s>>>(ws.hist, ws.state, ws.hist2);
-    // chunks per histogram workgroup: 1, or more while the grid keeps >= 4096 workgroups
+    // chunks per histogram workgroup: 1, or more while the grid keeps >= 1024 workgroups
+    // (4 per CU); fewer workgroups flush fewer partial histograms
     int per = 1;
-    while (per < 8 && (ws.nchunks + 2 * per - 1) / (2 * per) * h_q >= 4096) per *= 2;
+    while (per < 8 && (ws.nchunks + 2 * per - 1) / (2 * per) * h_q >= 1024) per *= 2;
     const dim3 hgrid((unsigned)((ws.nchunks + per - 1) / per), (unsigned)h_q);
     sel_hist<<<hgrid, kSelThreads, 0, s>>>(scores, ld, n, ws.hist, per);
   }
