@@ -22,6 +22,10 @@ fp64 attention); the GPU path selects the same keys (its parity tests), so the
 figures hold for it.  CPU only:
 
     python -m tests.fidelity_report [--n 131072] [--kv-heads 8] [--k 2048]
+    python -m tests.fidelity_report --workload w3_host_1m_B92 --n 1048576 --kv-heads 1
+
+(``--workload`` picks whose seeded keys and queries are drawn; the modes and
+k stay as above.)
 """
 
 from __future__ import annotations
@@ -48,10 +52,12 @@ MODES = (
 )
 
 
-def measure(n: int = 131072, kv_heads: int = 8, k: int = 2048, modes=MODES, wl_key: int = 2):
+def measure(n: int = 131072, kv_heads: int = 8, k: int = 2048, modes=MODES,
+            workload: str = "w2_hbm_131k_B92"):
     """Per mode: (label, bits, recall [h_q], attention error [h_q]); the first
     row is the exact top-k (fp32 keys, 32 d bits)."""
-    wl = synthetic.workloads()["w2_hbm_131k_B92"]
+    wl = synthetic.workloads()[workload]
+    wl_key = wl.key
     d, g = wl.d, wl.g
     scale = 1.0 / np.sqrt(d)
     kh = np.empty((kv_heads, n, d), np.float32)
@@ -93,10 +99,13 @@ def main(argv=None) -> None:
     ap.add_argument("--n", type=int, default=131072)
     ap.add_argument("--kv-heads", type=int, default=8)
     ap.add_argument("--k", type=int, default=2048)
+    ap.add_argument("--workload", default="w2_hbm_131k_B92",
+                    choices=["w2_hbm_131k_B92", "w3_host_1m_B92", "w5_sessions_262k_B68"])
     a = ap.parse_args(argv)
     t0 = time.time()
-    res = measure(a.n, a.kv_heads, a.k)
-    print(f"n = {a.n}, {a.kv_heads} KV heads x 4 query heads, k = {a.k} ({time.time() - t0:.0f} s)")
+    res = measure(a.n, a.kv_heads, a.k, workload=a.workload)
+    print(f"{a.workload} keys: n = {a.n}, {a.kv_heads} KV heads x 4 query heads, k = {a.k} "
+          f"({time.time() - t0:.0f} s)")
     print("| mode | bits per key | recall of the exact top-k: mean (min) | attention error: mean (max) |")
     print("|---|---|---|---|")
     for label, b, rec, err in res:
