@@ -29,6 +29,15 @@ HBM_PEAK_GBPS = 8000.0     # MI355X HBM3E
 # VALU lane-operations per second: 256 CUs x 64 lanes x 2.4 GHz (packed FP32 is
 # not used, so one lane-op per lane and clock)
 VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
+# The pages' own figures (NVIDIA A100, Qwen3-8B, 4-bit K cache), quoted for
+# context only: the Fathom arXiv abstract and the thedatum.uk "Key facts".
+PAGES_CONTEXT = {
+    "hardware": "A100 (the pages' setup; not this machine)",
+    "decode_step_speedup_vs_136bit_scans_at_1M": 1.67,
+    "fewer_bytes_than_68bit_sparq_r16_at_equal_gpu_time": 0.18,
+    "bits_reaching_the_136bit_step_agreement": 92,
+    "index_resident_in_gpu_memory": "no speedup (the kernel is arithmetic-bound)",
+}
 
 # rocprofv3 summaries whose FETCH_SIZE / WRITE_SIZE figures give the measured
 # traffic of the dominant kernel, keyed by (workload, residency)
@@ -219,6 +228,34 @@ def _oracle_heads(seconds: float, first: int):
     return heads, time.perf_counter() - t0
 
 
+def host_cpu_info() -> dict:
+    """The host CPU as /proc/cpuinfo shows it: the model string, its
+    family/model/stepping numbers, and how many logical CPUs and distinct
+    physical cores (physical id, core id) this process may run on."""
+    allowed = os.sched_getaffinity(0) if hasattr(os, "sched_getaffinity") else set(range(os.cpu_count() or 1))
+    model, fms, cores, sockets = "unknown CPU", "?", set(), set()
+    try:
+        with open("/proc/cpuinfo") as f:
+            text = f.read()
+        for block in text.strip().split("\n\n"):
+            kv = {}
+            for line in block.splitlines():
+                if ":" in line:
+                    key, val = line.split(":", 1)
+                    kv[key.strip()] = val.strip()
+            if "processor" not in kv:
+                continue
+            model = kv.get("model name", model)
+            fms = f"{kv.get('cpu family', '?')}/{kv.get('model', '?')}/{kv.get('stepping', '?')}"
+            if int(kv["processor"]) in allowed:
+                cores.add((kv.get("physical id", "0"), kv.get("core id", kv["processor"])))
+                sockets.add(kv.get("physical id", "0"))
+    except (OSError, ValueError):
+        pass
+    return {"model": model, "fms": fms, "logical": len(allowed), "physical": len(cores) or None,
+            "sockets": len(sockets) or None}
+
+
 def cpu_baseline(wl, budget, seconds=15.0, workers=12):
     """The oracle timed on this host, before anything touches the GPU: the query
     heads of KV head 0 over all n keys (codes precomputed, not timed), first on
@@ -239,15 +276,14 @@ def cpu_baseline(wl, budget, seconds=15.0, workers=12):
         res = pool.starmap(_oracle_heads, [(2 * seconds / 3, i) for i in range(workers)])
     _CPU.clear()
     rate = sum(h * wl.n / dt for h, dt in res)
-    model = "unknown CPU"
-    try:
-        with open("/proc/cpuinfo") as f:
-            model = next(line.split(":", 1)[1].strip() for line in f if line.startswith("model name"))
-    except (OSError, StopIteration):
-        pass
+    info = host_cpu_info()
     return {"value": round(rate, 1), "unit": "keys/s", "cores": workers, "kind": "oracle",
             "single_core_value": round(one_heads * wl.n / one_dt, 1),
-            "host": f"{model}, {os.cpu_count()} logical CPUs visible, numpy {np.__version__}",
+            "cpu_model": info["model"], "cpu_family_model_stepping": info["fms"],
+            "logical_cpus_visible": info["logical"], "physical_cores_visible": info["physical"],
+            "sockets": info["sockets"], "numpy": np.__version__,
+            "host": f"{info['model']} (family/model/stepping {info['fms']}), {info['logical']} logical CPUs "
+                    f"on {info['physical']} physical cores visible, numpy {np.__version__}",
             "sample": f"query-head scans of the {wl.g} heads of KV head 0 x {wl.n} keys (allocation + fp64 "
                       f"scores + top-{wl.k}, codes precomputed), numpy single-threaded per process: "
                       f"{sum(h for h, _ in res)} scans on {workers} forked processes in "
@@ -452,10 +488,13 @@ def main():
         # records in HBM: the reconstruction's VALU work bounds the scan, not HBM
         ops = algorithmic_ops(depth.cpu().numpy(), union_np, n)
         tops = ops / (scan_ms * 1e-3) / 1e12
-        roof = {"bound": "alu", "achieved": round(tops, 3), "peak": round(VALU_PEAK_TOPS, 2),
-                "unit": "T lane-op/s", "frac": round(tops / VALU_PEAK_TOPS, 4), **common,
-                "ops_per_launch": ops, "hbm_achieved_gbps": round(achieved, 2),
-                "hbm_frac": round(achieved / HBM_PEAK_GBPS, 4), "record_copies_cycled": len(copies)}
+        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), **common,
+                "limiter": "alu: the reconstruction's vector work, not HBM, sets the scan's time",
+                "alu_achieved": round(tops, 3), "alu_peak": round(VALU_PEAK_TOPS, 2), "alu_unit": "T lane-op/s",
+                "alu_frac": round(tops / VALU_PEAK_TOPS, 4), "ops_per_launch": ops,
+                "ns_per_kv_head_key": round(scan_ms * 1e6 / (hk * n), 5),
+                "record_copies_cycled": len(copies)}
     # The pages compare the method against fixed-depth scans: 136 bits (34
     # channels x 4 planes) and 68 bits (17 x 4), channels by largest |q_c|.
     # Same records, queries and stream, timed the same way.
@@ -463,8 +502,10 @@ def main():
     if not args.no_compare:
         def timed(b, m, steps):
             def one():
+                rec = copies[it[0] % len(copies)]   # HBM: cycled like the step's, so not cache-resident
+                it[0] += 1
                 F.allocate(q, s2, b, mode=m, depth=depth, union_depth=uni)
-                F.scan_topk(records, q, depth, uni, n, k, residency=residency, workspace=ws, idx=idx)
+                F.scan_topk(rec, q, depth, uni, n, k, residency=residency, workspace=ws, idx=idx)
             for _ in range(2):
                 one()
             torch.cuda.synchronize(dev)
@@ -679,6 +720,7 @@ def main():
                    "mode": wl.mode},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "pages_context": PAGES_CONTEXT,
         "comparison": comparison,
         "attention": attention,
         "append": append,

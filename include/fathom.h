@@ -22,7 +22,15 @@
  *     asynchronous on `stream` (a hipStream_t; NULL = the null stream) and
  *     returns after validating its arguments and enqueueing work.
  *   - The caller owns every buffer.  No call allocates device or host memory
- *     and none keeps state between calls.
+ *     and none keeps state between calls.  There is no context object to
+ *     create or destroy: the library owns no streams, events or memory, every
+ *     call enqueues on the caller's stream only (the host-staged residency too:
+ *     its copies and scans are kernels on that stream), and the device is the
+ *     one current on the calling thread.
+ *   - Non-finite inputs are reported through device status words (the
+ *     FATHOM_FLAG_* bits below), written by the kernels that read the values,
+ *     not by a return code: checking q or sigma2 on the host would need a
+ *     device-to-host copy and a synchronisation in every decode step.
  *   - Return value: FATHOM_OK or a negative fathom_status.  On a negative
  *     status nothing was enqueued and no output was written;
  *     fathom_last_error() gives a message (per calling thread).

@@ -34,8 +34,6 @@ Parity status (what pins it, in tests/test_oracle_attention.py):
                         two keys follow the logistic closed form; invariance
                         to the order of the index set; huge common logits do
                         not overflow; skipped indices equal the valid subset.
-  attention_tolerance   derived from the fp32 arithmetic of the GPU kernel
-                        (see its docstring); not a pin.
   topk_recall           pinned: identical, disjoint and half-overlapping sets
                         (exact fractions), order independence.
   attention_error       pinned: 0 for the full index set and for constant
@@ -94,34 +92,6 @@ def sparse_attention(q: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray, idx:
     p = w / total
     o = p @ bf16_to_f64(v_rows[valid])
     return o, m + np.log(total), p, valid
-
-
-def attention_tolerance(q, k_rows, v_rows, idx, scale, chain: int = 128):
-    """Bound on |o_gpu - o| per channel and on |lse_gpu - lse| for an fp32
-    kernel that forms each logit as scale * (a sum of d products with a
-    reduction chain of at most 24 roundings for d <= 256), exponentiates
-    s_j - M, and accumulates numerator and denominator along chains of at most
-    `chain` additions.  With u = 2^-24, A_j = |scale| sum_c |q_c K_jc|:
-      |ds_j| <= 26 u A_j =: e_s                      (logit)
-      relative error of each weight <= 2 e_s + u |s_j - M| + 4 u =: eta
-      |do_c| <= (2 eta + 2 chain u) sum_j p_j |V_jc|
-      |dlse| <= e_s + eta + chain u + 2 u |lse|.
-    The u |s_j - M| term is weighted by p_j <= e^-(M - s_j) in the sum, so it
-    is taken at its maximum over j of (M - s_j) e^-(M - s_j) <= 1/e per unit of
-    p.  A safety factor of 4 covers the expf error (a few ulp)."""
-    n, d = k_rows.shape
-    o, lse, p, valid = sparse_attention(q, k_rows, v_rows, idx, scale)
-    if valid.size == 0:
-        return np.zeros(d), 0.0
-    u = 2.0 ** -24
-    kk = bf16_to_f64(k_rows[valid])
-    a = abs(float(np.float32(scale))) * (np.abs(kk) @ np.abs(np.asarray(q, np.float32).astype(np.float64)))
-    e_s = 26 * u * a.max()
-    eta = 2 * e_s + u + 4 * u
-    pv = p @ np.abs(bf16_to_f64(v_rows[valid]))
-    tau_o = 4 * (2 * eta + 2 * chain * u) * pv
-    tau_lse = 4 * (e_s + eta + chain * u + 2 * u * abs(lse))
-    return tau_o, tau_lse
 
 
 def topk_recall(idx: np.ndarray, exact_idx: np.ndarray) -> float:

@@ -1,11 +1,11 @@
 // allocate_depths kernel: per-query read depth by reverse water-filling.
 //
-// Fathom abstract; ai-feeds digest, Method / key module 2: each query spreads
-// its bit budget over channels by reverse water-filling on variance-weighted
-// importance, so important channels are read deeper and unimportant ones
-// not at all.  Review "Strengths" (paper Sec 3.3): the rule follows from each
-// extra plane cutting the channel's error 4x, i.e. it minimises
-// sum_c w_c 4^(-t_c) subject to sum_c t_c = B, t_c in {0..4}.
+// Sources: the Fathom arXiv abstract and the ai-feeds digest (Method, key
+// module 2).  A query decides per channel how many planes to read; channels of
+// large importance w_c = q_c^2 sigma_c^2 get more planes, channels of small
+// importance few or none.  The evolve.pub review, "Strengths" (paper Sec 3.3),
+// derives the rule from the 4x drop in squared error per extra plane: the
+// depths minimise sum_c w_c 4^(-t_c) subject to sum_c t_c = B, t_c in {0..4}.
 //
 // One workgroup per KV head, one wavefront per query head of its group.  A
 // lane owns channels lane + 64 i, i < CPL (2 for d <= 128, else 4).
@@ -129,7 +129,9 @@ __global__ __launch_bounds__(1024) void allocate_kernel(const float* __restrict_
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
       const int c = lane + 64 * i;
-      const float v = mode == 1 ? aq[i] : (c < d ? sigma2[(int64_t)kv * d + c] : 0.0f);
+      // (sigma2 >= 0 here, so fabsf only folds -0 onto +0: the key orders values,
+      // not bit patterns)
+      const float v = mode == 1 ? aq[i] : (c < d ? fabsf(sigma2[(int64_t)kv * d + c]) : 0.0f);
       key[i] = c < d ? ((uint64_t)__float_as_uint(v) << 8 | (uint64_t)(255 - c)) : 0ull;
     }
     // a channel with |q| = +0 and c = 255 has key 0: count it via the >= test only

@@ -1,12 +1,12 @@
 // Scan kernels: reconstruct every key from its budgeted plane prefixes and
 // accumulate q . k_hat for the query heads of one KV head.
 //
-// ai-feeds digest, Method / key modules 4-5: the scan reads only the planes
-// the budget asks for and rebuilds each channel's value from the read prefix
-// (the paper's Sec 3.5 rule; its formula is not in the text, the reading here
-// is the midpoint of the prefix's cell of the t-bit mid-rise quantizer).
-// Fathom abstract: the prefix of t planes is exactly the channel's t-bit
-// quantizer, so with r_t = (code >> (4-t)) - 2^(t-1), a signed t-bit integer,
+// Sources: the ai-feeds digest, Method, key modules 4-5 (only the budgeted
+// planes are read, and each channel's value is rebuilt from what was read; the
+// paper's Sec 3.5 rule itself is not in the text, so the value taken is the
+// midpoint of the prefix's cell of the t-bit mid-rise quantizer), and the
+// Fathom arXiv abstract (a t-plane prefix is the t-bit quantizer of the
+// channel).  With r_t = (code >> (4-t)) - 2^(t-1), a signed t-bit integer,
 //   q * k_hat_t = q Delta 2^(4-t) (r_t + 1/2) = c (2 r_t + 1),  c = [q 2^(3-t) Delta],
 // and the scan accumulates it as (2c) r_t per key plus, once per block, c: with
 // c one fp32 rounding (2c exact), every term is bounded by |2 c r_t| <= 2 |q k_hat|

@@ -79,17 +79,43 @@ def _rng(*key) -> np.random.Generator:
     return np.random.default_rng(np.random.SeedSequence([SEED, *key]))
 
 
-def kv_head(wl_key: int, layer: int, session: int, g: int, n: int, d: int, outliers: int):
-    """(K float32 [n, d], sigma2 float32 [d]) of one KV head."""
-    rng = _rng(wl_key, layer, session, g)
+def _sigma(rng: np.random.Generator, d: int, outliers: int) -> np.ndarray:
+    """Per-channel std of one KV head: the first draws of its stream."""
     sigma = np.exp(rng.standard_normal(d)).astype(np.float32)
     if outliers:
         idx = rng.choice(d, outliers, replace=False)
         sigma[idx] *= np.float32(10.0)
+    return sigma
+
+
+def kv_head(wl_key: int, layer: int, session: int, g: int, n: int, d: int, outliers: int):
+    """(K float32 [n, d], sigma2 float32 [d]) of one KV head."""
+    rng = _rng(wl_key, layer, session, g)
+    sigma = _sigma(rng, d, outliers)
     k = rng.standard_normal((n, d), dtype=np.float32)
     k *= sigma
     sigma2 = (sigma * sigma).astype(np.float32)
     return k, sigma2
+
+
+def kv_sigma2(wl_key: int, layer: int, session: int, g: int, d: int, outliers: int) -> np.ndarray:
+    """sigma2 float32 [d] of one KV head, the same values kv_head() returns,
+    without drawing its keys."""
+    sigma = _sigma(_rng(wl_key, layer, session, g), d, outliers)
+    return (sigma * sigma).astype(np.float32)
+
+
+def layer_queries(wl: "Workload", layer: int = 0):
+    """(q [S*h_q, d], sigma2 [S*h_kv, d]) of one layer, equal to those of
+    layer_inputs(), without drawing any keys."""
+    hk = wl.sessions * wl.h_kv
+    s2 = np.empty((hk, wl.d), dtype=np.float32)
+    q = np.empty((hk * wl.g, wl.d), dtype=np.float32)
+    for v in range(hk):
+        s, g = divmod(v, wl.h_kv)
+        s2[v] = kv_sigma2(wl.key, layer, s, g, wl.d, wl.outliers)
+        q[v * wl.g:(v + 1) * wl.g] = queries(wl.key, layer, s, g, wl.g, wl.d)
+    return q, s2
 
 
 def queries(wl_key: int, layer: int, session: int, g: int, count: int, d: int) -> np.ndarray:

@@ -3,6 +3,8 @@ oracle, through the C ABI: every supported d, one and several splits of the
 index list, HBM and pinned-host caches, out-of-range and repeated entries, and
 the whole path pack -> allocate -> scan_topk -> attend_topk."""
 
+import zlib
+
 import numpy as np
 import pytest
 import torch
@@ -11,6 +13,7 @@ from oracle import attention_oracle as A
 from oracle import fathom_oracle as O
 from synthetic import small_case, to_bf16_bits
 from tests.parity import dev
+from tests.tolerances import attention_tolerance
 
 pytestmark = pytest.mark.gpu
 
@@ -44,19 +47,27 @@ def splits(d, k):
 
 
 def check(out, lse, q, kc, vc, idx, scale, g, where=""):
+    """Every head within the order-independent fp32 bound (sums of any order
+    over the list), and, as a second criterion, within the tighter bound of
+    this kernel's own reduction depths (26 roundings per logit; 16 additions
+    per lane, 6 across rows, 4 across wavefronts and one per split of the
+    list for the sums)."""
     h_q, d = q.shape
     worst = 0.0
     for h in range(h_q):
         o, l, _, valid = A.sparse_attention(q[h], kc[h // g], vc[h // g], idx[h], scale)
-        tau_o, tau_l = A.attention_tolerance(q[h], kc[h // g], vc[h // g], idx[h], scale,
-                                             chain=30 + splits(d, idx.shape[1]))
         if valid.size == 0:
             assert np.all(out[h] == 0) and lse[h] == -np.inf, f"{where} head {h}: empty set"
             continue
         err = np.abs(out[h].astype(np.float64) - o)
+        lerr = abs(float(lse[h]) - l)
+        tau_o, tau_l = attention_tolerance(q[h], kc[h // g], vc[h // g], idx[h], scale)
         assert np.all(err <= tau_o), (f"{where} head {h}: worst excess {float(np.max(err - tau_o)):.3e} "
                                       f"at channel {int(np.argmax(err - tau_o))}")
-        assert abs(float(lse[h]) - l) <= tau_l, f"{where} head {h}: lse {lse[h]} vs {l} (tol {tau_l:.2e})"
+        assert lerr <= tau_l, f"{where} head {h}: lse {lse[h]} vs {l} (tol {tau_l:.2e})"
+        st_o, st_l = attention_tolerance(q[h], kc[h // g], vc[h // g], idx[h], scale, logit_chain=26,
+                                         sum_chain=30 + splits(d, idx.shape[1]))
+        assert np.all(err <= st_o) and lerr <= st_l, f"{where} head {h}: outside the kernel's structural bound"
         worst = max(worst, float(np.max(err / np.maximum(tau_o, 1e-300))))
     return worst
 
@@ -87,7 +98,7 @@ CASES = [  # (h_kv, g, n, d, k)
 def test_attend_matches_oracle(F, case):
     h_kv, g, n, d, k = case
     print(f"attend case={case}", flush=True)
-    rng = np.random.default_rng(hash(case) % 1000)
+    rng = np.random.default_rng(zlib.crc32(repr(case).encode()) % 1000)
     kc, vc = cache(rng, h_kv, n, d, kscale=2.0)
     q = rng.standard_normal((h_kv * g, d)).astype(np.float32)
     idx = np.stack([np.sort(rng.choice(n, k, replace=False)) for _ in range(h_kv * g)])

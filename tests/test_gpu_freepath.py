@@ -3,6 +3,8 @@ pack_nibbles is bit-exact against the oracle's layout, and scan_topk_nibbles
 gives the bit-plane scan's scores and selection bit for bit (and so the
 oracle's), from HBM and from pinned host memory."""
 
+import zlib
+
 import numpy as np
 import pytest
 import torch
@@ -25,7 +27,7 @@ def F():
 @pytest.mark.parametrize("shape", [(2, 1000, 128), (1, 4096, 64), (3, 300, 32), (1, 129, 96)])
 def test_pack_nibbles_bit_exact(F, shape):
     h_kv, n, d = shape
-    k, _, _ = small_case(hash(shape) % 50, h_kv, 1, n, d, outliers=min(4, d))
+    k, _, _ = small_case(zlib.crc32(repr(shape).encode()) % 50, h_kv, 1, n, d, outliers=min(4, d))
     st = torch.full((1,), -1, dtype=torch.int32, device="cuda:0")
     codes, scales = F.pack_nibbles(dev(k), status=st)
     torch.cuda.synchronize()

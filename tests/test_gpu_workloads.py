@@ -16,8 +16,8 @@ import pytest
 import torch
 
 from oracle import fathom_oracle as O
-from synthetic import layer_inputs, workloads
-from tests.parity import check_scores, check_topk, oracle_depths
+from synthetic import layer_inputs, layer_queries, workloads
+from tests.parity import check_scores, check_topk, dev, oracle_depths
 
 pytestmark = pytest.mark.gpu
 
@@ -77,7 +77,8 @@ def check_records(rec_np, k_np, codes, blocks_per_head=6, seed=0):
                 assert np.array_equal(rec_np[v, :, off:off + 16], want), (v, b, plane)
 
 
-def run_and_check(F, wl, layer=0, sample_heads=(0, 1, 2, 3), host_modes=None, full_record_heads=(0,)):
+def run_and_check(F, wl, layer=0, sample_heads=(0, 1, 2, 3), host_modes=None, full_record_heads=(0,),
+                  select_heads=None):
     budget = wl.budgets[layer]
     mode = F.WATERFILL if wl.mode == "waterfill" else F.TOPQ
     print(f"workload {wl.name} layer {layer} budget {budget}", flush=True)
@@ -90,7 +91,8 @@ def run_and_check(F, wl, layer=0, sample_heads=(0, 1, 2, 3), host_modes=None, fu
     for v in sorted(set(full_record_heads) | {h // g for h in sample_heads}):
         delta = O.block_scales(k_np[v])
         codes[v] = (delta, O.quantize_codes(k_np[v], delta))
-    check_records(rec.numpy() if host else rec.cpu().numpy(), k_np, codes)
+    check_records(rec.numpy() if host else rec.cpu().numpy(), k_np,
+                  {v: codes[v] for v in full_record_heads})
     q = torch.from_numpy(q_np).to("cuda:0")
     dep, uni = F.allocate(q, torch.from_numpy(s2_np).to("cuda:0"), budget, mode=mode)
     rd, ru = oracle_depths(q_np, s2_np, budget, mode=wl.mode)
@@ -112,8 +114,8 @@ def run_and_check(F, wl, layer=0, sample_heads=(0, 1, 2, 3), host_modes=None, fu
         s, a = O.scores(q_np[h], kappa, delta, rd[h])
         check_scores(sg[h], s, a, where=f"{wl.name} head {h}")
         check_topk(idx[h], s, a, wl.k, s_gpu=sg[h], where=f"{wl.name} head {h}")
-    # every head: the selection is exact on the GPU's own scores
-    for h in range(idx.shape[0]):
+    # every head (or those named): the selection is exact on the GPU's own scores
+    for h in (range(idx.shape[0]) if select_heads is None else select_heads):
         assert np.array_equal(idx[h], O.topk(sg[h].astype(np.float64), wl.k)), f"select head {h}"
 
 
@@ -133,12 +135,89 @@ def test_w3_host_1m(F):
     run_and_check(F, wl, sample_heads=(0, 3))
 
 
-@pytest.mark.parametrize("layer", [int(np.argmin(WL["w4_host_1m_36layers"].budgets)),
-                                   int(np.argmax(WL["w4_host_1m_36layers"].budgets))])
-def test_w4_decode_layers(F, layer):
-    """Two layers of the 36-layer decode step (smallest and largest budget)."""
-    wl = WL["w4_host_1m_36layers"]
-    run_and_check(F, wl, layer=layer, sample_heads=(0,), host_modes=[F.HOST_DIRECT])
+W4 = WL["w4_host_1m_36layers"]
+
+
+def spread_layers(budgets, count=6):
+    """`count` layers whose budgets span the range: the smallest, the largest and
+    evenly spaced ranks between (lowest layer index among equal budgets)."""
+    order = sorted(range(len(budgets)), key=lambda layer: (budgets[layer], layer))
+    return [order[round(i * (len(order) - 1) / (count - 1))] for i in range(count)]
+
+
+def test_w4_every_layer_depths(F):
+    """All 36 layers of the decode step: every query head's depths and every KV
+    head's union depths bit-exact, and each head's depths spend its layer's
+    budget (the per-layer budgets of the ai-feeds digest, Method, key module 3).
+    Allocation reads only q and sigma2, so no keys are drawn."""
+    for layer in range(W4.layers):
+        budget = W4.budgets[layer]
+        q_np, s2_np = layer_queries(W4, layer)
+        dep, uni = F.allocate(dev(q_np), dev(s2_np), budget)
+        rd, ru = oracle_depths(q_np, s2_np, budget)
+        assert np.array_equal(dep.cpu().numpy(), rd), f"depths of layer {layer}"
+        assert np.array_equal(uni.cpu().numpy(), ru), f"union depths of layer {layer}"
+        assert np.all(rd.sum(axis=1) == budget), layer
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("layer", spread_layers(W4.budgets))
+def test_w4_decode_layer_full_size(F, layer):
+    """Six layers of the 36-layer step at full size (1M keys, pinned host records),
+    budgets from the smallest to the largest: records, depths and selection as in
+    the other workloads, oracle scores and top-k of one query head per layer (a
+    different head in each)."""
+    head = (5 * layer + 3) % W4.h_q
+    run_and_check(F, W4, layer=layer, sample_heads=(head,), host_modes=[F.HOST_DIRECT], full_record_heads=(),
+                  select_heads=sorted({head, (head + 8) % W4.h_q, (head + 16) % W4.h_q, (head + 24) % W4.h_q}))
+
+
+def test_w4_decode_step_loop(F):
+    """The whole 36-layer decode step as the benchmark runs it, at a reduced key
+    count (50152 keys per layer, a ragged last block; every layer's records
+    resident in pinned host memory together): one depth buffer and one
+    workspace reused by every layer, a union-depth buffer and an index buffer
+    per layer, the step run twice.  Every layer's selection: for all 32 query
+    heads exact on the GPU's own scores of that layer, for the 4 query heads of
+    one KV head (a different one per layer) equal to the oracle's top-k up to
+    boundary ties, and identical in both runs."""
+    n, k, hq, hk, d = 50152, W4.k, W4.h_q, W4.h_kv, W4.d
+    g = W4.g
+    layers, oracle_kv = [], []
+    for layer in range(W4.layers):
+        k_np, q_np, s2_np = layer_inputs(W4, layer, n=n)
+        rec = pack_layer(F, k_np, host=True)
+        v = layer % hk
+        delta = O.block_scales(k_np[v])
+        oracle_kv.append((v, delta, O.quantize_codes(k_np[v], delta)))
+        layers.append((rec, dev(q_np), dev(s2_np), q_np, s2_np))
+        del k_np
+    print(f"decode step loop: {W4.layers} layers of {n} keys packed", flush=True)
+    depth = torch.empty((hq, d), dtype=torch.uint8, device="cuda:0")
+    uni = [torch.empty((hk, d), dtype=torch.uint8, device="cuda:0") for _ in range(W4.layers)]
+    ws = torch.empty(F.workspace_bytes(hq, hk, n, d, k, F.HOST_DIRECT), dtype=torch.uint8, device="cuda:0")
+    runs = []
+    for _ in range(2):
+        idx = torch.empty((W4.layers, hq, k), dtype=torch.int32, device="cuda:0")
+        for layer, (rec, q, s2, _, _) in enumerate(layers):
+            F.allocate(q, s2, W4.budgets[layer], depth=depth, union_depth=uni[layer])
+            F.scan_topk(rec, q, depth, uni[layer], n, k, residency=F.HOST_DIRECT, workspace=ws, idx=idx[layer])
+        torch.cuda.synchronize()
+        runs.append(idx.cpu().numpy())
+    assert np.array_equal(runs[0], runs[1]), "the two runs of the step differ"
+    idx = runs[0]
+    for layer, (rec, q, s2, q_np, s2_np) in enumerate(layers):
+        rd, ru = oracle_depths(q_np, s2_np, W4.budgets[layer])
+        assert np.array_equal(uni[layer].cpu().numpy(), ru), f"union depths kept for layer {layer}"
+        sg = F.scan_scores(rec, q, dev(rd.astype(np.uint8)), uni[layer], n, residency=F.HOST_DIRECT)
+        sg = sg.cpu().numpy()
+        for h in range(hq):
+            assert np.array_equal(idx[layer, h], O.topk(sg[h].astype(np.float64), k)), f"layer {layer} head {h}"
+        v, delta, kappa = oracle_kv[layer]
+        for h in range(v * g, (v + 1) * g):
+            s, a = O.scores(q_np[h], kappa, delta, rd[h])
+            check_scores(sg[h], s, a, where=f"layer {layer} head {h}")
+            check_topk(idx[layer, h], s, a, k, where=f"layer {layer} head {h}")
 
 
 @pytest.mark.parametrize("name", ["w5_sessions_262k_B68", "w5_sessions_262k_fixed136",

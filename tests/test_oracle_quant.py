@@ -1,8 +1,9 @@
 """Pins of the oracle's quantiser and record packer against exact arithmetic.
 
-Fathom review (evolve.pub), "Strengths" (paper Sec 3.2) and FAQ: 4-bit uniform
-codes under one shared block scale, stored channel-major as bit planes, so the
-first t planes of a channel are exactly its t-bit mid-rise quantizer.
+Source: the evolve.pub review, "Strengths" (paper Sec 3.2) and FAQ.  Keys are
+quantised to 4-bit uniform codes with one scale per block and kept per channel
+as bit planes; reading the top t planes of a code yields the t-bit mid-rise
+quantiser of the same value, which these pins check.
 """
 
 import math
