@@ -84,21 +84,20 @@ def algorithmic_bytes(union: np.ndarray, n: int) -> int:
 
 
 def algorithmic_ops(depth: np.ndarray, union: np.ndarray, n: int) -> int:
-    """VALU lane-operations of the reconstruction for all keys: per KV head and
-    union channel with depth u > 0, 2u - 1 integer ops build the signed prefixes
-    r, 1 op per distinct depth read by some head converts r to float, and 1 FMA
-    (2c) r per query head that reads the channel; the term c of c (2r + 1) is
-    one add per (query head, channel, 128-key block), i.e. per block, not per
-    key.  Counted per KV-head key."""
+    """VALU lane-operations of the reconstruction for all keys.  A lane holds 4
+    keys' prefixes side by side in the bytes of one register, so per KV head,
+    union channel and 4 keys: 2 ops per plane of the union depth (a rotate and
+    an and-or), 5 per distinct depth read by some head (setting the midpoint
+    bit, then 4 signed-byte conversions to float), and 4 FMAs per query head
+    that reads the channel.  Counted over all KV-head keys."""
     hk, d = union.shape
     g = depth.shape[0] // hk
     dep = depth.reshape(hk, g, d).astype(np.int64)
     u = union.astype(np.int64)
-    chain = np.where(u > 0, 2 * u - 1, 0).sum()
+    planes = u.sum()
     levels = sum(((dep == t).any(axis=1)).sum() for t in range(1, 5))
     fmas = (dep > 0).sum()
-    per_block = fmas                       # one add per (head, channel) per block
-    return int((chain + levels + fmas) * n + per_block * ((n + 127) // 128))
+    return int((2 * planes + 5 * levels + 4 * fmas) * n // 4)
 
 
 def measured_traffic(workload: str, residency: str, kernel: str):

@@ -68,10 +68,10 @@ enum fathom_residency {
                               pin_memory); the scan kernel reads the budgeted plane
                               prefixes of each tile straight over the host link          */
   FATHOM_HOST_STAGED = 2   /* records in pinned host memory; each channel's budgeted prefix
-                              run is gathered into an HBM mirror in the workspace with long
-                              contiguous reads, and the copy of one KV head overlaps the
-                              scan of the previous one ([Review] Strengths, paper Sec 3.6:
-                              partial reads as contiguous host-link runs)                 */
+                              run is gathered with long contiguous reads into a ring of two
+                              KV heads' records in the workspace, and the copy of one KV head
+                              overlaps the scan of the previous one ([Review] Strengths, paper
+                              Sec 3.6: partial reads as contiguous host-link runs)          */
 };
 
 /* How allocate_depths spends the budget. */
@@ -164,7 +164,8 @@ int allocate_depths(const float* q, const float* sigma2, int h_q, int h_kv, int 
 
 /* Bytes of device workspace scan_topk (and fathom_scan_scores) needs for this
  * shape and residency: the fp32 scores and selection state, plus for
- * FATHOM_HOST_STAGED an HBM mirror of the records (h_kv * d * R bytes). */
+ * FATHOM_HOST_STAGED a ring of two KV heads' records in HBM
+ * (min(h_kv, 2) * d * R bytes) through which the prefix runs are staged. */
 size_t fathom_workspace_bytes(int h_q, int h_kv, int64_t n, int d, int k, int residency);
 
 /* scan_topk -- score every key from its read prefix and select the top k
@@ -194,7 +195,8 @@ int scan_topk(const void* records, int residency, const float* q, const uint8_t*
 /* fathom_scan_scores -- the scan stage alone (for tests and profiling): the same
  * scores scan_topk ranks, written to device float32 [h_q][ld] (ld >= n; the
  * first n entries of each row are written).  The workspace is used only by
- * FATHOM_HOST_STAGED (for its HBM mirror) and may be NULL otherwise. */
+ * FATHOM_HOST_STAGED (for its HBM ring of staged records) and may be NULL
+ * otherwise. */
 int fathom_scan_scores(const void* records, int residency, const float* q,
                        const uint8_t* depth, const uint8_t* union_depth, int h_q,
                        int h_kv, int64_t n, int d, float* scores, int64_t ld,

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -168,7 +169,8 @@ size_t fathom_workspace_bytes(int h_q, int h_kv, int64_t n, int d, int k, int re
   (void)k;
   if (h_q <= 0 || h_kv <= 0 || d <= 0 || n <= 0) return 0;
   size_t bytes = al256((size_t)h_q * (size_t)score_ld(n) * 4) + fathom::select_workspace_bytes(h_q, n, k > 0 ? k : 1);
-  if (residency == FATHOM_HOST_STAGED) bytes += al256((size_t)h_kv * (size_t)d * (size_t)fathom::make_layout(n).R);
+  if (residency == FATHOM_HOST_STAGED)
+    bytes += al256((size_t)std::min<int64_t>(h_kv, fathom::kStageRing) * (size_t)d * (size_t)fathom::make_layout(n).R);
   return bytes;
 }
 
@@ -206,17 +208,50 @@ hipError_t scan_for_select(const uint8_t* dev, const uint8_t* const* table, int6
   return e;
 }
 
+// Whether HBM-resident scans select on the fly (launch_scan_select).  Off: at
+// 131072 keys that kernel still costs more time than the score round trip it
+// saves (its cross-XCD atomics serialise), although it moves a third of the
+// bytes.
+constexpr bool kSelectInScan = false;
+
+// How the selection continues after run_scan: the full selection over the
+// scores (with what the scan prepared), or only the resolve over kept keys the
+// scan compacted itself (fused: chunks of `slot` keys, `nchunks` per head).
+struct ScanOutcome {
+  bool cleared = false;
+  bool hist_done = false;
+  bool fused = false;
+  int64_t nchunks = 0;
+  int slot = 0;
+};
+
 // Scores of every key into `scores` [h_q][ld]; staging comes from the workspace.
-// With a selection to follow (`sel`), the direct scans also prepare it.
+// With a selection to follow (`sel`), the direct scans also prepare it, and
+// HBM-resident scans select on the fly where every tile fits on the GPU at
+// once (k to select).
 int run_scan(const uint8_t* dev, int residency, const float* q, const uint8_t* depth,
              const uint8_t* union_depth, int h_q, int h_kv, int64_t n, int d, float* scores, int64_t ld,
-             uint8_t* staging, const fathom::SelectWorkspace* sel, bool* cleared, bool* hist_done,
-             hipStream_t s) {
+             uint8_t* staging, const fathom::SelectWorkspace* sel, int k, ScanOutcome* out, hipStream_t s) {
   const fathom::Layout L = fathom::make_layout(n);
   const int g = h_q / h_kv;
   const bool host = residency == FATHOM_HOST_DIRECT;
   hipError_t e;
-  *cleared = *hist_done = false;
+  bool* cleared = &out->cleared;
+  bool* hist_done = &out->hist_done;
+  *out = ScanOutcome();
+  if (kSelectInScan && sel && residency == FATHOM_HBM && !sel->small && L.nb > 0) {
+    e = fathom::launch_select_clear(*sel, h_q, s, true);
+    if (e != hipSuccess) return hip_fail(e, "select clear launch");
+    e = fathom::launch_scan_select(dev, q, depth, union_depth, h_kv, g, L, d, scores, ld, *sel, k, &out->nchunks,
+                                   &out->slot, s);
+    if (e == hipSuccess) {
+      out->fused = true;
+      return FATHOM_OK;
+    }
+    if (e != hipErrorCooperativeLaunchTooLarge) return hip_fail(e, "scan launch");
+    // too many tiles to be resident at once: scores through HBM (the clearing
+    // above is harmless; the scan clears again on the way)
+  }
   if (residency == FATHOM_HOST_STAGED) {
     e = fathom::launch_scan_staged(dev, staging, q, depth, union_depth, h_kv, g, L, d, scores, ld, s);
   } else if (sel && L.nb > 0) {
@@ -255,9 +290,9 @@ int fathom_scan_scores(const void* records, int residency, const float* q, const
     if (!aligned(workspace, 256)) return fail(FATHOM_EINVAL, "workspace must be 256-byte aligned");
     staging = static_cast<uint8_t*>(workspace) + staging_offset(h_q, n, 1);
   }
-  bool cleared = false, hist_done = false;
-  st = run_scan(dev, residency, q, depth, union_depth, h_q, h_kv, n, d, scores, ld, staging, nullptr, &cleared,
-                &hist_done, static_cast<hipStream_t>(stream));
+  ScanOutcome out;
+  st = run_scan(dev, residency, q, depth, union_depth, h_q, h_kv, n, d, scores, ld, staging, nullptr, 0, &out,
+                static_cast<hipStream_t>(stream));
   if (st) return st;
   return ok();
 }
@@ -282,11 +317,13 @@ int scan_topk(const void* records, int residency, const float* q, const uint8_t*
   uint8_t* sel_base = static_cast<uint8_t*>(workspace) + al256((size_t)h_q * (size_t)ld * 4);
   uint8_t* staging = static_cast<uint8_t*>(workspace) + staging_offset(h_q, n, k);
   const fathom::SelectWorkspace sel = fathom::carve_select(sel_base, h_q, n, k);
-  bool cleared = false, hist_done = false;
-  st = run_scan(dev, residency, q, depth, union_depth, h_q, h_kv, n, d, scores, ld, staging, &sel, &cleared,
-                &hist_done, s);
+  ScanOutcome out;
+  st = run_scan(dev, residency, q, depth, union_depth, h_q, h_kv, n, d, scores, ld, staging, &sel, k, &out, s);
   if (st) return st;
-  hipError_t e = fathom::launch_select(scores, ld, h_q, n, k, topk_idx, topk_score, sel, cleared, hist_done, s);
+  hipError_t e = out.fused ? fathom::launch_select_resolve(scores, ld, h_q, n, k, topk_idx, topk_score, sel,
+                                                           out.nchunks, out.slot, s)
+                           : fathom::launch_select(scores, ld, h_q, n, k, topk_idx, topk_score, sel, out.cleared,
+                                                   out.hist_done, s);
   if (e != hipSuccess) return hip_fail(e, "select launch");
   return ok();
 }

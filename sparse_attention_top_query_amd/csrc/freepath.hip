@@ -21,10 +21,9 @@
 // the blocks' scales.  Lane l of wavefront w owns keys 128 w + l and 128 w + l
 // + 64 (both in block w).  Channels are visited in order; for a union channel c
 // read to depth t by some head, u = code >> (4 - t) is one bit-field extract,
-// r = u - 2^(t-1), and the term 2c r (2c = 2 [q 2^(3-t) Delta]) joins the
-// score, 2c the head's per-lane sum (half of it is added at the end), the
-// same fp32 operations in the same order as the bit-plane scan, so the scores
-// are bit-identical to it.
+// r = u - 2^(t-1), z = 2^(7-t) (2 r + 1), and the term a z (a = [q Delta / 16])
+// joins the score of every head reading t planes: the same fp32 operations in
+// the same order as the bit-plane scan, so the scores are bit-identical to it.
 #include <hip/hip_fp16.h>
 
 #include "fathom_internal.h"
@@ -86,8 +85,8 @@ __global__ __launch_bounds__(256) void pack_nibbles_kernel(const float* __restri
 template <int G>
 struct NibSmem {
   uint32_t rows[kNibKeys][kNibMaxD / 8 + 1];   // codes of the tile's keys, 8 channels per word, padded
-  float coef[kNibBlocks][kNibMaxD][G];         // 2 [q_h 2^(3-t_h) Delta] of each block and channel
-  float cq[kNibMaxD][G];                       // q_h 2^(3-t_h) per channel (0 when not read)
+  float coef[kNibBlocks][kNibMaxD][G];         // [q_h Delta / 16] of each block and channel
+  float cq[kNibMaxD][G];                       // q_h / 16 per channel (0 when not read)
   uint64_t cw[kNibMaxD];                       // union depth | depths in use | head depths
   uint32_t wmask[kNibMaxD / 8];                // channels of the union per code word
 };
@@ -124,7 +123,7 @@ __global__ __launch_bounds__(kNibThreads) void nibble_scan_kernel(
       const int th = u > 0 ? depth[row] : 0;
       if (th > 0) word |= (uint64_t)1 << (2 + th);
       word |= (uint64_t)th << (8 + 3 * h);
-      sm.cq[c][h] = u > 0 ? ldexpf(q[row], 3 - th) : 0.0f;   // exact power-of-two scaling
+      sm.cq[c][h] = u > 0 ? ldexpf(q[row], -4) : 0.0f;   // exact power-of-two scaling
     }
     sm.cw[c] = u > 0 ? word : 0ull;
   }
@@ -157,15 +156,13 @@ __global__ __launch_bounds__(kNibThreads) void nibble_scan_kernel(
     const int64_t b = tile * kNibBlocks + bl;
     const float dl = b < nb ? __half2float(scales[(g * nb + b) * d + c]) : 0.0f;
 #pragma unroll
-    for (int h = 0; h < G; ++h) sm.coef[bl][c][h] = 2.0f * (sm.cq[c][h] * dl);   // rounded, then doubled
+    for (int h = 0; h < G; ++h) sm.coef[bl][c][h] = sm.cq[c][h] * dl;   // one rounding
   }
   __syncthreads();
 
   float acc[2][G];
-  float half_sum[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    half_sum[h] = 0.0f;
 #pragma unroll
     for (int s = 0; s < 2; ++s) acc[s][h] = 0.0f;
   }
@@ -191,26 +188,20 @@ __global__ __launch_bounds__(kNibThreads) void nibble_scan_kernel(
 #pragma unroll
         for (int t = 1; t <= kPlanes; ++t) {
           if (!(word & (8u << (t - 1)))) continue;
-          // u = code >> (4 - t): the top t bits of the nibble
+          // u = code >> (4 - t): the top t bits of the nibble; z = 2^(7-t) (2 (u - 2^(t-1)) + 1)
           const int u0 = (int)__builtin_amdgcn_ubfe(c0, 4 * x + 4 - t, t);
           const int u1 = (int)__builtin_amdgcn_ubfe(c1, 4 * x + 4 - t, t);
-          const float f0 = (float)(u0 - (1 << (t - 1)));
-          const float f1 = (float)(u1 - (1 << (t - 1)));
+          const float f0 = (float)((2 * u0 + 1 - (1 << t)) * (1 << (7 - t)));
+          const float f1 = (float)((2 * u1 + 1 - (1 << t)) * (1 << (7 - t)));
 #pragma unroll
           for (int h = 0; h < G; ++h) {
             if (nword_th(word, h) != t) continue;
             acc[0][h] = fmaf(cf[h], f0, acc[0][h]);
             acc[1][h] = fmaf(cf[h], f1, acc[1][h]);
-            half_sum[h] += cf[h];
           }
         }
       }
     }
-  }
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    acc[0][h] += 0.5f * half_sum[h];
-    acc[1][h] += 0.5f * half_sum[h];
   }
 #pragma unroll
   for (int s = 0; s < 2; ++s) {

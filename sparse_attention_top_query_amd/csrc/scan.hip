@@ -7,17 +7,18 @@
 // midpoint of the prefix's cell of the t-bit mid-rise quantizer), and the
 // Fathom arXiv abstract (a t-plane prefix is the t-bit quantizer of the
 // channel).  With r_t = (code >> (4-t)) - 2^(t-1), a signed t-bit integer,
-//   q * k_hat_t = q Delta 2^(4-t) (r_t + 1/2) = c (2 r_t + 1),  c = [q 2^(3-t) Delta],
-// and the scan accumulates it as (2c) r_t per key plus, once per block, c: with
-// c one fp32 rounding (2c exact), every term is bounded by |2 c r_t| <= 2 |q k_hat|
-// and |c| <= |q k_hat| (|2 r_t + 1| >= 1), so the fp32 sum over m channels stays
-// within about 3 (m + 2) 2^-24 sum_c |q_c k_hat_c|.
+//   q * k_hat_t = q Delta 2^(4-t) (r_t + 1/2) = a z_t,
+//   a = [q Delta / 16] (one fp32 rounding),  z_t = 2^(7-t) (2 r_t + 1),
+// where z_t is an integer in [-127, 127] (a signed byte) and a does not depend
+// on the depth.  Each term a z_t is an exact product in the fma, within one
+// rounding of q k_hat, so the fp32 sum over m channels stays within about
+// (m + 1) 2^-24 sum_c |q_c k_hat_c|.
 //
 // Work decomposition: one workgroup scores a tile of TB 128-key blocks of one KV
 // head for all of its G query heads; each wavefront owns 2 blocks (256 keys):
-// lanes 0-31 one block, lanes 32-63 the other, and lane l scores the 4
-// consecutive keys 4 (l%32) .. 4 (l%32) + 3 of its block, which one 32-bit
-// word of each plane row holds.
+// lanes 0-31 one block, lanes 32-63 the other.  Lane l owns the keys
+// 32 i + jj + 8 s (s = 0..3) of its block, i = (l%32)/8, jj = l%8: the bits
+// jj + 8 s of 32-bit word i of each plane row of the block.
 //  1. The union depths of the KV head list the channels to read; every query
 //     head of the group is scored from the one read of the longest prefix.
 //  2. Staging, channel group by channel group (about 64 channel-planes): the
@@ -26,21 +27,24 @@
 //     registers -- all issued before any LDS write, and those of the next group
 //     while the current group is computed -- then stored to LDS, the most
 //     significant plane complemented.  The same code reads HBM, an HBM staging
-//     mirror, or pinned host memory over the host link; the tile size sets the
+//     ring, or pinned host memory over the host link; the tile size sets the
 //     contiguous run per channel-plane (16 B per block).
-//  3. Per (channel, block) the doubled coefficients 2 c = 2 [q_h 2^(3-t_h) Delta]
-//     are formed once in LDS.  Per key, each lane reads its own plane words and
-//     builds the signed prefix MSB first: r_1 = -(complemented bit) = b_0 - 1,
-//     then r_{t+1} = 2 r_t + b_t, which yields every shorter prefix on the way
-//     for heads that read fewer planes; float(r_t) once per depth in use, and
-//     per head one fma with 2c and one add of 2c to the lane's per-head sum,
-//     half of which joins every score at the end.
+//  3. Per (channel, block) the coefficients a = [q_h Delta / 16] are formed once
+//     in LDS.  Per channel, each lane reads its word of each plane row and
+//     builds the 4 keys' prefixes side by side, one per byte of a register y:
+//     plane p's word rotated right by jj + p - 7 puts the lane's 4 bits at bit
+//     7 - p of bytes 0..3, and one and-or adds them to y (two operations per
+//     plane for 4 keys).  The complemented MSB is the byte's sign bit, so after
+//     t planes byte s of y is 2^(8-t) r_t of key s; setting bit 7 - t of every
+//     byte makes it z_t.  Per depth in use: that one or, then 4 signed-byte
+//     conversions to float; per head reading the channel: one fma per key.
 #include <hip/hip_fp16.h>
 
 #include <algorithm>
 #include <type_traits>
 
 #include "fathom_internal.h"
+#include "select_parts.h"
 
 namespace fathom {
 namespace {
@@ -71,7 +75,7 @@ struct ScanSmem {
   float coef[kStageChunks][TB][G];                 // 2 [q_h 2^(3-t_h) Delta_b] per block and head, in the
                                                    // row of the entry's first chunk (for G = 4 a row has the
                                                    // planes' stride: one address serves both)
-  float ent_q[kMaxD][G];                           // q_h 2^(3-t_h) of each list entry
+  float ent_q[kMaxD][G];                           // q_h / 16 of each list entry
   uint64_t ent_word[kMaxD + 1];                    // level masks: bit (t-1) G + h iff head h reads t planes
   uint16_t ent_base[kMaxD + 1];                    // first chunk of entry e (prefix sum)
   uint16_t grp[kMaxChunks / kGroupChunks + 2];     // first entry of each staging group
@@ -98,6 +102,8 @@ struct ScanArgs {
   const uint8_t* const* pages;
   int64_t npages;
   int64_t page_tiles;
+  // ring of staged heads (0: none): KV head g's records are at slot g % ring
+  int64_t ring;
 };
 
 // Entry word: one G-bit mask per depth t = 1..4, bit (t - 1) G + h set iff head h
@@ -113,12 +119,12 @@ template <int G, int TB>
 constexpr int kHistHeads = (int)(sizeof(ScanSmem<G, TB>) / 4 / kHistWords) < G
                                ? (int)(sizeof(ScanSmem<G, TB>) / 4 / kHistWords) : G;
 
-// Scores of tile `tile` (TB blocks) of KV head g, all its query heads.  With
-// FUSE, the tile's scores are also counted into a.hist by their first
-// selection digit (an LDS histogram per round of heads, then one global atomic
-// per non-empty bin).
-template <int G, int TB, bool FUSE = false>
-__device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t tile, ScanSmem<G, TB>& sm) {
+// Scores of tile `tile` (TB blocks) of KV head g for all its query heads, left
+// in acc: acc[s][h] is the score for query head g G + h of the key
+// tile_key(s) of the tile.
+template <int G, int TB>
+__device__ __forceinline__ void scan_tile_acc(const ScanArgs& a, int64_t g, int64_t tile, ScanSmem<G, TB>& sm,
+                                              float (&acc)[kSub][G]) {
   using C = Cfg<G, TB>;
   constexpr int SLOTS = C::slots;
   constexpr int NT = C::threads;
@@ -176,7 +182,7 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t 
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         if (th[h] > 0) word |= (uint64_t)1 << ((th[h] - 1) * G + h);
-        sm.ent_q[e][h] = ldexpf(qc[h], 3 - th[h]);   // exact power-of-two scaling
+        sm.ent_q[e][h] = ldexpf(qc[h], -4);   // exact power-of-two scaling
       }
       sm.ent_word[e] = word;
       sm.ent_base[e] = (uint16_t)base;
@@ -200,11 +206,8 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t 
     __syncthreads();
   }
 
-  float acc[kSub][G];
-  float half_sum[G];   // per head: the sum of its coefficients 2 c over the channels it reads
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    half_sum[h] = 0.0f;
 #pragma unroll
     for (int s = 0; s < kSub; ++s) acc[s][h] = 0.0f;
   }
@@ -216,7 +219,7 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t 
     recg = a.pages[g * a.npages + tile / a.page_tiles];
     ablk0 = (tile % a.page_tiles) * TB;
   } else {
-    recg = rec + g * d * R;
+    recg = rec + (a.ring ? g % a.ring : g) * d * R;
     ablk0 = blk0;
   }
   const int64_t unit0 = ablk0 / kUnitBlocks;
@@ -289,7 +292,7 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t 
     const int ch_lo = __builtin_amdgcn_readfirstlane(sm.ent_base[e_lo]);
     commit(gi);
     __syncthreads();
-    // coefficients q_h 2^(3-t_h) Delta_b for every entry, block and head of the group
+    // coefficients a = [q_h Delta_b / 16] for every entry, block and head of the group
     for (int i = tid; i < (e_hi - e_lo) * TB; i += NT) {   // one (entry, block) per thread, all heads
       const int el = i / TB;
       const int b = i % TB;
@@ -299,17 +302,21 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t 
 #pragma unroll
       for (int h = 0; h < G; ++h) qh[h] = sm.ent_q[e_lo + el][h];
 #pragma unroll
-      for (int h = 0; h < G; ++h) sm.coef[row][b][h] = 2.0f * (qh[h] * dl);   // rounded, then doubled
+      for (int h = 0; h < G; ++h) sm.coef[row][b][h] = qh[h] * dl;   // one rounding
     }
     __syncthreads();
     if (gi + 1 < n_grp) issue(gi + 1);
 
     // ---- 3. reconstruct and accumulate.  Lane l owns block bl = 2wv + l/32 and,
-    // in it, keys 4 (l%32) .. 4 (l%32) + 3, bits 4 (l%8) .. of the block's word
-    // (l%32)/8: a lane reads one 32-bit word per plane row (a quarter of the
-    // row), which keeps the loop's LDS reads to what it uses.
+    // in it, the keys 32 i + jj + 8 s (s = 0..3) of its block's 32-key word
+    // i = (l%32)/8, jj = l%8: bits jj + 8 s of that word of each plane row, so
+    // a lane reads one 32-bit word per plane row and finds its 4 bits one per
+    // byte.  Rotating the word right by jj + p - 7 brings them to bit 7 - p of
+    // bytes 0..3, where plane p belongs in the byte-wise signed prefix.
     if (kWaveBlocks * wv < nvalid) {
-      const int bit0 = 4 * (lane & 7);
+      const int jj = lane & 7;
+      const uint32_t rot0 = (uint32_t)(jj + 25) & 31u, rot1 = (uint32_t)(jj + 26) & 31u;
+      const uint32_t rot2 = (uint32_t)(jj + 27) & 31u, rot3 = (uint32_t)(jj + 28) & 31u;
       // the group's entries (at most 64: each starts in one of its 64 chunk
       // slots), one per lane; the loop reads them lane by lane into scalars
       // Per lane: chunk base within the group (< 128) | union depth << 8, and
@@ -345,38 +352,34 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t 
         float cf[G];
 #pragma unroll
         for (int h = 0; h < G; ++h) cf[h] = sm.coef[cb][bl][h];
-        int r[kSub];
-        // one depth t: float(r_t) once, then every head that reads exactly t planes
-        // adds (2c) r_t per key and 2c to its per-lane sum (c (2 r_t + 1) in total)
+        // y: byte s holds the signed prefix of key s read so far, MSB at bit 7
+        // (plane 0 is stored complemented, so bit 7 is the sign); one depth t:
+        // z = y | 2^(7-t) per byte is 2^(7-t) (2 r_t + 1), converted once
+        // (signed byte to float), then every head that reads exactly t planes
+        // adds a z per key
+        uint32_t y = __builtin_amdgcn_alignbit(w0, w0, rot0) & 0x80808080u;
         auto level = [&](int t) {
+          const uint32_t z = y | (0x01010101u << (7 - t));
           float f[kSub];
 #pragma unroll
-          for (int s2 = 0; s2 < kSub; ++s2) f[s2] = (float)r[s2];
+          for (int s2 = 0; s2 < kSub; ++s2) f[s2] = (float)(int)(int8_t)(z >> (8 * s2));
 #pragma unroll
           for (int h = 0; h < G; ++h) {
             if (!(word & ((Word)1 << ((t - 1) * G + h)))) continue;
 #pragma unroll
             for (int s2 = 0; s2 < kSub; ++s2) acc[s2][h] = fmaf(cf[h], f[s2], acc[s2][h]);
-            half_sum[h] += cf[h];
           }
         };
-        // signed prefixes MSB first (plane 0 is stored complemented): r_1 = b_0 - 1,
-        // r_{t+1} = 2 r_t + b_t
-#pragma unroll
-        for (int s2 = 0; s2 < kSub; ++s2) r[s2] = __builtin_amdgcn_sbfe((int)w0, bit0 + s2, 1);
         constexpr Word kHeads = (Word)((1ull << G) - 1ull);
         if (word & kHeads) level(1);
         if (tb > 1) {
-#pragma unroll
-          for (int s2 = 0; s2 < kSub; ++s2) r[s2] = 2 * r[s2] + (int)__builtin_amdgcn_ubfe(w1, bit0 + s2, 1);
+          y |= __builtin_amdgcn_alignbit(w1, w1, rot1) & 0x40404040u;
           if (word & (kHeads << G)) level(2);
           if (tb > 2) {
-#pragma unroll
-            for (int s2 = 0; s2 < kSub; ++s2) r[s2] = 2 * r[s2] + (int)__builtin_amdgcn_ubfe(w2, bit0 + s2, 1);
+            y |= __builtin_amdgcn_alignbit(w2, w2, rot2) & 0x20202020u;
             if (word & (kHeads << (2 * G))) level(3);
             if (tb > 3) {
-#pragma unroll
-              for (int s2 = 0; s2 < kSub; ++s2) r[s2] = 2 * r[s2] + (int)__builtin_amdgcn_ubfe(w3, bit0 + s2, 1);
+              y |= __builtin_amdgcn_alignbit(w3, w3, rot3) & 0x10101010u;
               level(4);
             }
           }
@@ -386,70 +389,291 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t 
     __syncthreads();
   }
 
-  // ---- 4. scores: sum_c (2c) r + (1/2) sum_c 2c = sum_c c (2 r + 1) ----
+}
+
+// Key of acc[s] of this thread within its tile: block 2 w + l/32, word
+// (l%32)/8, bit l%8 + 8 s of that word.
+template <int TB>
+__device__ __forceinline__ int tile_key(int s) {
+  const int lane = threadIdx.x & 63;
+  return (kWaveBlocks * (int)(threadIdx.x >> 6) + (lane >> 5)) * kBlock + 32 * ((lane & 31) >> 3) + (lane & 7) +
+         8 * s;
+}
+
+// Scores of the tile to a.scores, one store per key and head.
+template <int G, int TB>
+__device__ __forceinline__ void store_tile(const ScanArgs& a, int64_t g, int64_t tile, const float (&acc)[kSub][G]) {
+  const int64_t key0 = tile * TB * kBlock;
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
+  for (int s2 = 0; s2 < kSub; ++s2) {
+    const int64_t j = key0 + tile_key<TB>(s2);
+    if (j < a.n) {
 #pragma unroll
-    for (int s = 0; s < kSub; ++s) acc[s][h] += 0.5f * half_sum[h];
-  }
-  if (bl < nvalid) {
-    // a lane's 4 keys are consecutive: one 16-byte store per head where the rows
-    // allow it (so a wavefront writes 1 KB runs), else one store per key
-    const int64_t j0 = (blk0 + bl) * kBlock + 4 * (lane & 31);
-    const bool vec = (a.ld & 3) == 0 && (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0;
-    if (vec && j0 + 3 < a.n) {
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-        store_global(reinterpret_cast<float4*>(a.scores + (g * G + h) * a.ld + j0),
-                     make_float4(acc[0][h], acc[1][h], acc[2][h], acc[3][h]));
-    } else {
-#pragma unroll
-      for (int s2 = 0; s2 < kSub; ++s2) {
-        if (j0 + s2 < a.n) {
-#pragma unroll
-          for (int h = 0; h < G; ++h) a.scores[(g * G + h) * a.ld + j0 + s2] = acc[s2][h];
-        }
-      }
+      for (int h = 0; h < G; ++h) store_global(a.scores + (g * G + h) * a.ld + j, acc[s2][h]);
     }
   }
+}
 
-  // ---- 5. fused first-digit histogram of the selection ----
-  if constexpr (FUSE) {
-    constexpr int HR = kHistHeads<G, TB>;
-    static_assert(HR >= 1 && TB * kBlock < 65536, "16-bit counts of at least one head must fit");
-    uint32_t* lh = reinterpret_cast<uint32_t*>(&sm);
+// The tile's scores counted into hist[h][kSelBins] by their first selection
+// digit: an LDS histogram per round of heads (16-bit counts in the staging
+// memory, dead once the tile is scored), then one global atomic per non-empty
+// bin.
+template <int G, int TB>
+__device__ __forceinline__ void hist_tile(const ScanArgs& a, uint32_t* hist, int64_t g, int64_t tile,
+                                          const float (&acc)[kSub][G], ScanSmem<G, TB>& sm) {
+  constexpr int NT = Cfg<G, TB>::threads;
+  constexpr int HR = kHistHeads<G, TB>;
+  static_assert(HR >= 1 && TB * kBlock < 65536, "16-bit counts of at least one head must fit");
+  const int tid = threadIdx.x;
+  const int64_t key0 = tile * TB * kBlock;
+  uint32_t* lh = reinterpret_cast<uint32_t*>(&sm);
 #pragma unroll
-    for (int h0 = 0; h0 < G; h0 += HR) {
-      __syncthreads();   // every wave is past the staging memory (or the previous round's flush)
-      for (int i = tid; i < HR * kHistWords; i += NT) lh[i] = 0u;
-      __syncthreads();
-      if (bl < nvalid) {
+  for (int h0 = 0; h0 < G; h0 += HR) {
+    __syncthreads();   // every wave is past the staging memory (or the previous round's flush)
+    for (int i = tid; i < HR * kHistWords; i += NT) lh[i] = 0u;
+    __syncthreads();
 #pragma unroll
-        for (int s2 = 0; s2 < kSub; ++s2) {
-          const int64_t j = (blk0 + bl) * kBlock + 4 * (lane & 31) + s2;
-          if (j < a.n) {
+    for (int s2 = 0; s2 < kSub; ++s2) {
+      if (key0 + tile_key<TB>(s2) < a.n) {
 #pragma unroll
-            for (int hh = 0; hh < HR; ++hh) {
-              if (h0 + hh < G) {
-                const uint32_t b = order_key(acc[s2][h0 + hh]) >> kSelDigit0;
-                atomicAdd(&lh[hh * kHistWords + (b >> 1)], 1u << (16 * (b & 1u)));
-              }
-            }
+        for (int hh = 0; hh < HR; ++hh) {
+          if (h0 + hh < G) {
+            const uint32_t b = order_key(acc[s2][h0 + hh]) >> kSelDigit0;
+            atomicAdd(&lh[hh * kHistWords + (b >> 1)], 1u << (16 * (b & 1u)));
           }
         }
       }
-      __syncthreads();
-      for (int i = tid; i < HR * kHistWords; i += NT) {
-        const int hh = h0 + i / kHistWords;
-        const uint32_t v = lh[i];
-        if (hh < G && v) {
-          uint32_t* gh = a.hist + (g * G + hh) * kSelBins + 2 * (i % kHistWords);
-          if (v & 0xffffu) atomicAdd(gh, v & 0xffffu);
-          if (v >> 16) atomicAdd(gh + 1, v >> 16);
-        }
+    }
+    __syncthreads();
+    for (int i = tid; i < HR * kHistWords; i += NT) {
+      const int hh = h0 + i / kHistWords;
+      const uint32_t v = lh[i];
+      if (hh < G && v) {
+        uint32_t* gh = hist + (g * G + hh) * kSelBins + 2 * (i % kHistWords);
+        if (v & 0xffffu) atomicAdd(gh, v & 0xffffu);
+        if (v >> 16) atomicAdd(gh + 1, v >> 16);
       }
     }
   }
+}
+
+// Device-scope atomic accesses (performed coherently across the XCDs), and a
+// wait for this wavefront's outstanding vector memory operations.
+__device__ __forceinline__ uint32_t load_coherent(uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_vmem() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Wavefront-wide sum and maximum of a float (DPP moves within rows of 16 lanes,
+// then the row-15 and row-31 broadcasts; lane 63 ends with the result, which is
+// returned to every lane).  Every lane must be active.
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#define FATHOM_DPP_ADD(ctrl, rm) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, rm, 0xf, true))
+  FATHOM_DPP_ADD(0x111, 0xf);   // row_shr:1
+  FATHOM_DPP_ADD(0x112, 0xf);   // row_shr:2
+  FATHOM_DPP_ADD(0x114, 0xf);   // row_shr:4
+  FATHOM_DPP_ADD(0x118, 0xf);   // row_shr:8
+  FATHOM_DPP_ADD(0x142, 0xa);   // row_bcast:15
+  FATHOM_DPP_ADD(0x143, 0xc);   // row_bcast:31
+#undef FATHOM_DPP_ADD
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#define FATHOM_DPP_MAX(ctrl, rm) v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, ctrl, rm, 0xf, true))
+  FATHOM_DPP_MAX(0x111, 0xf);
+  FATHOM_DPP_MAX(0x112, 0xf);
+  FATHOM_DPP_MAX(0x114, 0xf);
+  FATHOM_DPP_MAX(0x118, 0xf);
+  FATHOM_DPP_MAX(0x142, 0xa);
+  FATHOM_DPP_MAX(0x143, 0xc);
+#undef FATHOM_DPP_MAX
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// The tile's part of the heads' first-digit histograms for the selection on the
+// fly (the histograms of the tiles on its XCD), limited to its upper scores.
+// Per head the cut is the first digit of
+// mean + sd/2 of the tile's scores (about the top third for a bell-shaped
+// spread), raised if needed so that the bins from the cut to the tile's
+// largest fit a window of kCutWindow; only keys at or above the cut are counted
+// (an LDS histogram of the window, then one atomic per non-empty bin), and the
+// head's highest cut over the XCD's tiles is kept.
+// Every bin at or above that highest cut is then exact; the selection needs
+// only those, provided the k-th largest key lies among them, which it checks.
+constexpr int kCutWindow = 512;
+
+template <int G, int TB>
+__device__ __forceinline__ void cut_hist_tile(const ScanArgs& a, uint32_t* xhist, uint32_t* sync, int h_q,
+                                              int xcd, int64_t g, int64_t tile, const float (&acc)[kSub][G],
+                                              ScanSmem<G, TB>& sm) {
+  constexpr int NT = Cfg<G, TB>::threads;
+  constexpr int NW = NT / 64;
+  static_assert((3 * G * NW + G * kCutWindow) * 4 <= (int)sizeof(ScanSmem<G, TB>), "the window fits the staging memory");
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int64_t key0 = tile * TB * kBlock;
+  const int nkeys = (int)min<int64_t>(TB * kBlock, a.n - key0);
+  float* red = reinterpret_cast<float*>(&sm);                        // [G][2][NW] sums
+  uint32_t* bmax = reinterpret_cast<uint32_t*>(&sm) + 2 * G * NW;     // [G][NW] largest bin
+  uint32_t* lh = reinterpret_cast<uint32_t*>(&sm) + 3 * G * NW;       // [G][kCutWindow]
+  __syncthreads();   // every wave is past the staging memory
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float m1 = 0.0f, m2 = 0.0f;
+    uint32_t mb = 0;
+#pragma unroll
+    for (int s2 = 0; s2 < kSub; ++s2) {
+      if (tile_key<TB>(s2) < nkeys) {
+        m1 += acc[s2][h];
+        m2 = fmaf(acc[s2][h], acc[s2][h], m2);
+        mb = max(mb, order_key(acc[s2][h]) >> kSelDigit0);
+      }
+    }
+    m1 = wave_sum_f32(m1);
+    m2 = wave_sum_f32(m2);
+    mb = wave_max_u32(mb);
+    if (lane == 0) {
+      red[(2 * h) * NW + wv] = m1;
+      red[(2 * h + 1) * NW + wv] = m2;
+      bmax[h * NW + wv] = mb;
+    }
+  }
+  for (int i = tid; i < G * kCutWindow; i += NT) lh[i] = 0u;
+  __syncthreads();
+  uint32_t lo[G], hi[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float m1 = 0.0f, m2 = 0.0f;
+    uint32_t mb = 0;
+#pragma unroll
+    for (int x = 0; x < NW; ++x) {
+      m1 += red[(2 * h) * NW + x];
+      m2 += red[(2 * h + 1) * NW + x];
+      mb = max(mb, bmax[h * NW + x]);
+    }
+    const float mean = m1 / (float)nkeys;
+    const float var = fmaxf(m2 / (float)nkeys - mean * mean, 0.0f);
+    const uint32_t cut = order_key(mean + 0.5f * sqrtf(var)) >> kSelDigit0;
+    hi[h] = mb;
+    lo[h] = min(mb, max(cut, mb + 1 >= (uint32_t)kCutWindow ? mb + 1 - kCutWindow : 0u));
+  }
+  if (tid < G) {
+    uint32_t c = lo[0];
+#pragma unroll
+    for (int h = 1; h < G; ++h)
+      if (tid == h) c = lo[h];
+    atomicMax(&sync[sel::kSyncWords * (g * G + tid) + sel::kSyncXcdCut + xcd], c);
+  }
+#pragma unroll
+  for (int s2 = 0; s2 < kSub; ++s2) {
+    if (tile_key<TB>(s2) < nkeys) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const uint32_t b = order_key(acc[s2][h]) >> kSelDigit0;
+        if (b >= lo[h]) atomicAdd(&lh[h * kCutWindow + (b - lo[h])], 1u);
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    for (int b = tid; b <= (int)(hi[h] - lo[h]); b += NT) {
+      const uint32_t v = lh[h * kCutWindow + b];
+      if (v) atomicAdd(&xhist[((int64_t)xcd * h_q + g * G + h) * kSelBins + lo[h] + b], v);
+    }
+  }
+}
+
+// One workgroup's threshold bins for the heads [h0, h0 + HB) of KV head g from
+// their first-digit histograms (exact from each head's cut upward), written to
+// the selection state: word 0 the bin, 1 the keys above it, 2 the overflow flag
+// (2 if the bin is unknown: the k-th key lies below the cut or fewer than k
+// keys were counted, so the resolve counts the row itself; 1 if the bin's
+// candidates exceed the resolve's on-chip buffer).  Thread t holds bins
+// 16 t .. 16 t + 15 in registers.
+template <int NT, int HB>
+__device__ __forceinline__ void find_thresholds(const uint32_t* hist, const uint32_t* sync, uint32_t* state,
+                                                int64_t h0, uint32_t k, uint32_t* wsum) {
+  constexpr int NW = NT / 64;
+  constexpr int PER = kSelBins / NT;
+  static_assert(PER == 16, "16 bins per thread");
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  uint32_t v[HB][PER];
+  uint32_t cut[HB];
+#pragma unroll
+  for (int hh = 0; hh < HB; ++hh) {
+    const uint4* src = reinterpret_cast<const uint4*>(hist + (h0 + hh) * kSelBins + PER * tid);
+#pragma unroll
+    for (int r = 0; r < PER / 4; ++r) {
+      const uint4 x = src[r];
+      v[hh][4 * r] = x.x;
+      v[hh][4 * r + 1] = x.y;
+      v[hh][4 * r + 2] = x.z;
+      v[hh][4 * r + 3] = x.w;
+    }
+    cut[hh] = sync[sel::kSyncWords * (h0 + hh) + sel::kSyncCut];
+  }
+  // per head: the thread's total and its total at or above the cut, then
+  // suffix sums over the workgroup (wavefront scans, then wavefront totals)
+  uint32_t mine[HB], part[HB], inc[HB], incp[HB];
+#pragma unroll
+  for (int hh = 0; hh < HB; ++hh) {
+    mine[hh] = part[hh] = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      mine[hh] += v[hh][i];
+      part[hh] += (uint32_t)(PER * tid + i) >= cut[hh] ? v[hh][i] : 0u;
+    }
+    inc[hh] = wave_inclusive_sum(mine[hh]);
+    incp[hh] = wave_inclusive_sum(part[hh]);
+    if (lane == 63) {
+      wsum[(2 * hh) * NW + wv] = inc[hh];
+      wsum[(2 * hh + 1) * NW + wv] = incp[hh];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int hh = 0; hh < HB; ++hh) {
+    uint32_t* st = state + (h0 + hh) * sel::kStateWords;
+    uint32_t wtot = (uint32_t)__builtin_amdgcn_readlane((int)inc[hh], 63);
+    uint32_t above = wtot - inc[hh];   // this wavefront's lanes above this one
+    uint32_t counted = 0;
+    for (int x = 0; x < NW; ++x) {
+      if (x > wv) above += wsum[(2 * hh) * NW + x];
+      counted += wsum[(2 * hh + 1) * NW + x];
+    }
+    if (tid == 0 && counted < k) store_coherent(&st[2], 2u);
+#pragma unroll
+    for (int i = PER - 1; i >= 0; --i) {
+      if (above < k && above + v[hh][i] >= k) {
+        const uint32_t bin = (uint32_t)(PER * tid + i);
+        const bool known = counted >= k && bin >= cut[hh];
+        store_coherent(&st[0], known ? bin : 0u);
+        store_coherent(&st[1], known ? above : 0u);
+        store_coherent(&st[2], !known ? 2u : above + v[hh][i] > (uint32_t)sel::kKeep ? 1u : 0u);
+      }
+      above += v[hh][i];
+    }
+  }
+  wait_vmem();
+  __syncthreads();
+}
+
+// Scores of tile `tile` (TB blocks) of KV head g, all its query heads.  With
+// FUSE, the tile's scores are also counted into a.hist by their first
+// selection digit.
+template <int G, int TB, bool FUSE = false>
+__device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t tile, ScanSmem<G, TB>& sm) {
+  float acc[kSub][G];
+  scan_tile_acc<G, TB>(a, g, tile, sm, acc);
+  store_tile<G, TB>(a, g, tile, acc);
+  if constexpr (FUSE) hist_tile<G, TB>(a, a.hist, g, tile, acc, sm);
 }
 
 // Tile size per residency: device memory likes many small tiles (occupancy);
@@ -487,13 +711,194 @@ __global__ __launch_bounds__((Cfg<G, TB>::threads)) void scan_kernel(ScanArgs a,
 }
 
 // ---------------------------------------------------------------------------
+// HBM-resident records, selecting on the fly.  Read from HBM the scan is bound
+// by its vector work, so a round trip of the fp32 scores through HBM (written
+// once, read by the histogram and the collect) would cost more traffic than the
+// records themselves.  Instead every tile of a launch stays resident (a
+// cooperative launch) and keeps its scores in registers:
+//  1. score the tile, count its scores into the heads' first-digit histograms;
+//  2. one arrival per tile on its KV head's counter; the last tile of a KV head
+//     finds each of its heads' threshold bin b (the bin of the k-th largest
+//     key), records it in the selection state, and raises the head's ready
+//     flag; the others wait for the flag;
+//  3. every tile compacts its keys in bin b or above, in index order, into its
+//     slot of the kept keys (or a spill segment), exactly as the collect does
+//     for a chunk.  A head whose candidates exceed what the resolve holds on
+//     chip writes its whole row of scores instead, for the resolve's row path.
+// The resolve then finishes the selection.  The wait is bounded (about a
+// second) so the kernel ends even if residency were ever violated; the
+// selection would then be unspecified.
+// ---------------------------------------------------------------------------
+
+using sel::kTileSlot;                        // kept keys per 1024-key tile slot
+
+constexpr int kTileSelect = 8;    // tiles of the scan that selects on the fly: 1024 keys, 256 threads
+static_assert(sel::kTileChunk == kTileSelect * kBlock, "the selection sizes its counts for these tiles");
+constexpr uint32_t kSpinLimit = 1u << 24;    // ready-flag polls (s_sleep 2 apart)
+
+struct FuseSel {
+  uint32_t* hist;     // [h_q][kSelBins], zero on entry
+  uint32_t* xhist;    // [8][h_q][kSelBins], zero on entry
+  int h_q;
+  uint32_t* state;    // [h_q][8], zero on entry
+  uint32_t* sync;     // [h_q][2] (words 2g, 2g + 1 per KV head g), zero on entry
+  uint32_t* counts;   // [h_q][tiles] kept keys per tile
+  uint32_t* soff;     // [h_q][tiles] spill offsets
+  uint64_t* kept;     // [h_q][tiles][kTileSlot]
+  uint64_t* spill;    // [h_q][spill_cap]
+  int64_t spill_cap;
+  int k;
+};
+
+template <int G>
+__global__ __launch_bounds__((Cfg<G, kTileSelect>::threads)) void scan_select_kernel(ScanArgs a, FuseSel f,
+                                                                                      int64_t tiles) {
+  constexpr int TB = kTileSelect;
+  constexpr int NT = Cfg<G, TB>::threads;
+  constexpr int NW = NT / 64;
+  constexpr int TK = TB * kBlock;   // keys per tile
+  static_assert(NT == sel::kSelThreads && TK == 4 * NT, "one quad of the tile's keys per thread");
+  static_assert(sizeof(ScanSmem<G, TB>) >= (size_t)G * TK * 4, "the tile's scores fit the staging memory");
+  __shared__ ScanSmem<G, TB> sm;
+  __shared__ uint32_t head_info[G][2];   // threshold bin, overflow flag
+  __shared__ uint32_t cnt[1][NW];
+  __shared__ uint64_t* dst_sh;
+  __shared__ uint32_t cap_sh;
+  __shared__ uint32_t last_sh;
+  const int64_t w = blockIdx.x;
+  const int64_t t8 = (tiles + kXcds - 1) / kXcds;
+  const int64_t j = w / kXcds;
+  const int64_t g = j / t8;
+  const int64_t tile = (w % kXcds) * t8 + j % t8;
+  if (tile >= tiles) return;   // grid padding: not counted among the KV head's tiles
+  const int tid = threadIdx.x;
+
+  float acc[kSub][G];
+  scan_tile_acc<G, TB>(a, g, tile, sm, acc);
+  const int xcd = (int)(w % kXcds);
+  cut_hist_tile<G, TB>(a, f.xhist, f.sync, f.h_q, xcd, g, tile, acc, sm);
+
+  // ---- 2. arrival; the KV head's last tile finds the thresholds ----
+  // Everything tiles exchange inside the launch -- histogram bins, arrival
+  // counts, cuts, state and the ready flag -- is accessed with device-scope
+  // atomic operations, and a wavefront's own accesses are ordered by waiting
+  // for them to complete; a device-scope fence is taken only by the workgroups
+  // that read what other tiles wrote (the last tile of a KV head on each XCD,
+  // and the last XCD), not by every tile, since it writes back and invalidates
+  // the XCD's L2 under the tiles still reading records.  Tiles count on their
+  // XCD's counter, and only the last one of each XCD forwards its XCD's
+  // histogram bins and cut to the KV head's, so no address takes more atomics
+  // than a KV head has XCDs or an XCD has tiles of it.
+  const uint32_t on_xcd = (uint32_t)min<int64_t>(t8, tiles - xcd * t8);   // this KV head's tiles on this XCD
+  const uint32_t xcds = (uint32_t)((tiles + t8 - 1) / t8);                // XCDs holding its tiles
+  uint32_t* gsync = f.sync + sel::kSyncWords * g;
+  wait_vmem();   // every wavefront's histogram additions are performed
+  __syncthreads();
+  if (tid == 0) last_sh = atomicAdd(&gsync[xcd], 1u) == on_xcd - 1 ? 1u : 0u;
+  __syncthreads();
+  if (last_sh) {
+    // last tile of this KV head on this XCD: forward the XCD's bins from its
+    // highest cut upward, and the cut
+    __threadfence();
+    for (int hh = 0; hh < G; ++hh) {
+      const int64_t h = g * G + hh;
+      const uint32_t xc = f.sync[sel::kSyncWords * h + sel::kSyncXcdCut + xcd];
+      const uint32_t* src = f.xhist + ((int64_t)xcd * f.h_q + h) * kSelBins;
+      for (int b = (int)xc + tid; b < kSelBins; b += NT) {
+        const uint32_t v = src[b];
+        if (v) atomicAdd(&f.hist[h * kSelBins + b], v);
+      }
+      if (tid == 0) atomicMax(&f.sync[sel::kSyncWords * h + sel::kSyncCut], xc);
+    }
+    wait_vmem();
+    __syncthreads();
+    if (tid == 0) last_sh = atomicAdd(&gsync[sel::kSyncXcdsArrived], 1u) == xcds - 1 ? 2u : 0u;
+    __syncthreads();
+  }
+  uint32_t* ready = &gsync[sel::kSyncReady];
+  if (last_sh == 2u) {
+    // last XCD of the KV head: one device-scope acquire, then plain loads of
+    // the heads' histograms and cuts
+    __threadfence();
+    constexpr int HB = G < 4 ? G : 4;
+    static_assert(G % HB == 0, "whole rounds of heads");
+    __shared__ uint32_t fw[2 * HB * NW];
+    for (int h0 = 0; h0 < G; h0 += HB)
+      find_thresholds<NT, HB>(f.hist, f.sync, f.state, g * G + h0, (uint32_t)f.k, fw);
+    if (tid == 0) store_coherent(ready, 1u);   // every thread's state writes were performed
+  } else if (tid == 0) {
+    for (uint32_t it = 0; it < kSpinLimit; ++it) {
+      if (load_coherent(ready) != 0u) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  __syncthreads();
+  if (tid < G) {
+    uint32_t* st = f.state + (g * G + tid) * sel::kStateWords;
+    head_info[tid][0] = load_coherent(&st[0]);
+    head_info[tid][1] = load_coherent(&st[2]);
+  }
+  __syncthreads();   // head_info, and the staging memory is free again
+
+  // ---- 3. the tile's scores in index order through LDS, a quad per thread ----
+  float* ls = reinterpret_cast<float*>(&sm);
+#pragma unroll
+  for (int s2 = 0; s2 < kSub; ++s2) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) ls[h * TK + tile_key<TB>(s2)] = acc[s2][h];
+  }
+  __syncthreads();
+  const int64_t j0 = tile * TK;
+  for (int hh = 0; hh < G; ++hh) {
+    const int64_t h = g * G + hh;
+    float4 f4[1];
+    f4[0] = *reinterpret_cast<const float4*>(ls + hh * TK + 4 * tid);
+    if (head_info[hh][1]) {
+      // too many candidates for the resolve's on-chip buffer: the row path
+      // ranks this head from its whole row of scores
+      const int64_t jq = j0 + 4 * tid;
+      float* dst = a.scores + h * a.ld + jq;
+      if (jq + 3 < a.n) {
+        store_global(reinterpret_cast<float4*>(dst), f4[0]);
+      } else {
+        const float e4[4] = {f4[0].x, f4[0].y, f4[0].z, f4[0].w};
+        for (int e = 0; e < 4; ++e)
+          if (jq + e < a.n) dst[e] = e4[e];
+      }
+    } else {
+      uint32_t* st = f.state + h * sel::kStateWords;
+      sel::compact_chunk<NW, 1, kTileSlot>(f4, a.n, j0, kSelDigit0, head_info[hh][0], &st[3], &st[2],
+                                           h * tiles + tile, f.kept, f.counts, f.soff, f.spill + h * f.spill_cap,
+                                           f.spill_cap, cnt, &dst_sh, &cap_sh);
+    }
+  }
+}
+
+template <int G>
+hipError_t launch_scan_select_g(const uint8_t* rec, const float* q, const uint8_t* depth, const uint8_t* uni,
+                                int h_kv, const Layout& L, int d, float* scores, int64_t ld,
+                                const SelectWorkspace& ws, int k, int64_t tiles, hipStream_t s) {
+  constexpr int TB = kTileSelect;
+  ScanArgs a{rec, q, depth, uni, L.n, L.nb, L.H, L.P, L.R, d, scores, ld, nullptr, 0, nullptr, nullptr, 0, 1};
+  FuseSel f{ws.hist, ws.xhist, h_kv * G, ws.state, ws.sync, ws.counts, ws.soff, ws.kept, ws.spill, ws.spill_cap, k};
+  const int64_t grid = kXcds * h_kv * ((tiles + kXcds - 1) / kXcds);
+  void* args[] = {&a, &f, &tiles};
+  hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&scan_select_kernel<G>), dim3((unsigned)grid),
+                                            dim3(Cfg<G, TB>::threads), args, 0, s);
+  if (e != hipSuccess) (void)hipGetLastError();   // a refused launch leaves no error behind
+  return e;
+}
+
+// ---------------------------------------------------------------------------
 // Host-resident records, staged: the scan's input is first gathered from
-// pinned host memory into an HBM mirror of the records with long contiguous
-// reads (each channel's prefix run of the union depth, split into 32 KB
-// pieces), which keeps the host link at its streaming rate.  Launch i copies
-// KV heads [i*hb, (i+1)*hb) while the same launch's other workgroups scan the
-// heads staged by launch i-1, so the copy of one head overlaps the compute of
-// the previous one; kernel boundaries order the copy before its scan.
+// pinned host memory into HBM with long contiguous reads (each channel's
+// prefix run of the union depth, split into 32 KB pieces), which keeps the
+// host link at its streaming rate.  The HBM side is a ring of two KV heads'
+// records: launch i copies KV head i into slot i % 2 while the same launch's
+// other workgroups scan head i - 1 from slot (i - 1) % 2, so the copy of one
+// head overlaps the compute of the previous one; kernel boundaries order each
+// copy before its scan, and the scan of head i - 2 (launch i - 1) before the
+// copy that reuses its slot.
 // ---------------------------------------------------------------------------
 
 constexpr int64_t kCopyPiece = 32768;   // bytes per copy workgroup
@@ -535,7 +940,7 @@ __device__ __forceinline__ void copy_piece(const uint8_t* __restrict__ src, uint
   const int64_t u0 = (int64_t)sm.wsum[1][0] * (kCopyPiece / 16);
   const int64_t units = sm.wsum[1][1];
   const uint4* s4 = reinterpret_cast<const uint4*>(src + (g * d + owner) * R);
-  uint4* d4 = reinterpret_cast<uint4*>(dst + (g * d + owner) * R);
+  uint4* d4 = reinterpret_cast<uint4*>(dst + ((g % kStageRing) * d + owner) * R);
   uint4 v[PER];
 #pragma unroll
   for (int r = 0; r < PER; ++r) {
@@ -606,22 +1011,15 @@ hipError_t launch_staged_g(const uint8_t* host, uint8_t* staging, const float* q
                            int64_t ld, hipStream_t s) {
   constexpr int TB = kTileDevice;
   const ScanArgs a{staging, q, depth, uni, L.n, L.nb, L.H, L.P, L.R, d, scores, ld, nullptr, 0, nullptr,
-                   nullptr, 0, 1};
+                   nullptr, 0, 1, kStageRing};
   const int64_t tiles = (L.nb + TB - 1) / TB;
   const int64_t ncopy = copy_pieces_per_head(L, d);
-  // heads per launch: about 64 MB of records per launch
-  const int64_t head_bytes = (int64_t)d * L.R;
-  const int hb = (int)std::max<int64_t>(
-      1, std::min<int64_t>(h_kv, (int64_t(64) << 20) / std::max<int64_t>(head_bytes, 1)));
-  const int steps = (h_kv + hb - 1) / hb;
-  for (int i = 0; i <= steps; ++i) {
-    const int64_t cg0 = (int64_t)i * hb;
-    const int ch = i < steps ? (int)std::min<int64_t>(hb, h_kv - cg0) : 0;
-    const int64_t sg0 = (int64_t)(i - 1) * hb;
-    const int sh = i > 0 ? (int)std::min<int64_t>(hb, h_kv - sg0) : 0;
+  for (int i = 0; i <= h_kv; ++i) {
+    const int ch = i < h_kv ? 1 : 0;   // copy head i (none in the last launch)
+    const int sh = i > 0 ? 1 : 0;      // scan head i - 1 (none in the first)
     const int64_t blocks = ncopy * ch + tiles * sh;
-    stage_scan_kernel<G, TB><<<(unsigned)blocks, Cfg<G, TB>::threads, 0, s>>>(a, host, cg0, ch, ncopy, sg0,
-                                                                               sh, tiles);
+    stage_scan_kernel<G, TB><<<(unsigned)blocks, Cfg<G, TB>::threads, 0, s>>>(a, host, i, ch, ncopy, i - 1, sh,
+                                                                               tiles);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -659,6 +1057,25 @@ hipError_t launch_scan_paged(const uint8_t* rec, const uint8_t* const* table, in
     case 4: return launch_any<4>(rec, host, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words, hist, pg, s);
     case 8: return launch_any<8>(rec, host, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words, hist, pg, s);
     case 16: return launch_any<16>(rec, host, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words, hist, pg, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_scan_select(const uint8_t* rec, const float* q, const uint8_t* depth, const uint8_t* uni,
+                              int h_kv, int g, const Layout& L, int d, float* scores, int64_t ld,
+                              const SelectWorkspace& ws, int k, int64_t* nchunks, int* slot, hipStream_t s) {
+  const int64_t tiles = (L.nb + kTileSelect - 1) / kTileSelect;
+  // the kept keys of every tile must fit the selection workspace's chunk slots
+  if (L.nb == 0 || tiles * kTileSlot > ws.nchunks * sel::kSlot || ws.spill_cap < sel::kKeep)
+    return hipErrorCooperativeLaunchTooLarge;
+  *nchunks = tiles;
+  *slot = kTileSlot;
+  switch (g) {
+    case 1: return launch_scan_select_g<1>(rec, q, depth, uni, h_kv, L, d, scores, ld, ws, k, tiles, s);
+    case 2: return launch_scan_select_g<2>(rec, q, depth, uni, h_kv, L, d, scores, ld, ws, k, tiles, s);
+    case 4: return launch_scan_select_g<4>(rec, q, depth, uni, h_kv, L, d, scores, ld, ws, k, tiles, s);
+    case 8: return launch_scan_select_g<8>(rec, q, depth, uni, h_kv, L, d, scores, ld, ws, k, tiles, s);
+    case 16: return launch_scan_select_g<16>(rec, q, depth, uni, h_kv, L, d, scores, ld, ws, k, tiles, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -32,68 +32,26 @@
 #include <algorithm>
 
 #include "fathom_internal.h"
+#include "select_parts.h"
 
 namespace fathom {
 namespace {
 
-constexpr int kSelThreads = 256;
-constexpr int kPerThread = 16;
-constexpr int kChunk = kSelThreads * kPerThread;   // keys per hist/collect workgroup
-constexpr int kBins = kSelBins;                    // first digit: top 12 key bits
-constexpr int kDigit0 = kSelDigit0;                // shift of the first digit
-constexpr int kResolveThreads = 1024;
-constexpr int kSlot = 512;                         // kept keys per 4096-key chunk
-constexpr int kKeep = 16384;                       // kept keys per head resolved in LDS (128 KB)
-constexpr int kKeepPer = kKeep / kResolveThreads;
-constexpr int k2ndBins = 1024;                     // second digit: the next 10 key bits
-constexpr int64_t kRefineMin = 262144;             // rows at least this long get the refinement stage
-// State per head: [0] first-digit bin b of the k-th key, [1] keys above bin b,
-// [2] spill overflow of the collect, [3] its spill counter, [4] the refined
-// second digit b2 | kRefined, [5] keys of bin b above b2, [6] spill overflow
-// of the recollect, [7] its spill counter.
-constexpr int kStateWords = 8;
-constexpr int kSmallRow = 16384;                   // rows up to this long are selected by sel_small
-constexpr uint32_t kRefined = 0x80000000u;
+using namespace sel;
 
-__global__ __launch_bounds__(kSelThreads) void sel_init(uint32_t* hist, uint32_t* state, uint32_t* hist2) {
+
+__global__ __launch_bounds__(kSelThreads) void sel_init(uint32_t* hist, uint32_t* state, uint32_t* sync,
+                                                        uint32_t* hist2, uint32_t* xhist, int h_q) {
   const int h = blockIdx.x;
   for (int b = threadIdx.x; b < kBins; b += kSelThreads) hist[(int64_t)h * kBins + b] = 0u;
+  if (xhist)
+    for (int x = 0; x < kXcdCount; ++x)
+      for (int b = threadIdx.x; b < kBins / 4; b += kSelThreads)
+        reinterpret_cast<uint4*>(xhist + ((int64_t)x * h_q + h) * kBins)[b] = make_uint4(0u, 0u, 0u, 0u);
   if (threadIdx.x < kStateWords) state[h * kStateWords + threadIdx.x] = 0u;
+  if (threadIdx.x < kSyncWords) sync[kSyncWords * h + threadIdx.x] = 0u;
   if (hist2)
     for (int b = threadIdx.x; b < k2ndBins; b += kSelThreads) hist2[(int64_t)h * k2ndBins + b] = 0u;
-}
-
-// inclusive suffix sum over the workgroup's threads (thread t gets sum over t' >= t)
-template <int NT>
-__device__ __forceinline__ uint32_t block_suffix_inclusive(uint32_t v, uint32_t* wsum) {
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const uint32_t inc = wave_inclusive_sum(v);
-  const uint32_t s = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63) - inc + v;   // lanes >= this one
-  __syncthreads();
-  if (lane == 0) wsum[w] = s;
-  __syncthreads();
-  uint32_t above = 0;
-  for (int x = w + 1; x < NT / 64; ++x) above += wsum[x];
-  return s + above;
-}
-
-// exclusive prefix sum over the workgroup's threads, in thread order; *total = sum
-template <int NT>
-__device__ __forceinline__ uint32_t block_exclusive(uint32_t v, uint32_t* wsum, uint32_t* total) {
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const uint32_t inc = wave_inclusive_sum(v);
-  __syncthreads();
-  if (lane == 63) wsum[w] = inc;
-  __syncthreads();
-  uint32_t base = 0, all = 0;
-  for (int x = 0; x < NT / 64; ++x) {
-    if (x < w) base += wsum[x];
-    all += wsum[x];
-  }
-  *total = all;
-  return base + inc - v;
 }
 
 // First-digit histogram of `per` consecutive chunks per workgroup (long rows
@@ -129,83 +87,6 @@ __global__ __launch_bounds__(kSelThreads) void sel_hist(const float* __restrict_
   for (int b = threadIdx.x; b < kBins; b += kSelThreads) {
     const uint32_t v = lh[b];
     if (v) atomicAdd(&hist[(int64_t)h * kBins + b], v);
-  }
-}
-
-// Compacts the keys of chunk c of a head (its scores f, first key j0) whose
-// key >> shift is at least thr, in index order, into the chunk's slot or, if
-// they do not fit there, a segment of the head's spill area claimed with one
-// atomic on *ctr (all of the head's kept keys must fit the resolve's on-chip
-// buffer, so the area has that size; beyond it *overflow is set and the head
-// takes the resolve's full-row path).  Quad i of wavefront w holds keys
-// j0 + 4 (256 i + 64 w + lane) + e, e < 4, so (i, w, lane, e) order is index
-// order.  Called by every thread of the workgroup.
-template <int NW, int NQ>
-__device__ __forceinline__ void compact_chunk(const float4 (&f)[NQ], int64_t n, int64_t j0, int shift, uint32_t thr,
-                                              uint32_t* ctr, uint32_t* overflow, int64_t c, uint64_t* kept,
-                                              uint32_t* counts, uint32_t* soff, uint64_t* spill_h,
-                                              int64_t spill_cap, uint32_t (*cnt)[NW], uint64_t** dst_sh,
-                                              uint32_t* cap_sh) {
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  uint32_t key[NQ][4];
-  uint64_t mask[NQ][4];
-#pragma unroll
-  for (int i = 0; i < NQ; ++i) {
-    const int64_t j = j0 + 4 * ((int64_t)i * kSelThreads + threadIdx.x);
-    const float e4[4] = {f[i].x, f[i].y, f[i].z, f[i].w};
-    uint32_t cc = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      key[i][e] = order_key(e4[e]);
-      mask[i][e] = __ballot(j + e < n && (key[i][e] >> shift) >= thr);
-      cc += (uint32_t)__popcll(mask[i][e]);
-    }
-    if (lane == 0) cnt[i][w] = cc;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t tot = 0;
-    for (int i = 0; i < NQ; ++i)
-      for (int x = 0; x < NW; ++x) tot += cnt[i][x];
-    uint64_t* dst = kept + c * kSlot;
-    uint32_t cap = (uint32_t)kSlot;
-    if (tot > (uint32_t)kSlot) {
-      const uint32_t base = atomicAdd(ctr, tot);
-      if ((int64_t)base + tot <= spill_cap) {
-        dst = spill_h + base;
-        cap = tot;
-        soff[c] = base;
-      } else {
-        *overflow = 1u;
-        cap = 0;
-      }
-    }
-    counts[c] = tot;
-    *dst_sh = dst;
-    *cap_sh = cap;
-  }
-  __syncthreads();
-  // offset of (i, w): keys kept by the (i', w') pairs before it
-  uint64_t* dst = *dst_sh;
-  const uint32_t cap = *cap_sh;
-  const uint64_t lt = (1ull << lane) - 1ull;
-  uint32_t run = 0;
-#pragma unroll
-  for (int i = 0; i < NQ; ++i) {
-    uint32_t off = run;   // kept keys of the quads before (i, w, lane)
-    for (int x = 0; x < w; ++x) off += cnt[i][x];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) off += (uint32_t)__popcll(mask[i][e] & lt);
-    const int64_t j = j0 + 4 * ((int64_t)i * kSelThreads + threadIdx.x);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if ((mask[i][e] >> lane) & 1ull) {
-        if (off < cap) store_global(dst + off, ((uint64_t)key[i][e] << 32) | (uint32_t)(j + e));
-        ++off;
-      }
-    }
-    for (int x = 0; x < NW; ++x) run += cnt[i][x];
   }
 }
 
@@ -377,31 +258,6 @@ __global__ __launch_bounds__(kSelThreads) void sel_recollect(const float* __rest
   }
 }
 
-// The bin of an NB-bin histogram holding the need-th largest key: sh[0] = bin,
-// sh[1] = keys in higher bins.  Called by every thread; needs 1 <= need <= total.
-template <int NT, int NB = kBins>
-__device__ __forceinline__ void find_bin(const uint32_t* lh, uint32_t need, uint32_t* wsum, uint32_t* sh) {
-  static_assert(NB % NT == 0, "whole bins per thread");
-  constexpr int kPer = NB / NT;
-  uint32_t v[kPer];
-  uint32_t mine = 0;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    v[i] = lh[threadIdx.x * kPer + i];
-    mine += v[i];
-  }
-  uint32_t above = block_suffix_inclusive<NT>(mine, wsum) - mine;
-#pragma unroll
-  for (int i = kPer - 1; i >= 0; --i) {
-    if (above < need && above + v[i] >= need) {
-      sh[0] = threadIdx.x * kPer + i;
-      sh[1] = above;
-    }
-    above += v[i];
-  }
-  __syncthreads();
-}
-
 // Streams wavefront w's contiguous part of a row -- the w-th of NW parts, each a
 // multiple of 256 keys -- in sweeps of 256 keys, lane l taking keys 4l .. 4l+3 of
 // each (so lane-major order within a sweep is index order), U sweeps of loads in
@@ -457,13 +313,28 @@ __device__ __forceinline__ float key_to_float(uint32_t key) {
 // keys above T and the first `need` keys equal to T in index order.  Barriers:
 // a handful in all, none per sweep.
 __device__ void resolve_row(const float* __restrict__ row, int64_t n, int k, uint32_t bin, uint32_t above,
-                            int32_t* __restrict__ out, float* __restrict__ outv, uint32_t* lh, uint32_t* wsum,
-                            uint32_t* sh) {
+                            bool bin_known, int32_t* __restrict__ out, float* __restrict__ outv, uint32_t* lh,
+                            uint32_t* wsum, uint32_t* sh) {
   constexpr int NT = kResolveThreads;
   constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const uint64_t lt = (1ull << lane) - 1ull;
+  if (!bin_known) {
+    // no histogram of the row exists: count its first digits here (lh holds kBins words)
+    for (int b = threadIdx.x; b < kBins; b += NT) lh[b] = 0u;
+    __syncthreads();
+    stream_part<NW>(row, n, [&](int64_t, const float (&v)[4], int valid) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (i < valid) atomicAdd(&lh[order_key(v[i]) >> kDigit0], 1u);
+    });
+    __syncthreads();
+    find_bin<NT, kBins>(lh, (uint32_t)k, wsum, sh);
+    bin = sh[0];
+    above = sh[1];
+    __syncthreads();
+  }
   uint32_t prefix = bin, need = (uint32_t)k - above;
   for (int pass = 0; pass < 2; ++pass) {
     const int shift = pass == 0 ? 10 : 0;
@@ -570,7 +441,7 @@ __global__ __launch_bounds__(kResolveThreads) void sel_resolve(const float* __re
                                                                const uint32_t* __restrict__ counts,
                                                                const uint32_t* __restrict__ soff,
                                                                const uint64_t* __restrict__ spill, int64_t spill_cap,
-                                                               int64_t nchunks, int32_t* __restrict__ idx,
+                                                               int64_t nchunks, int slot, int32_t* __restrict__ idx,
                                                                float* __restrict__ val) {
   constexpr int NT = kResolveThreads;
   __shared__ uint64_t buf[kKeep];          // kept (key, index) of the head, in index order
@@ -611,13 +482,16 @@ __global__ __launch_bounds__(kResolveThreads) void sel_resolve(const float* __re
     fallback = total > (uint32_t)kKeep;
   }
   if (fallback) {
-    resolve_row(row, n, k, bin, above, out, outv, lh, wsum, sh);
+    // state word 2 (or 6) is 2 where the threshold bin was never found: the scan
+    // that selects on the fly gave the head its whole row of scores but no
+    // exact histogram
+    resolve_row(row, n, k, bin, above, st[refined ? 6 : 2] != 2u, out, outv, lh, wsum, sh);
     return;
   }
   __syncthreads();
   // a chunk's kept keys: its slot, or its spill segment when they overflowed it
   auto src_of = [&](int64_t c, uint32_t cn) -> const uint64_t* {
-    return cn <= (uint32_t)kSlot ? kept + ((int64_t)h * nchunks + c) * kSlot
+    return cn <= (uint32_t)slot ? kept + ((int64_t)h * nchunks + c) * slot
                                  : spill + (int64_t)h * spill_cap + soff[(int64_t)h * nchunks + c];
   };
   // gather in chunk order, every load of a batch issued before its stores; keys
@@ -826,6 +700,12 @@ size_t al256(size_t x) { return (x + 255) / 256 * 256; }
 
 int64_t select_chunks(int64_t n) { return (n + kChunk - 1) / kChunk; }
 
+// Entries per head of the kept-key counts and spill offsets: one per chunk of
+// the smallest kind that compacts into them, the 1024-key tiles of the scan that
+// selects on the fly (their slots are a quarter of a 4096-key chunk's, so the
+// kept keys' area fits both).
+static int64_t count_entries(int64_t n) { return (n + kTileChunk - 1) / kTileChunk; }
+
 // Spill entries per head: the resolve holds at most kKeep kept keys (rows of at
 // most kSmallRow keys are selected by sel_small and need none).
 int64_t spill_entries(int64_t n) { return n <= kSmallRow ? 0 : kKeep; }
@@ -837,13 +717,15 @@ static size_t hist2_bytes(int h_q, int64_t n) { return n >= kRefineMin ? al256((
 size_t select_workspace_bytes(int h_q, int64_t n, int k) {
   (void)k;
   const size_t nc = (size_t)select_chunks(n);
-  return al256((size_t)h_q * kBins * 4) + al256((size_t)h_q * kStateWords * 4) + hist2_bytes(h_q, n) +
-         2 * al256((size_t)h_q * nc * 4) + al256((size_t)h_q * nc * kSlot * 8) +
+  return al256((size_t)h_q * kBins * 4) + al256((size_t)h_q * kStateWords * 4) + al256((size_t)h_q * kSyncWords * 4) +
+         hist2_bytes(h_q, n) +
+         2 * al256((size_t)h_q * (size_t)count_entries(n) * 4) + al256((size_t)h_q * nc * kSlot * 8) +
+         (n > kSmallRow ? al256((size_t)kXcdCount * h_q * kBins * 4) : 0) +
          al256((size_t)h_q * (size_t)spill_entries(n) * 8);
 }
 
 size_t select_clear_words(const SelectWorkspace& ws, int h_q) {
-  return (al256((size_t)h_q * kBins * 4) + al256((size_t)h_q * kStateWords * 4) +
+  return (al256((size_t)h_q * kBins * 4) + al256((size_t)h_q * kStateWords * 4) + al256((size_t)h_q * kSyncWords * 4) +
           (ws.hist2 ? al256((size_t)h_q * k2ndBins * 4) : 0)) / 4;
 }
 
@@ -856,22 +738,26 @@ SelectWorkspace carve_select(void* base, int h_q, int64_t n, int k) {
   p += al256((size_t)h_q * kBins * 4);
   ws.state = reinterpret_cast<uint32_t*>(p);
   p += al256((size_t)h_q * kStateWords * 4);
+  ws.sync = reinterpret_cast<uint32_t*>(p);
+  p += al256((size_t)h_q * kSyncWords * 4);
   ws.hist2 = n >= kRefineMin ? reinterpret_cast<uint32_t*>(p) : nullptr;
   p += hist2_bytes(h_q, n);
   ws.counts = reinterpret_cast<uint32_t*>(p);
-  p += al256((size_t)h_q * (size_t)ws.nchunks * 4);
+  p += al256((size_t)h_q * (size_t)count_entries(n) * 4);
   ws.soff = reinterpret_cast<uint32_t*>(p);
-  p += al256((size_t)h_q * (size_t)ws.nchunks * 4);
+  p += al256((size_t)h_q * (size_t)count_entries(n) * 4);
   ws.kept = reinterpret_cast<uint64_t*>(p);
   p += al256((size_t)h_q * (size_t)ws.nchunks * kSlot * 8);
   ws.spill = reinterpret_cast<uint64_t*>(p);
   ws.spill_cap = spill_entries(n);
+  p += al256((size_t)h_q * (size_t)spill_entries(n) * 8);
+  ws.xhist = n > kSmallRow ? reinterpret_cast<uint32_t*>(p) : nullptr;
   ws.small = n <= kSmallRow;
   return ws;
 }
 
-hipError_t launch_select_clear(const SelectWorkspace& ws, int h_q, hipStream_t s) {
-  sel_init<<<h_q, kSelThreads, 0, s>>>(ws.hist, ws.state, ws.hist2);
+hipError_t launch_select_clear(const SelectWorkspace& ws, int h_q, hipStream_t s, bool xcd_hists) {
+  sel_init<<<h_q, kSelThreads, 0, s>>>(ws.hist, ws.state, ws.sync, ws.hist2, xcd_hists ? ws.xhist : nullptr, h_q);
   return hipGetLastError();
 }
 
@@ -884,7 +770,7 @@ hipError_t launch_select(const float* scores, int64_t ld, int h_q, int64_t n, in
   }
   dim3 grid((unsigned)ws.nchunks, (unsigned)h_q);
   if (!hist_done) {
-    if (!cleared) sel_init<<<h_q, kSelThreads, 0, s>>>(ws.hist, ws.state, ws.hist2);
+    if (!cleared) sel_init<<<h_q, kSelThreads, 0, s>>>(ws.hist, ws.state, ws.sync, ws.hist2, nullptr, h_q);
     // chunks per histogram workgroup: 1, or more while the grid keeps >= 1024 workgroups
     // (4 per CU); fewer workgroups flush fewer partial histograms
     int per = 1;
@@ -903,7 +789,15 @@ hipError_t launch_select(const float* scores, int64_t ld, int h_q, int64_t n, in
                                                 ws.soff, ws.spill, ws.spill_cap, ws.nchunks, rper);
   }
   sel_resolve<<<h_q, kResolveThreads, 0, s>>>(scores, ld, n, k, ws.state, ws.kept, ws.counts, ws.soff, ws.spill,
-                                              ws.spill_cap, ws.nchunks, idx, val);
+                                              ws.spill_cap, ws.nchunks, kSlot, idx, val);
+  return hipGetLastError();
+}
+
+hipError_t launch_select_resolve(const float* scores, int64_t ld, int h_q, int64_t n, int k, int32_t* idx,
+                                 float* val, const SelectWorkspace& ws, int64_t nchunks, int slot, hipStream_t s) {
+  if (k == 0 || n == 0 || h_q == 0) return hipSuccess;
+  sel_resolve<<<h_q, kResolveThreads, 0, s>>>(scores, ld, n, k, ws.state, ws.kept, ws.counts, ws.soff, ws.spill,
+                                              ws.spill_cap, nchunks, slot, idx, val);
   return hipGetLastError();
 }
 

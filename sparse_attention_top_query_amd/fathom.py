@@ -173,7 +173,7 @@ def scan_topk(records: torch.Tensor, q: torch.Tensor, depth: torch.Tensor, union
 
     ``records`` may be a device tensor (HBM residency) or a pinned host tensor
     (read in place over the host link by default; HOST_STAGED gathers the
-    prefix runs into an HBM mirror first)."""
+    prefix runs into a ring of two KV heads' records in HBM first)."""
     _need(q, "q", torch.float32, 2)
     _need(depth, "depth", torch.uint8)
     _need(union_depth, "union_depth", torch.uint8)

@@ -56,7 +56,11 @@ def test_workspace_bytes_monotone(lib):
     assert a > b > 0
     assert a >= 32 * (1 << 20) * 4       # holds the fp32 scores of every head
     staged = lib.fathom_workspace_bytes(32, 8, 1 << 20, 128, 2048, 2)
-    assert staged - a >= 8 * 128 * O.record_layout(1 << 20)[3]   # plus an HBM mirror of the records
+    r = O.record_layout(1 << 20)[3]
+    # plus a ring of two KV heads' records (not a mirror of all eight)
+    assert 2 * 128 * r <= staged - a < 2 * 128 * r + 256
+    assert lib.fathom_workspace_bytes(4, 1, 1 << 20, 128, 2048, 2) - lib.fathom_workspace_bytes(
+        4, 1, 1 << 20, 128, 2048, 0) < 128 * r + 256                 # one KV head: one slot
     assert lib.fathom_workspace_bytes(32, 8, 0, 128, 0, 0) == 0
 
 

@@ -35,11 +35,10 @@ def test_algorithmic_ops_hand_count(bench):
                       [0, 3, 2, 1]], np.uint8)
     union = depth.max(axis=0)[None]                  # [0, 3, 2, 4]
     n = 256                                          # two 128-key blocks
-    # chain 2u-1 per union channel: 0 + 5 + 3 + 7 = 15
-    # one conversion per distinct depth in use per channel: 0 + 2 + 1 + 2 = 5
-    # one fma per reading head: 0 + 2 + 2 + 2 = 6
-    # plus one add per (reading head, channel) per block: 6 * 2 blocks
-    assert bench.algorithmic_ops(depth, union, n) == (15 + 5 + 6) * n + 6 * 2
+    # per 4 keys: 2 ops per union plane: 2 * (0 + 3 + 2 + 4) = 18
+    # 5 per distinct depth in use per channel: 5 * (0 + 2 + 1 + 2) = 25
+    # 4 fmas per reading head: 4 * (0 + 2 + 2 + 2) = 24
+    assert bench.algorithmic_ops(depth, union, n) == (18 + 25 + 24) * (n // 4)
 
 
 def test_algorithmic_ops_of_an_empty_budget(bench):

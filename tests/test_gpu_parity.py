@@ -330,9 +330,10 @@ def test_host_direct_topk_equals_hbm(F, case):
         assert np.array_equal(idd.cpu().numpy()[h], O.topk(sg[h].astype(np.float64), k))
 
 
-def test_staged_many_heads_per_launch(F):
-    """Records of ~10 MB per KV head put 6 KV heads in each copy/scan launch, with a
-    ragged last launch (13 = 6 + 6 + 1): staged must still equal HBM-resident."""
+def test_staged_ring_of_many_heads(F):
+    """13 KV heads of ~10 MB of records each staged through the ring of two KV
+    heads' slots (every slot reused six or seven times, odd head count): staged
+    must still equal HBM-resident, bit for bit."""
     case = (13, 4, 160000, 128, 68)
     h_kv, g, n, d, budget = case
     k, q, s2, rec, dq, dep, uni, sg = run_case(F, case)
@@ -396,7 +397,7 @@ def test_scan_rejects_bad_residency_and_workspace(F):
         assert e.value.status == -7
     host = rec.cpu().pin_memory()
     small = torch.empty(1024, dtype=torch.uint8, device="cuda:0")
-    with pytest.raises(F.FathomError) as e:       # no room for the staging mirror
+    with pytest.raises(F.FathomError) as e:       # no room for the staging ring
         F.scan_scores(host, dq, dep, uni, 1024, residency=F.HOST_STAGED, workspace=small)
     assert e.value.status == -5
     small = torch.empty(16, dtype=torch.uint8, device="cuda:0")

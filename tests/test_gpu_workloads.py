@@ -11,6 +11,8 @@ oracle computes one by one:
   * host residencies (in place and staged): bit-identical to each other.
 """
 
+import time
+
 import numpy as np
 import pytest
 import torch
@@ -32,12 +34,27 @@ def F():
     return fathom
 
 
-def pack_layer(F, k_np, host):
-    """Pack every KV head on the GPU (one head resident at a time)."""
+_PINNED = {}
+
+
+def pinned_records(shape):
+    """A pinned host buffer of this shape, allocated once per module (pinning
+    half a gigabyte takes seconds; the full-size layers reuse one buffer)."""
+    if shape not in _PINNED:
+        _PINNED.clear()
+        _PINNED[shape] = torch.empty(shape, dtype=torch.uint8, pin_memory=True)
+    return _PINNED[shape]
+
+
+def pack_layer(F, k_np, host, fresh=False):
+    """Pack every KV head on the GPU (one head resident at a time); host records
+    go to a reused pinned buffer unless `fresh`."""
     hk, n, d = k_np.shape
     r = F.record_bytes(n)
-    rec = torch.empty((hk, d, r), dtype=torch.uint8, pin_memory=True) if host else \
-        torch.empty((hk, d, r), dtype=torch.uint8, device="cuda:0")
+    if host:
+        rec = torch.empty((hk, d, r), dtype=torch.uint8, pin_memory=True) if fresh else pinned_records((hk, d, r))
+    else:
+        rec = torch.empty((hk, d, r), dtype=torch.uint8, device="cuda:0")
     stage = torch.empty((1, d, r), dtype=torch.uint8, device="cuda:0")
     status = torch.zeros(1, dtype=torch.int32, device="cuda:0")
     for v in range(hk):
@@ -81,18 +98,27 @@ def run_and_check(F, wl, layer=0, sample_heads=(0, 1, 2, 3), host_modes=None, fu
                   select_heads=None):
     budget = wl.budgets[layer]
     mode = F.WATERFILL if wl.mode == "waterfill" else F.TOPQ
+    t0 = time.perf_counter()
+
+    def mark(what):
+        print(f"  {what}: {time.perf_counter() - t0:.1f} s", flush=True)
+
     print(f"workload {wl.name} layer {layer} budget {budget}", flush=True)
     k_np, q_np, s2_np = layer_inputs(wl, layer)
+    mark("inputs drawn")
     hk, n, d = k_np.shape
     g = wl.g
     host = wl.residency == "host"
     rec = pack_layer(F, k_np, host)
+    mark("packed")
     codes = {}
     for v in sorted(set(full_record_heads) | {h // g for h in sample_heads}):
         delta = O.block_scales(k_np[v])
         codes[v] = (delta, O.quantize_codes(k_np[v], delta))
+    mark("oracle codes")
     check_records(rec.numpy() if host else rec.cpu().numpy(), k_np,
                   {v: codes[v] for v in full_record_heads})
+    mark("records checked")
     q = torch.from_numpy(q_np).to("cuda:0")
     dep, uni = F.allocate(q, torch.from_numpy(s2_np).to("cuda:0"), budget, mode=mode)
     rd, ru = oracle_depths(q_np, s2_np, budget, mode=wl.mode)
@@ -109,6 +135,7 @@ def run_and_check(F, wl, layer=0, sample_heads=(0, 1, 2, 3), host_modes=None, fu
         assert np.array_equal(results[res][0].view(np.uint32), first[0].view(np.uint32)), res
         assert np.array_equal(results[res][1], first[1]), res
     sg, idx = first
+    mark("scanned")
     for h in sample_heads:
         delta, kappa = codes[h // g]
         s, a = O.scores(q_np[h], kappa, delta, rd[h])
@@ -117,6 +144,7 @@ def run_and_check(F, wl, layer=0, sample_heads=(0, 1, 2, 3), host_modes=None, fu
     # every head (or those named): the selection is exact on the GPU's own scores
     for h in (range(idx.shape[0]) if select_heads is None else select_heads):
         assert np.array_equal(idx[h], O.topk(sg[h].astype(np.float64), wl.k)), f"select head {h}"
+    mark("checked")
 
 
 def test_w1_single_head_4k(F):
@@ -186,7 +214,7 @@ def test_w4_decode_step_loop(F):
     layers, oracle_kv = [], []
     for layer in range(W4.layers):
         k_np, q_np, s2_np = layer_inputs(W4, layer, n=n)
-        rec = pack_layer(F, k_np, host=True)
+        rec = pack_layer(F, k_np, host=True, fresh=True)
         v = layer % hk
         delta = O.block_scales(k_np[v])
         oracle_kv.append((v, delta, O.quantize_codes(k_np[v], delta)))
