@@ -202,6 +202,26 @@ int fathom_scan_scores(const void* records, int residency, const float* q,
                        int h_kv, int64_t n, int d, float* scores, int64_t ld,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* scan_topk_noalloc -- scan_topk with no workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  The workspace is a fixed device
+ * array inside the library, fathom_noalloc_scratch_bytes() (32 MiB) on every
+ * GPU the library runs on, held until the process ends; the call allocates
+ * nothing and frees nothing.
+ *   residency   FATHOM_HBM or FATHOM_HOST_DIRECT (not the staged residency,
+ *               whose HBM ring of staged records does not fit the scratch).
+ *   all other arguments and results as for scan_topk (bit-identical output).
+ * A shape whose fathom_workspace_bytes(...) exceeds the scratch returns
+ * FATHOM_EWORKSPACE and enqueues nothing (e.g. 32 query heads of 131072 keys
+ * fit; 32 heads of 1M keys do not).  Every call on a GPU uses that GPU's one
+ * scratch, which keeps the last call's contents (each call clears what it
+ * needs): calls that overlap on one GPU -- on different streams, or from
+ * different threads -- race on it and must be serialised by the caller. */
+size_t fathom_noalloc_scratch_bytes(void);
+int scan_topk_noalloc(const void* records, int residency, const float* q, const uint8_t* depth,
+                      const uint8_t* union_depth, int h_q, int h_kv, int64_t n, int d, int k,
+                      int32_t* topk_idx, float* topk_score, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Appending keys during decoding.  The block scale is shared by a whole
  * 128-key block ([Review] Strengths, paper Sec 3.2), so a key can only be

@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libfathom.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "pack.hip", "allocate.hip", "scan.hip", "select.hip", "attend.hip", "tail.hip",
-           "freepath.hip"]
+           "freepath.hip", "noalloc.hip"]
 
 # IEEE behaviour matters (exact threshold compares, fp16 RNE, fp32 products that
 # must not fuse): no fast-math.  Packed FP32 instructions are disabled.

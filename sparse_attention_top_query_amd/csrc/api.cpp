@@ -328,6 +328,30 @@ int scan_topk(const void* records, int residency, const float* q, const uint8_t*
   return ok();
 }
 
+size_t fathom_noalloc_scratch_bytes(void) { return fathom::kNoallocScratchBytes; }
+
+int scan_topk_noalloc(const void* records, int residency, const float* q, const uint8_t* depth,
+                      const uint8_t* union_depth, int h_q, int h_kv, int64_t n, int d, int k, int32_t* topk_idx,
+                      float* topk_score, void* stream) {
+  if (residency != FATHOM_HBM && residency != FATHOM_HOST_DIRECT)
+    return fail(FATHOM_ERESIDENCY, "scan_topk_noalloc reads records from HBM or in place from pinned host memory");
+  int st = check_heads(h_q, h_kv, d);
+  if (st) return st;
+  st = check_n(n, h_kv, "n");
+  if (st) return st;
+  const size_t need = fathom_workspace_bytes(h_q, h_kv, n, d, k, residency);
+  if (need > fathom::kNoallocScratchBytes)
+    return fail(FATHOM_EWORKSPACE,
+                "scan_topk_noalloc: h_q=%d, n=%lld, k=%d needs %zu bytes of workspace, more than the %zu bytes "
+                "of the library's fixed scratch (use scan_topk with a caller workspace)",
+                h_q, (long long)n, k, need, fathom::kNoallocScratchBytes);
+  void* scratch = nullptr;
+  hipError_t e = fathom::noalloc_scratch(&scratch);
+  if (e != hipSuccess) return hip_fail(e, "scratch address");
+  return scan_topk(records, residency, q, depth, union_depth, h_q, h_kv, n, d, k, topk_idx, topk_score, scratch,
+                   fathom::kNoallocScratchBytes, stream);
+}
+
 size_t fathom_attend_workspace_bytes(int h_q, int d, int k) {
   if (h_q <= 0 || d <= 0 || k <= 0) return 0;
   return fathom::attend_workspace_bytes(h_q, d, k);

@@ -93,6 +93,12 @@ __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v) {
   return v;
 }
 
+// Size of the fixed device scratch of scan_topk_noalloc (one copy per GPU).
+constexpr size_t kNoallocScratchBytes = size_t(32) << 20;
+// The current device's address of that scratch (looked up on the first call
+// per device, then cached).
+hipError_t noalloc_scratch(void** out);
+
 // ---- launchers (each returns hipSuccess or the launch error) ----
 hipError_t launch_pack(const float* k, int h_kv, const Layout& L, int d, uint8_t* rec,
                        uint32_t* status, hipStream_t s);

@@ -64,6 +64,8 @@ def load() -> ctypes.CDLL:
         "fathom_workspace_bytes": (S, [I, I, L, I, I, I]),
         "scan_topk": (I, [P, I, P, P, P, I, I, L, I, I, P, P, P, S, P]),
         "fathom_scan_scores": (I, [P, I, P, P, P, I, I, L, I, P, L, P, S, P]),
+        "fathom_noalloc_scratch_bytes": (S, []),
+        "scan_topk_noalloc": (I, [P, I, P, P, P, I, I, L, I, I, P, P, P]),
         "fathom_attend_workspace_bytes": (S, [I, I, I]),
         "pack_blocks": (I, [P, I, L, L, L, I, P, P, P]),
         "fathom_device_address": (I, [P, I, ctypes.POINTER(ctypes.c_void_p)]),
@@ -199,6 +201,36 @@ def scan_topk(records: torch.Tensor, q: torch.Tensor, depth: torch.Tensor, union
                             n, d, k, _ptr(idx), _ptr(scores), _ptr(workspace), workspace.numel(),
                             _stream(q)))
     return (idx, scores) if want_scores or scores is not None else idx
+
+
+def noalloc_scratch_bytes() -> int:
+    """Size of the library's fixed device scratch used by scan_topk_noalloc."""
+    return int(load().fathom_noalloc_scratch_bytes())
+
+
+def scan_topk_noalloc(records: torch.Tensor, q: torch.Tensor, depth: torch.Tensor, union_depth: torch.Tensor,
+                      n: int, k: int, idx: torch.Tensor, scores: torch.Tensor | None = None,
+                      residency: int | None = None):
+    """scan_topk_noalloc: scan_topk with the library's fixed scratch as workspace.
+    The outputs are passed in (nothing is allocated here either)."""
+    _need(q, "q", torch.float32, 2)
+    _need(depth, "depth", torch.uint8)
+    _need(union_depth, "union_depth", torch.uint8)
+    _need(records, "records", torch.uint8, device=False)
+    _need(idx, "idx", torch.int32)
+    if scores is not None:
+        _need(scores, "scores", torch.float32)
+    if residency is None:
+        residency = _residency_of(records)
+    h_q, d = q.shape
+    h_kv = union_depth.shape[0]
+    if records.numel() < h_kv * d * record_bytes(n):
+        raise ValueError("records buffer too small for (h_kv, d, n)")
+    if idx.numel() < h_q * k or (scores is not None and scores.numel() < h_q * k):
+        raise ValueError("idx/scores smaller than [h_q, k]")
+    _check(load().scan_topk_noalloc(_ptr(records), residency, _ptr(q), _ptr(depth), _ptr(union_depth), h_q, h_kv,
+                                    n, d, k, _ptr(idx), _ptr(scores), _stream(q)))
+    return idx
 
 
 def scan_scores(records: torch.Tensor, q: torch.Tensor, depth: torch.Tensor, union_depth: torch.Tensor,

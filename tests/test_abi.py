@@ -93,6 +93,19 @@ def test_host_validation_errors(lib):
     assert lib.fathom_scan_scores(fake, 0, None, fake, fake, 4, 1, 128, 8, fake, 128, None, 0, None) == -1
 
 
+def test_noalloc_validation(lib):
+    P = ctypes.c_void_p
+    fake = P(0x1000)
+    assert lib.fathom_noalloc_scratch_bytes() == 32 << 20
+    # shapes whose workspace exceeds the fixed scratch are refused before any HIP call
+    assert lib.scan_topk_noalloc(fake, 0, fake, fake, fake, 32, 8, 1 << 20, 128, 2048, fake, None, None) == -5
+    assert "scratch" in _err(lib)
+    assert lib.scan_topk_noalloc(fake, 2, fake, fake, fake, 4, 1, 4096, 128, 64, fake, None, None) == -7
+    assert lib.scan_topk_noalloc(fake, 0, fake, fake, fake, 6, 4, 4096, 128, 64, fake, None, None) == -2
+    # 32 query heads of 131072 keys fit
+    assert lib.fathom_workspace_bytes(32, 8, 1 << 17, 128, 2048, 0) <= lib.fathom_noalloc_scratch_bytes()
+
+
 def test_attend_workspace_and_validation(lib):
     P = ctypes.c_void_p
     f = ctypes.c_float
