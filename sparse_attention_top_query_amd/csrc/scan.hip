@@ -800,15 +800,37 @@ __global__ __launch_bounds__((Cfg<G, kTileSelect>::threads)) void scan_select_ke
     // last tile of this KV head on this XCD: forward the XCD's bins from its
     // highest cut upward, and the cut
     __threadfence();
-    for (int hh = 0; hh < G; ++hh) {
-      const int64_t h = g * G + hh;
-      const uint32_t xc = f.sync[sel::kSyncWords * h + sel::kSyncXcdCut + xcd];
-      const uint32_t* src = f.xhist + ((int64_t)xcd * f.h_q + h) * kSelBins;
-      for (int b = (int)xc + tid; b < kSelBins; b += NT) {
-        const uint32_t v = src[b];
-        if (v) atomicAdd(&f.hist[h * kSelBins + b], v);
+    // all loads of a round of heads in flight before any atomic: thread t
+    // takes the 16-byte words t, t + NT, ... of each head's bins from the cut
+    constexpr int HF = G < 4 ? G : 4;
+    constexpr int QW = kSelBins / 4 / NT;   // 16-byte words per thread and head
+    for (int h0 = 0; h0 < G; h0 += HF) {
+      uint32_t xc[HF];
+      uint4 v[HF][QW];
+#pragma unroll
+      for (int hh = 0; hh < HF; ++hh) {
+        const int64_t h = g * G + h0 + hh;
+        xc[hh] = f.sync[sel::kSyncWords * h + sel::kSyncXcdCut + xcd];
+        const uint4* src = reinterpret_cast<const uint4*>(f.xhist + ((int64_t)xcd * f.h_q + h) * kSelBins);
+#pragma unroll
+        for (int r = 0; r < QW; ++r) {
+          const int q4 = tid + r * NT;
+          v[hh][r] = 4 * q4 + 3 >= (int)xc[hh] ? src[q4] : make_uint4(0u, 0u, 0u, 0u);
+        }
       }
-      if (tid == 0) atomicMax(&f.sync[sel::kSyncWords * h + sel::kSyncCut], xc);
+#pragma unroll
+      for (int hh = 0; hh < HF; ++hh) {
+        const int64_t h = g * G + h0 + hh;
+#pragma unroll
+        for (int r = 0; r < QW; ++r) {
+          const int b0 = 4 * (tid + r * NT);
+          const uint32_t e4[4] = {v[hh][r].x, v[hh][r].y, v[hh][r].z, v[hh][r].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (e4[e] && b0 + e >= (int)xc[hh]) atomicAdd(&f.hist[h * kSelBins + b0 + e], e4[e]);
+        }
+        if (tid == 0) atomicMax(&f.sync[sel::kSyncWords * h + sel::kSyncCut], xc[hh]);
+      }
     }
     wait_vmem();
     __syncthreads();
