@@ -208,30 +208,17 @@ hipError_t scan_for_select(const uint8_t* dev, const uint8_t* const* table, int6
   return e;
 }
 
-// Whether HBM-resident scans select on the fly (launch_scan_select).  Off: at
-// 131072 keys that kernel still costs more time than the score round trip it
-// saves (its cross-XCD atomics serialise), although it moves a third of the
-// bytes.
-constexpr bool kSelectInScan = false;
-
-// How the selection continues after run_scan: the full selection over the
-// scores (with what the scan prepared), or only the resolve over kept keys the
-// scan compacted itself (fused: chunks of `slot` keys, `nchunks` per head).
+// How the selection continues after run_scan: with what the scan prepared.
 struct ScanOutcome {
   bool cleared = false;
   bool hist_done = false;
-  bool fused = false;
-  int64_t nchunks = 0;
-  int slot = 0;
 };
 
 // Scores of every key into `scores` [h_q][ld]; staging comes from the workspace.
-// With a selection to follow (`sel`), the direct scans also prepare it, and
-// HBM-resident scans select on the fly where every tile fits on the GPU at
-// once (k to select).
+// With a selection to follow (`sel`), the direct scans also prepare it.
 int run_scan(const uint8_t* dev, int residency, const float* q, const uint8_t* depth,
              const uint8_t* union_depth, int h_q, int h_kv, int64_t n, int d, float* scores, int64_t ld,
-             uint8_t* staging, const fathom::SelectWorkspace* sel, int k, ScanOutcome* out, hipStream_t s) {
+             uint8_t* staging, const fathom::SelectWorkspace* sel, ScanOutcome* out, hipStream_t s) {
   const fathom::Layout L = fathom::make_layout(n);
   const int g = h_q / h_kv;
   const bool host = residency == FATHOM_HOST_DIRECT;
@@ -239,19 +226,6 @@ int run_scan(const uint8_t* dev, int residency, const float* q, const uint8_t* d
   bool* cleared = &out->cleared;
   bool* hist_done = &out->hist_done;
   *out = ScanOutcome();
-  if (kSelectInScan && sel && residency == FATHOM_HBM && !sel->small && L.nb > 0) {
-    e = fathom::launch_select_clear(*sel, h_q, s, true);
-    if (e != hipSuccess) return hip_fail(e, "select clear launch");
-    e = fathom::launch_scan_select(dev, q, depth, union_depth, h_kv, g, L, d, scores, ld, *sel, k, &out->nchunks,
-                                   &out->slot, s);
-    if (e == hipSuccess) {
-      out->fused = true;
-      return FATHOM_OK;
-    }
-    if (e != hipErrorCooperativeLaunchTooLarge) return hip_fail(e, "scan launch");
-    // too many tiles to be resident at once: scores through HBM (the clearing
-    // above is harmless; the scan clears again on the way)
-  }
   if (residency == FATHOM_HOST_STAGED) {
     e = fathom::launch_scan_staged(dev, staging, q, depth, union_depth, h_kv, g, L, d, scores, ld, s);
   } else if (sel && L.nb > 0) {
@@ -291,7 +265,7 @@ int fathom_scan_scores(const void* records, int residency, const float* q, const
     staging = static_cast<uint8_t*>(workspace) + staging_offset(h_q, n, 1);
   }
   ScanOutcome out;
-  st = run_scan(dev, residency, q, depth, union_depth, h_q, h_kv, n, d, scores, ld, staging, nullptr, 0, &out,
+  st = run_scan(dev, residency, q, depth, union_depth, h_q, h_kv, n, d, scores, ld, staging, nullptr, &out,
                 static_cast<hipStream_t>(stream));
   if (st) return st;
   return ok();
@@ -318,12 +292,10 @@ int scan_topk(const void* records, int residency, const float* q, const uint8_t*
   uint8_t* staging = static_cast<uint8_t*>(workspace) + staging_offset(h_q, n, k);
   const fathom::SelectWorkspace sel = fathom::carve_select(sel_base, h_q, n, k);
   ScanOutcome out;
-  st = run_scan(dev, residency, q, depth, union_depth, h_q, h_kv, n, d, scores, ld, staging, &sel, k, &out, s);
+  st = run_scan(dev, residency, q, depth, union_depth, h_q, h_kv, n, d, scores, ld, staging, &sel, &out, s);
   if (st) return st;
-  hipError_t e = out.fused ? fathom::launch_select_resolve(scores, ld, h_q, n, k, topk_idx, topk_score, sel,
-                                                           out.nchunks, out.slot, s)
-                           : fathom::launch_select(scores, ld, h_q, n, k, topk_idx, topk_score, sel, out.cleared,
-                                                   out.hist_done, s);
+  hipError_t e = fathom::launch_select(scores, ld, h_q, n, k, topk_idx, topk_score, sel, out.cleared,
+                                       out.hist_done, s);
   if (e != hipSuccess) return hip_fail(e, "select launch");
   return ok();
 }

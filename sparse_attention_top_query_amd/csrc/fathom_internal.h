@@ -136,9 +136,6 @@ struct SelectWorkspace {
   uint32_t* hist;     // [h_q][4096] histogram of the top 12 key bits
   uint32_t* state;    // [h_q][8]: threshold bin, keys above it, overflow flag, spill fill, and the same
                       // four for the refinement stage's second digit
-  uint32_t* sync;     // [h_q][32]: the scan that selects on the fly counts each KV head's finished
-                      // tiles, raises its ready flag and keeps each head's histogram cuts there
-  uint32_t* xhist;    // [8][h_q][4096]: its per-XCD first-digit histograms
   uint32_t* counts;   // [h_q][nchunks] kept keys per 4096-key chunk
   uint32_t* soff;     // [h_q][nchunks] spill offset of a chunk whose kept keys overflow its slot
   uint64_t* kept;     // [h_q][nchunks][512] (key, index) at or above the threshold bin
@@ -161,23 +158,5 @@ size_t select_clear_words(const SelectWorkspace& ws, int h_q);
 hipError_t launch_select(const float* scores, int64_t ld, int h_q, int64_t n, int k,
                          int32_t* idx, float* val, const SelectWorkspace& ws, bool cleared, bool hist_done,
                          hipStream_t s);
-// Zeroes the histograms, state and sync words (and with xcd_hists the per-XCD
-// histograms of the scan that selects on the fly).
-hipError_t launch_select_clear(const SelectWorkspace& ws, int h_q, hipStream_t s, bool xcd_hists = false);
-// The resolve alone, over kept keys that a scan compacted itself into slots of
-// `slot` keys per chunk (nchunks chunks per head).
-hipError_t launch_select_resolve(const float* scores, int64_t ld, int h_q, int64_t n, int k, int32_t* idx,
-                                 float* val, const SelectWorkspace& ws, int64_t nchunks, int slot, hipStream_t s);
-// HBM-resident records with the selection's histogram, threshold and
-// compaction done inside the scan, so the scores never leave the chip (they
-// are written only for heads whose candidates overflow, which the resolve
-// then ranks from the whole row).  Needs every tile of the launch resident at
-// once (a cooperative launch): hipErrorCooperativeLaunchTooLarge otherwise,
-// with nothing enqueued.  ws's histograms, state and sync words must be zero
-// (launch_select_clear).  On success the resolve follows with the chunk count
-// and slot size returned in *nchunks and *slot.
-hipError_t launch_scan_select(const uint8_t* rec, const float* q, const uint8_t* depth, const uint8_t* uni,
-                              int h_kv, int g, const Layout& L, int d, float* scores, int64_t ld,
-                              const SelectWorkspace& ws, int k, int64_t* nchunks, int* slot, hipStream_t s);
-
+hipError_t launch_select_clear(const SelectWorkspace& ws, int h_q, hipStream_t s);
 }  // namespace fathom

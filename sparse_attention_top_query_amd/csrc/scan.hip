@@ -44,7 +44,6 @@
 #include <type_traits>
 
 #include "fathom_internal.h"
-#include "select_parts.h"
 
 namespace fathom {
 namespace {
@@ -457,214 +456,6 @@ __device__ __forceinline__ void hist_tile(const ScanArgs& a, uint32_t* hist, int
   }
 }
 
-// Device-scope atomic accesses (performed coherently across the XCDs), and a
-// wait for this wavefront's outstanding vector memory operations.
-__device__ __forceinline__ uint32_t load_coherent(uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void store_coherent(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void wait_vmem() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// Wavefront-wide sum and maximum of a float (DPP moves within rows of 16 lanes,
-// then the row-15 and row-31 broadcasts; lane 63 ends with the result, which is
-// returned to every lane).  Every lane must be active.
-__device__ __forceinline__ float wave_sum_f32(float v) {
-#define FATHOM_DPP_ADD(ctrl, rm) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, rm, 0xf, true))
-  FATHOM_DPP_ADD(0x111, 0xf);   // row_shr:1
-  FATHOM_DPP_ADD(0x112, 0xf);   // row_shr:2
-  FATHOM_DPP_ADD(0x114, 0xf);   // row_shr:4
-  FATHOM_DPP_ADD(0x118, 0xf);   // row_shr:8
-  FATHOM_DPP_ADD(0x142, 0xa);   // row_bcast:15
-  FATHOM_DPP_ADD(0x143, 0xc);   // row_bcast:31
-#undef FATHOM_DPP_ADD
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-}
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#define FATHOM_DPP_MAX(ctrl, rm) v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, ctrl, rm, 0xf, true))
-  FATHOM_DPP_MAX(0x111, 0xf);
-  FATHOM_DPP_MAX(0x112, 0xf);
-  FATHOM_DPP_MAX(0x114, 0xf);
-  FATHOM_DPP_MAX(0x118, 0xf);
-  FATHOM_DPP_MAX(0x142, 0xa);
-  FATHOM_DPP_MAX(0x143, 0xc);
-#undef FATHOM_DPP_MAX
-  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
-}
-
-// The tile's part of the heads' first-digit histograms for the selection on the
-// fly (the histograms of the tiles on its XCD), limited to its upper scores.
-// Per head the cut is the first digit of
-// mean + sd/2 of the tile's scores (about the top third for a bell-shaped
-// spread), raised if needed so that the bins from the cut to the tile's
-// largest fit a window of kCutWindow; only keys at or above the cut are counted
-// (an LDS histogram of the window, then one atomic per non-empty bin), and the
-// head's highest cut over the XCD's tiles is kept.
-// Every bin at or above that highest cut is then exact; the selection needs
-// only those, provided the k-th largest key lies among them, which it checks.
-constexpr int kCutWindow = 512;
-
-template <int G, int TB>
-__device__ __forceinline__ void cut_hist_tile(const ScanArgs& a, uint32_t* xhist, uint32_t* sync, int h_q,
-                                              int xcd, int64_t g, int64_t tile, const float (&acc)[kSub][G],
-                                              ScanSmem<G, TB>& sm) {
-  constexpr int NT = Cfg<G, TB>::threads;
-  constexpr int NW = NT / 64;
-  static_assert((3 * G * NW + G * kCutWindow) * 4 <= (int)sizeof(ScanSmem<G, TB>), "the window fits the staging memory");
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wv = tid >> 6;
-  const int64_t key0 = tile * TB * kBlock;
-  const int nkeys = (int)min<int64_t>(TB * kBlock, a.n - key0);
-  float* red = reinterpret_cast<float*>(&sm);                        // [G][2][NW] sums
-  uint32_t* bmax = reinterpret_cast<uint32_t*>(&sm) + 2 * G * NW;     // [G][NW] largest bin
-  uint32_t* lh = reinterpret_cast<uint32_t*>(&sm) + 3 * G * NW;       // [G][kCutWindow]
-  __syncthreads();   // every wave is past the staging memory
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float m1 = 0.0f, m2 = 0.0f;
-    uint32_t mb = 0;
-#pragma unroll
-    for (int s2 = 0; s2 < kSub; ++s2) {
-      if (tile_key<TB>(s2) < nkeys) {
-        m1 += acc[s2][h];
-        m2 = fmaf(acc[s2][h], acc[s2][h], m2);
-        mb = max(mb, order_key(acc[s2][h]) >> kSelDigit0);
-      }
-    }
-    m1 = wave_sum_f32(m1);
-    m2 = wave_sum_f32(m2);
-    mb = wave_max_u32(mb);
-    if (lane == 0) {
-      red[(2 * h) * NW + wv] = m1;
-      red[(2 * h + 1) * NW + wv] = m2;
-      bmax[h * NW + wv] = mb;
-    }
-  }
-  for (int i = tid; i < G * kCutWindow; i += NT) lh[i] = 0u;
-  __syncthreads();
-  uint32_t lo[G], hi[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float m1 = 0.0f, m2 = 0.0f;
-    uint32_t mb = 0;
-#pragma unroll
-    for (int x = 0; x < NW; ++x) {
-      m1 += red[(2 * h) * NW + x];
-      m2 += red[(2 * h + 1) * NW + x];
-      mb = max(mb, bmax[h * NW + x]);
-    }
-    const float mean = m1 / (float)nkeys;
-    const float var = fmaxf(m2 / (float)nkeys - mean * mean, 0.0f);
-    const uint32_t cut = order_key(mean + 0.5f * sqrtf(var)) >> kSelDigit0;
-    hi[h] = mb;
-    lo[h] = min(mb, max(cut, mb + 1 >= (uint32_t)kCutWindow ? mb + 1 - kCutWindow : 0u));
-  }
-  if (tid < G) {
-    uint32_t c = lo[0];
-#pragma unroll
-    for (int h = 1; h < G; ++h)
-      if (tid == h) c = lo[h];
-    atomicMax(&sync[sel::kSyncWords * (g * G + tid) + sel::kSyncXcdCut + xcd], c);
-  }
-#pragma unroll
-  for (int s2 = 0; s2 < kSub; ++s2) {
-    if (tile_key<TB>(s2) < nkeys) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const uint32_t b = order_key(acc[s2][h]) >> kSelDigit0;
-        if (b >= lo[h]) atomicAdd(&lh[h * kCutWindow + (b - lo[h])], 1u);
-      }
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    for (int b = tid; b <= (int)(hi[h] - lo[h]); b += NT) {
-      const uint32_t v = lh[h * kCutWindow + b];
-      if (v) atomicAdd(&xhist[((int64_t)xcd * h_q + g * G + h) * kSelBins + lo[h] + b], v);
-    }
-  }
-}
-
-// One workgroup's threshold bins for the heads [h0, h0 + HB) of KV head g from
-// their first-digit histograms (exact from each head's cut upward), written to
-// the selection state: word 0 the bin, 1 the keys above it, 2 the overflow flag
-// (2 if the bin is unknown: the k-th key lies below the cut or fewer than k
-// keys were counted, so the resolve counts the row itself; 1 if the bin's
-// candidates exceed the resolve's on-chip buffer).  Thread t holds bins
-// 16 t .. 16 t + 15 in registers.
-template <int NT, int HB>
-__device__ __forceinline__ void find_thresholds(const uint32_t* hist, const uint32_t* sync, uint32_t* state,
-                                                int64_t h0, uint32_t k, uint32_t* wsum) {
-  constexpr int NW = NT / 64;
-  constexpr int PER = kSelBins / NT;
-  static_assert(PER == 16, "16 bins per thread");
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wv = tid >> 6;
-  uint32_t v[HB][PER];
-  uint32_t cut[HB];
-#pragma unroll
-  for (int hh = 0; hh < HB; ++hh) {
-    const uint4* src = reinterpret_cast<const uint4*>(hist + (h0 + hh) * kSelBins + PER * tid);
-#pragma unroll
-    for (int r = 0; r < PER / 4; ++r) {
-      const uint4 x = src[r];
-      v[hh][4 * r] = x.x;
-      v[hh][4 * r + 1] = x.y;
-      v[hh][4 * r + 2] = x.z;
-      v[hh][4 * r + 3] = x.w;
-    }
-    cut[hh] = sync[sel::kSyncWords * (h0 + hh) + sel::kSyncCut];
-  }
-  // per head: the thread's total and its total at or above the cut, then
-  // suffix sums over the workgroup (wavefront scans, then wavefront totals)
-  uint32_t mine[HB], part[HB], inc[HB], incp[HB];
-#pragma unroll
-  for (int hh = 0; hh < HB; ++hh) {
-    mine[hh] = part[hh] = 0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      mine[hh] += v[hh][i];
-      part[hh] += (uint32_t)(PER * tid + i) >= cut[hh] ? v[hh][i] : 0u;
-    }
-    inc[hh] = wave_inclusive_sum(mine[hh]);
-    incp[hh] = wave_inclusive_sum(part[hh]);
-    if (lane == 63) {
-      wsum[(2 * hh) * NW + wv] = inc[hh];
-      wsum[(2 * hh + 1) * NW + wv] = incp[hh];
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int hh = 0; hh < HB; ++hh) {
-    uint32_t* st = state + (h0 + hh) * sel::kStateWords;
-    uint32_t wtot = (uint32_t)__builtin_amdgcn_readlane((int)inc[hh], 63);
-    uint32_t above = wtot - inc[hh];   // this wavefront's lanes above this one
-    uint32_t counted = 0;
-    for (int x = 0; x < NW; ++x) {
-      if (x > wv) above += wsum[(2 * hh) * NW + x];
-      counted += wsum[(2 * hh + 1) * NW + x];
-    }
-    if (tid == 0 && counted < k) store_coherent(&st[2], 2u);
-#pragma unroll
-    for (int i = PER - 1; i >= 0; --i) {
-      if (above < k && above + v[hh][i] >= k) {
-        const uint32_t bin = (uint32_t)(PER * tid + i);
-        const bool known = counted >= k && bin >= cut[hh];
-        store_coherent(&st[0], known ? bin : 0u);
-        store_coherent(&st[1], known ? above : 0u);
-        store_coherent(&st[2], !known ? 2u : above + v[hh][i] > (uint32_t)sel::kKeep ? 1u : 0u);
-      }
-      above += v[hh][i];
-    }
-  }
-  wait_vmem();
-  __syncthreads();
-}
-
 // Scores of tile `tile` (TB blocks) of KV head g, all its query heads.  With
 // FUSE, the tile's scores are also counted into a.hist by their first
 // selection digit.
@@ -708,207 +499,6 @@ __global__ __launch_bounds__((Cfg<G, TB>::threads)) void scan_kernel(ScanArgs a,
     for (int64_t i = L * slice + threadIdx.x; i < z1; i += Cfg<G, TB>::threads) a.zero[i] = 0u;
   }
   scan_tile<G, TB, FUSE>(a, g, tile, sm);
-}
-
-// ---------------------------------------------------------------------------
-// HBM-resident records, selecting on the fly.  Read from HBM the scan is bound
-// by its vector work, so a round trip of the fp32 scores through HBM (written
-// once, read by the histogram and the collect) would cost more traffic than the
-// records themselves.  Instead every tile of a launch stays resident (a
-// cooperative launch) and keeps its scores in registers:
-//  1. score the tile, count its scores into the heads' first-digit histograms;
-//  2. one arrival per tile on its KV head's counter; the last tile of a KV head
-//     finds each of its heads' threshold bin b (the bin of the k-th largest
-//     key), records it in the selection state, and raises the head's ready
-//     flag; the others wait for the flag;
-//  3. every tile compacts its keys in bin b or above, in index order, into its
-//     slot of the kept keys (or a spill segment), exactly as the collect does
-//     for a chunk.  A head whose candidates exceed what the resolve holds on
-//     chip writes its whole row of scores instead, for the resolve's row path.
-// The resolve then finishes the selection.  The wait is bounded (about a
-// second) so the kernel ends even if residency were ever violated; the
-// selection would then be unspecified.
-// ---------------------------------------------------------------------------
-
-using sel::kTileSlot;                        // kept keys per 1024-key tile slot
-
-constexpr int kTileSelect = 8;    // tiles of the scan that selects on the fly: 1024 keys, 256 threads
-static_assert(sel::kTileChunk == kTileSelect * kBlock, "the selection sizes its counts for these tiles");
-constexpr uint32_t kSpinLimit = 1u << 24;    // ready-flag polls (s_sleep 2 apart)
-
-struct FuseSel {
-  uint32_t* hist;     // [h_q][kSelBins], zero on entry
-  uint32_t* xhist;    // [8][h_q][kSelBins], zero on entry
-  int h_q;
-  uint32_t* state;    // [h_q][8], zero on entry
-  uint32_t* sync;     // [h_q][2] (words 2g, 2g + 1 per KV head g), zero on entry
-  uint32_t* counts;   // [h_q][tiles] kept keys per tile
-  uint32_t* soff;     // [h_q][tiles] spill offsets
-  uint64_t* kept;     // [h_q][tiles][kTileSlot]
-  uint64_t* spill;    // [h_q][spill_cap]
-  int64_t spill_cap;
-  int k;
-};
-
-template <int G>
-__global__ __launch_bounds__((Cfg<G, kTileSelect>::threads)) void scan_select_kernel(ScanArgs a, FuseSel f,
-                                                                                      int64_t tiles) {
-  constexpr int TB = kTileSelect;
-  constexpr int NT = Cfg<G, TB>::threads;
-  constexpr int NW = NT / 64;
-  constexpr int TK = TB * kBlock;   // keys per tile
-  static_assert(NT == sel::kSelThreads && TK == 4 * NT, "one quad of the tile's keys per thread");
-  static_assert(sizeof(ScanSmem<G, TB>) >= (size_t)G * TK * 4, "the tile's scores fit the staging memory");
-  __shared__ ScanSmem<G, TB> sm;
-  __shared__ uint32_t head_info[G][2];   // threshold bin, overflow flag
-  __shared__ uint32_t cnt[1][NW];
-  __shared__ uint64_t* dst_sh;
-  __shared__ uint32_t cap_sh;
-  __shared__ uint32_t last_sh;
-  const int64_t w = blockIdx.x;
-  const int64_t t8 = (tiles + kXcds - 1) / kXcds;
-  const int64_t j = w / kXcds;
-  const int64_t g = j / t8;
-  const int64_t tile = (w % kXcds) * t8 + j % t8;
-  if (tile >= tiles) return;   // grid padding: not counted among the KV head's tiles
-  const int tid = threadIdx.x;
-
-  float acc[kSub][G];
-  scan_tile_acc<G, TB>(a, g, tile, sm, acc);
-  const int xcd = (int)(w % kXcds);
-  cut_hist_tile<G, TB>(a, f.xhist, f.sync, f.h_q, xcd, g, tile, acc, sm);
-
-  // ---- 2. arrival; the KV head's last tile finds the thresholds ----
-  // Everything tiles exchange inside the launch -- histogram bins, arrival
-  // counts, cuts, state and the ready flag -- is accessed with device-scope
-  // atomic operations, and a wavefront's own accesses are ordered by waiting
-  // for them to complete; a device-scope fence is taken only by the workgroups
-  // that read what other tiles wrote (the last tile of a KV head on each XCD,
-  // and the last XCD), not by every tile, since it writes back and invalidates
-  // the XCD's L2 under the tiles still reading records.  Tiles count on their
-  // XCD's counter, and only the last one of each XCD forwards its XCD's
-  // histogram bins and cut to the KV head's, so no address takes more atomics
-  // than a KV head has XCDs or an XCD has tiles of it.
-  const uint32_t on_xcd = (uint32_t)min<int64_t>(t8, tiles - xcd * t8);   // this KV head's tiles on this XCD
-  const uint32_t xcds = (uint32_t)((tiles + t8 - 1) / t8);                // XCDs holding its tiles
-  uint32_t* gsync = f.sync + sel::kSyncWords * g;
-  wait_vmem();   // every wavefront's histogram additions are performed
-  __syncthreads();
-  if (tid == 0) last_sh = atomicAdd(&gsync[xcd], 1u) == on_xcd - 1 ? 1u : 0u;
-  __syncthreads();
-  if (last_sh) {
-    // last tile of this KV head on this XCD: forward the XCD's bins from its
-    // highest cut upward, and the cut
-    __threadfence();
-    // all loads of a round of heads in flight before any atomic: thread t
-    // takes the 16-byte words t, t + NT, ... of each head's bins from the cut
-    constexpr int HF = G < 4 ? G : 4;
-    constexpr int QW = kSelBins / 4 / NT;   // 16-byte words per thread and head
-    for (int h0 = 0; h0 < G; h0 += HF) {
-      uint32_t xc[HF];
-      uint4 v[HF][QW];
-#pragma unroll
-      for (int hh = 0; hh < HF; ++hh) {
-        const int64_t h = g * G + h0 + hh;
-        xc[hh] = f.sync[sel::kSyncWords * h + sel::kSyncXcdCut + xcd];
-        const uint4* src = reinterpret_cast<const uint4*>(f.xhist + ((int64_t)xcd * f.h_q + h) * kSelBins);
-#pragma unroll
-        for (int r = 0; r < QW; ++r) {
-          const int q4 = tid + r * NT;
-          v[hh][r] = 4 * q4 + 3 >= (int)xc[hh] ? src[q4] : make_uint4(0u, 0u, 0u, 0u);
-        }
-      }
-#pragma unroll
-      for (int hh = 0; hh < HF; ++hh) {
-        const int64_t h = g * G + h0 + hh;
-#pragma unroll
-        for (int r = 0; r < QW; ++r) {
-          const int b0 = 4 * (tid + r * NT);
-          const uint32_t e4[4] = {v[hh][r].x, v[hh][r].y, v[hh][r].z, v[hh][r].w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (e4[e] && b0 + e >= (int)xc[hh]) atomicAdd(&f.hist[h * kSelBins + b0 + e], e4[e]);
-        }
-        if (tid == 0) atomicMax(&f.sync[sel::kSyncWords * h + sel::kSyncCut], xc[hh]);
-      }
-    }
-    wait_vmem();
-    __syncthreads();
-    if (tid == 0) last_sh = atomicAdd(&gsync[sel::kSyncXcdsArrived], 1u) == xcds - 1 ? 2u : 0u;
-    __syncthreads();
-  }
-  uint32_t* ready = &gsync[sel::kSyncReady];
-  if (last_sh == 2u) {
-    // last XCD of the KV head: one device-scope acquire, then plain loads of
-    // the heads' histograms and cuts
-    __threadfence();
-    constexpr int HB = G < 4 ? G : 4;
-    static_assert(G % HB == 0, "whole rounds of heads");
-    __shared__ uint32_t fw[2 * HB * NW];
-    for (int h0 = 0; h0 < G; h0 += HB)
-      find_thresholds<NT, HB>(f.hist, f.sync, f.state, g * G + h0, (uint32_t)f.k, fw);
-    if (tid == 0) store_coherent(ready, 1u);   // every thread's state writes were performed
-  } else if (tid == 0) {
-    for (uint32_t it = 0; it < kSpinLimit; ++it) {
-      if (load_coherent(ready) != 0u) break;
-      __builtin_amdgcn_s_sleep(2);
-    }
-  }
-  __syncthreads();
-  if (tid < G) {
-    uint32_t* st = f.state + (g * G + tid) * sel::kStateWords;
-    head_info[tid][0] = load_coherent(&st[0]);
-    head_info[tid][1] = load_coherent(&st[2]);
-  }
-  __syncthreads();   // head_info, and the staging memory is free again
-
-  // ---- 3. the tile's scores in index order through LDS, a quad per thread ----
-  float* ls = reinterpret_cast<float*>(&sm);
-#pragma unroll
-  for (int s2 = 0; s2 < kSub; ++s2) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) ls[h * TK + tile_key<TB>(s2)] = acc[s2][h];
-  }
-  __syncthreads();
-  const int64_t j0 = tile * TK;
-  for (int hh = 0; hh < G; ++hh) {
-    const int64_t h = g * G + hh;
-    float4 f4[1];
-    f4[0] = *reinterpret_cast<const float4*>(ls + hh * TK + 4 * tid);
-    if (head_info[hh][1]) {
-      // too many candidates for the resolve's on-chip buffer: the row path
-      // ranks this head from its whole row of scores
-      const int64_t jq = j0 + 4 * tid;
-      float* dst = a.scores + h * a.ld + jq;
-      if (jq + 3 < a.n) {
-        store_global(reinterpret_cast<float4*>(dst), f4[0]);
-      } else {
-        const float e4[4] = {f4[0].x, f4[0].y, f4[0].z, f4[0].w};
-        for (int e = 0; e < 4; ++e)
-          if (jq + e < a.n) dst[e] = e4[e];
-      }
-    } else {
-      uint32_t* st = f.state + h * sel::kStateWords;
-      sel::compact_chunk<NW, 1, kTileSlot>(f4, a.n, j0, kSelDigit0, head_info[hh][0], &st[3], &st[2],
-                                           h * tiles + tile, f.kept, f.counts, f.soff, f.spill + h * f.spill_cap,
-                                           f.spill_cap, cnt, &dst_sh, &cap_sh);
-    }
-  }
-}
-
-template <int G>
-hipError_t launch_scan_select_g(const uint8_t* rec, const float* q, const uint8_t* depth, const uint8_t* uni,
-                                int h_kv, const Layout& L, int d, float* scores, int64_t ld,
-                                const SelectWorkspace& ws, int k, int64_t tiles, hipStream_t s) {
-  constexpr int TB = kTileSelect;
-  ScanArgs a{rec, q, depth, uni, L.n, L.nb, L.H, L.P, L.R, d, scores, ld, nullptr, 0, nullptr, nullptr, 0, 1};
-  FuseSel f{ws.hist, ws.xhist, h_kv * G, ws.state, ws.sync, ws.counts, ws.soff, ws.kept, ws.spill, ws.spill_cap, k};
-  const int64_t grid = kXcds * h_kv * ((tiles + kXcds - 1) / kXcds);
-  void* args[] = {&a, &f, &tiles};
-  hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&scan_select_kernel<G>), dim3((unsigned)grid),
-                                            dim3(Cfg<G, TB>::threads), args, 0, s);
-  if (e != hipSuccess) (void)hipGetLastError();   // a refused launch leaves no error behind
-  return e;
 }
 
 // ---------------------------------------------------------------------------
@@ -1079,25 +669,6 @@ hipError_t launch_scan_paged(const uint8_t* rec, const uint8_t* const* table, in
     case 4: return launch_any<4>(rec, host, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words, hist, pg, s);
     case 8: return launch_any<8>(rec, host, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words, hist, pg, s);
     case 16: return launch_any<16>(rec, host, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words, hist, pg, s);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-hipError_t launch_scan_select(const uint8_t* rec, const float* q, const uint8_t* depth, const uint8_t* uni,
-                              int h_kv, int g, const Layout& L, int d, float* scores, int64_t ld,
-                              const SelectWorkspace& ws, int k, int64_t* nchunks, int* slot, hipStream_t s) {
-  const int64_t tiles = (L.nb + kTileSelect - 1) / kTileSelect;
-  // the kept keys of every tile must fit the selection workspace's chunk slots
-  if (L.nb == 0 || tiles * kTileSlot > ws.nchunks * sel::kSlot || ws.spill_cap < sel::kKeep)
-    return hipErrorCooperativeLaunchTooLarge;
-  *nchunks = tiles;
-  *slot = kTileSlot;
-  switch (g) {
-    case 1: return launch_scan_select_g<1>(rec, q, depth, uni, h_kv, L, d, scores, ld, ws, k, tiles, s);
-    case 2: return launch_scan_select_g<2>(rec, q, depth, uni, h_kv, L, d, scores, ld, ws, k, tiles, s);
-    case 4: return launch_scan_select_g<4>(rec, q, depth, uni, h_kv, L, d, scores, ld, ws, k, tiles, s);
-    case 8: return launch_scan_select_g<8>(rec, q, depth, uni, h_kv, L, d, scores, ld, ws, k, tiles, s);
-    case 16: return launch_scan_select_g<16>(rec, q, depth, uni, h_kv, L, d, scores, ld, ws, k, tiles, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -40,16 +40,10 @@ namespace {
 using namespace sel;
 
 
-__global__ __launch_bounds__(kSelThreads) void sel_init(uint32_t* hist, uint32_t* state, uint32_t* sync,
-                                                        uint32_t* hist2, uint32_t* xhist, int h_q) {
+__global__ __launch_bounds__(kSelThreads) void sel_init(uint32_t* hist, uint32_t* state, uint32_t* hist2) {
   const int h = blockIdx.x;
   for (int b = threadIdx.x; b < kBins; b += kSelThreads) hist[(int64_t)h * kBins + b] = 0u;
-  if (xhist)
-    for (int x = 0; x < kXcdCount; ++x)
-      for (int b = threadIdx.x; b < kBins / 4; b += kSelThreads)
-        reinterpret_cast<uint4*>(xhist + ((int64_t)x * h_q + h) * kBins)[b] = make_uint4(0u, 0u, 0u, 0u);
   if (threadIdx.x < kStateWords) state[h * kStateWords + threadIdx.x] = 0u;
-  if (threadIdx.x < kSyncWords) sync[kSyncWords * h + threadIdx.x] = 0u;
   if (hist2)
     for (int b = threadIdx.x; b < k2ndBins; b += kSelThreads) hist2[(int64_t)h * k2ndBins + b] = 0u;
 }
@@ -313,28 +307,13 @@ __device__ __forceinline__ float key_to_float(uint32_t key) {
 // keys above T and the first `need` keys equal to T in index order.  Barriers:
 // a handful in all, none per sweep.
 __device__ void resolve_row(const float* __restrict__ row, int64_t n, int k, uint32_t bin, uint32_t above,
-                            bool bin_known, int32_t* __restrict__ out, float* __restrict__ outv, uint32_t* lh,
-                            uint32_t* wsum, uint32_t* sh) {
+                            int32_t* __restrict__ out, float* __restrict__ outv, uint32_t* lh, uint32_t* wsum,
+                            uint32_t* sh) {
   constexpr int NT = kResolveThreads;
   constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const uint64_t lt = (1ull << lane) - 1ull;
-  if (!bin_known) {
-    // no histogram of the row exists: count its first digits here (lh holds kBins words)
-    for (int b = threadIdx.x; b < kBins; b += NT) lh[b] = 0u;
-    __syncthreads();
-    stream_part<NW>(row, n, [&](int64_t, const float (&v)[4], int valid) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (i < valid) atomicAdd(&lh[order_key(v[i]) >> kDigit0], 1u);
-    });
-    __syncthreads();
-    find_bin<NT, kBins>(lh, (uint32_t)k, wsum, sh);
-    bin = sh[0];
-    above = sh[1];
-    __syncthreads();
-  }
   uint32_t prefix = bin, need = (uint32_t)k - above;
   for (int pass = 0; pass < 2; ++pass) {
     const int shift = pass == 0 ? 10 : 0;
@@ -441,7 +420,7 @@ __global__ __launch_bounds__(kResolveThreads) void sel_resolve(const float* __re
                                                                const uint32_t* __restrict__ counts,
                                                                const uint32_t* __restrict__ soff,
                                                                const uint64_t* __restrict__ spill, int64_t spill_cap,
-                                                               int64_t nchunks, int slot, int32_t* __restrict__ idx,
+                                                               int64_t nchunks, int32_t* __restrict__ idx,
                                                                float* __restrict__ val) {
   constexpr int NT = kResolveThreads;
   __shared__ uint64_t buf[kKeep];          // kept (key, index) of the head, in index order
@@ -482,16 +461,13 @@ __global__ __launch_bounds__(kResolveThreads) void sel_resolve(const float* __re
     fallback = total > (uint32_t)kKeep;
   }
   if (fallback) {
-    // state word 2 (or 6) is 2 where the threshold bin was never found: the scan
-    // that selects on the fly gave the head its whole row of scores but no
-    // exact histogram
-    resolve_row(row, n, k, bin, above, st[refined ? 6 : 2] != 2u, out, outv, lh, wsum, sh);
+    resolve_row(row, n, k, bin, above, out, outv, lh, wsum, sh);
     return;
   }
   __syncthreads();
   // a chunk's kept keys: its slot, or its spill segment when they overflowed it
   auto src_of = [&](int64_t c, uint32_t cn) -> const uint64_t* {
-    return cn <= (uint32_t)slot ? kept + ((int64_t)h * nchunks + c) * slot
+    return cn <= (uint32_t)kSlot ? kept + ((int64_t)h * nchunks + c) * kSlot
                                  : spill + (int64_t)h * spill_cap + soff[(int64_t)h * nchunks + c];
   };
   // gather in chunk order, every load of a batch issued before its stores; keys
@@ -700,11 +676,7 @@ size_t al256(size_t x) { return (x + 255) / 256 * 256; }
 
 int64_t select_chunks(int64_t n) { return (n + kChunk - 1) / kChunk; }
 
-// Entries per head of the kept-key counts and spill offsets: one per chunk of
-// the smallest kind that compacts into them, the 1024-key tiles of the scan that
-// selects on the fly (their slots are a quarter of a 4096-key chunk's, so the
-// kept keys' area fits both).
-static int64_t count_entries(int64_t n) { return (n + kTileChunk - 1) / kTileChunk; }
+
 
 // Spill entries per head: the resolve holds at most kKeep kept keys (rows of at
 // most kSmallRow keys are selected by sel_small and need none).
@@ -717,15 +689,14 @@ static size_t hist2_bytes(int h_q, int64_t n) { return n >= kRefineMin ? al256((
 size_t select_workspace_bytes(int h_q, int64_t n, int k) {
   (void)k;
   const size_t nc = (size_t)select_chunks(n);
-  return al256((size_t)h_q * kBins * 4) + al256((size_t)h_q * kStateWords * 4) + al256((size_t)h_q * kSyncWords * 4) +
+  return al256((size_t)h_q * kBins * 4) + al256((size_t)h_q * kStateWords * 4) +
          hist2_bytes(h_q, n) +
-         2 * al256((size_t)h_q * (size_t)count_entries(n) * 4) + al256((size_t)h_q * nc * kSlot * 8) +
-         (n > kSmallRow ? al256((size_t)kXcdCount * h_q * kBins * 4) : 0) +
+         2 * al256((size_t)h_q * nc * 4) + al256((size_t)h_q * nc * kSlot * 8) +
          al256((size_t)h_q * (size_t)spill_entries(n) * 8);
 }
 
 size_t select_clear_words(const SelectWorkspace& ws, int h_q) {
-  return (al256((size_t)h_q * kBins * 4) + al256((size_t)h_q * kStateWords * 4) + al256((size_t)h_q * kSyncWords * 4) +
+  return (al256((size_t)h_q * kBins * 4) + al256((size_t)h_q * kStateWords * 4) +
           (ws.hist2 ? al256((size_t)h_q * k2ndBins * 4) : 0)) / 4;
 }
 
@@ -738,26 +709,23 @@ SelectWorkspace carve_select(void* base, int h_q, int64_t n, int k) {
   p += al256((size_t)h_q * kBins * 4);
   ws.state = reinterpret_cast<uint32_t*>(p);
   p += al256((size_t)h_q * kStateWords * 4);
-  ws.sync = reinterpret_cast<uint32_t*>(p);
-  p += al256((size_t)h_q * kSyncWords * 4);
   ws.hist2 = n >= kRefineMin ? reinterpret_cast<uint32_t*>(p) : nullptr;
   p += hist2_bytes(h_q, n);
   ws.counts = reinterpret_cast<uint32_t*>(p);
-  p += al256((size_t)h_q * (size_t)count_entries(n) * 4);
+  p += al256((size_t)h_q * (size_t)ws.nchunks * 4);
   ws.soff = reinterpret_cast<uint32_t*>(p);
-  p += al256((size_t)h_q * (size_t)count_entries(n) * 4);
+  p += al256((size_t)h_q * (size_t)ws.nchunks * 4);
   ws.kept = reinterpret_cast<uint64_t*>(p);
   p += al256((size_t)h_q * (size_t)ws.nchunks * kSlot * 8);
   ws.spill = reinterpret_cast<uint64_t*>(p);
   ws.spill_cap = spill_entries(n);
-  p += al256((size_t)h_q * (size_t)spill_entries(n) * 8);
-  ws.xhist = n > kSmallRow ? reinterpret_cast<uint32_t*>(p) : nullptr;
+
   ws.small = n <= kSmallRow;
   return ws;
 }
 
-hipError_t launch_select_clear(const SelectWorkspace& ws, int h_q, hipStream_t s, bool xcd_hists) {
-  sel_init<<<h_q, kSelThreads, 0, s>>>(ws.hist, ws.state, ws.sync, ws.hist2, xcd_hists ? ws.xhist : nullptr, h_q);
+hipError_t launch_select_clear(const SelectWorkspace& ws, int h_q, hipStream_t s) {
+  sel_init<<<h_q, kSelThreads, 0, s>>>(ws.hist, ws.state, ws.hist2);
   return hipGetLastError();
 }
 
@@ -770,7 +738,7 @@ hipError_t launch_select(const float* scores, int64_t ld, int h_q, int64_t n, in
   }
   dim3 grid((unsigned)ws.nchunks, (unsigned)h_q);
   if (!hist_done) {
-    if (!cleared) sel_init<<<h_q, kSelThreads, 0, s>>>(ws.hist, ws.state, ws.sync, ws.hist2, nullptr, h_q);
+    if (!cleared) sel_init<<<h_q, kSelThreads, 0, s>>>(ws.hist, ws.state, ws.hist2);
     // chunks per histogram workgroup: 1, or more while the grid keeps >= 1024 workgroups
     // (4 per CU); fewer workgroups flush fewer partial histograms
     int per = 1;
@@ -789,15 +757,7 @@ hipError_t launch_select(const float* scores, int64_t ld, int h_q, int64_t n, in
                                                 ws.soff, ws.spill, ws.spill_cap, ws.nchunks, rper);
   }
   sel_resolve<<<h_q, kResolveThreads, 0, s>>>(scores, ld, n, k, ws.state, ws.kept, ws.counts, ws.soff, ws.spill,
-                                              ws.spill_cap, ws.nchunks, kSlot, idx, val);
-  return hipGetLastError();
-}
-
-hipError_t launch_select_resolve(const float* scores, int64_t ld, int h_q, int64_t n, int k, int32_t* idx,
-                                 float* val, const SelectWorkspace& ws, int64_t nchunks, int slot, hipStream_t s) {
-  if (k == 0 || n == 0 || h_q == 0) return hipSuccess;
-  sel_resolve<<<h_q, kResolveThreads, 0, s>>>(scores, ld, n, k, ws.state, ws.kept, ws.counts, ws.soff, ws.spill,
-                                              ws.spill_cap, nchunks, slot, idx, val);
+                                              ws.spill_cap, ws.nchunks, idx, val);
   return hipGetLastError();
 }
 

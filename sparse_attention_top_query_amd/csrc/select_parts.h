@@ -1,7 +1,6 @@
-// Pieces of the top-k selection shared by the selection kernels and the scan
-// that selects on the fly (its scores never leave the chip): constants, the
-// per-head state layout, workgroup scans, the threshold-bin search and the
-// ordered compaction of kept keys.
+// Pieces of the top-k selection: constants, the per-head state layout,
+// workgroup scans, the threshold-bin search and the ordered compaction of kept
+// keys.
 #pragma once
 
 #include "fathom_internal.h"
@@ -16,8 +15,6 @@ constexpr int kBins = kSelBins;                    // first digit: top 12 key bi
 constexpr int kDigit0 = kSelDigit0;                // shift of the first digit
 constexpr int kResolveThreads = 1024;
 constexpr int kSlot = 512;                         // kept keys per 4096-key chunk
-constexpr int kTileChunk = 1024;                   // keys per chunk of the scan that selects on the fly
-constexpr int kTileSlot = kSlot * kTileChunk / kChunk;   // its kept keys per chunk (128)
 constexpr int kKeep = 16384;                       // kept keys per head resolved in LDS (128 KB)
 constexpr int kKeepPer = kKeep / kResolveThreads;
 constexpr int k2ndBins = 1024;                     // second digit: the next 10 key bits
@@ -27,19 +24,6 @@ constexpr int64_t kRefineMin = 262144;             // rows at least this long ge
 // second digit b2 | kRefined, [5] keys of bin b above b2, [6] spill overflow
 // of the recollect, [7] its spill counter.
 constexpr int kStateWords = 8;
-// The on-the-fly selection's synchronisation area, kSyncWords words per query
-// head.  For KV head g, from word kSyncWords g: [x] its tiles on XCD x that
-// have arrived (x < 8), [8] its XCDs that have arrived, [9] its ready flag.  For
-// query head h, from word kSyncWords h: [16 + x] the highest histogram cut of
-// its tiles on XCD x, [24] the highest over all of them.  Per-XCD counters and
-// histograms keep the many same-address atomics of a launch inside one XCD's
-// L2; only one workgroup per XCD and KV head forwards them.
-constexpr int kXcdCount = 8;
-constexpr int kSyncWords = 32;
-constexpr int kSyncXcdsArrived = 8;
-constexpr int kSyncReady = 9;
-constexpr int kSyncXcdCut = 16;
-constexpr int kSyncCut = 24;
 constexpr int kSmallRow = 16384;                   // rows up to this long are selected by sel_small
 constexpr uint32_t kRefined = 0x80000000u;
 
@@ -109,7 +93,7 @@ __device__ __forceinline__ void find_bin(const uint32_t* lh, uint32_t need, uint
 // takes the resolve's full-row path).  Quad i of wavefront w holds keys
 // j0 + 4 (256 i + 64 w + lane) + e, e < 4, so (i, w, lane, e) order is index
 // order.  Called by every thread of the workgroup.
-template <int NW, int NQ, int SLOT = kSlot>
+template <int NW, int NQ>
 __device__ __forceinline__ void compact_chunk(const float4 (&f)[NQ], int64_t n, int64_t j0, int shift, uint32_t thr,
                                               uint32_t* ctr, uint32_t* overflow, int64_t c, uint64_t* kept,
                                               uint32_t* counts, uint32_t* soff, uint64_t* spill_h,
@@ -137,9 +121,9 @@ __device__ __forceinline__ void compact_chunk(const float4 (&f)[NQ], int64_t n, 
     uint32_t tot = 0;
     for (int i = 0; i < NQ; ++i)
       for (int x = 0; x < NW; ++x) tot += cnt[i][x];
-    uint64_t* dst = kept + c * SLOT;
-    uint32_t cap = (uint32_t)SLOT;
-    if (tot > (uint32_t)SLOT) {
+    uint64_t* dst = kept + c * kSlot;
+    uint32_t cap = (uint32_t)kSlot;
+    if (tot > (uint32_t)kSlot) {
       const uint32_t base = atomicAdd(ctr, tot);
       if ((int64_t)base + tot <= spill_cap) {
         dst = spill_h + base;
