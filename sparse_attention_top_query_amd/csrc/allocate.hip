@@ -14,16 +14,24 @@
 // channel c (t = 0..3) is an item with marginal gain w_c 4^(-t); gains fall
 // with t, so the greedy takes items in the order (gain desc, channel asc,
 // plane asc) and after B steps holds exactly the B first items of that order.
-// Each item gets a distinct integer key that sorts in that order:
-//   key = bits(double(w_c) * 4^(-t)) >> 29 << 11 | (256 - c) << 2 | (3 - t).
-// w_c is an fp32 value, so as a double its low 29 significand bits are zero and
-// scaling by 4^(-t) is exact (no double underflow for t <= 3); non-negative
-// doubles order like their bit patterns, and dropping the 29 zero bits keeps
-// the key within 45 bits.  The B-th largest key K is found by a bitwise search
-// from bit 44 down (each step counts the keys >= a candidate, one wave ballot
-// per item), and t_c is the number of channel c's items with key >= K.  The
-// fixed top-|q| mode selects m channels the same way with
-// key = bits(|q_c|) << 8 | (255 - c).
+// Gains are compared exactly through the bits of w_c as a double (w_c is an
+// fp32 value, so its low 29 significand bits are zero and scaling by 4^(-t)
+// only lowers the exponent by 2t, never underflowing): with x_c = bits >> 29,
+// the item (c, t) of a nonzero channel has the level L_c - t, L_c = x_c >> 24,
+// and the fraction F_c = x_c mod 2^24, and items order by (level, fraction,
+// lower channel).  So the B-th item is found in two short searches:
+//   1. its level m, the largest m with A(m) = sum_c clamp(L_c - m + 1, 0, 4)
+//      >= B (A(m) counts the items of level >= m), bit by bit over 10 bits,
+//      each count one wave sum;
+//   2. among the channels with an item at level m (L_c - m in 0..3), the
+//      r = B - A(m + 1) largest keys F_c << 8 | (255 - c), by a bitwise search
+//      over 32 bits with one ballot per channel slot.
+// Then t_c = clamp(L_c - m, 0, 4), plus one for the r chosen channels.  Items
+// of zero importance come after every other item, channel by channel in
+// ascending order, so when B exceeds the nonzero items the lowest zero
+// channels take the rest, 4 planes each.  The fixed top-|q| mode selects m
+// channels by a bitwise search over the 41-bit keys bits(|q_c|) << 8 |
+// (255 - c).
 //
 // Static mode (mode 3) selects the same way with key = bits(sigma2_c) << 8 |
 // (255 - c); sigma2 >= 0, so its bits order like its values.
@@ -102,23 +110,66 @@ __global__ __launch_bounds__(1024) void allocate_kernel(const float* __restrict_
   flag = wave_or(flag);
 
   if (flag == 0 && (mode == 0 || mode == 2) && budget > 0) {
-    uint64_t key[kPlanes * CPL];   // item (channel lane + 64 i, plane t) at 4 i + t; 0 = no item
+    const uint32_t B = (uint32_t)budget;
+    int lvl[CPL];          // L_c of a nonzero channel, else 0 (which counts no item at any level >= 1)
+    uint32_t frac[CPL];    // F_c << 8 | (255 - c)
+    uint64_t nzm[CPL];     // lanes whose channel lane + 64 i has nonzero importance
+    uint64_t zm[CPL];      // ... zero importance
+    uint32_t nz = 0;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
       const int c = lane + 64 * i;
-#pragma unroll
-      for (int t = 0; t < kPlanes; ++t) {
-        const uint64_t gain = (uint64_t)__double_as_longlong(ldexp((double)w[i], -2 * t)) >> 29;
-        key[4 * i + t] = c < d ? (gain << 11 | (uint64_t)(256 - c) << 2 | (uint64_t)(3 - t)) : 0ull;
-      }
+      const uint64_t x = (uint64_t)__double_as_longlong((double)w[i]) >> 29;
+      const bool valid = c < d;
+      const bool pos = valid && w[i] > 0.0f;
+      lvl[i] = pos ? (int)(x >> 24) : 0;
+      frac[i] = (uint32_t)(x & 0xffffffu) << 8 | (uint32_t)(255 - c);
+      nzm[i] = __ballot(pos);
+      zm[i] = __ballot(valid && !pos);
+      nz += 4u * (uint32_t)__popcll(nzm[i]);
     }
-    const uint64_t K = wave_kth_key(key, (uint32_t)budget, 44);
+    if (B <= nz) {
+      // items of level >= m, summed over the wave
+      auto count_from = [&](int m) -> uint32_t {
+        uint32_t v = 0;
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-      int tc = 0;
+        for (int i = 0; i < CPL; ++i) v += (uint32_t)min(max(lvl[i] - m + 1, 0), 4);
+        return (uint32_t)__builtin_amdgcn_readlane((int)wave_inclusive_sum(v), 63);
+      };
+      int m = 0;   // A(0) = nz >= B
+      for (int bit = 9; bit >= 0; --bit) {
+        const int cand = m | (1 << bit);
+        if (count_from(cand) >= B) m = cand;
+      }
+      const uint32_t r = B - count_from(m + 1);   // >= 1 items still to take at level m
+      uint64_t cm[CPL];
 #pragma unroll
-      for (int t = 0; t < kPlanes; ++t) tc += key[4 * i + t] >= K;
-      t[i] = lane + 64 * i < d ? tc : 0;
+      for (int i = 0; i < CPL; ++i) cm[i] = __ballot(lvl[i] - m >= 0 && lvl[i] - m <= 3) & nzm[i];
+      uint32_t T = 0;
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = T | (1u << bit);
+        uint32_t cnt = 0;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) cnt += (uint32_t)__popcll(__ballot(frac[i] >= cand) & cm[i]);
+        if (cnt >= r) T = cand;
+      }
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        const bool chosen = ((cm[i] >> lane) & 1ull) && frac[i] >= T;
+        t[i] = ((nzm[i] >> lane) & 1ull) ? min(max(lvl[i] - m, 0), 4) + (chosen ? 1 : 0) : 0;
+      }
+    } else {
+      // every nonzero channel reads 4 planes; the B - nz remaining items go to the
+      // zero channels in ascending order, 4 each
+      const uint32_t rest = B - nz;
+      uint32_t before = 0;   // zero channels in earlier slots
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        const uint32_t rank = before + (uint32_t)__popcll(zm[i] & ((1ull << lane) - 1ull));
+        const int fill = (int)min<uint32_t>(rest - min(rest, 4u * rank), 4u);
+        t[i] = ((nzm[i] >> lane) & 1ull) ? 4 : (((zm[i] >> lane) & 1ull) ? fill : 0);
+        before += (uint32_t)__popcll(zm[i]);
+      }
     }
   } else if (flag == 0 && (mode == 1 || mode == 3) && budget > 0) {
     // fixed-depth comparison modes: 4 planes on the m channels of largest |q_c|

@@ -305,6 +305,14 @@ __device__ __forceinline__ void scan_tile_acc(const ScanArgs& a, int64_t g, int6
     }
     __syncthreads();
     if (gi + 1 < n_grp) issue(gi + 1);
+    // A CU runs several tiles at once and its arbiter favours the oldest
+    // wavefronts, so the youngest tile would finish alone with the VALU half
+    // idle.  Lowering a wavefront's priority as its tile advances lets the
+    // laggards catch up, group by group.
+    if (gi == 0) __builtin_amdgcn_s_setprio(3);
+    else if (gi == 1) __builtin_amdgcn_s_setprio(2);
+    else if (gi == 2) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
 
     // ---- 3. reconstruct and accumulate.  Lane l owns block bl = 2wv + l/32 and,
     // in it, the keys 32 i + jj + 8 s (s = 0..3) of its block's 32-key word
