@@ -94,6 +94,7 @@ struct ScanArgs {
   int64_t ld;
   uint32_t* zero;            // words to clear on the way (may be null)
   int64_t zero_words;
+  int64_t zero_slice;        // words per workgroup: ceil(zero_words / workgroups)
   uint32_t* hist;            // selection histograms [h_q][kSelBins] to add to (fused scans)
   // paged records (may be null): pages[g * npages + p] is the device-visible
   // base of page p of KV head g, [d][R] bytes for page_tiles tiles of keys,
@@ -215,10 +216,12 @@ __device__ __forceinline__ void scan_tile_acc(const ScanArgs& a, int64_t g, int6
   const uint8_t* recg;
   int64_t ablk0;   // first block of the tile within those records
   if (a.pages) {
-    recg = a.pages[g * a.npages + tile / a.page_tiles];
-    ablk0 = (tile % a.page_tiles) * TB;
+    const uint32_t pt = (uint32_t)a.page_tiles;
+    const uint32_t pg = (uint32_t)tile / pt;
+    recg = a.pages[g * a.npages + pg];
+    ablk0 = (int64_t)((uint32_t)tile - pg * pt) * TB;
   } else {
-    recg = rec + (a.ring ? g % a.ring : g) * d * R;
+    recg = rec + (a.ring ? (int64_t)((uint32_t)g % (uint32_t)a.ring) : g) * d * R;
     ablk0 = blk0;
   }
   const int64_t unit0 = ablk0 / kUnitBlocks;
@@ -494,17 +497,18 @@ constexpr int kXcds = 8;
 template <int G, int TB, bool FUSE>
 __global__ __launch_bounds__((Cfg<G, TB>::threads)) void scan_kernel(ScanArgs a, int64_t tiles, int64_t total) {
   __shared__ ScanSmem<G, TB> sm;
-  const int64_t w = blockIdx.x;
-  const int64_t t8 = (tiles + kXcds - 1) / kXcds;
-  const int64_t j = w / kXcds;
-  const int64_t g = j / t8;
-  const int64_t tile = (w % kXcds) * t8 + j % t8;
+  // 32-bit index arithmetic (tiles and grids stay far below 2^31): a 64-bit
+  // division by a run-time value is a long scalar sequence at every start
+  const uint32_t w = blockIdx.x;
+  const uint32_t t8 = (uint32_t)((tiles + kXcds - 1) / kXcds);
+  const uint32_t j = w / kXcds;
+  const uint32_t g = j / t8;
+  const int64_t tile = (int64_t)((w % kXcds) * t8 + (j - g * t8));
   if (tile >= tiles) return;
-  const int64_t L = g * tiles + tile;   // distinct in [0, total)
-  if (a.zero) {   // the selection's counters: one slice per workgroup
-    const int64_t slice = (a.zero_words + total - 1) / total;
-    const int64_t z1 = min((L + 1) * slice, a.zero_words);
-    for (int64_t i = L * slice + threadIdx.x; i < z1; i += Cfg<G, TB>::threads) a.zero[i] = 0u;
+  const int64_t L = (int64_t)g * tiles + tile;   // distinct in [0, total)
+  if (a.zero) {   // the selection's counters: one slice of zero_slice words per workgroup
+    const int64_t z1 = min((L + 1) * a.zero_slice, a.zero_words);
+    for (int64_t i = L * a.zero_slice + threadIdx.x; i < z1; i += Cfg<G, TB>::threads) a.zero[i] = 0u;
   }
   scan_tile<G, TB, FUSE>(a, g, tile, sm);
 }
@@ -579,15 +583,18 @@ __global__ __launch_bounds__((Cfg<G, TB>::threads)) void stage_scan_kernel(
     ScanArgs a, const uint8_t* __restrict__ host, int64_t copy_g0, int copy_heads, int64_t ncopy,
     int64_t scan_g0, int scan_heads, int64_t tiles) {
   __shared__ ScanSmem<G, TB> sm;
-  const int64_t b = blockIdx.x;
-  const int64_t scan_blocks = tiles * scan_heads;
+  const uint32_t b = blockIdx.x;
+  const uint32_t scan_blocks = (uint32_t)(tiles * scan_heads);
   if (b < scan_blocks) {
-    scan_tile<G, TB>(a, scan_g0 + b / tiles, b % tiles, sm);
+    const uint32_t hb = b / (uint32_t)tiles;
+    scan_tile<G, TB>(a, scan_g0 + hb, (int64_t)(b - hb * (uint32_t)tiles), sm);
   } else {
-    const int64_t cb = b - scan_blocks;
-    if (cb < ncopy * copy_heads)
-      copy_piece<G, TB>(host, const_cast<uint8_t*>(a.rec), a.uni, copy_g0 + cb / ncopy, a.d, a.H, a.P,
-                        a.R, cb % ncopy, sm);
+    const uint32_t cb = b - scan_blocks;
+    if (cb < (uint32_t)(ncopy * copy_heads)) {
+      const uint32_t hc = cb / (uint32_t)ncopy;
+      copy_piece<G, TB>(host, const_cast<uint8_t*>(a.rec), a.uni, copy_g0 + hc, a.d, a.H, a.P,
+                        a.R, (int64_t)(cb - hc * (uint32_t)ncopy), sm);
+    }
   }
 }
 
@@ -602,7 +609,7 @@ template <int G, int TB>
 hipError_t launch_g(const uint8_t* rec, const float* q, const uint8_t* depth, const uint8_t* uni,
                     int h_kv, const Layout& L, int d, float* scores, int64_t ld, uint32_t* zero,
                     int64_t zero_words, uint32_t* hist, const Paging& pg, hipStream_t s) {
-  ScanArgs a{rec, q, depth, uni, L.n, L.nb, L.H, L.P, L.R, d, scores, ld, zero, zero_words, hist, nullptr, 0, 1};
+  ScanArgs a{rec, q, depth, uni, L.n, L.nb, L.H, L.P, L.R, d, scores, ld, zero, zero_words, 0, hist, nullptr, 0, 1};
   if (pg.table) {
     // page records are laid out for page_keys keys; tiles never straddle pages
     const Layout P = make_layout(pg.page_keys);
@@ -617,6 +624,7 @@ hipError_t launch_g(const uint8_t* rec, const float* q, const uint8_t* depth, co
   const int64_t tiles = (L.nb + TB - 1) / TB;
   const int64_t total = tiles * h_kv;
   const int64_t grid = kXcds * h_kv * ((tiles + kXcds - 1) / kXcds);
+  a.zero_slice = (zero_words + total - 1) / total;
   if (hist) {
     scan_kernel<G, TB, true><<<(unsigned)grid, Cfg<G, TB>::threads, 0, s>>>(a, tiles, total);
     return hipGetLastError();
@@ -630,7 +638,7 @@ hipError_t launch_staged_g(const uint8_t* host, uint8_t* staging, const float* q
                            const uint8_t* uni, int h_kv, const Layout& L, int d, float* scores,
                            int64_t ld, hipStream_t s) {
   constexpr int TB = kTileDevice;
-  const ScanArgs a{staging, q, depth, uni, L.n, L.nb, L.H, L.P, L.R, d, scores, ld, nullptr, 0, nullptr,
+  const ScanArgs a{staging, q, depth, uni, L.n, L.nb, L.H, L.P, L.R, d, scores, ld, nullptr, 0, 0, nullptr,
                    nullptr, 0, 1, kStageRing};
   const int64_t tiles = (L.nb + TB - 1) / TB;
   const int64_t ncopy = copy_pieces_per_head(L, d);
