@@ -100,11 +100,25 @@ def algorithmic_ops(depth: np.ndarray, union: np.ndarray, n: int) -> int:
     return int((2 * planes + 5 * levels + 4 * fmas) * n // 4)
 
 
+def kernel_code_digest(files=("scan.hip", "fathom_internal.h")) -> str:
+    """sha256 of the kernel sources' code: comments dropped and whitespace
+    collapsed, so that a comment edit does not disown counters taken from the
+    same code."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for f in files:
+        text = open(os.path.join(ROOT, "sparse_attention_top_query_amd", "csrc", f)).read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+    return h.hexdigest()
+
+
 def measured_traffic(workload: str, residency: str, kernel: str):
     """Scaled FETCH_SIZE + WRITE_SIZE bytes per launch from the committed
     rocprofv3 summary of this workload, or None when there is none or the scan
-    sources have changed since the counters were taken."""
-    import hashlib
+    code has changed since the counters were taken."""
     name = PROFILES.get((workload, residency))
     path = os.path.join(ROOT, "profiles", name) if name else None
     if not path or not os.path.exists(path):
@@ -116,10 +130,7 @@ def measured_traffic(workload: str, residency: str, kernel: str):
     for line in text.split("```figures", 1)[1].split("```", 1)[0].strip().splitlines():
         key, _, val = line.partition(":")
         fig[key.strip()] = val.strip()
-    h = hashlib.sha256()
-    for f in ("scan.hip", "fathom_internal.h"):
-        h.update(open(os.path.join(ROOT, "sparse_attention_top_query_amd", "csrc", f), "rb").read())
-    if fig.get("kernel_source_sha256") != h.hexdigest() or "fetch_bytes_per_dispatch" not in fig:
+    if fig.get("kernel_code_sha256") != kernel_code_digest() or "fetch_bytes_per_dispatch" not in fig:
         return None
     if not kernel.startswith(fig.get("kernel", "?").split("<")[0]):
         return None

@@ -71,9 +71,9 @@ struct ScanSmem {
   uint4 planes[kStageChunks + kPlanes - 1][TB];    // staged plane bits (plane 0 complemented); the last
                                                    // rows pad reads of a prefix's unread planes
   uint4 scales[kStageEntries][TB / kUnitBlocks];   // staged fp16 scales per entry of the group
-  float coef[kStageChunks][TB][G];                 // 2 [q_h 2^(3-t_h) Delta_b] per block and head, in the
+  float coef[kStageChunks][TB][G];                 // a = [q_h Delta_b / 16] per block and head, in the
                                                    // row of the entry's first chunk (for G = 4 a row has the
-                                                   // planes' stride: one address serves both)
+                                                   // planes' stride)
   float ent_q[kMaxD][G];                           // q_h / 16 of each list entry
   uint64_t ent_word[kMaxD + 1];                    // level masks: bit (t-1) G + h iff head h reads t planes
   uint16_t ent_base[kMaxD + 1];                    // first chunk of entry e (prefix sum)
