@@ -328,17 +328,27 @@ __device__ __forceinline__ void scan_tile_acc(const ScanArgs& a, int64_t g, int6
       const uint32_t rot0 = (uint32_t)(jj + 25) & 31u, rot1 = (uint32_t)(jj + 26) & 31u;
       const uint32_t rot2 = (uint32_t)(jj + 27) & 31u, rot3 = (uint32_t)(jj + 28) & 31u;
       // the group's entries (at most 64: each starts in one of its 64 chunk
-      // slots), one per lane; the loop reads them lane by lane into scalars
-      // Per lane: chunk base within the group (< 128) | union depth << 8, and
-      // for G <= 4 the level masks in bits 12 .. 27 of the same word.
+      // slots), one per lane; the loop reads them lane by lane into scalars.
+      // Per lane: chunk base within the group (< 128) in bits 0..7; for G <= 4
+      // the level masks in bits 8..23, a flag per depth read by some head in
+      // bits 24..27 and flags for union depth > 1, > 2, > 3 in bits 28..30, so
+      // every test of the loop is one scalar bit test; for larger G the union
+      // depth in bits 8..11 and the masks read separately.
       constexpr int MB = 4 * G;
       const bool mine = e_lo + lane < e_hi;
       const uint64_t lword = mine ? sm.ent_word[e_lo + lane] : 0ull;
       int linfo = 0;
       if (mine) {
         const int b0 = sm.ent_base[e_lo + lane], b1 = sm.ent_base[e_lo + lane + 1];
-        linfo = (b0 - ch_lo) | (b1 - b0) << 8;
-        if (MB <= 16) linfo |= (int)lword << 12;
+        const int u = b1 - b0;
+        if constexpr (MB <= 16) {
+          int any = 0;
+#pragma unroll
+          for (int t = 0; t < kPlanes; ++t) any |= ((lword >> (G * t)) & ((1u << G) - 1u)) ? 1 << t : 0;
+          linfo = (b0 - ch_lo) | (int)lword << 8 | any << 24 | (u > 1) << 28 | (u > 2) << 29 | (u > 3) << 30;
+        } else {
+          linfo = (b0 - ch_lo) | u << 8;
+        }
       }
       // a 32-bit word where the masks fit, so a mask test sets the branch condition
       using Word = std::conditional_t<(MB <= 32), uint32_t, uint64_t>;
@@ -346,15 +356,23 @@ __device__ __forceinline__ void scan_tile_acc(const ScanArgs& a, int64_t g, int6
         const uint32_t info = (uint32_t)__builtin_amdgcn_readlane(linfo, e - e_lo);
         Word word;
         if constexpr (MB <= 16) {
-          word = info >> 12;
+          word = info >> 8;
         } else if constexpr (MB <= 32) {
           word = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)lword, e - e_lo);
         } else {
           word = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)lword, e - e_lo) |
                  (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(lword >> 32), e - e_lo) << 32;
         }
+        // some head reads exactly t planes; the union depth exceeds t
+        auto has_level = [&](int t) -> bool {
+          if constexpr (MB <= 16) return (info >> (23 + t)) & 1u;
+          else return (word & ((Word)((1ull << G) - 1ull) << (G * (t - 1)))) != 0;
+        };
+        auto deeper = [&](int t) -> bool {
+          if constexpr (MB <= 16) return (info >> (27 + t)) & 1u;
+          else return (int)((info >> 8) & 0xfu) > t;
+        };
         const int cb = (int)(info & 0xffu);
-        const int tb = (int)((info >> 8) & 0xfu);
         const uint32_t* pp = reinterpret_cast<const uint32_t*>(&sm.planes[cb][bl]) + ((lane & 31) >> 3);
         // the lane's word of each plane row: all four rows are read (within the
         // padded array), only tb of them used
@@ -380,15 +398,14 @@ __device__ __forceinline__ void scan_tile_acc(const ScanArgs& a, int64_t g, int6
             for (int s2 = 0; s2 < kSub; ++s2) acc[s2][h] = fmaf(cf[h], f[s2], acc[s2][h]);
           }
         };
-        constexpr Word kHeads = (Word)((1ull << G) - 1ull);
-        if (word & kHeads) level(1);
-        if (tb > 1) {
+        if (has_level(1)) level(1);
+        if (deeper(1)) {
           y |= __builtin_amdgcn_alignbit(w1, w1, rot1) & 0x40404040u;
-          if (word & (kHeads << G)) level(2);
-          if (tb > 2) {
+          if (has_level(2)) level(2);
+          if (deeper(2)) {
             y |= __builtin_amdgcn_alignbit(w2, w2, rot2) & 0x20202020u;
-            if (word & (kHeads << (2 * G))) level(3);
-            if (tb > 3) {
+            if (has_level(3)) level(3);
+            if (deeper(3)) {
               y |= __builtin_amdgcn_alignbit(w3, w3, rot3) & 0x10101010u;
               level(4);
             }
