@@ -376,7 +376,7 @@ def run_layers(args, torch, F, wl, dev):
                      "unit": "GB/s", "frac": round(achieved / peak, 4), "traffic": None,
                      "measured_h2d_peak": round(h2d_peak, 2) if host else None,
                      "frac_of_measured_h2d": round(achieved / h2d_peak, 4) if host else None,
-                     "kernel": "scan_kernel<4, 32>" if host else "scan_kernel<4, 8>",
+                     "kernel": "scan_kernel<4, 64>" if host else "scan_kernel<4, 8>",
                      "scan_ms_all_layers": round(scan_ms, 3), "bytes_all_layers": alg},
         "cpu_baseline": None,
         "record_bytes_resident": wl.layers * hk * d * F.record_bytes(n),
@@ -481,7 +481,7 @@ def main():
     if host and residency == F.HOST_STAGED:
         kname = f"stage_scan_kernel<{g}, 8>"
     else:
-        kname = f"scan_kernel<{g}, {32 if g <= 4 else 16}>" if host else f"scan_kernel<{g}, 8>"
+        kname = f"scan_kernel<{g}, {64 if g <= 4 else 16}>" if host else f"scan_kernel<{g}, 8>"
     res_key = args.residency if host else "hbm"
     traffic = measured_traffic(args.workload, res_key, kname)
     common = {"traffic": traffic["total"] if traffic else None,

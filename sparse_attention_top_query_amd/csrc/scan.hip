@@ -15,10 +15,12 @@
 // (m + 1) 2^-24 sum_c |q_c k_hat_c|.
 //
 // Work decomposition: one workgroup scores a tile of TB 128-key blocks of one KV
-// head for all of its G query heads; each wavefront owns 2 blocks (256 keys):
-// lanes 0-31 one block, lanes 32-63 the other.  Lane l owns the keys
+// head for all of its G query heads; each wavefront owns 2 KW blocks, 32 / KW
+// lanes per block (KW = 1 from device memory; KW = 2 and 8192-key tiles for
+// reading pinned host memory in place).  With KW = 1, lane l owns the keys
 // 32 i + jj + 8 s (s = 0..3) of its block, i = (l%32)/8, jj = l%8: the bits
-// jj + 8 s of 32-bit word i of each plane row of the block.
+// jj + 8 s of 32-bit word i of each plane row of the block; with KW = 2 it owns
+// two such groups of 4 keys, 4 bits apart in the same word.
 //  1. The union depths of the KV head list the channels to read; every query
 //     head of the group is scored from the one read of the longest prefix.
 //  2. Staging, channel group by channel group (about 64 channel-planes): the
@@ -31,10 +33,10 @@
 //     contiguous run per channel-plane (16 B per block).
 //  3. Per (channel, block) the coefficients a = [q_h Delta / 16] are formed once
 //     in LDS.  Per channel, each lane reads its word of each plane row and
-//     builds the 4 keys' prefixes side by side, one per byte of a register y:
-//     plane p's word rotated right by jj + p - 7 puts the lane's 4 bits at bit
-//     7 - p of bytes 0..3, and one and-or adds them to y (two operations per
-//     plane for 4 keys).  The complemented MSB is the byte's sign bit, so after
+//     builds each group of 4 keys' prefixes side by side, one per byte of a
+//     register y: plane p's word rotated right by jj + p - 7 puts the group's 4
+//     bits at bit 7 - p of bytes 0..3, and one and-or adds them to y (two
+//     operations per plane for 4 keys).  The complemented MSB is the byte's sign bit, so after
 //     t planes byte s of y is 2^(8-t) r_t of key s; setting bit 7 - t of every
 //     byte makes it z_t.  Per depth in use: that one or, then 4 signed-byte
 //     conversions to float; per head reading the channel: one fma per key.
@@ -53,12 +55,18 @@ constexpr int kSlackChunks = kPlanes - 1;      // an entry starting in a group e
 constexpr int kStageChunks = kGroupChunks + kSlackChunks;
 constexpr int kStageEntries = kStageChunks;    // entries have >= 1 chunk
 constexpr int kMaxChunks = kPlanes * kMaxD;
-constexpr int kWaveBlocks = 2;                 // 128-key blocks per wavefront
-constexpr int kSub = kBlock / 32;              // 32-key words per block; a lane scores one key of each
+constexpr int kSub = kBlock / 32;              // 32-key words per block, keys per byte register
 
-template <int G, int TB>
+// KW byte registers of 4 keys per lane: a wavefront covers 2 KW blocks, 32 / KW
+// lanes per block.  One (KW = 1, 4 wavefronts per SIMD at 131k keys) where
+// the arithmetic must hide latency; two where the tile must be long (the
+// host-link scan: 8192-key tiles, 1-KB runs per channel-plane, still 1024
+// threads).
+template <int G, int TB, int KW = 1>
 struct Cfg {
-  static constexpr int threads = 64 * TB / kWaveBlocks;
+  static constexpr int keys = kSub * KW;              // keys per lane
+  static constexpr int wave_blocks = 2 * KW;          // 128-key blocks per wavefront
+  static constexpr int threads = 64 * TB / wave_blocks;
   static constexpr int units = TB / kUnitBlocks;      // 1024-key record units per tile
   static constexpr int slots = TB + units;            // 16-byte pieces per chunk slot
   static constexpr int ppt = (kStageChunks * slots + threads - 1) / threads;
@@ -122,10 +130,10 @@ constexpr int kHistHeads = (int)(sizeof(ScanSmem<G, TB>) / 4 / kHistWords) < G
 // Scores of tile `tile` (TB blocks) of KV head g for all its query heads, left
 // in acc: acc[s][h] is the score for query head g G + h of the key
 // tile_key(s) of the tile.
-template <int G, int TB>
+template <int G, int TB, int KW>
 __device__ __forceinline__ void scan_tile_acc(const ScanArgs& a, int64_t g, int64_t tile, ScanSmem<G, TB>& sm,
-                                              float (&acc)[kSub][G]) {
-  using C = Cfg<G, TB>;
+                                              float (&acc)[Cfg<G, TB, KW>::keys][G]) {
+  using C = Cfg<G, TB, KW>;
   constexpr int SLOTS = C::slots;
   constexpr int NT = C::threads;
   constexpr int PPT = C::ppt;
@@ -138,7 +146,8 @@ __device__ __forceinline__ void scan_tile_acc(const ScanArgs& a, int64_t g, int6
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int64_t blk0 = tile * TB;
-  const int bl = kWaveBlocks * wv + (lane >> 5);   // block of this lane within the tile
+  constexpr int LB = 32 / KW;                        // lanes per block
+  const int bl = C::wave_blocks * wv + lane / LB;    // block of this lane within the tile
   const int nvalid = (int)min<int64_t>(TB, nb - blk0);
 
   // ---- 1. list of union channels, in channel order, and staging groups ----
@@ -209,7 +218,7 @@ __device__ __forceinline__ void scan_tile_acc(const ScanArgs& a, int64_t g, int6
 #pragma unroll
   for (int h = 0; h < G; ++h) {
 #pragma unroll
-    for (int s = 0; s < kSub; ++s) acc[s][h] = 0.0f;
+    for (int s = 0; s < C::keys; ++s) acc[s][h] = 0.0f;
   }
 
   // the tile's records: the KV head's own, or its page (addressed page-locally)
@@ -317,16 +326,21 @@ __device__ __forceinline__ void scan_tile_acc(const ScanArgs& a, int64_t g, int6
     else if (gi == 2) __builtin_amdgcn_s_setprio(1);
     else __builtin_amdgcn_s_setprio(0);
 
-    // ---- 3. reconstruct and accumulate.  Lane l owns block bl = 2wv + l/32 and,
-    // in it, the keys 32 i + jj + 8 s (s = 0..3) of its block's 32-key word
-    // i = (l%32)/8, jj = l%8: bits jj + 8 s of that word of each plane row, so
-    // a lane reads one 32-bit word per plane row and finds its 4 bits one per
-    // byte.  Rotating the word right by jj + p - 7 brings them to bit 7 - p of
-    // bytes 0..3, where plane p belongs in the byte-wise signed prefix.
-    if (kWaveBlocks * wv < nvalid) {
-      const int jj = lane & 7;
-      const uint32_t rot0 = (uint32_t)(jj + 25) & 31u, rot1 = (uint32_t)(jj + 26) & 31u;
-      const uint32_t rot2 = (uint32_t)(jj + 27) & 31u, rot3 = (uint32_t)(jj + 28) & 31u;
+    // ---- 3. reconstruct and accumulate.  Lane l owns block bl = 2 KW wv + l/LB
+    // and, in it, the keys 32 i + jj + JS k + 8 s (k < KW, s = 0..3) of its
+    // block's 32-key word i = (l%LB)/JS, jj = l%JS, JS = 8/KW: bits jj + JS k +
+    // 8 s of that word of each plane row, so a lane reads one 32-bit word per
+    // plane row and finds its KW groups of 4 bits at a stride of 8.  Rotating
+    // the word right by jj + JS k + p - 7 brings group k to bit 7 - p of bytes
+    // 0..3, where plane p belongs in the byte-wise signed prefix y[k].
+    if (C::wave_blocks * wv < nvalid) {
+      constexpr int JS = 8 / KW;
+      const int jj = lane % JS;
+      uint32_t rot[kPlanes][KW];
+#pragma unroll
+      for (int p = 0; p < kPlanes; ++p)
+#pragma unroll
+        for (int k = 0; k < KW; ++k) rot[p][k] = (uint32_t)(jj + JS * k + 25 + p) & 31u;
       // the group's entries (at most 64: each starts in one of its 64 chunk
       // slots), one per lane; the loop reads them lane by lane into scalars.
       // Per lane: chunk base within the group (< 128) in bits 0..7; for G <= 4
@@ -373,40 +387,49 @@ __device__ __forceinline__ void scan_tile_acc(const ScanArgs& a, int64_t g, int6
           else return (int)((info >> 8) & 0xfu) > t;
         };
         const int cb = (int)(info & 0xffu);
-        const uint32_t* pp = reinterpret_cast<const uint32_t*>(&sm.planes[cb][bl]) + ((lane & 31) >> 3);
+        const uint32_t* pp = reinterpret_cast<const uint32_t*>(&sm.planes[cb][bl]) + (lane % LB) / JS;
         // the lane's word of each plane row: all four rows are read (within the
         // padded array), only tb of them used
         const uint32_t w0 = pp[0], w1 = pp[4 * TB], w2 = pp[8 * TB], w3 = pp[12 * TB];
         float cf[G];
 #pragma unroll
         for (int h = 0; h < G; ++h) cf[h] = sm.coef[cb][bl][h];
-        // y: byte s holds the signed prefix of key s read so far, MSB at bit 7
-        // (plane 0 is stored complemented, so bit 7 is the sign); one depth t:
-        // z = y | 2^(7-t) per byte is 2^(7-t) (2 r_t + 1), converted once
-        // (signed byte to float), then every head that reads exactly t planes
-        // adds a z per key
-        uint32_t y = __builtin_amdgcn_alignbit(w0, w0, rot0) & 0x80808080u;
-        auto level = [&](int t) {
-          const uint32_t z = y | (0x01010101u << (7 - t));
-          float f[kSub];
+        // y[k]: byte s holds the signed prefix of key (k, s) read so far, MSB at
+        // bit 7 (plane 0 is stored complemented, so bit 7 is the sign); one
+        // depth t: z = y | 2^(7-t) per byte is 2^(7-t) (2 r_t + 1), converted
+        // once (signed byte to float), then every head that reads exactly t
+        // planes adds a z per key
+        uint32_t y[KW];
 #pragma unroll
-          for (int s2 = 0; s2 < kSub; ++s2) f[s2] = (float)(int)(int8_t)(z >> (8 * s2));
+        for (int k = 0; k < KW; ++k) y[k] = __builtin_amdgcn_alignbit(w0, w0, rot[0][k]) & 0x80808080u;
+        auto plane = [&](uint32_t w, int p) {
+#pragma unroll
+          for (int k = 0; k < KW; ++k) y[k] |= __builtin_amdgcn_alignbit(w, w, rot[p][k]) & (0x80808080u >> p);
+        };
+        auto level = [&](int t) {
+          float f[C::keys];
+#pragma unroll
+          for (int k = 0; k < KW; ++k) {
+            const uint32_t z = y[k] | (0x01010101u << (7 - t));
+#pragma unroll
+            for (int s2 = 0; s2 < kSub; ++s2) f[kSub * k + s2] = (float)(int)(int8_t)(z >> (8 * s2));
+          }
 #pragma unroll
           for (int h = 0; h < G; ++h) {
             if (!(word & ((Word)1 << ((t - 1) * G + h)))) continue;
 #pragma unroll
-            for (int s2 = 0; s2 < kSub; ++s2) acc[s2][h] = fmaf(cf[h], f[s2], acc[s2][h]);
+            for (int s2 = 0; s2 < C::keys; ++s2) acc[s2][h] = fmaf(cf[h], f[s2], acc[s2][h]);
           }
         };
         if (has_level(1)) level(1);
         if (deeper(1)) {
-          y |= __builtin_amdgcn_alignbit(w1, w1, rot1) & 0x40404040u;
+          plane(w1, 1);
           if (has_level(2)) level(2);
           if (deeper(2)) {
-            y |= __builtin_amdgcn_alignbit(w2, w2, rot2) & 0x20202020u;
+            plane(w2, 2);
             if (has_level(3)) level(3);
             if (deeper(3)) {
-              y |= __builtin_amdgcn_alignbit(w3, w3, rot3) & 0x10101010u;
+              plane(w3, 3);
               level(4);
             }
           }
@@ -418,22 +441,24 @@ __device__ __forceinline__ void scan_tile_acc(const ScanArgs& a, int64_t g, int6
 
 }
 
-// Key of acc[s] of this thread within its tile: block 2 w + l/32, word
-// (l%32)/8, bit l%8 + 8 s of that word.
-template <int TB>
+// Key of acc[s] of this thread within its tile: block 2 KW w + l/LB, word
+// (l%LB)/JS, bit l%JS + JS (s/4) + 8 (s%4) of that word (LB = 32/KW, JS = 8/KW).
+template <int TB, int KW>
 __device__ __forceinline__ int tile_key(int s) {
+  constexpr int LB = 32 / KW, JS = 8 / KW;
   const int lane = threadIdx.x & 63;
-  return (kWaveBlocks * (int)(threadIdx.x >> 6) + (lane >> 5)) * kBlock + 32 * ((lane & 31) >> 3) + (lane & 7) +
-         8 * s;
+  return (2 * KW * (int)(threadIdx.x >> 6) + lane / LB) * kBlock + 32 * ((lane % LB) / JS) + lane % JS +
+         JS * (s / kSub) + 8 * (s % kSub);
 }
 
 // Scores of the tile to a.scores, one store per key and head.
-template <int G, int TB>
-__device__ __forceinline__ void store_tile(const ScanArgs& a, int64_t g, int64_t tile, const float (&acc)[kSub][G]) {
+template <int G, int TB, int KW>
+__device__ __forceinline__ void store_tile(const ScanArgs& a, int64_t g, int64_t tile,
+                                           const float (&acc)[Cfg<G, TB, KW>::keys][G]) {
   const int64_t key0 = tile * TB * kBlock;
 #pragma unroll
-  for (int s2 = 0; s2 < kSub; ++s2) {
-    const int64_t j = key0 + tile_key<TB>(s2);
+  for (int s2 = 0; s2 < Cfg<G, TB, KW>::keys; ++s2) {
+    const int64_t j = key0 + tile_key<TB, KW>(s2);
     if (j < a.n) {
 #pragma unroll
       for (int h = 0; h < G; ++h) store_global(a.scores + (g * G + h) * a.ld + j, acc[s2][h]);
@@ -445,10 +470,10 @@ __device__ __forceinline__ void store_tile(const ScanArgs& a, int64_t g, int64_t
 // digit: an LDS histogram per round of heads (16-bit counts in the staging
 // memory, dead once the tile is scored), then one global atomic per non-empty
 // bin.
-template <int G, int TB>
+template <int G, int TB, int KW>
 __device__ __forceinline__ void hist_tile(const ScanArgs& a, uint32_t* hist, int64_t g, int64_t tile,
-                                          const float (&acc)[kSub][G], ScanSmem<G, TB>& sm) {
-  constexpr int NT = Cfg<G, TB>::threads;
+                                          const float (&acc)[Cfg<G, TB, KW>::keys][G], ScanSmem<G, TB>& sm) {
+  constexpr int NT = Cfg<G, TB, KW>::threads;
   constexpr int HR = kHistHeads<G, TB>;
   static_assert(HR >= 1 && TB * kBlock < 65536, "16-bit counts of at least one head must fit");
   const int tid = threadIdx.x;
@@ -460,8 +485,8 @@ __device__ __forceinline__ void hist_tile(const ScanArgs& a, uint32_t* hist, int
     for (int i = tid; i < HR * kHistWords; i += NT) lh[i] = 0u;
     __syncthreads();
 #pragma unroll
-    for (int s2 = 0; s2 < kSub; ++s2) {
-      if (key0 + tile_key<TB>(s2) < a.n) {
+    for (int s2 = 0; s2 < Cfg<G, TB, KW>::keys; ++s2) {
+      if (key0 + tile_key<TB, KW>(s2) < a.n) {
 #pragma unroll
         for (int hh = 0; hh < HR; ++hh) {
           if (h0 + hh < G) {
@@ -487,21 +512,32 @@ __device__ __forceinline__ void hist_tile(const ScanArgs& a, uint32_t* hist, int
 // Scores of tile `tile` (TB blocks) of KV head g, all its query heads.  With
 // FUSE, the tile's scores are also counted into a.hist by their first
 // selection digit.
-template <int G, int TB, bool FUSE = false>
+template <int G, int TB, int KW = 1, bool FUSE = false>
 __device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t tile, ScanSmem<G, TB>& sm) {
-  float acc[kSub][G];
-  scan_tile_acc<G, TB>(a, g, tile, sm, acc);
-  store_tile<G, TB>(a, g, tile, acc);
-  if constexpr (FUSE) hist_tile<G, TB>(a, a.hist, g, tile, acc, sm);
+  float acc[Cfg<G, TB, KW>::keys][G];
+  scan_tile_acc<G, TB, KW>(a, g, tile, sm, acc);
+  store_tile<G, TB, KW>(a, g, tile, acc);
+  if constexpr (FUSE) hist_tile<G, TB, KW>(a, a.hist, g, tile, acc, sm);
 }
 
 // Tile size per residency: device memory likes many small tiles (occupancy);
 // reading pinned host memory in place wants long contiguous runs per
-// channel-plane (>= 512 bytes keeps the host link near its streaming rate).
+// channel-plane (>= 512 bytes keeps the host link near its streaming rate; 1 KB
+// runs, 8192-key tiles at 8 keys per lane, scan 1% faster than 512-byte ones).
+// Paged host records keep 4096-key tiles so that pages of any multiple of 4096
+// keys hold whole tiles.
 constexpr int kTileDevice = 8;    // 1024 keys, 256 threads
 template <int G>
 struct HostTile {
-  static constexpr int TB = G <= 4 ? 32 : 16;   // LDS for the coefficients bounds it for large G
+  // 8 keys per lane needs twice the accumulators; the coefficients' LDS bounds
+  // the tile for larger G
+  static constexpr int KW = G <= 4 ? 2 : 1;
+  static constexpr int TB = G <= 4 ? 64 : 16;
+};
+template <int G>
+struct PagedHostTile {
+  static constexpr int KW = 1;
+  static constexpr int TB = G <= 4 ? 32 : 16;
 };
 
 // Workgroup ids are dealt round-robin to the 8 XCDs, each with its own L2.  The
@@ -511,8 +547,8 @@ struct HostTile {
 // every XCD gets the same mix of heads (whose union depths, and so work, differ).
 constexpr int kXcds = 8;
 
-template <int G, int TB, bool FUSE>
-__global__ __launch_bounds__((Cfg<G, TB>::threads)) void scan_kernel(ScanArgs a, int64_t tiles, int64_t total) {
+template <int G, int TB, int KW, bool FUSE>
+__global__ __launch_bounds__((Cfg<G, TB, KW>::threads)) void scan_kernel(ScanArgs a, int64_t tiles, int64_t total) {
   __shared__ ScanSmem<G, TB> sm;
   // 32-bit index arithmetic (tiles and grids stay far below 2^31): a 64-bit
   // division by a run-time value is a long scalar sequence at every start
@@ -525,9 +561,9 @@ __global__ __launch_bounds__((Cfg<G, TB>::threads)) void scan_kernel(ScanArgs a,
   const int64_t L = (int64_t)g * tiles + tile;   // distinct in [0, total)
   if (a.zero) {   // the selection's counters: one slice of zero_slice words per workgroup
     const int64_t z1 = min((L + 1) * a.zero_slice, a.zero_words);
-    for (int64_t i = L * a.zero_slice + threadIdx.x; i < z1; i += Cfg<G, TB>::threads) a.zero[i] = 0u;
+    for (int64_t i = L * a.zero_slice + threadIdx.x; i < z1; i += Cfg<G, TB, KW>::threads) a.zero[i] = 0u;
   }
-  scan_tile<G, TB, FUSE>(a, g, tile, sm);
+  scan_tile<G, TB, KW, FUSE>(a, g, tile, sm);
 }
 
 // ---------------------------------------------------------------------------
@@ -622,7 +658,7 @@ struct Paging {
   int64_t page_keys;
 };
 
-template <int G, int TB>
+template <int G, int TB, int KW>
 hipError_t launch_g(const uint8_t* rec, const float* q, const uint8_t* depth, const uint8_t* uni,
                     int h_kv, const Layout& L, int d, float* scores, int64_t ld, uint32_t* zero,
                     int64_t zero_words, uint32_t* hist, const Paging& pg, hipStream_t s) {
@@ -643,10 +679,10 @@ hipError_t launch_g(const uint8_t* rec, const float* q, const uint8_t* depth, co
   const int64_t grid = kXcds * h_kv * ((tiles + kXcds - 1) / kXcds);
   a.zero_slice = (zero_words + total - 1) / total;
   if (hist) {
-    scan_kernel<G, TB, true><<<(unsigned)grid, Cfg<G, TB>::threads, 0, s>>>(a, tiles, total);
+    scan_kernel<G, TB, KW, true><<<(unsigned)grid, Cfg<G, TB, KW>::threads, 0, s>>>(a, tiles, total);
     return hipGetLastError();
   }
-  scan_kernel<G, TB, false><<<(unsigned)grid, Cfg<G, TB>::threads, 0, s>>>(a, tiles, total);
+  scan_kernel<G, TB, KW, false><<<(unsigned)grid, Cfg<G, TB, KW>::threads, 0, s>>>(a, tiles, total);
   return hipGetLastError();
 }
 
@@ -675,9 +711,13 @@ template <int G>
 hipError_t launch_any(const uint8_t* rec, bool host, const float* q, const uint8_t* depth,
                       const uint8_t* uni, int h_kv, const Layout& L, int d, float* scores, int64_t ld,
                       uint32_t* zero, int64_t zero_words, uint32_t* hist, const Paging& pg, hipStream_t s) {
+  if (host && pg.table)
+    return launch_g<G, PagedHostTile<G>::TB, PagedHostTile<G>::KW>(rec, q, depth, uni, h_kv, L, d, scores, ld, zero,
+                                                                     zero_words, hist, pg, s);
   if (host)
-    return launch_g<G, HostTile<G>::TB>(rec, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words, hist, pg, s);
-  return launch_g<G, kTileDevice>(rec, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words, hist, pg, s);
+    return launch_g<G, HostTile<G>::TB, HostTile<G>::KW>(rec, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words,
+                                                         hist, pg, s);
+  return launch_g<G, kTileDevice, 1>(rec, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words, hist, pg, s);
 }
 
 }  // namespace
