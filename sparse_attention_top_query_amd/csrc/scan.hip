@@ -50,10 +50,15 @@
 namespace fathom {
 namespace {
 
-constexpr int kGroupChunks = 64;               // channel-planes per staging group (+3 slack)
 constexpr int kSlackChunks = kPlanes - 1;      // an entry starting in a group ends in it
-constexpr int kStageChunks = kGroupChunks + kSlackChunks;
-constexpr int kStageEntries = kStageChunks;    // entries have >= 1 chunk
+// Channel-planes per staging group (+3 slack): 64, or 32 for the 8192-key host
+// tiles, whose 1024 threads each hold one group's pieces in registers.
+template <int TB>
+struct Stage {
+  static constexpr int group = TB >= 64 ? 32 : 64;
+  static constexpr int chunks = group + kSlackChunks;
+  static constexpr int entries = chunks;        // entries have >= 1 chunk
+};
 constexpr int kMaxChunks = kPlanes * kMaxD;
 constexpr int kSub = kBlock / 32;              // 32-key words per block, keys per byte register
 
@@ -69,23 +74,23 @@ struct Cfg {
   static constexpr int threads = 64 * TB / wave_blocks;
   static constexpr int units = TB / kUnitBlocks;      // 1024-key record units per tile
   static constexpr int slots = TB + units;            // 16-byte pieces per chunk slot
-  static constexpr int ppt = (kStageChunks * slots + threads - 1) / threads;
+  static constexpr int ppt = (Stage<TB>::chunks * slots + threads - 1) / threads;
   static_assert(threads >= kMaxD && threads <= 1024, "one thread per channel in the list build");
   static_assert(TB % kUnitBlocks == 0, "tiles hold whole 1024-key units");
 };
 
 template <int G, int TB>
 struct ScanSmem {
-  uint4 planes[kStageChunks + kPlanes - 1][TB];    // staged plane bits (plane 0 complemented); the last
+  uint4 planes[Stage<TB>::chunks + kPlanes - 1][TB];   // staged plane bits (plane 0 complemented); the last
                                                    // rows pad reads of a prefix's unread planes
-  uint4 scales[kStageEntries][TB / kUnitBlocks];   // staged fp16 scales per entry of the group
-  float coef[kStageChunks][TB][G];                 // a = [q_h Delta_b / 16] per block and head, in the
+  uint4 scales[Stage<TB>::entries][TB / kUnitBlocks];  // staged fp16 scales per entry of the group
+  float coef[Stage<TB>::chunks][TB][G];            // a = [q_h Delta_b / 16] per block and head, in the
                                                    // row of the entry's first chunk (for G = 4 a row has the
                                                    // planes' stride)
   float ent_q[kMaxD][G];                           // q_h / 16 of each list entry
   uint64_t ent_word[kMaxD + 1];                    // level masks: bit (t-1) G + h iff head h reads t planes
   uint16_t ent_base[kMaxD + 1];                    // first chunk of entry e (prefix sum)
-  uint16_t grp[kMaxChunks / kGroupChunks + 2];     // first entry of each staging group
+  uint16_t grp[kMaxChunks / Stage<TB>::group + 2];  // first entry of each staging group
   uint32_t chunk_meta[kMaxChunks];                 // entry | channel << 8 | plane << 16 of each chunk
   int wsum[2][16];
   int n_grp;
@@ -198,9 +203,9 @@ __device__ __forceinline__ void scan_tile_acc(const ScanArgs& a, int64_t g, int6
       if (e == n_ent - 1) {
         sm.ent_base[n_ent] = (uint16_t)(base + u);
         // an entry joins the group holding its first chunk; first chunks are at
-        // most 4 apart, so groups 0 .. base/64 are all non-empty
-        sm.n_grp = base / kGroupChunks + 1;
-        sm.grp[base / kGroupChunks + 1] = (uint16_t)n_ent;
+        // most 4 apart, so every group up to this one is non-empty
+        sm.n_grp = base / Stage<TB>::group + 1;
+        sm.grp[base / Stage<TB>::group + 1] = (uint16_t)n_ent;
       }
 #pragma unroll
       for (int p = 0; p < kPlanes; ++p)
@@ -209,8 +214,8 @@ __device__ __forceinline__ void scan_tile_acc(const ScanArgs& a, int64_t g, int6
     if (tid == 0 && n_ent == 0) sm.n_grp = 0;
     __syncthreads();
     if (act) {
-      const int gi = base / kGroupChunks;
-      if (e == 0 || sm.ent_base[e - 1] / kGroupChunks != gi) sm.grp[gi] = (uint16_t)e;
+      const int gi = base / Stage<TB>::group;
+      if (e == 0 || sm.ent_base[e - 1] / Stage<TB>::group != gi) sm.grp[gi] = (uint16_t)e;
     }
     __syncthreads();
   }
@@ -341,7 +346,7 @@ __device__ __forceinline__ void scan_tile_acc(const ScanArgs& a, int64_t g, int6
       for (int p = 0; p < kPlanes; ++p)
 #pragma unroll
         for (int k = 0; k < KW; ++k) rot[p][k] = (uint32_t)(jj + JS * k + 25 + p) & 31u;
-      // the group's entries (at most 64: each starts in one of its 64 chunk
+      // the group's entries (at most 64: each starts in one of its <= 64 chunk
       // slots), one per lane; the loop reads them lane by lane into scalars.
       // Per lane: chunk base within the group (< 128) in bits 0..7; for G <= 4
       // the level masks in bits 8..23, a flag per depth read by some head in
