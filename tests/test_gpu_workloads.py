@@ -34,6 +34,25 @@ def F():
     return fathom
 
 
+def oracle_codes(k_head, threads=8):
+    """The oracle's scales and codes of one KV head.  The codes of a 128-key
+    block depend only on that block's keys and scale, so long heads are cut into
+    block-aligned ranges quantised by the oracle side by side (numpy drops the
+    interpreter lock inside its loops); the result is the same array."""
+    from concurrent.futures import ThreadPoolExecutor
+    delta = O.block_scales(k_head)
+    n = k_head.shape[0]
+    nb = delta.shape[1]
+    per = -(-nb // threads)
+    if n < 131072:
+        return delta, O.quantize_codes(k_head, delta)
+    spans = [(b0, min(b0 + per, nb)) for b0 in range(0, nb, per)]
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        parts = list(ex.map(lambda sp: O.quantize_codes(k_head[sp[0] * O.BLOCK:sp[1] * O.BLOCK],
+                                                        delta[:, sp[0]:sp[1]]), spans))
+    return delta, np.concatenate(parts, axis=0)
+
+
 _PINNED = {}
 
 
@@ -113,8 +132,7 @@ def run_and_check(F, wl, layer=0, sample_heads=(0, 1, 2, 3), host_modes=None, fu
     mark("packed")
     codes = {}
     for v in sorted(set(full_record_heads) | {h // g for h in sample_heads}):
-        delta = O.block_scales(k_np[v])
-        codes[v] = (delta, O.quantize_codes(k_np[v], delta))
+        codes[v] = oracle_codes(k_np[v])
     mark("oracle codes")
     check_records(rec.numpy() if host else rec.cpu().numpy(), k_np,
                   {v: codes[v] for v in full_record_heads})
