@@ -126,7 +126,7 @@ struct ScanArgs {
 
 // The fused first-digit histograms live in the tile's staging memory, which is
 // dead once the last group is scored: 16-bit counts, two bins per word (a tile
-// holds at most 4096 keys), for as many heads per round as fit.
+// holds at most 8192 keys), for as many heads per round as fit.
 constexpr int kHistWords = kSelBins / 2;
 template <int G, int TB>
 constexpr int kHistHeads = (int)(sizeof(ScanSmem<G, TB>) / 4 / kHistWords) < G
