@@ -3,9 +3,11 @@
 Everything the oracle can afford is compared in full; the rest on samples the
 oracle computes one by one:
   * depths and union depths: every query head, bit-exact;
-  * records: full KV heads where affordable, else every channel of sampled
-    128-key blocks, bit-exact against the oracle's quantisation of those blocks;
-  * scores and top-k: sampled query heads over all n keys, scores within
+  * records: whole KV heads (all of them at 131072 keys), else every channel of
+    sampled 128-key blocks, bit-exact against the oracle's quantisation;
+  * scores and top-k over all n keys: every query head at 4096, 131072 and 1M
+    keys, one session's 32 heads (and one more) of the 8-session workload, one
+    KV head's 4 heads in each of six layers of the 36-layer step; scores within
     1e-4 * sum|q k_hat|, exact selection on the GPU's own scores, top-k equal
     to the oracle's up to boundary ties inside the tolerance;
   * host residencies (in place and staged): bit-identical to each other.
@@ -154,9 +156,16 @@ def run_and_check(F, wl, layer=0, sample_heads=(0, 1, 2, 3), host_modes=None, fu
         assert np.array_equal(results[res][1], first[1]), res
     sg, idx = first
     mark("scanned")
-    for h in sample_heads:
+    # the oracle's scores of the sampled heads, side by side on 8 threads
+    from concurrent.futures import ThreadPoolExecutor
+
+    def oracle_head(h):
         delta, kappa = codes[h // g]
-        s, a = O.scores(q_np[h], kappa, delta, rd[h])
+        return O.scores(q_np[h], kappa, delta, rd[h])
+
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        oracle_scores = list(ex.map(oracle_head, sample_heads))
+    for h, (s, a) in zip(sample_heads, oracle_scores):
         check_scores(sg[h], s, a, where=f"{wl.name} head {h}")
         check_topk(idx[h], s, a, wl.k, s_gpu=sg[h], where=f"{wl.name} head {h}")
     # every head (or those named): the selection is exact on the GPU's own scores
@@ -173,12 +182,12 @@ def test_w1_single_head_4k(F):
 @pytest.mark.parametrize("name", ["w2_hbm_131k_B46", "w2_hbm_131k_B68", "w2_hbm_131k_B92"])
 def test_w2_hbm_131k(F, name):
     wl = WL[name]
-    run_and_check(F, wl, sample_heads=(0, 5, 13, 31), full_record_heads=(0, 7))
+    run_and_check(F, wl, sample_heads=tuple(range(wl.h_q)), full_record_heads=tuple(range(wl.h_kv)))
 
 
 def test_w3_host_1m(F):
     wl = WL["w3_host_1m_B92"]
-    run_and_check(F, wl, sample_heads=(0, 3))
+    run_and_check(F, wl, sample_heads=tuple(range(wl.h_q)), full_record_heads=(0, 7))
 
 
 W4 = WL["w4_host_1m_36layers"]
@@ -211,11 +220,13 @@ def test_w4_every_layer_depths(F):
 def test_w4_decode_layer_full_size(F, layer):
     """Six layers of the 36-layer step at full size (1M keys, pinned host records),
     budgets from the smallest to the largest: records, depths and selection as in
-    the other workloads, oracle scores and top-k of one query head per layer (a
-    different head in each)."""
-    head = (5 * layer + 3) % W4.h_q
-    run_and_check(F, W4, layer=layer, sample_heads=(head,), host_modes=[F.HOST_DIRECT], full_record_heads=(),
-                  select_heads=sorted({head, (head + 8) % W4.h_q, (head + 16) % W4.h_q, (head + 24) % W4.h_q}))
+    the other workloads, oracle scores and top-k of the 4 query heads of one KV
+    head per layer (a different KV head in each), exact selection on the GPU's
+    own scores for every head."""
+    v = (5 * layer + 3) % W4.h_kv
+    heads = tuple(range(v * W4.g, (v + 1) * W4.g))
+    run_and_check(F, W4, layer=layer, sample_heads=heads, host_modes=[F.HOST_DIRECT], full_record_heads=(v,),
+                  select_heads=None)
 
 
 def test_w4_decode_step_loop(F):
@@ -270,5 +281,6 @@ def test_w4_decode_step_loop(F):
                                   "w5_sessions_262k_fixed68"])
 def test_w5_sessions(F, name):
     wl = WL[name]
-    # sessions 0 and 7 (virtual KV heads 0 and 56): query heads 0 and 224
-    run_and_check(F, wl, sample_heads=(0, 224), full_record_heads=(0,))
+    # every query head of session 0 (virtual KV heads 0-7) and query head 224
+    # of session 7 (virtual KV head 56)
+    run_and_check(F, wl, sample_heads=tuple(range(wl.h_q)) + (224,), full_record_heads=(0,))
