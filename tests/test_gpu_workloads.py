@@ -6,10 +6,11 @@ oracle computes one by one:
   * records: whole KV heads (all of them at 131072 keys), else every channel of
     sampled 128-key blocks, bit-exact against the oracle's quantisation;
   * scores and top-k over all n keys: every query head at 4096, 131072 and 1M
-    keys, one session's 32 heads (and one more) of the 8-session workload, one
-    KV head's 4 heads in each of six layers of the 36-layer step; scores within
-    1e-4 * sum|q k_hat|, exact selection on the GPU's own scores, top-k equal
-    to the oracle's up to boundary ties inside the tolerance;
+    keys and of all 8 sessions of the 8-session workload (one session's 32 and
+    one more in its fixed-depth modes), one KV head's 4 heads in each of six
+    layers of the 36-layer step; scores within 1e-4 * sum|q k_hat|, exact
+    selection on the GPU's own scores, top-k equal to the oracle's up to
+    boundary ties inside the tolerance;
   * host residencies (in place and staged): bit-identical to each other.
 """
 
@@ -281,6 +282,11 @@ def test_w4_decode_step_loop(F):
                                   "w5_sessions_262k_fixed68"])
 def test_w5_sessions(F, name):
     wl = WL[name]
-    # every query head of session 0 (virtual KV heads 0-7) and query head 224
-    # of session 7 (virtual KV head 56)
-    run_and_check(F, wl, sample_heads=tuple(range(wl.h_q)) + (224,), full_record_heads=(0,))
+    if wl.mode == "waterfill":
+        # the method: every query head of all 8 sessions
+        heads = tuple(range(wl.sessions * wl.h_q))
+    else:
+        # the fixed-depth comparison modes: every query head of session 0
+        # (virtual KV heads 0-7) and query head 224 of session 7 (virtual KV head 56)
+        heads = tuple(range(wl.h_q)) + (224,)
+    run_and_check(F, wl, sample_heads=heads, full_record_heads=(0,))
