@@ -290,3 +290,55 @@ def test_w5_sessions(F, name):
         # (virtual KV heads 0-7) and query head 224 of session 7 (virtual KV head 56)
         heads = tuple(range(wl.h_q)) + (224,)
     run_and_check(F, wl, sample_heads=heads, full_record_heads=(0,))
+
+
+@pytest.mark.parametrize("name", ["w2_hbm_131k_B92", "w3_host_1m_B92"])
+def test_attention_at_full_size(F, name):
+    """attend_topk at the benchmark's shapes: the method's own top-2048 of each of
+    the 32 query heads (scan_topk over the full records), attention over those
+    rows of the workload's bf16 K/V caches (HBM at 131072 keys, pinned host
+    memory at 1M keys), every head against the oracle's attention within the
+    order-independent fp32 bound."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from oracle import attention_oracle as A
+    from synthetic import to_bf16_bits, values
+    from tests.tolerances import attention_tolerance
+    wl = WL[name]
+    host = wl.residency == "host"
+    print(f"attention at full size: {wl.name}", flush=True)
+    k_np, q_np, s2_np = layer_inputs(wl, 0)
+    hk, n, d = k_np.shape
+    rec = pack_layer(F, k_np, host)
+    q = dev(q_np)
+    dep, uni = F.allocate(q, dev(s2_np), wl.budgets[0])
+    idx = F.scan_topk(rec, q, dep, uni, n, wl.k, residency=F.HOST_DIRECT if host else F.HBM)
+    kc = to_bf16_bits(k_np)
+    del k_np
+    vc = np.stack([to_bf16_bits(values(wl.key, 0, 0, v, n, d)) for v in range(hk)])
+
+    def cache(a):
+        t = torch.from_numpy(a.view(np.int16))
+        if not host:
+            return t.to("cuda:0")
+        p = torch.empty(t.shape, dtype=torch.int16, pin_memory=True)
+        p.copy_(t)
+        return p
+
+    scale = float(1 / np.sqrt(d))
+    out, lse = F.attend(cache(kc), cache(vc), q, idx, scale)
+    torch.cuda.synchronize()
+    out, lse, idx = out.cpu().numpy(), lse.cpu().numpy(), idx.cpu().numpy()
+
+    def one(h):
+        v = h // wl.g
+        o, l, _, _ = A.sparse_attention(q_np[h], kc[v], vc[v], idx[h], scale)
+        tau_o, tau_l = attention_tolerance(q_np[h], kc[v], vc[v], idx[h], scale)
+        return o, l, tau_o, tau_l
+
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        ref = list(ex.map(one, range(wl.h_q)))
+    for h, (o, l, tau_o, tau_l) in enumerate(ref):
+        err = np.abs(out[h].astype(np.float64) - o)
+        assert np.all(err <= tau_o), f"{wl.name} head {h}: worst excess {float(np.max(err - tau_o)):.3e}"
+        assert abs(float(lse[h]) - l) <= tau_l, f"{wl.name} head {h}: lse {lse[h]} vs {l}"
