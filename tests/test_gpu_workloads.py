@@ -11,7 +11,9 @@ oracle computes one by one:
     layers of the 36-layer step; scores within 1e-4 * sum|q k_hat|, exact
     selection on the GPU's own scores, top-k equal to the oracle's up to
     boundary ties inside the tolerance;
-  * host residencies (in place and staged): bit-identical to each other.
+  * host residencies (in place and staged): bit-identical to each other, and
+    at 1M keys to the same records scanned from HBM (the HBM scan's long-row
+    case: eight generations of tiles per CU).
 """
 
 import time
@@ -117,7 +119,7 @@ def check_records(rec_np, k_np, codes, blocks_per_head=6, seed=0):
 
 
 def run_and_check(F, wl, layer=0, sample_heads=(0, 1, 2, 3), host_modes=None, full_record_heads=(0,),
-                  select_heads=None):
+                  select_heads=None, hbm_too=False):
     budget = wl.budgets[layer]
     mode = F.WATERFILL if wl.mode == "waterfill" else F.TOPQ
     t0 = time.perf_counter()
@@ -151,6 +153,14 @@ def run_and_check(F, wl, layer=0, sample_heads=(0, 1, 2, 3), host_modes=None, fu
         idx = F.scan_topk(rec, q, dep, uni, n, wl.k, residency=res)
         torch.cuda.synchronize()
         results[res] = (sg.cpu().numpy(), idx.cpu().numpy())
+    if host and hbm_too:   # the same records copied to HBM
+        rec_dev = rec.to("cuda:0")
+        sg = F.scan_scores(rec_dev, q, dep, uni, n, residency=F.HBM)
+        idx = F.scan_topk(rec_dev, q, dep, uni, n, wl.k, residency=F.HBM)
+        torch.cuda.synchronize()
+        results[F.HBM] = (sg.cpu().numpy(), idx.cpu().numpy())
+        del rec_dev, sg, idx
+        residencies = residencies + [F.HBM]
     first = results[residencies[0]]
     for res in residencies[1:]:
         assert np.array_equal(results[res][0].view(np.uint32), first[0].view(np.uint32)), res
@@ -188,7 +198,7 @@ def test_w2_hbm_131k(F, name):
 
 def test_w3_host_1m(F):
     wl = WL["w3_host_1m_B92"]
-    run_and_check(F, wl, sample_heads=tuple(range(wl.h_q)), full_record_heads=(0, 7))
+    run_and_check(F, wl, sample_heads=tuple(range(wl.h_q)), full_record_heads=(0, 7), hbm_too=True)
 
 
 W4 = WL["w4_host_1m_36layers"]
