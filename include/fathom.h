@@ -22,8 +22,9 @@
  *     asynchronous on `stream` (a hipStream_t; NULL = the null stream) and
  *     returns after validating its arguments and enqueueing work.
  *   - The caller owns every buffer.  No call allocates device or host memory
- *     and none keeps state between calls.  There is no context object to
- *     create or destroy: the library owns no streams, events or memory, every
+ *     and none keeps state between calls (scan_topk_noalloc aside, whose fixed
+ *     scratch array lives in the library).  There is no context object to
+ *     create or destroy: the library owns no streams or events, every
  *     call enqueues on the caller's stream only (the host-staged residency too:
  *     its copies and scans are kernels on that stream), and the device is the
  *     one current on the calling thread.
