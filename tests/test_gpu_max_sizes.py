@@ -10,7 +10,9 @@ checks, copied back).  At these sizes the oracle checks samples:
     keys, within 1e-4 * sum|q k_hat|;
   * selection, on the GPU's own scores of the whole row: k strictly ascending
     in-range indices whose returned scores are the row's, every key above the
-    k-th score selected, and among the keys equal to it the lowest indices.
+    k-th score selected, and among the keys equal to it the lowest indices;
+  * the longest row read in place from pinned host memory: scores and
+    selection bit-identical to the HBM scan's.
 """
 
 import numpy as np
@@ -23,9 +25,9 @@ from tests.parity import check_scores, oracle_depths
 pytestmark = pytest.mark.gpu
 
 CASES = {
-    # (h_kv, g, n, d, budget, k)
-    "longest_row": (1, 1, (1 << 30) - 77, 2, 6, 2048),
-    "most_key_heads": (8, 1, 1 << 30, 1, 3, 2048),
+    # (h_kv, g, n, d, budget, k, host copy too)
+    "longest_row": (1, 1, (1 << 30) - 77, 2, 6, 2048, True),
+    "most_key_heads": (8, 1, 1 << 30, 1, 3, 2048, False),
 }
 
 
@@ -82,7 +84,7 @@ def check_block_records(rec_v, b, kb, layout):
 
 @pytest.mark.parametrize("case", list(CASES))
 def test_size_limits(F, case):
-    h_kv, g, n, d, budget, k = CASES[case]
+    h_kv, g, n, d, budget, k, host_too = CASES[case]
     h_q = h_kv * g
     print(f"max-size case {case}: h_kv={h_kv} g={g} n={n} d={d} B={budget} k={k}", flush=True)
     rng = np.random.default_rng(4242 + h_kv)
@@ -121,6 +123,16 @@ def test_size_limits(F, case):
     idx, val = F.scan_topk(rec, q, dep, uni, n, k, want_scores=True)
     torch.cuda.synchronize()
     print("  scanned and selected", flush=True)
+    if host_too:
+        pinned = torch.empty(rec.shape, dtype=torch.uint8, pin_memory=True)
+        pinned.copy_(rec)
+        s_host = F.scan_scores(pinned, q, dep, uni, n, residency=F.HOST_DIRECT)
+        idx_host = F.scan_topk(pinned, q, dep, uni, n, k, residency=F.HOST_DIRECT)
+        torch.cuda.synchronize()
+        assert torch.equal(s_host.view(torch.int32), scores.view(torch.int32)), "host scores differ from HBM"
+        assert torch.equal(idx_host, idx), "host selection differs from HBM"
+        del pinned, s_host, idx_host
+        print("  pinned host records: bit-identical", flush=True)
 
     for h in range(h_q):
         v = h // g
