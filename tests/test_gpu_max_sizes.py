@@ -1,5 +1,6 @@
 """The size limits the C ABI accepts, run on the GPU: 2^30 keys in one row
-(with a ragged tail) and 2^33 (KV head, key) pairs in one call.
+(with a ragged tail), 2^33 (KV head, key) pairs in one call, and 65535 query
+heads in one call.
 
 Keys come from a seeded device generator (the oracle gets the exact values it
 checks, copied back).  At these sizes the oracle checks samples:
@@ -159,3 +160,54 @@ def test_size_limits(F, case):
         so, ao = oracle_block_scores(q_np[h], rd[h], kb[valid], cnt)
         check_scores(sb[valid], so, ao, where=f"{case} head {h} ({len(blocks)} blocks)")
     print("  checked", flush=True)
+
+
+def test_most_query_heads(F):
+    """65535 query heads (the most one call takes: one grid row per head in the
+    allocation and the attention), as 65535 KV heads of 200 keys: every head's
+    depths bit-exact, every head's selection exact on the GPU's own scores,
+    and the oracle's scores and attention on heads spread over the range."""
+    from oracle import attention_oracle as A
+    from synthetic import to_bf16_bits
+    from tests.parity import dev, gpu_pack
+    from tests.tolerances import attention_tolerance
+    h_kv, n, d, budget, k = 65535, 200, 8, 12, 5
+    print(f"most query heads: h_kv={h_kv} g=1 n={n} d={d} B={budget} k={k}", flush=True)
+    rng = np.random.default_rng(65535)
+    sigma = np.exp(rng.standard_normal((h_kv, 1, d))).astype(np.float32)
+    kk = (rng.standard_normal((h_kv, n, d), dtype=np.float32) * sigma).astype(np.float32)
+    q_np = rng.standard_normal((h_kv, d), dtype=np.float32)
+    s2_np = (sigma[:, 0] * sigma[:, 0]).astype(np.float32)
+    rec, st = gpu_pack(kk)
+    assert st == 0
+    q = dev(q_np)
+    dep, uni = F.allocate(q, dev(s2_np), budget)
+    rd, ru = oracle_depths(q_np, s2_np, budget)
+    assert np.array_equal(dep.cpu().numpy(), rd) and np.array_equal(uni.cpu().numpy(), ru)
+    scores = F.scan_scores(rec, q, dep, uni, n)
+    idx = F.scan_topk(rec, q, dep, uni, n, k)
+    torch.cuda.synchronize()
+    sg, ig = scores.cpu().numpy(), idx.cpu().numpy()
+    # the selection of every head: the k largest, lowest index first among
+    # equal scores (a stable sort of the negated scores), in ascending order
+    want = np.sort(np.argsort(-sg.astype(np.float64), axis=1, kind="stable")[:, :k], axis=1)
+    assert np.array_equal(ig, want), f"{int(np.sum(np.any(ig != want, axis=1)))} heads select differently"
+    heads = sorted({0, 1, h_kv - 1, *rng.choice(h_kv, size=9, replace=False).tolist()})
+    for h in heads:
+        delta, kappa, recs = O.pack_head(kk[h])
+        assert np.array_equal(rec[h].cpu().numpy(), recs), f"records of KV head {h}"
+        so, ao = O.scores(q_np[h], kappa, delta, rd[h])
+        check_scores(sg[h], so, ao, where=f"head {h}")
+    print("  scan checked", flush=True)
+    kc = to_bf16_bits(kk)
+    vc = to_bf16_bits(rng.standard_normal((h_kv, n, d), dtype=np.float32))
+    scale = float(1 / np.sqrt(d))
+    out, lse = F.attend(dev(kc.view(np.int16)), dev(vc.view(np.int16)), q, idx, scale)
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    for h in heads:
+        o, l, _, _ = A.sparse_attention(q_np[h], kc[h], vc[h], ig[h], scale)
+        tau_o, tau_l = attention_tolerance(q_np[h], kc[h], vc[h], ig[h], scale)
+        assert np.all(np.abs(out[h].astype(np.float64) - o) <= tau_o), f"attention of head {h}"
+        assert abs(float(lse[h]) - l) <= tau_l, f"lse of head {h}"
+    print("  attention checked", flush=True)
