@@ -264,6 +264,21 @@ def test_budget_zero_selects_lowest_indices(F):
     assert np.array_equal(idx, np.tile(np.arange(100), (4, 1)))
 
 
+def test_empty_rows_and_selections(F):
+    """n = 0 keys and k = 0 selections succeed and write nothing."""
+    case = (1, 2, 700, 16, 20)
+    *_, rec, dq, dep, uni, sg = run_case(F, case)
+    out = torch.full((2, 64), 7.0, device="cuda:0")
+    assert F.scan_scores(rec, dq, dep, uni, 0, out=out).shape == (2, 0)
+    idx = torch.full((2, 8), -3, dtype=torch.int32, device="cuda:0")
+    for n in (700, 0):
+        F.scan_topk(rec, dq, dep, uni, n, 0, idx=idx)
+        F.scan_topk(rec.cpu().pin_memory(), dq, dep, uni, n, 0, idx=idx)
+        F.scan_topk_noalloc(rec, dq, dep, uni, n, 0, idx=idx)
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0) and torch.all(idx == -3)
+
+
 def test_budget_zero_large_n_takes_row_fallback(F):
     """All scores equal (B = 0): every key is a candidate, more than the LDS sort
     holds, so selection runs the exact in-order fallback; lowest indices win."""
