@@ -23,14 +23,15 @@
 // two such groups of 4 keys, 4 bits apart in the same word.
 //  1. The union depths of the KV head list the channels to read; every query
 //     head of the group is scored from the one read of the longest prefix.
-//  2. Staging, channel group by channel group (about 64 channel-planes): the
-//     tile's slice of each channel's record head (its units' fp16 scales and
-//     plane-0 bits) and of planes 1..t-1 are loaded with 16-byte loads into
-//     registers -- all issued before any LDS write, and those of the next group
-//     while the current group is computed -- then stored to LDS, the most
-//     significant plane complemented.  The same code reads HBM, an HBM staging
-//     ring, or pinned host memory over the host link; the tile size sets the
-//     contiguous run per channel-plane (16 B per block).
+//  2. Staging, channel group by channel group (64 channel-planes, 32 in the
+//     8192-key host tiles): the tile's slice of each channel's record head
+//     (its units' fp16 scales and plane-0 bits) and of planes 1..t-1 are
+//     loaded with 16-byte loads into registers -- all issued before any LDS
+//     write, and those of the next group while the current group is computed
+//     -- then stored to LDS, the most significant plane complemented.  The
+//     same code reads HBM, an HBM staging ring, or pinned host memory over the
+//     host link; the tile size sets the contiguous run per channel-plane (16 B
+//     per block).
 //  3. Per (channel, block) the coefficients a = [q_h Delta / 16] are formed once
 //     in LDS.  Per channel, each lane reads its word of each plane row and
 //     builds each group of 4 keys' prefixes side by side, one per byte of a
@@ -122,7 +123,6 @@ struct ScanArgs {
 // Entry word: one G-bit mask per depth t = 1..4, bit (t - 1) G + h set iff head h
 // reads exactly t planes of the channel (at most 64 bits for G <= 16).  The
 // union depth is the entry's chunk count.
-
 
 // The fused first-digit histograms live in the tile's staging memory, which is
 // dead once the last group is scored: 16-bit counts, two bins per word (a tile
