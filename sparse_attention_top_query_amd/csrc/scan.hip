@@ -23,15 +23,15 @@
 // two such groups of 4 keys, 4 bits apart in the same word.
 //  1. The union depths of the KV head list the channels to read; every query
 //     head of the group is scored from the one read of the longest prefix.
-//  2. Staging, channel group by channel group (64 channel-planes, 32 in the
-//     8192-key host tiles): the tile's slice of each channel's record head
-//     (its units' fp16 scales and plane-0 bits) and of planes 1..t-1 are
-//     loaded with 16-byte loads into registers -- all issued before any LDS
-//     write, and those of the next group while the current group is computed
-//     -- then stored to LDS, the most significant plane complemented.  The
-//     same code reads HBM, an HBM staging ring, or pinned host memory over the
-//     host link; the tile size sets the contiguous run per channel-plane (16 B
-//     per block).
+//  2. Staging, channel group by channel group (64 channel-planes from device
+//     memory, 4 from pinned host memory): the tile's slice of each channel's
+//     record head (its units' fp16 scales and plane-0 bits) and of planes
+//     1..t-1 are loaded with 16-byte loads into registers -- all issued before
+//     any LDS write, and those of the next group while the current group is
+//     computed -- then stored to LDS, the most significant plane complemented.
+//     The same code reads HBM, an HBM staging ring, or pinned host memory over
+//     the host link; the tile size sets the contiguous run per channel-plane
+//     (16 B per block).
 //  3. Per (channel, block) the coefficients a = [q_h Delta / 16] are formed once
 //     in LDS.  Per channel, each lane reads its word of each plane row and
 //     builds each group of 4 keys' prefixes side by side, one per byte of a
@@ -52,11 +52,18 @@ namespace fathom {
 namespace {
 
 constexpr int kSlackChunks = kPlanes - 1;      // an entry starting in a group ends in it
-// Channel-planes per staging group (+3 slack): 64, or 32 for the 8192-key host
-// tiles, whose 1024 threads each hold one group's pieces in registers.
+constexpr int kTileDevice = 8;                 // blocks per tile from device memory: 1024 keys, 256 threads
+// Channel-planes per staging group (+3 slack).  64 for the 1024-key tiles that
+// read device memory, where each group boundary costs the arithmetic two
+// barriers.  4, the least that keeps every group non-empty (an entry's first
+// chunk is at most 4 past the previous one's), for the longer tiles that read
+// pinned host memory: the link then sees each workgroup's reads as a stream of
+// small batches from a few channels at a time, which it serves at up to 99% of
+// the copy engine's rate, against 96% with 32-plane batches (the arithmetic is
+// idle enough to take the extra group boundaries).
 template <int TB>
 struct Stage {
-  static constexpr int group = TB >= 64 ? 32 : 64;
+  static constexpr int group = TB > kTileDevice ? 4 : 64;
   static constexpr int chunks = group + kSlackChunks;
   static constexpr int entries = chunks;        // entries have >= 1 chunk
 };
@@ -531,7 +538,6 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t 
 // runs, 8192-key tiles at 8 keys per lane, scan 1% faster than 512-byte ones).
 // Paged host records keep 4096-key tiles so that pages of any multiple of 4096
 // keys hold whole tiles.
-constexpr int kTileDevice = 8;    // 1024 keys, 256 threads
 template <int G>
 struct HostTile {
   // 8 keys per lane needs twice the accumulators; the coefficients' LDS bounds
