@@ -579,9 +579,10 @@ __global__ __launch_bounds__((Cfg<G, TB, KW>::threads)) void scan_kernel(ScanArg
 
 // ---------------------------------------------------------------------------
 // Host-resident records, staged: the scan's input is first gathered from
-// pinned host memory into HBM with long contiguous reads (each channel's
-// prefix run of the union depth, split into 32 KB pieces), which keeps the
-// host link at its streaming rate.  The HBM side is a ring of two KV heads'
+// pinned host memory into HBM with contiguous reads (each channel's prefix run
+// of the union depth, split into 4 KB pieces, one per copy workgroup: the link
+// serves many small batches better than fewer large ones, 54.5 GB/s against
+// 52.3 with 32 KB pieces).  The HBM side is a ring of two KV heads'
 // records: launch i copies KV head i into slot i % 2 while the same launch's
 // other workgroups scan head i - 1 from slot (i - 1) % 2, so the copy of one
 // head overlaps the compute of the previous one; kernel boundaries order each
@@ -589,7 +590,7 @@ __global__ __launch_bounds__((Cfg<G, TB, KW>::threads)) void scan_kernel(ScanArg
 // copy that reuses its slot.
 // ---------------------------------------------------------------------------
 
-constexpr int64_t kCopyPiece = 32768;   // bytes per copy workgroup
+constexpr int64_t kCopyPiece = 4096;    // bytes per copy workgroup: one 16-byte piece per thread
 
 inline int64_t copy_pieces_per_head(const Layout& L, int d) {
   return (int64_t)d * ((L.R + kCopyPiece - 1) / kCopyPiece);
@@ -602,6 +603,7 @@ __device__ __forceinline__ void copy_piece(const uint8_t* __restrict__ src, uint
                                            ScanSmem<G, TB>& sm) {
   constexpr int NT = Cfg<G, TB>::threads;
   constexpr int PER = (int)(kCopyPiece / 16 / NT);
+  static_assert(PER >= 1 && (int64_t)PER * 16 * NT == kCopyPiece, "whole 16-byte pieces per thread");
   const int tid = threadIdx.x;
   const int wv = tid >> 6;
   const int lane = tid & 63;
