@@ -12,8 +12,8 @@ checks, copied back).  At these sizes the oracle checks samples:
   * selection, on the GPU's own scores of the whole row: k strictly ascending
     in-range indices whose returned scores are the row's, every key above the
     k-th score selected, and among the keys equal to it the lowest indices;
-  * the longest row read in place from pinned host memory: scores and
-    selection bit-identical to the HBM scan's.
+  * the longest row read from pinned host memory, in place and staged
+    through HBM: scores and selection bit-identical to the HBM scan's.
 """
 
 import numpy as np
@@ -127,13 +127,15 @@ def test_size_limits(F, case):
     if host_too:
         pinned = torch.empty(rec.shape, dtype=torch.uint8, pin_memory=True)
         pinned.copy_(rec)
-        s_host = F.scan_scores(pinned, q, dep, uni, n, residency=F.HOST_DIRECT)
-        idx_host = F.scan_topk(pinned, q, dep, uni, n, k, residency=F.HOST_DIRECT)
-        torch.cuda.synchronize()
-        assert torch.equal(s_host.view(torch.int32), scores.view(torch.int32)), "host scores differ from HBM"
-        assert torch.equal(idx_host, idx), "host selection differs from HBM"
-        del pinned, s_host, idx_host
-        print("  pinned host records: bit-identical", flush=True)
+        for res in (F.HOST_DIRECT, F.HOST_STAGED):
+            s_host = F.scan_scores(pinned, q, dep, uni, n, residency=res)
+            idx_host = F.scan_topk(pinned, q, dep, uni, n, k, residency=res)
+            torch.cuda.synchronize()
+            assert torch.equal(s_host.view(torch.int32), scores.view(torch.int32)), f"residency {res}: scores"
+            assert torch.equal(idx_host, idx), f"residency {res}: selection"
+            del s_host, idx_host
+        del pinned
+        print("  pinned host records, in place and staged: bit-identical", flush=True)
 
     for h in range(h_q):
         v = h // g
