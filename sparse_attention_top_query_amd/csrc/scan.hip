@@ -53,17 +53,27 @@ namespace {
 
 constexpr int kSlackChunks = kPlanes - 1;      // an entry starting in a group ends in it
 constexpr int kTileDevice = 8;                 // blocks per tile from device memory: 1024 keys, 256 threads
-// Channel-planes per staging group (+3 slack).  64 for the 1024-key tiles that
-// read device memory, where each group boundary costs the arithmetic two
-// barriers.  4, the least that keeps every group non-empty (an entry's first
-// chunk is at most 4 past the previous one's), for the longer tiles that read
-// pinned host memory: the link then sees each workgroup's reads as a stream of
-// small batches from a few channels at a time, which it serves at up to 99% of
-// the copy engine's rate, against 96% with 32-plane batches (the arithmetic is
-// idle enough to take the extra group boundaries).
+// Channel-planes per staging group (GS, +3 slack).  For the 1024-key tiles
+// that read device memory: 64 as a rule, since each group boundary costs the
+// arithmetic two barriers; 32 for rows of more than 8 tiles per CU in all when
+// 2 to 8 query heads share a KV head, where the smaller staging memory and
+// registers raise the workgroups a CU holds at once (for 4 heads 71 against 82
+// VGPRs, 7 workgroups instead of 5), so fewer generations of tiles start up in
+// turn (10-14% faster scans from 393216 keys up; with 1 or 16 heads the
+// occupancy does not change and 64 stays).  For the longer tiles that read
+// pinned host memory: 4, the least that keeps every group non-empty (an
+// entry's first chunk is at most 4 past the previous one's).  The link then
+// sees each workgroup's reads as a stream of small batches from a few channels
+// at a time, which it serves at up to 99% of the copy engine's rate, against
+// 96% with 32-plane batches (the arithmetic is idle enough to take the extra
+// group boundaries).
 template <int TB>
+constexpr int kStageGroup = TB > kTileDevice ? 4 : 64;
+constexpr int kDeviceRunGroup = 32;
+constexpr int64_t kDeviceRunTiles = 2048;     // 8 per CU
+template <int GS>
 struct Stage {
-  static constexpr int group = TB > kTileDevice ? 4 : 64;
+  static constexpr int group = GS;
   static constexpr int chunks = group + kSlackChunks;
   static constexpr int entries = chunks;        // entries have >= 1 chunk
 };
@@ -75,30 +85,30 @@ constexpr int kSub = kBlock / 32;              // 32-key words per block, keys p
 // the arithmetic must hide latency; two where the tile must be long (the
 // host-link scan: 8192-key tiles, 1-KB runs per channel-plane, still 1024
 // threads).
-template <int G, int TB, int KW = 1>
+template <int G, int TB, int KW = 1, int GS = kStageGroup<TB>>
 struct Cfg {
   static constexpr int keys = kSub * KW;              // keys per lane
   static constexpr int wave_blocks = 2 * KW;          // 128-key blocks per wavefront
   static constexpr int threads = 64 * TB / wave_blocks;
   static constexpr int units = TB / kUnitBlocks;      // 1024-key record units per tile
   static constexpr int slots = TB + units;            // 16-byte pieces per chunk slot
-  static constexpr int ppt = (Stage<TB>::chunks * slots + threads - 1) / threads;
+  static constexpr int ppt = (Stage<GS>::chunks * slots + threads - 1) / threads;
   static_assert(threads >= kMaxD && threads <= 1024, "one thread per channel in the list build");
   static_assert(TB % kUnitBlocks == 0, "tiles hold whole 1024-key units");
 };
 
-template <int G, int TB>
+template <int G, int TB, int GS = kStageGroup<TB>>
 struct ScanSmem {
-  uint4 planes[Stage<TB>::chunks + kPlanes - 1][TB];   // staged plane bits (plane 0 complemented); the last
+  uint4 planes[Stage<GS>::chunks + kPlanes - 1][TB];   // staged plane bits (plane 0 complemented); the last
                                                    // rows pad reads of a prefix's unread planes
-  uint4 scales[Stage<TB>::entries][TB / kUnitBlocks];  // staged fp16 scales per entry of the group
-  float coef[Stage<TB>::chunks][TB][G];            // a = [q_h Delta_b / 16] per block and head, in the
+  uint4 scales[Stage<GS>::entries][TB / kUnitBlocks];  // staged fp16 scales per entry of the group
+  float coef[Stage<GS>::chunks][TB][G];            // a = [q_h Delta_b / 16] per block and head, in the
                                                    // row of the entry's first chunk (for G = 4 a row has the
                                                    // planes' stride)
   float ent_q[kMaxD][G];                           // q_h / 16 of each list entry
   uint64_t ent_word[kMaxD + 1];                    // level masks: bit (t-1) G + h iff head h reads t planes
   uint16_t ent_base[kMaxD + 1];                    // first chunk of entry e (prefix sum)
-  uint16_t grp[kMaxChunks / Stage<TB>::group + 2];  // first entry of each staging group
+  uint16_t grp[kMaxChunks / Stage<GS>::group + 2];  // first entry of each staging group
   uint32_t chunk_meta[kMaxChunks];                 // entry | channel << 8 | plane << 16 of each chunk
   int wsum[2][16];
   int n_grp;
@@ -135,17 +145,17 @@ struct ScanArgs {
 // dead once the last group is scored: 16-bit counts, two bins per word (a tile
 // holds at most 8192 keys), for as many heads per round as fit.
 constexpr int kHistWords = kSelBins / 2;
-template <int G, int TB>
-constexpr int kHistHeads = (int)(sizeof(ScanSmem<G, TB>) / 4 / kHistWords) < G
-                               ? (int)(sizeof(ScanSmem<G, TB>) / 4 / kHistWords) : G;
+template <int G, int TB, int GS = kStageGroup<TB>>
+constexpr int kHistHeads = (int)(sizeof(ScanSmem<G, TB, GS>) / 4 / kHistWords) < G
+                               ? (int)(sizeof(ScanSmem<G, TB, GS>) / 4 / kHistWords) : G;
 
 // Scores of tile `tile` (TB blocks) of KV head g for all its query heads, left
 // in acc: acc[s][h] is the score for query head g G + h of the key
 // tile_key(s) of the tile.
-template <int G, int TB, int KW>
-__device__ __forceinline__ void scan_tile_acc(const ScanArgs& a, int64_t g, int64_t tile, ScanSmem<G, TB>& sm,
+template <int G, int TB, int KW, int GS>
+__device__ __forceinline__ void scan_tile_acc(const ScanArgs& a, int64_t g, int64_t tile, ScanSmem<G, TB, GS>& sm,
                                               float (&acc)[Cfg<G, TB, KW>::keys][G]) {
-  using C = Cfg<G, TB, KW>;
+  using C = Cfg<G, TB, KW, GS>;
   constexpr int SLOTS = C::slots;
   constexpr int NT = C::threads;
   constexpr int PPT = C::ppt;
@@ -211,8 +221,8 @@ __device__ __forceinline__ void scan_tile_acc(const ScanArgs& a, int64_t g, int6
         sm.ent_base[n_ent] = (uint16_t)(base + u);
         // an entry joins the group holding its first chunk; first chunks are at
         // most 4 apart, so every group up to this one is non-empty
-        sm.n_grp = base / Stage<TB>::group + 1;
-        sm.grp[base / Stage<TB>::group + 1] = (uint16_t)n_ent;
+        sm.n_grp = base / Stage<GS>::group + 1;
+        sm.grp[base / Stage<GS>::group + 1] = (uint16_t)n_ent;
       }
 #pragma unroll
       for (int p = 0; p < kPlanes; ++p)
@@ -221,8 +231,8 @@ __device__ __forceinline__ void scan_tile_acc(const ScanArgs& a, int64_t g, int6
     if (tid == 0 && n_ent == 0) sm.n_grp = 0;
     __syncthreads();
     if (act) {
-      const int gi = base / Stage<TB>::group;
-      if (e == 0 || sm.ent_base[e - 1] / Stage<TB>::group != gi) sm.grp[gi] = (uint16_t)e;
+      const int gi = base / Stage<GS>::group;
+      if (e == 0 || sm.ent_base[e - 1] / Stage<GS>::group != gi) sm.grp[gi] = (uint16_t)e;
     }
     __syncthreads();
   }
@@ -482,11 +492,11 @@ __device__ __forceinline__ void store_tile(const ScanArgs& a, int64_t g, int64_t
 // digit: an LDS histogram per round of heads (16-bit counts in the staging
 // memory, dead once the tile is scored), then one global atomic per non-empty
 // bin.
-template <int G, int TB, int KW>
+template <int G, int TB, int KW, int GS>
 __device__ __forceinline__ void hist_tile(const ScanArgs& a, uint32_t* hist, int64_t g, int64_t tile,
-                                          const float (&acc)[Cfg<G, TB, KW>::keys][G], ScanSmem<G, TB>& sm) {
+                                          const float (&acc)[Cfg<G, TB, KW>::keys][G], ScanSmem<G, TB, GS>& sm) {
   constexpr int NT = Cfg<G, TB, KW>::threads;
-  constexpr int HR = kHistHeads<G, TB>;
+  constexpr int HR = kHistHeads<G, TB, GS>;
   static_assert(HR >= 1 && TB * kBlock < 65536, "16-bit counts of at least one head must fit");
   const int tid = threadIdx.x;
   const int64_t key0 = tile * TB * kBlock;
@@ -524,12 +534,12 @@ __device__ __forceinline__ void hist_tile(const ScanArgs& a, uint32_t* hist, int
 // Scores of tile `tile` (TB blocks) of KV head g, all its query heads.  With
 // FUSE, the tile's scores are also counted into a.hist by their first
 // selection digit.
-template <int G, int TB, int KW = 1, bool FUSE = false>
-__device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t tile, ScanSmem<G, TB>& sm) {
+template <int G, int TB, int KW = 1, bool FUSE = false, int GS = kStageGroup<TB>>
+__device__ __forceinline__ void scan_tile(const ScanArgs& a, int64_t g, int64_t tile, ScanSmem<G, TB, GS>& sm) {
   float acc[Cfg<G, TB, KW>::keys][G];
-  scan_tile_acc<G, TB, KW>(a, g, tile, sm, acc);
+  scan_tile_acc<G, TB, KW, GS>(a, g, tile, sm, acc);
   store_tile<G, TB, KW>(a, g, tile, acc);
-  if constexpr (FUSE) hist_tile<G, TB, KW>(a, a.hist, g, tile, acc, sm);
+  if constexpr (FUSE) hist_tile<G, TB, KW, GS>(a, a.hist, g, tile, acc, sm);
 }
 
 // Tile size per residency: device memory likes many small tiles (occupancy);
@@ -558,9 +568,9 @@ struct PagedHostTile {
 // every XCD gets the same mix of heads (whose union depths, and so work, differ).
 constexpr int kXcds = 8;
 
-template <int G, int TB, int KW, bool FUSE>
+template <int G, int TB, int KW, bool FUSE, int GS = kStageGroup<TB>>
 __global__ __launch_bounds__((Cfg<G, TB, KW>::threads)) void scan_kernel(ScanArgs a, int64_t tiles, int64_t total) {
-  __shared__ ScanSmem<G, TB> sm;
+  __shared__ ScanSmem<G, TB, GS> sm;
   // 32-bit index arithmetic (tiles and grids stay far below 2^31): a 64-bit
   // division by a run-time value is a long scalar sequence at every start
   const uint32_t w = blockIdx.x;
@@ -574,7 +584,7 @@ __global__ __launch_bounds__((Cfg<G, TB, KW>::threads)) void scan_kernel(ScanArg
     const int64_t z1 = min((L + 1) * a.zero_slice, a.zero_words);
     for (int64_t i = L * a.zero_slice + threadIdx.x; i < z1; i += Cfg<G, TB, KW>::threads) a.zero[i] = 0u;
   }
-  scan_tile<G, TB, KW, FUSE>(a, g, tile, sm);
+  scan_tile<G, TB, KW, FUSE, GS>(a, g, tile, sm);
 }
 
 // ---------------------------------------------------------------------------
@@ -671,7 +681,7 @@ struct Paging {
   int64_t page_keys;
 };
 
-template <int G, int TB, int KW>
+template <int G, int TB, int KW, int GS = kStageGroup<TB>>
 hipError_t launch_g(const uint8_t* rec, const float* q, const uint8_t* depth, const uint8_t* uni,
                     int h_kv, const Layout& L, int d, float* scores, int64_t ld, uint32_t* zero,
                     int64_t zero_words, uint32_t* hist, const Paging& pg, hipStream_t s) {
@@ -692,10 +702,10 @@ hipError_t launch_g(const uint8_t* rec, const float* q, const uint8_t* depth, co
   const int64_t grid = kXcds * h_kv * ((tiles + kXcds - 1) / kXcds);
   a.zero_slice = (zero_words + total - 1) / total;
   if (hist) {
-    scan_kernel<G, TB, KW, true><<<(unsigned)grid, Cfg<G, TB, KW>::threads, 0, s>>>(a, tiles, total);
+    scan_kernel<G, TB, KW, true, GS><<<(unsigned)grid, Cfg<G, TB, KW>::threads, 0, s>>>(a, tiles, total);
     return hipGetLastError();
   }
-  scan_kernel<G, TB, KW, false><<<(unsigned)grid, Cfg<G, TB, KW>::threads, 0, s>>>(a, tiles, total);
+  scan_kernel<G, TB, KW, false, GS><<<(unsigned)grid, Cfg<G, TB, KW>::threads, 0, s>>>(a, tiles, total);
   return hipGetLastError();
 }
 
@@ -730,6 +740,13 @@ hipError_t launch_any(const uint8_t* rec, bool host, const float* q, const uint8
   if (host)
     return launch_g<G, HostTile<G>::TB, HostTile<G>::KW>(rec, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words,
                                                          hist, pg, s);
+  // long rows take the smaller staging groups (more workgroups resident at once)
+  if constexpr (G >= 2 && G <= 8) {
+    const int64_t tiles = (L.nb + kTileDevice - 1) / kTileDevice;
+    if (tiles * h_kv > kDeviceRunTiles)
+      return launch_g<G, kTileDevice, 1, kDeviceRunGroup>(rec, q, depth, uni, h_kv, L, d, scores, ld, zero,
+                                                           zero_words, hist, pg, s);
+  }
   return launch_g<G, kTileDevice, 1>(rec, q, depth, uni, h_kv, L, d, scores, ld, zero, zero_words, hist, pg, s);
 }
 

@@ -357,6 +357,28 @@ def test_staged_ring_of_many_heads(F):
     assert np.array_equal(sh.view(np.uint32), sg.view(np.uint32))
 
 
+@pytest.mark.parametrize("case", [(2, 2, 1_100_001, 32, 40), (1, 8, 2_200_000, 16, 24)])
+def test_long_hbm_rows_match_oracle_and_host(F, case):
+    """HBM rows of more than 2048 tiles in all (2 and 8 query heads per KV head,
+    where such rows stage 32 channel-planes per group instead of 64): scores
+    of the first and last query head within the tolerance of the oracle over
+    the whole row, selection exact, and scores and selection bit-identical to
+    the same records read in place from pinned host memory."""
+    h_kv, g, n, d, budget = case
+    k, q, s2, rec, dq, dep, uni, sg = run_case(F, case)
+    host = rec.cpu().pin_memory()
+    sh = F.scan_scores(host, dq, dep, uni, n, residency=F.HOST_DIRECT).cpu().numpy()
+    assert np.array_equal(sh.view(np.uint32), sg.view(np.uint32))
+    idx = F.scan_topk(rec, dq, dep, uni, n, 2048).cpu().numpy()
+    assert np.array_equal(F.scan_topk(host, dq, dep, uni, n, 2048).cpu().numpy(), idx)
+    rd, _ = oracle_depths(q, s2, budget)
+    for h in (0, h_kv * g - 1):
+        delta, kappa, _ = O.pack_head(k[h // g])
+        s, a = O.scores(q[h], kappa, delta, rd[h])
+        check_scores(sg[h], s, a, where=f"head {h}")
+        check_topk(idx[h], s, a, 2048, s_gpu=sg[h], where=f"head {h}")
+
+
 def test_topq_scan_parity(F):
     case = (2, 4, 4096, 128, 68)
     k, q, s2, rec, dq, dep, uni, sg = run_case(F, case, mode="topq")
