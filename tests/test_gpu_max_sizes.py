@@ -165,8 +165,8 @@ def test_size_limits(F, case):
 
 
 def test_most_query_heads(F):
-    """65535 query heads (the most one call takes: one grid row per head in the
-    allocation and the attention), as 65535 KV heads of 200 keys: every head's
+    """65535 query heads (the most one call takes; the attention launches one
+    grid row per query head), as 65535 KV heads of 200 keys: every head's
     depths bit-exact, every head's selection exact on the GPU's own scores,
     and the oracle's scores and attention on heads spread over the range."""
     from oracle import attention_oracle as A
