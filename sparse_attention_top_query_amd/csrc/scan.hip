@@ -73,6 +73,7 @@ constexpr int kDeviceRunGroup = 32;
 constexpr int64_t kDeviceRunTiles = 2048;     // 8 per CU
 template <int GS>
 struct Stage {
+  static_assert(GS >= kPlanes, "first chunks of consecutive entries are at most 4 apart: groups of >= 4 are never empty");
   static constexpr int group = GS;
   static constexpr int chunks = group + kSlackChunks;
   static constexpr int entries = chunks;        // entries have >= 1 chunk
