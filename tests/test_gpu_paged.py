@@ -61,6 +61,8 @@ PAGED_CASES = [  # (h_kv, g, n_sealed, n_tail, page_keys, d, budget, k)
     (1, 1, 4096, 0, 4096, 128, 64, 50),
     (2, 8, 12288 + 128, 5, 4096, 64, 40, 200),
     (1, 4, 20480, 127, 16384, 128, 68, 2048),
+    # more than 2048 tiles of 1024 keys in all: the long-row HBM staging
+    (2, 4, (1 << 20) + 4096, 33, 65536, 32, 40, 2048),
 ]
 
 
